@@ -1,0 +1,165 @@
+"""Workload shapes for the EAGLE draft-and-verify round.
+
+Pure data: dimensions, tree shapes, seeds.  Nothing here computes any part of
+the method.
+
+Sources (page titles as printed in the reference text):
+  * "transformer_math / tm_eagle_deep" -- section "The recurrence, written out"
+    (x = [f; emb(t)], fc [2d, d], one decoder layer, frozen LM head) and
+    section "EAGLE-2: expand and rerank" (top-k expansion, keep top-m by value).
+  * "Speculative Decoding Deep Dive III: EAGLE, DFlash" -- section "EAGLE-3"
+    (g = FC([l; m; h]), later steps feed back a + emb(t)).
+  * "EAGLE: Drafting in Feature Space" -- section "Drafting a Tree, Not a
+    Chain" (EAGLE-1 uses one fixed tree shape for every context).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional, Tuple
+
+# enum values shared with include/eagle.h (kept in sync by a host test)
+DTYPE_BF16, DTYPE_F32 = 0, 1
+ACT_SWIGLU, ACT_GELU = 0, 1
+NORM_RMS, NORM_LAYER = 0, 1
+MODE_EAGLE1, MODE_EAGLE3 = 1, 3
+TREE_CHAIN, TREE_STATIC, TREE_DYNAMIC = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class HeadCfg:
+    d: int                  # draft width (also the EAGLE-3 hidden size k)
+    vocab: int              # |V|
+    n_q: int                # query heads
+    n_kv: int               # key/value heads (GQA when n_kv < n_q)
+    head_dim: int
+    ffn: int                # MLP hidden width
+    act: int = ACT_SWIGLU
+    norm: int = NORM_RMS
+    dtype: int = DTYPE_BF16
+    eps: float = 1e-5
+    rope_theta: float = 500000.0   # 0 = no positional encoding
+    mode: int = MODE_EAGLE1        # EAGLE-1 fc([f; emb]) or EAGLE-3 FC([l; m; h])
+
+    @property
+    def q_dim(self) -> int:
+        return self.n_q * self.head_dim
+
+    @property
+    def kv_dim(self) -> int:
+        return self.n_kv * self.head_dim
+
+    @property
+    def group(self) -> int:
+        return self.n_q // self.n_kv
+
+
+@dataclass(frozen=True)
+class RoundCfg:
+    name: str
+    head: HeadCfg
+    B: int
+    n: Tuple[int, ...] = ()           # fixed per-request context lengths (len B) ...
+    n_range: Optional[Tuple[int, int]] = None   # ... or uniform integers in [lo, hi]
+    tree: int = TREE_CHAIN
+    gamma: int = 4                    # draft depth = number of draft steps
+    top_k: int = 1
+    top_m: int = 0                    # nodes kept by rerank (dynamic trees)
+    template: Tuple[int, ...] = ()    # static tree: parent of template node i+1
+    inv_temp: float = 1.0             # s in conf = softmax(s * logits)
+    seed_w: int = 0
+    seed_in: int = 0
+    seed_t: int = 0
+    note: str = ""
+
+    @property
+    def n_final(self) -> int:
+        """Non-root nodes of the final (verified) tree per request."""
+        if self.tree == TREE_CHAIN:
+            return self.gamma
+        if self.tree == TREE_STATIC:
+            return len(self.template)
+        return self.top_m
+
+    @property
+    def positions(self) -> int:
+        """Positions per request in the verify tree (root + n_final)."""
+        return self.n_final + 1
+
+
+# EAGLE-1 static tree used at the 8B shape: 25 non-root nodes, depth 4, max
+# fan-out (4, 3, 2, 1) per depth.  Entry i is the parent of node i+1 (node 0
+# is the root); siblings are listed in rank order (rank r = the r-th best
+# token of the parent's top-k).
+STATIC_TREE_25 = (0, 0, 0, 0,            # nodes 1-4   (depth 1)
+                  1, 1, 1, 2, 2, 2, 3, 3, 4,   # nodes 5-13  (depth 2)
+                  5, 5, 8, 8, 11, 11, 13, 13,  # nodes 14-21 (depth 3)
+                  14, 16, 18, 20)               # nodes 22-25 (depth 4)
+
+HEAD_TINY_F32 = HeadCfg(d=256, vocab=4096, n_q=4, n_kv=4, head_dim=64, ffn=1024,
+                        act=ACT_GELU, norm=NORM_LAYER, dtype=DTYPE_F32,
+                        rope_theta=0.0)
+HEAD_8B = HeadCfg(d=4096, vocab=128256, n_q=32, n_kv=8, head_dim=128, ffn=14336)
+HEAD_8B_E3 = replace(HEAD_8B, mode=MODE_EAGLE3)
+HEAD_70B = HeadCfg(d=8192, vocab=128256, n_q=64, n_kv=8, head_dim=128, ffn=28672)
+
+# Inverse temperature for the EAGLE-2 dynamic tree at the 8B shape.  The random
+# head's draft logits are rescaled so that the mean top-1 confidence of the
+# first draft step is close to 0.6 (calibrated by oracle/calibrate_inv_temp.py).
+C2_INV_TEMP = 1.0
+
+CONFIGS = {
+    "c0_tiny_chain": RoundCfg(
+        name="c0_tiny_chain", head=HEAD_TINY_F32, B=1, n=(64,), tree=TREE_CHAIN,
+        gamma=4, top_k=1, seed_w=1000, seed_in=2000, seed_t=3000,
+        note="tiny EAGLE-1 chain, fp32, B=1, n=64, gamma=4, greedy top-1"),
+    "c1_8b_static": RoundCfg(
+        name="c1_8b_static", head=HEAD_8B, B=1, n=(2048,), tree=TREE_STATIC,
+        gamma=4, top_k=4, template=STATIC_TREE_25, seed_w=1001, seed_in=2001,
+        seed_t=3001,
+        note="Llama-3-8B-shaped head, bf16, B=1, n=2048, static 25-node tree"),
+    "c2_8b_dynamic": RoundCfg(
+        name="c2_8b_dynamic", head=HEAD_8B, B=8, n=(4096,) * 8, tree=TREE_DYNAMIC,
+        gamma=6, top_k=10, top_m=60, inv_temp=C2_INV_TEMP, seed_w=1002,
+        seed_in=2002, seed_t=3002,
+        note="EAGLE-2 dynamic tree on the 8B head, B=8, n=4096, top-k 10, depth 6, top-m 60"),
+    "c3_8b_eagle3": RoundCfg(
+        name="c3_8b_eagle3", head=HEAD_8B_E3, B=32, n_range=(256, 1024),
+        tree=TREE_CHAIN, gamma=7, top_k=1, seed_w=1003, seed_in=2003, seed_t=3003,
+        note="EAGLE-3 fused-feature chain, B=32, packed n in [256,1024], gamma=7"),
+    "c4_70b_dynamic": RoundCfg(
+        name="c4_70b_dynamic", head=HEAD_70B, B=64, n=(8192,) * 64,
+        tree=TREE_DYNAMIC, gamma=6, top_k=8, top_m=60, seed_w=1004,
+        seed_in=2004, seed_t=3004,
+        note="70B-shaped head, B=64, n=8192, EAGLE-2 top-k 8, depth 6, top-m 60"),
+}
+
+# Small shapes for parity at sizes the oracle finishes in seconds.  They cover
+# every tree mode, both dtypes, GQA, RoPE, ragged vocab / MLP / context sizes
+# and an empty context.
+_HEAD_SMALL = HeadCfg(d=256, vocab=3001, n_q=4, n_kv=2, head_dim=128, ffn=704,
+                      rope_theta=10000.0)
+SMALL_CONFIGS = {
+    "c0r_tiny_chain_rope": replace(
+        CONFIGS["c0_tiny_chain"], name="c0r_tiny_chain_rope",
+        head=replace(HEAD_TINY_F32, rope_theta=10000.0), seed_w=1100,
+        seed_in=2100, seed_t=3100),
+    "s1_static": RoundCfg(
+        name="s1_static", head=_HEAD_SMALL, B=1, n=(77,), tree=TREE_STATIC,
+        gamma=4, top_k=4, template=STATIC_TREE_25, seed_w=1101, seed_in=2101,
+        seed_t=3101),
+    "s2_dynamic": RoundCfg(
+        name="s2_dynamic", head=_HEAD_SMALL, B=3, n=(130, 1, 64),
+        tree=TREE_DYNAMIC, gamma=4, top_k=4, top_m=12, inv_temp=4.0,
+        seed_w=1102, seed_in=2102, seed_t=3102),
+    "s3_eagle3": RoundCfg(
+        name="s3_eagle3", head=replace(_HEAD_SMALL, mode=MODE_EAGLE3), B=3,
+        n=(33, 100, 7), tree=TREE_CHAIN, gamma=5, top_k=1, seed_w=1103,
+        seed_in=2103, seed_t=3103),
+    "s4_dynamic_wide": RoundCfg(
+        name="s4_dynamic_wide", head=replace(_HEAD_SMALL, d=384, n_q=8, n_kv=2,
+                                             ffn=1024, vocab=5000),
+        B=5, n=(300, 17, 0, 64, 129), tree=TREE_DYNAMIC, gamma=5, top_k=8,
+        top_m=40, inv_temp=6.0, seed_w=1104, seed_in=2104, seed_t=3104),
+}
+
+ALL_CONFIGS = {**CONFIGS, **SMALL_CONFIGS}
