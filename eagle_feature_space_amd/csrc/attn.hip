@@ -1,0 +1,265 @@
+// Tree-masked decode attention ("Tree attention in one verification pass":
+// every node attends only to its ancestors, position ids from the depth) over
+// a request's context cache plus the K/V of its expanded tree nodes.
+//
+// One wave owns (request b, kv head, key split, group of <= 16*RB query rows).
+// Query rows of a request are (row, head-in-group) pairs, so all G = Hq/Hkv
+// heads that share a kv head are served by one pass over its keys (GQA).
+// Per 64-key tile:
+//   S^T[key][qrow] = K Q^T   (MFMA; K rows go straight from HBM into the A
+//                             operand, Q sits in registers as the B operand)
+//   online softmax per query row (exp2 domain, fully masked rows stay empty)
+//   O^T[d][qrow] += V^T P^T  (MFMA; P^T is already in B-operand layout, V is
+//                             staged transposed in the wave's LDS slice)
+// Keys inside a tile are permuted so that lane group g owns keys
+// [16g, 16g+16): the S^T accumulator of key block j, row 4g+i holds key
+// 16g + 4j + i, which makes the P^T operand a plain register repack and the
+// V^T operand a contiguous 16-byte LDS read.
+#include "kernels.h"
+
+namespace eagle {
+
+constexpr int kAttnWaves = 2;   // kv heads per workgroup
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T, int HD, int RB>
+__global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
+  constexpr int VEC = DT<T>::VEC;
+  constexpr int DSTEPS = HD / (4 * VEC);    // MFMA steps over the head dim
+  constexpr int DB = HD / 16;               // output d blocks
+  constexpr int NV = 16 / VEC;              // 16-byte vectors per lane group per tile
+  constexpr int ROWB = 64 * (int)sizeof(T) + 16;
+  __shared__ __attribute__((aligned(16))) char vts[kAttnWaves][HD * ROWB];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int kvgroups = (a.Hkv + kAttnWaves - 1) / kAttnWaves;
+  const int kvh = (blockIdx.y % kvgroups) * kAttnWaves + w;
+  const int rg = blockIdx.y / kvgroups;
+  if (kvh >= a.Hkv) return;
+  const int b = blockIdx.z;
+  const int split = blockIdx.x;
+  const int G = a.Hq / a.Hkv;
+  const int R = a.W * G;
+  const int M = a.B * a.W;
+  char* vt = vts[w];
+
+  // query fragments
+  u32x4 qf[RB][DSTEPS];
+  uint64_t msk[RB];
+  int qm[RB], qh[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qrow = rg * 16 * RB + rb * 16 + c;
+    const bool ok = qrow < R;
+    const int rl = ok ? qrow / G : 0, gi = ok ? qrow % G : 0;
+    qm[rb] = ok ? b * a.W + rl : -1;
+    qh[rb] = kvh * G + gi;
+    msk[rb] = ok ? a.mask[b * a.W + rl] : 0ull;
+    const T* qp = (const T*)a.q + ((int64_t)(b * a.W + rl) * a.Hq + qh[rb]) * HD;
+#pragma unroll
+    for (int u = 0; u < DSTEPS; ++u)
+      qf[rb][u] = ok ? ld16(qp + u * 4 * VEC + g * VEC) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const bool extra = split == a.nsplit;
+  int kbeg, kend;
+  const T *kb, *vb;
+  const int64_t kstride = (int64_t)a.Hkv * HD;
+  if (!extra) {
+    const int nb = a.n[b];
+    kbeg = split * a.split_len;
+    kend = min(kbeg + a.split_len, nb);
+    kb = (const T*)a.k_ctx + (int64_t)a.cu_n[b] * kstride + kvh * HD;
+    vb = (const T*)a.v_ctx + (int64_t)a.cu_n[b] * kstride + kvh * HD;
+  } else {
+    uint64_t any = 0;
+    for (int r = 0; r < a.W; ++r) any |= a.mask[b * a.W + r];
+    kbeg = 0;
+    kend = any ? 64 - __builtin_clzll(any) : 0;
+    kb = (const T*)a.k_ex + (int64_t)b * kSlots * kstride + kvh * HD;
+    vb = (const T*)a.v_ex + (int64_t)b * kSlots * kstride + kvh * HD;
+  }
+
+  float mrun[RB], lrun[RB];
+  f32x4 o[DB][RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    mrun[rb] = -INFINITY;
+    lrun[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int t0 = kbeg; t0 < kend; t0 += 64) {
+    // ---- V tile -> LDS, transposed: vt[d][key]
+    wave_lds_sync();
+    {
+      constexpr int DG = HD / VEC;            // d groups of VEC
+      constexpr int UNITS = 16 * DG;          // (key quad, d group)
+#pragma unroll
+      for (int un = lane; un < UNITS; un += 64) {
+        const int kq = un / DG, dg = un % DG;
+        u32x4 v4[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int key = min(t0 + 4 * kq + kk, kend - 1);
+          v4[kk] = ld16(vb + (int64_t)key * kstride + dg * VEC);
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          char* dst = vt + (dg * VEC + e) * ROWB + 4 * kq * (int)sizeof(T);
+          if constexpr (sizeof(T) == 2) {
+            const int sh = (e & 1) * 16;
+            uint32_t w0 = ((v4[0][e >> 1] >> sh) & 0xffffu) | (((v4[1][e >> 1] >> sh) & 0xffffu) << 16);
+            uint32_t w1 = ((v4[2][e >> 1] >> sh) & 0xffffu) | (((v4[3][e >> 1] >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+          } else {
+            st16(dst, u32x4{v4[0][e], v4[1][e], v4[2][e], v4[3][e]});
+          }
+        }
+      }
+    }
+    // ---- S^T = K Q^T
+    f32x4 s[4][RB];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = min(t0 + (c >> 2) * 16 + j * 4 + (c & 3), kend - 1);
+      const T* kp = kb + (int64_t)key * kstride;
+      u32x4 kf[DSTEPS];
+#pragma unroll
+      for (int u = 0; u < DSTEPS; ++u) kf[u] = ld16(kp + u * 4 * VEC + g * VEC);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < DSTEPS; ++u) acc = DT<T>::mma(kf[u], qf[rb][u], acc);
+        s[j][rb] = acc;
+      }
+    }
+    wave_lds_sync();
+    // ---- online softmax and O^T += V^T P^T
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = t0 + g * 16 + j * 4 + i;
+          bool valid = key < kend;
+          if (extra) valid = valid && ((msk[rb] >> key) & 1ull);
+          const float v = valid ? s[j][rb][i] * a.scale_log2 : -INFINITY;
+          s[j][rb][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun[rb], tmax);
+      const bool empty = mnew == -INFINITY;
+      const float alpha = empty ? 1.f : exp2f(mrun[rb] - mnew);
+      float p[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = empty ? 0.f : exp2f(s[j][rb][i] - mnew);
+          p[4 * j + i] = e;
+          psum += e;
+        }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      lrun[rb] = lrun[rb] * alpha + psum;
+      mrun[rb] = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const u32x4 pf = DT<T>::pack(p + v * VEC);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 vf = ld16(vt + (db * 16 + c) * ROWB + (g * 16 + v * VEC) * (int)sizeof(T));
+          o[db][rb] = DT<T>::mma(vf, pf, o[db][rb]);
+        }
+      }
+    }
+  }
+
+  // ---- partial (m, l, O) of this split
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (qm[rb] < 0) continue;
+    const int64_t idx = ((int64_t)split * M + qm[rb]) * a.Hq + qh[rb];
+    if (g == 0) {
+      a.part_ml[2 * idx] = mrun[rb];
+      a.part_ml[2 * idx + 1] = lrun[rb];
+    }
+    float* po = a.part_o + idx * HD;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * g) = o[db][rb];
+  }
+}
+
+template <typename T, int HD>
+static void launch_rb(const AttnArgs& a, int RB, dim3 grid, hipStream_t st) {
+  dim3 block(64 * kAttnWaves);
+  switch (RB) {
+    case 1: hipLaunchKernelGGL((k_attn<T, HD, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn<T, HD, 2>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_attn<T, HD, 4>), grid, block, 0, st, a); break;
+  }
+}
+
+void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
+  AttnArgs a = a0;
+  const int R = a.W * (a.Hq / a.Hkv);
+  const int RB = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
+  a.rowgroups = (R + 16 * RB - 1) / (16 * RB);
+  const int kvgroups = (a.Hkv + kAttnWaves - 1) / kAttnWaves;
+  dim3 grid(a.nsplit + 1, kvgroups * a.rowgroups, a.B);
+  if (dtype == EAGLE_BF16) {
+    if (a.hd == 128) launch_rb<bf16s, 128>(a, RB, grid, st);
+    else launch_rb<bf16s, 64>(a, RB, grid, st);
+  } else {
+    if (a.hd == 128) launch_rb<float, 128>(a, RB, grid, st);
+    else launch_rb<float, 64>(a, RB, grid, st);
+  }
+}
+
+// out[m][h][d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
+  const int m = blockIdx.x;
+  const int HD = a.hd;
+  for (int idx = threadIdx.x; idx < a.Hq * HD; idx += 256) {
+    const int h = idx / HD, d = idx % HD;
+    float mx = -INFINITY;
+    for (int s = 0; s < a.nparts; ++s)
+      mx = fmaxf(mx, a.part_ml[2 * (((int64_t)s * a.M + m) * a.Hq + h)]);
+    float L = 0.f, O = 0.f;
+    if (mx != -INFINITY) {
+      for (int s = 0; s < a.nparts; ++s) {
+        const int64_t i = ((int64_t)s * a.M + m) * a.Hq + h;
+        const float ms = a.part_ml[2 * i];
+        if (ms == -INFINITY) continue;
+        const float f = exp2f(ms - mx);
+        L += f * a.part_ml[2 * i + 1];
+        O += f * a.part_o[i * HD + d];
+      }
+    }
+    DT<T>::st((T*)a.out + (int64_t)m * a.Hq * HD + idx, L > 0.f ? O / L : 0.f);
+  }
+}
+
+void launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t st) {
+  if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_attn_combine<bf16s>, dim3(a.M), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_attn_combine<float>, dim3(a.M), dim3(256), 0, st, a);
+}
+
+}  // namespace eagle

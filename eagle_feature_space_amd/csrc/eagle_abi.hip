@@ -1,0 +1,678 @@
+// C-ABI entry points of libeagle: argument validation, tree geometry,
+// workspace layout and the launch sequence of one draft step.  No device
+// memory is allocated here; every launch goes to the caller's stream.
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace eagle;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+// ---------------------------------------------------------------- tree shape
+struct Geo {
+  int kind = 0, B = 0, gamma = 0, top_k = 0, top_m = 0;
+  int pool_cap = 0, max_rows = 0, positions = 0, slots = 0;
+  std::vector<int> rows;              // rows per request of each step
+  std::vector<StaticPlan> plans;      // chain / static: children of each step
+};
+
+int build_geo(const eagle_tree* t, Geo* g) {
+  if (!t) return EAGLE_EINVAL;
+  if (t->B < 1 || t->gamma < 1 || t->top_k < 1) return EAGLE_EINVAL;
+  if (t->top_k > EAGLE_MAX_TOPK) return EAGLE_EUNSUPPORTED;
+  if (!(t->inv_temp > 0.f)) return EAGLE_EINVAL;
+  g->kind = t->kind;
+  g->B = t->B;
+  g->gamma = t->gamma;
+  g->top_k = t->top_k;
+  g->top_m = t->top_m;
+  g->rows.assign(t->gamma, 0);
+  g->plans.assign(t->gamma, StaticPlan{});
+  if (t->kind == EAGLE_TREE_CHAIN) {
+    g->pool_cap = t->gamma + 1;
+    g->positions = t->gamma + 1;
+    for (int s = 0; s < t->gamma; ++s) {
+      g->rows[s] = 1;
+      StaticPlan& p = g->plans[s];
+      p.nchild = 1;
+      p.row[0] = 0;
+      p.rank[0] = 0;
+      p.expand[0] = s + 1 < t->gamma;
+      p.nnext = p.expand[0];
+    }
+  } else if (t->kind == EAGLE_TREE_STATIC) {
+    const int nt = t->n_template;
+    if (nt < 1 || !t->template_parent) return EAGLE_EINVAL;
+    if (nt + 1 > EAGLE_MAX_POSITIONS) return EAGLE_ECAPACITY;
+    std::vector<std::vector<int>> ch(nt + 1);
+    std::vector<int> depth(nt + 1, 0);
+    for (int i = 0; i < nt; ++i) {
+      const int p = t->template_parent[i];
+      if (p < 0 || p > i) return EAGLE_EINVAL;
+      ch[p].push_back(i + 1);
+      depth[i + 1] = depth[p] + 1;
+    }
+    const int maxd = *std::max_element(depth.begin(), depth.end());
+    if (maxd != t->gamma) return EAGLE_EINVAL;
+    for (int u = 0; u <= nt; ++u)
+      if ((int)ch[u].size() > t->top_k) return EAGLE_EINVAL;
+    std::vector<int> frontier{0};
+    for (int s = 0; s < t->gamma; ++s) {
+      if (frontier.empty()) return EAGLE_EINVAL;
+      g->rows[s] = (int)frontier.size();
+      StaticPlan& p = g->plans[s];
+      std::vector<int> next;
+      int k = 0;
+      for (size_t r = 0; r < frontier.size(); ++r) {
+        const auto& kids = ch[frontier[r]];
+        for (size_t rank = 0; rank < kids.size(); ++rank) {
+          if (k >= 64) return EAGLE_ECAPACITY;
+          const int tc = kids[rank];
+          const bool ex = !ch[tc].empty() && s + 1 < t->gamma;
+          p.row[k] = (uint8_t)r;
+          p.rank[k] = (uint8_t)rank;
+          p.expand[k] = ex;
+          ++k;
+          if (ex) next.push_back(tc);
+        }
+      }
+      p.nchild = k;
+      p.nnext = (int)next.size();
+      frontier = next;
+    }
+    g->pool_cap = nt + 1;
+    g->positions = nt + 1;
+  } else if (t->kind == EAGLE_TREE_DYNAMIC) {
+    const int64_t cap = 1 + (int64_t)t->top_k + (int64_t)(t->gamma - 1) * t->top_k * t->top_k;
+    if (cap > 1024) return EAGLE_ECAPACITY;
+    g->pool_cap = (int)cap;
+    if (t->top_m < 1 || t->top_m > cap - 1) return EAGLE_EINVAL;
+    if (t->top_m + 1 > EAGLE_MAX_POSITIONS) return EAGLE_ECAPACITY;
+    g->positions = t->top_m + 1;
+    for (int s = 0; s < t->gamma; ++s) g->rows[s] = s == 0 ? 1 : t->top_k;
+  } else {
+    return EAGLE_EINVAL;
+  }
+  g->max_rows = *std::max_element(g->rows.begin(), g->rows.end());
+  int slots = 0;
+  for (int r : g->rows) slots += r;
+  g->slots = slots;
+  if (slots > EAGLE_MAX_SLOTS) return EAGLE_ECAPACITY;
+  return EAGLE_OK;
+}
+
+void layout_of(const Geo& g, eagle_tree_layout* L) {
+  memset(L, 0, sizeof(*L));
+  Bump bp;
+  const size_t B = g.B, P = g.pool_cap, R = (size_t)g.B * g.max_rows, K = g.top_k;
+  L->pool_cap = g.pool_cap;
+  L->max_rows = g.max_rows;
+  L->positions = g.positions;
+  L->pool_tok = bp.take(B * P * 4);
+  L->pool_parent = bp.take(B * P * 4);
+  L->pool_depth = bp.take(B * P * 4);
+  L->pool_slot = bp.take(B * P * 4);
+  L->pool_conf = bp.take(B * P * 4);
+  L->pool_value = bp.take(B * P * 4);
+  L->pool_count = bp.take(B * 4);
+  L->slot_count = bp.take(B * 4);
+  L->root_pos = bp.take(B * 4);
+  L->slot_mask = bp.take(B * kSlots * 8);
+  L->row_node = bp.take(R * 4);
+  L->row_tok = bp.take(R * 4);
+  L->row_pos = bp.take(R * 4);
+  L->row_slot = bp.take(R * 4);
+  L->row_pidx = bp.take(R * 4);
+  L->row_mask = bp.take(R * 8);
+  L->topk_id = bp.take(R * K * 4);
+  L->topk_conf = bp.take(R * K * 4);
+  L->lse = bp.take(R * 4);
+  L->f_node = bp.take(B * kMaxPos * 4);
+  L->f_tok = bp.take(B * kMaxPos * 4);
+  L->f_parent = bp.take(B * kMaxPos * 4);
+  L->f_depth = bp.take(B * kMaxPos * 4);
+  L->f_pos = bp.take(B * kMaxPos * 4);
+  L->f_mask = bp.take(B * kMaxPos * 8);
+  L->f_count = bp.take(B * 4);
+  L->choice = bp.take(B * kMaxPos * 4);
+  L->total = bp.off;
+}
+
+TreeDev tree_dev(const eagle_tree* t, const Geo& g) {
+  eagle_tree_layout L;
+  layout_of(g, &L);
+  char* s = (char*)t->state;
+  TreeDev d;
+  d.pool_tok = (int32_t*)(s + L.pool_tok);
+  d.pool_parent = (int32_t*)(s + L.pool_parent);
+  d.pool_depth = (int32_t*)(s + L.pool_depth);
+  d.pool_slot = (int32_t*)(s + L.pool_slot);
+  d.pool_conf = (float*)(s + L.pool_conf);
+  d.pool_value = (float*)(s + L.pool_value);
+  d.pool_count = (int32_t*)(s + L.pool_count);
+  d.slot_count = (int32_t*)(s + L.slot_count);
+  d.root_pos = (int32_t*)(s + L.root_pos);
+  d.slot_mask = (uint64_t*)(s + L.slot_mask);
+  d.row_node = (int32_t*)(s + L.row_node);
+  d.row_tok = (int32_t*)(s + L.row_tok);
+  d.row_pos = (int32_t*)(s + L.row_pos);
+  d.row_slot = (int32_t*)(s + L.row_slot);
+  d.row_pidx = (int32_t*)(s + L.row_pidx);
+  d.row_mask = (uint64_t*)(s + L.row_mask);
+  d.topk_id = (int32_t*)(s + L.topk_id);
+  d.topk_conf = (float*)(s + L.topk_conf);
+  d.lse = (float*)(s + L.lse);
+  d.f_node = (int32_t*)(s + L.f_node);
+  d.f_tok = (int32_t*)(s + L.f_tok);
+  d.f_parent = (int32_t*)(s + L.f_parent);
+  d.f_depth = (int32_t*)(s + L.f_depth);
+  d.f_pos = (int32_t*)(s + L.f_pos);
+  d.f_mask = (uint64_t*)(s + L.f_mask);
+  d.f_count = (int32_t*)(s + L.f_count);
+  d.choice = (int32_t*)(s + L.choice);
+  d.pool_cap = g.pool_cap;
+  d.max_rows = g.max_rows;
+  d.positions = g.positions;
+  return d;
+}
+
+int check_tree_state(const eagle_tree* t, const Geo& g) {
+  if (!t->state) return EAGLE_EINVAL;
+  eagle_tree_layout L;
+  layout_of(g, &L);
+  if (t->state_bytes < L.total) return EAGLE_ECAPACITY;
+  return EAGLE_OK;
+}
+
+// ---------------------------------------------------------------- head / kv
+int esz(const eagle_head* h) { return h->dtype == EAGLE_BF16 ? 2 : 4; }
+
+int check_head(const eagle_head* h) {
+  if (!h) return EAGLE_EINVAL;
+  if (h->dtype != EAGLE_BF16 && h->dtype != EAGLE_F32) return EAGLE_EINVAL;
+  if (h->act != EAGLE_ACT_SWIGLU && h->act != EAGLE_ACT_GELU) return EAGLE_EINVAL;
+  if (h->norm != EAGLE_NORM_RMS && h->norm != EAGLE_NORM_LAYER) return EAGLE_EINVAL;
+  if (h->mode != EAGLE_MODE_1 && h->mode != EAGLE_MODE_3) return EAGLE_EINVAL;
+  if (h->d < 64 || h->ffn < 32 || h->vocab < 16 || h->n_q_heads < 1 || h->n_kv_heads < 1)
+    return EAGLE_EINVAL;
+  if (!(h->eps > 0.f) || h->rope_theta < 0.f) return EAGLE_EINVAL;
+  if (h->d % 64 || h->ffn % 32) return EAGLE_EUNSUPPORTED;
+  if (h->head_dim != 64 && h->head_dim != 128) return EAGLE_EUNSUPPORTED;
+  if (h->n_q_heads % h->n_kv_heads) return EAGLE_EUNSUPPORTED;
+  if (h->d > 16384 || h->ffn > 65536 || (int64_t)h->n_q_heads * h->head_dim > 16384)
+    return EAGLE_EUNSUPPORTED;
+  if (h->mode == EAGLE_MODE_1 && !h->w_fc) return EAGLE_EINVAL;
+  if (h->mode == EAGLE_MODE_3 && !h->w_fuse) return EAGLE_EINVAL;
+  if (!h->w_q || !h->w_k || !h->w_v || !h->w_o || !h->w_up || !h->w_down) return EAGLE_EINVAL;
+  if (h->act == EAGLE_ACT_SWIGLU && !h->w_gate) return EAGLE_EINVAL;
+  if (!h->norm1_g || !h->norm2_g || !h->emb || !h->lm_head) return EAGLE_EINVAL;
+  if (h->norm == EAGLE_NORM_LAYER && (!h->norm1_b || !h->norm2_b)) return EAGLE_EINVAL;
+  return EAGLE_OK;
+}
+
+int check_kv(const eagle_kv* kv, int B) {
+  if (!kv) return EAGLE_EINVAL;
+  if (kv->B != B || B < 1 || kv->max_n < 0 || kv->total_n < 0) return EAGLE_EINVAL;
+  if (!kv->n || !kv->cu_n || !kv->k_slot || !kv->v_slot || !kv->feat_slot) return EAGLE_EINVAL;
+  if (kv->total_n > 0 && (!kv->k_ctx || !kv->v_ctx)) return EAGLE_EINVAL;
+  if (kv->total_n > INT32_MAX || kv->max_n > kv->total_n) return EAGLE_EINVAL;
+  return EAGLE_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+struct AttnPlan {
+  int split_len, nsplit;
+};
+AttnPlan plan_attn(const eagle_head* h, const eagle_kv* kv) {
+  AttnPlan p;
+  const int64_t work = (int64_t)std::max(kv->max_n, 1) * kv->B * h->n_kv_heads;
+  int64_t units = (work + 64 * 1024 - 1) / (64 * 1024);
+  if (units < 1) units = 1;
+  p.split_len = (int)(64 * units);
+  p.nsplit = (std::max(kv->max_n, 1) + p.split_len - 1) / p.split_len;
+  return p;
+}
+
+struct Ws {
+  size_t h, hn, h1, h1n, f, q, o, act, P;
+  size_t att_o, att_ml, lm_max, lm_sum, lm_id, lm_val;
+  size_t tk, tv, t_tok, t_kv, t_pos, t_mask;
+  size_t x_in, xn_in, P_in;
+  size_t total;
+  AttnPlan ap;
+};
+
+size_t gemm_bytes(int dtype, int M, int N, int K) {
+  if (M <= 0) return 0;
+  GemmShape s = plan_gemm(dtype, M, N, K);
+  return (size_t)s.S * M * N * 4;
+}
+
+Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
+  Ws w;
+  Bump bp;
+  const int e = esz(h), d = h->d, qd = h->n_q_heads * h->head_dim,
+            kvd = h->n_kv_heads * h->head_dim;
+  const int nact = h->act == EAGLE_ACT_SWIGLU ? 2 * h->ffn : h->ffn;
+  const int Mmax = g.B * g.max_rows;
+  const int Mt = g.B * g.positions;
+  const int Mr = std::max(Mmax, Mt);
+  w.h = bp.take((size_t)Mr * d * e);
+  w.hn = bp.take((size_t)Mr * d * e);
+  w.h1 = bp.take((size_t)Mmax * d * e);
+  w.h1n = bp.take((size_t)Mmax * d * e);
+  w.f = bp.take((size_t)Mmax * d * e);
+  w.q = bp.take((size_t)Mr * qd * e);
+  w.o = bp.take((size_t)Mr * qd * e);
+  w.act = bp.take((size_t)Mmax * h->ffn * e);
+  size_t P = gemm_bytes(h->dtype, Mt, qd + 2 * kvd, d);
+  for (int s = 0; s < g.gamma; ++s) {
+    const int M = g.B * g.rows[s];
+    if (h->mode == EAGLE_MODE_1) P = std::max(P, gemm_bytes(h->dtype, M, d, 2 * d));
+    P = std::max(P, gemm_bytes(h->dtype, M, qd + 2 * kvd, d));
+    P = std::max(P, gemm_bytes(h->dtype, M, d, qd));
+    P = std::max(P, gemm_bytes(h->dtype, M, nact, d));
+    P = std::max(P, gemm_bytes(h->dtype, M, d, h->ffn));
+  }
+  w.P = bp.take(P);
+  w.ap = plan_attn(h, kv);
+  const size_t nparts = (size_t)w.ap.nsplit + 1;
+  w.att_o = bp.take(nparts * Mr * h->n_q_heads * h->head_dim * 4);
+  w.att_ml = bp.take(nparts * Mr * h->n_q_heads * 2 * 4);
+  LmShape ls = plan_lmhead(h->dtype, Mmax, h->vocab);
+  w.lm_max = bp.take((size_t)ls.ntiles * Mmax * 4);
+  w.lm_sum = bp.take((size_t)ls.ntiles * Mmax * 4);
+  w.lm_id = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
+  w.lm_val = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
+  w.tk = bp.take((size_t)g.B * kSlots * kvd * e);
+  w.tv = bp.take((size_t)g.B * kSlots * kvd * e);
+  w.t_tok = bp.take((size_t)Mt * 4);
+  w.t_kv = bp.take((size_t)Mt * 4);
+  w.t_pos = bp.take((size_t)Mt * 4);
+  w.t_mask = bp.take((size_t)Mt * 8);
+  if (h->mode == EAGLE_MODE_3) {
+    const int Tn = (int)kv->total_n;
+    w.x_in = bp.take((size_t)Tn * d * e);
+    w.xn_in = bp.take((size_t)Tn * d * e);
+    w.P_in = bp.take(std::max(gemm_bytes(h->dtype, Tn, d, 3 * d),
+                              gemm_bytes(h->dtype, Tn, 2 * kvd, d)));
+  } else {
+    w.x_in = w.xn_in = w.P_in = 0;
+  }
+  w.total = bp.off;
+  return w;
+}
+
+hipError_t last_error() { return hipGetLastError(); }
+
+RowSrc rs(const void* base, const int32_t* idx, int64_t stride, int64_t limit = 0) {
+  return RowSrc{base, idx, stride, limit};
+}
+
+void gemm(const eagle_head* h, RowSrc x0, RowSrc x1, int ksplit, int M, int N, int K,
+          const void* w0, const void* w1, const void* w2, int nseg1, int nseg2, float* P,
+          GemmShape* shape, hipStream_t st) {
+  GemmArgs a;
+  a.xs[0] = x0;
+  a.xs[1] = x1;
+  a.ksplit_x = ksplit;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.w[0] = w0;
+  a.w[1] = w1 ? w1 : w0;
+  a.w[2] = w2 ? w2 : (w1 ? w1 : w0);
+  a.nseg1 = nseg1;
+  a.nseg2 = nseg2;
+  a.P = P;
+  a.kps = 0;
+  *shape = plan_gemm(h->dtype, M, N, K);
+  launch_gemm(h->dtype, a, *shape, st);
+}
+
+void reduce(const eagle_head* h, const float* P, int S, int M, int N, RowSrc s1, RowSrc s2,
+            void* out, RowSrc scatter, void* out_norm, int which_norm, hipStream_t st) {
+  ReduceArgs a;
+  a.P = P;
+  a.S = S;
+  a.M = M;
+  a.N = N;
+  a.src1 = s1;
+  a.src2 = s2;
+  a.out = out;
+  a.out_scatter = scatter;
+  a.out_norm = out_norm;
+  a.gain = which_norm == 1 ? h->norm1_g : h->norm2_g;
+  a.bias = h->norm == EAGLE_NORM_LAYER ? (which_norm == 1 ? h->norm1_b : h->norm2_b) : nullptr;
+  a.layer_norm = h->norm == EAGLE_NORM_LAYER;
+  a.eps = h->eps;
+  launch_reduce_rows(h->dtype, a, st);
+}
+
+const RowSrc kNone{nullptr, nullptr, 0, 0};
+
+// q|k|v projection of rows already normalised in `hn`, RoPE, scatter
+void qkv_rope(const eagle_head* h, const char* ws, const Ws& w, const void* hn, int M,
+              const int32_t* pos, void* kdst, void* vdst, const int32_t* kv_idx, hipStream_t st) {
+  const int d = h->d, qd = h->n_q_heads * h->head_dim, kvd = h->n_kv_heads * h->head_dim;
+  GemmShape sh;
+  float* P = (float*)(ws + w.P);
+  gemm(h, rs(hn, nullptr, d), kNone, d, M, qd + 2 * kvd, d, h->w_q, h->w_k, h->w_v, qd, qd + kvd,
+       P, &sh, st);
+  QkvArgs q;
+  q.P = P;
+  q.S = sh.S;
+  q.M = M;
+  q.Hq = h->n_q_heads;
+  q.Hkv = h->n_kv_heads;
+  q.hd = h->head_dim;
+  q.theta = h->rope_theta;
+  q.pos = pos;
+  q.cu_n = nullptr;
+  q.B = 0;
+  q.q = (void*)(ws + w.q);
+  q.k = kdst;
+  q.v = vdst;
+  q.kv_idx = kv_idx;
+  launch_epi_qkv(h->dtype, q, st);
+}
+
+void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w, int W,
+            const void* k_ex, const void* v_ex, const uint64_t* mask, void* out, hipStream_t st) {
+  AttnArgs a;
+  a.q = ws + w.q;
+  a.B = kv->B;
+  a.W = W;
+  a.Hq = h->n_q_heads;
+  a.Hkv = h->n_kv_heads;
+  a.hd = h->head_dim;
+  a.n = kv->n;
+  a.cu_n = kv->cu_n;
+  a.k_ctx = kv->k_ctx;
+  a.v_ctx = kv->v_ctx;
+  a.k_ex = k_ex;
+  a.v_ex = v_ex;
+  a.mask = mask;
+  a.split_len = w.ap.split_len;
+  a.nsplit = w.ap.nsplit;
+  a.rowgroups = 1;
+  a.scale_log2 = 1.4426950408889634f / sqrtf((float)h->head_dim);
+  a.part_o = (float*)(ws + w.att_o);
+  a.part_ml = (float*)(ws + w.att_ml);
+  launch_attention(h->dtype, a, st);
+  CombineArgs c;
+  c.part_o = a.part_o;
+  c.part_ml = a.part_ml;
+  c.nparts = a.nsplit + 1;
+  c.M = kv->B * W;
+  c.Hq = h->n_q_heads;
+  c.hd = h->head_dim;
+  c.out = out;
+  launch_attn_combine(h->dtype, c, st);
+}
+
+int finish(int status) {
+  if (status != EAGLE_OK) return status;
+  return last_error() == hipSuccess ? EAGLE_OK : EAGLE_EHIP;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+const char* eagle_version(void) { return "eagle-mi355x 0.1 (gfx950)"; }
+
+const char* eagle_strerror(int s) {
+  switch (s) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_EINVAL: return "invalid argument";
+    case EAGLE_EUNSUPPORTED: return "unsupported shape";
+    case EAGLE_ECAPACITY: return "capacity exceeded (workspace, tree state, slots or positions)";
+    case EAGLE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int eagle_tree_layout_of(const eagle_tree* tree, eagle_tree_layout* out) {
+  if (!out) return EAGLE_EINVAL;
+  Geo g;
+  int s = build_geo(tree, &g);
+  if (s) return s;
+  layout_of(g, out);
+  return EAGLE_OK;
+}
+
+size_t eagle_tree_state_bytes(const eagle_tree* tree) {
+  eagle_tree_layout L;
+  return eagle_tree_layout_of(tree, &L) == EAGLE_OK ? L.total : 0;
+}
+
+int eagle_step_rows(const eagle_tree* tree, int step) {
+  Geo g;
+  if (build_geo(tree, &g)) return 0;
+  if (step < 0 || step >= g.gamma) return 0;
+  return g.rows[step];
+}
+
+size_t eagle_workspace_bytes(const eagle_head* head, const eagle_kv* kv, const eagle_tree* tree) {
+  Geo g;
+  if (check_head(head) || build_geo(tree, &g) || check_kv(kv, g.B)) return 0;
+  return plan_ws(head, kv, g).total;
+}
+
+int eagle_tree_init(const eagle_head* head, const eagle_kv* kv, const eagle_tree* tree,
+                    const int32_t* root_tokens, void* stream) {
+  Geo g;
+  int s;
+  if ((s = check_head(head))) return s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_kv(kv, g.B))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (!root_tokens) return EAGLE_EINVAL;
+  if (head->mode == EAGLE_MODE_3 && kv->total_n < kv->B) return EAGLE_EINVAL;
+  launch_tree_init(tree_dev(tree, g), g.B, head->mode == EAGLE_MODE_3, head->vocab, root_tokens,
+                   kv->n, kv->cu_n, (hipStream_t)stream);
+  return finish(EAGLE_OK);
+}
+
+int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* tree, int step,
+                     const void* f_root, const void* lmh, const int32_t* ctx_tokens,
+                     float* logits_out, void* feat_out, void* ws_v, size_t ws_bytes,
+                     void* stream) {
+  Geo g;
+  int s;
+  if ((s = check_head(h))) return s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_kv(kv, g.B))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (step < 0 || step >= g.gamma) return EAGLE_EINVAL;
+  if (g.top_k > h->vocab) return EAGLE_EINVAL;
+  const bool e3 = h->mode == EAGLE_MODE_3;
+  if (step == 0 && !e3 && !f_root) return EAGLE_EINVAL;
+  if (step == 0 && e3 && (!lmh || !ctx_tokens || kv->total_n < 1)) return EAGLE_EINVAL;
+  if (!ws_v) return EAGLE_EINVAL;
+  const Ws w = plan_ws(h, kv, g);
+  if (ws_bytes < w.total) return EAGLE_ECAPACITY;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)ws_v;
+  const TreeDev td = tree_dev(tree, g);
+  const int B = g.B, W = g.rows[step], M = B * W;
+  const int d = h->d, qd = h->n_q_heads * h->head_dim, ffn = h->ffn;
+  const bool swiglu = h->act == EAGLE_ACT_SWIGLU;
+  float* P = (float*)(ws + w.P);
+  void* hbuf = ws + w.h;
+  void* hn = ws + w.hn;
+  GemmShape sh;
+
+  // ---- layer input h and N1(h)
+  if (!e3) {
+    const void* fsrc = step == 0 ? f_root : kv->feat_slot;
+    gemm(h, rs(fsrc, td.row_pidx, d, step == 0 ? (int64_t)B : (int64_t)B * kSlots), rs(h->emb, td.row_tok, d, h->vocab), d, M, d, 2 * d, h->w_fc,
+         nullptr, nullptr, d, d, P, &sh, st);
+    reduce(h, P, sh.S, M, d, kNone, kNone, hbuf, kNone, hn, 1, st);
+  } else if (step > 0) {
+    reduce(h, nullptr, 0, M, d, rs(kv->feat_slot, td.row_pidx, d, (int64_t)B * kSlots), rs(h->emb, td.row_tok, d, h->vocab),
+           hbuf, kNone, hn, 1, st);
+  } else {
+    // ingest of every verified position: g = [l;m;h] W_fuse^T, x = g + emb(t_next)
+    const int Tn = (int)kv->total_n, kvd = h->n_kv_heads * h->head_dim;
+    float* Pin = (float*)(ws + w.P_in);
+    gemm(h, rs(lmh, nullptr, 3 * d), kNone, 3 * d, Tn, d, 3 * d, h->w_fuse, nullptr, nullptr, d,
+         d, Pin, &sh, st);
+    reduce(h, Pin, sh.S, Tn, d, kNone, rs(h->emb, ctx_tokens, d, h->vocab), ws + w.x_in, kNone,
+           ws + w.xn_in, 1, st);
+    gemm(h, rs(ws + w.xn_in, nullptr, d), kNone, d, Tn, 2 * kvd, d, h->w_k, h->w_v, nullptr, kvd,
+         2 * kvd, Pin, &sh, st);
+    QkvArgs q;
+    q.P = Pin;
+    q.S = sh.S;
+    q.M = Tn;
+    q.Hq = 0;
+    q.Hkv = h->n_kv_heads;
+    q.hd = h->head_dim;
+    q.theta = h->rope_theta;
+    q.pos = nullptr;
+    q.cu_n = kv->cu_n;
+    q.B = B;
+    q.q = nullptr;
+    q.k = kv->k_ctx;
+    q.v = kv->v_ctx;
+    q.kv_idx = nullptr;
+    launch_epi_qkv(h->dtype, q, st);
+    // root rows = each request's last verified position
+    reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, kv->total_n), kNone, hbuf, kNone, hn, 1, st);
+  }
+
+  // ---- attention sub-layer
+  qkv_rope(h, ws, w, hn, M, td.row_pos, kv->k_slot, kv->v_slot, td.row_slot, st);
+  attend(h, kv, ws, w, W, kv->k_slot, kv->v_slot, td.row_mask, ws + w.o, st);
+  gemm(h, rs(ws + w.o, nullptr, qd), kNone, qd, M, d, qd, h->w_o, nullptr, nullptr, d, d, P, &sh,
+       st);
+  reduce(h, P, sh.S, M, d, rs(hbuf, nullptr, d), kNone, ws + w.h1, kNone, ws + w.h1n, 2, st);
+
+  // ---- MLP sub-layer
+  if (swiglu)
+    gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, 2 * ffn, d, h->w_gate, h->w_up, nullptr, ffn,
+         2 * ffn, P, &sh, st);
+  else
+    gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn, P,
+         &sh, st);
+  ActArgs aa;
+  aa.P = P;
+  aa.S = sh.S;
+  aa.M = M;
+  aa.F = ffn;
+  aa.swiglu = swiglu;
+  aa.out = ws + w.act;
+  launch_epi_act(h->dtype, aa, st);
+  gemm(h, rs(ws + w.act, nullptr, ffn), kNone, ffn, M, d, ffn, h->w_down, nullptr, nullptr, d, d,
+       P, &sh, st);
+  void* fout = feat_out ? feat_out : (void*)(ws + w.f);
+  reduce(h, P, sh.S, M, d, rs(ws + w.h1, nullptr, d), kNone, fout,
+         rs(kv->feat_slot, td.row_slot, d), nullptr, 0, st);
+
+  // ---- LM head + softmax / top-k
+  LmShape ls = plan_lmhead(h->dtype, M, h->vocab);
+  LmArgs la;
+  la.x = rs(fout, nullptr, d);
+  la.M = M;
+  la.K = d;
+  la.V = h->vocab;
+  la.w = h->lm_head;
+  la.top_k = g.top_k;
+  la.inv_temp = tree->inv_temp;
+  la.logits = logits_out;
+  la.part_max = (float*)(ws + w.lm_max);
+  la.part_sum = (float*)(ws + w.lm_sum);
+  la.part_id = (int*)(ws + w.lm_id);
+  la.part_val = (float*)(ws + w.lm_val);
+  launch_lmhead(h->dtype, la, ls, st);
+  MergeArgs ma;
+  ma.part_max = la.part_max;
+  ma.part_sum = la.part_sum;
+  ma.part_id = la.part_id;
+  ma.part_val = la.part_val;
+  ma.ntiles = ls.ntiles;
+  ma.M = M;
+  ma.top_k = g.top_k;
+  ma.inv_temp = tree->inv_temp;
+  ma.topk_id = td.topk_id;
+  ma.topk_conf = td.topk_conf;
+  ma.lse = td.lse;
+  ma.vocab = h->vocab;
+  launch_topk_merge(ma, st);
+  return finish(EAGLE_OK);
+}
+
+int eagle_tree_expand_rerank(const eagle_tree* tree, int step, void* stream) {
+  Geo g;
+  int s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (step < 0 || step >= g.gamma) return EAGLE_EINVAL;
+  const bool fin = step == g.gamma - 1;
+  launch_tree_expand(tree_dev(tree, g), g.B, g.kind, step, g.gamma, g.rows[step], g.top_k,
+                     g.top_m, fin, g.plans[step], (hipStream_t)stream);
+  return finish(EAGLE_OK);
+}
+
+int eagle_tree_attend(const eagle_head* h, const eagle_kv* kv, const eagle_tree* tree, void* out,
+                      void* ws_v, size_t ws_bytes, void* stream) {
+  Geo g;
+  int s;
+  if ((s = check_head(h))) return s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_kv(kv, g.B))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (!out || !ws_v) return EAGLE_EINVAL;
+  const Ws w = plan_ws(h, kv, g);
+  if (ws_bytes < w.total) return EAGLE_ECAPACITY;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)ws_v;
+  const TreeDev td = tree_dev(tree, g);
+  const int Wt = g.positions, M = g.B * Wt, d = h->d;
+  int32_t* t_tok = (int32_t*)(ws + w.t_tok);
+  int32_t* t_kv = (int32_t*)(ws + w.t_kv);
+  int32_t* t_pos = (int32_t*)(ws + w.t_pos);
+  uint64_t* t_mask = (uint64_t*)(ws + w.t_mask);
+  launch_tree_rows_final(td, g.B, t_tok, t_kv, t_pos, t_mask, st);
+  reduce(h, nullptr, 0, M, d, rs(h->emb, t_tok, d, h->vocab), kNone, nullptr, kNone, ws + w.hn, 1, st);
+  qkv_rope(h, ws, w, ws + w.hn, M, t_pos, ws + w.tk, ws + w.tv, t_kv, st);
+  attend(h, kv, ws, w, Wt, ws + w.tk, ws + w.tv, t_mask, out, st);
+  return finish(EAGLE_OK);
+}
+
+int eagle_tree_verify(const eagle_tree* tree, const void* target_logits, int positions, int vocab,
+                      int dtype, int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                      void* stream) {
+  Geo g;
+  int s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (!target_logits || !accept_len || !accept_path || !out_tokens) return EAGLE_EINVAL;
+  if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_EINVAL;
+  if (vocab < 1 || positions < g.positions) return EAGLE_EINVAL;
+  launch_verify(tree_dev(tree, g), g.B, target_logits, positions, vocab, dtype, g.gamma,
+                accept_len, accept_path, out_tokens, (hipStream_t)stream);
+  return finish(EAGLE_OK);
+}
+
+}  // extern "C"

@@ -1,0 +1,305 @@
+// Weight-streaming GEMM for the draft head's linear maps, and the epilogues
+// that follow it (residual + norm, RoPE + K/V scatter, SwiGLU / GELU).
+//
+// The draft step runs M = B * rows-per-request <= a few hundred rows through
+// matrices of d x 2d ... ffn x d ("What is actually in the head": an fc of
+// shape [2d, d] and one decoder layer of width d).  At M <= 80 every weight
+// byte is used M times, far below the MFMA ridge, so the kernel is built to
+// stream W from HBM once: each wave owns 16*NB output columns, loads its W
+// rows straight from global memory into registers (16 B per lane, the four
+// lanes of a row reading 64 contiguous bytes) and multiplies them against the
+// activation chunk staged once per workgroup in LDS.  Split-K over grid.z
+// gives the launch enough waves; partial sums go to an fp32 workspace that
+// the epilogue kernels reduce in a fixed order (bit-reproducible).
+#include "kernels.h"
+
+namespace eagle {
+
+template <typename T, int MB, int NB>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+  constexpr int VEC = DT<T>::VEC;
+  constexpr int KC = 32 * VEC;                 // K elements per chunk
+  constexpr int MT = 16 * MB;                  // rows per workgroup
+  constexpr int ROWB = KC * (int)sizeof(T) + 16;
+  __shared__ __attribute__((aligned(16))) char xl[MT * ROWB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int n_base = (blockIdx.x * 4 + wave) * (16 * NB);
+  const int m0 = blockIdx.y * MT;
+  const int k_begin = blockIdx.z * a.kps;
+  const int k_end = min(a.K, k_begin + a.kps);
+
+  const T* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int n = min(n_base + nb * 16 + c, a.N - 1);
+    const T* base;
+    int off;
+    if (n < a.nseg1) { base = (const T*)a.w[0]; off = 0; }
+    else if (n < a.nseg2) { base = (const T*)a.w[1]; off = a.nseg1; }
+    else { base = (const T*)a.w[2]; off = a.nseg2; }
+    wrow[nb] = base + (int64_t)(n - off) * a.K;
+  }
+
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = k_begin; k0 < k_end; k0 += KC) {
+    const int L = min(KC, k_end - k0);         // multiple of 4*VEC
+    const int U = L / (4 * VEC);
+    u32x4 wv[NB][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        if (u < U) wv[nb][u] = ld16(wrow[nb] + k0 + u * 4 * VEC + g * VEC);
+
+    __syncthreads();
+    const int pieces = L / VEC;
+    for (int p = tid; p < MT * pieces; p += 256) {
+      const int r = p / pieces, j = p - r * pieces;
+      const int m = m0 + r;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (m < a.M) {
+        const int k = k0 + j * VEC;
+        if (k < a.ksplit_x) v = ld16(row_ptr<T>(a.xs[0], m) + k);
+        else v = ld16(row_ptr<T>(a.xs[1], m) + (k - a.ksplit_x));
+      }
+      st16(xl + r * ROWB + j * 16, v);
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < U) {
+        u32x4 xf[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xf[mb] = ld16(xl + (mb * 16 + c) * ROWB + (u * 4 * VEC + g * VEC) * (int)sizeof(T));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = DT<T>::mma(wv[nb][u], xf[mb], acc[nb][mb]);
+      }
+    }
+  }
+
+  // acc[nb][mb]: lane holds out[m = m0 + 16mb + c][n = n_base + 16nb + 4g + 0..3]
+  float* P = a.P + (int64_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n_base + nb * 16 + 4 * g;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + mb * 16 + c;
+      if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
+    }
+  }
+}
+
+// ----------------------------------------------------------------- planning
+static int kc_of(int dtype) { return dtype == EAGLE_BF16 ? 256 : 128; }
+
+GemmShape plan_gemm(int dtype, int M, int N, int K) {
+  GemmShape s;
+  s.MB = M >= 80 ? 5 : (M + 15) / 16;
+  if (s.MB < 1) s.MB = 1;
+  s.mtiles = (M + 16 * s.MB - 1) / (16 * s.MB);
+  s.NB = N >= 4096 ? 2 : 1;
+  s.ntiles = (N + 64 * s.NB - 1) / (64 * s.NB);
+  const int kc = kc_of(dtype);
+  const int esz = dtype == EAGLE_BF16 ? 2 : 4;
+  const int kchunks = (K + kc - 1) / kc;
+  int want = (1024 + s.ntiles * s.mtiles - 1) / (s.ntiles * s.mtiles);
+  // keep the fp32 partial traffic under ~1/8 of the weight bytes
+  int cap = (int)((int64_t)K * esz / (32 * (int64_t)M));
+  if (cap < 1) cap = 1;
+  int S = want < cap ? want : cap;
+  if (S > kchunks) S = kchunks;
+  if (S < 1) S = 1;
+  int cps = (kchunks + S - 1) / S;
+  s.kps = cps * kc;
+  s.S = (K + s.kps - 1) / s.kps;
+  return s;
+}
+
+template <typename T, int NB>
+static void launch_mb(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+  dim3 grid(s.ntiles, s.mtiles, s.S), block(256);
+  switch (s.MB) {
+    case 1: hipLaunchKernelGGL((k_gemm<T, 1, NB>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm<T, 2, NB>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm<T, 3, NB>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_gemm<T, 4, NB>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_gemm<T, 5, NB>), grid, block, 0, st, a); break;
+  }
+}
+
+void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st) {
+  a.kps = s.kps;
+  if (dtype == EAGLE_BF16) {
+    if (s.NB == 2) launch_mb<bf16s, 2>(a, s, st); else launch_mb<bf16s, 1>(a, s, st);
+  } else {
+    if (s.NB == 2) launch_mb<float, 2>(a, s, st); else launch_mb<float, 1>(a, s, st);
+  }
+}
+
+// ----------------------------------------------------------------- epilogues
+// y = sum_s P[s][m] + src1[m] + src2[m] (fp32), one workgroup per row; writes
+// y (dense and/or scattered) in T and, optionally, yn = Norm(y).
+template <typename T>
+__global__ __launch_bounds__(256) void k_reduce_rows(ReduceArgs a) {
+  extern __shared__ float ys[];
+  __shared__ float red[2][4];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N = a.N;
+  const float* P = a.P;
+  const T* s1 = a.src1.base ? row_ptr<T>(a.src1, m) : nullptr;
+  const T* s2 = a.src2.base ? row_ptr<T>(a.src2, m) : nullptr;
+  float sum = 0.f;
+  for (int n = tid; n < N; n += 256) {
+    float y = 0.f;
+    if (P) {
+      for (int s = 0; s < a.S; ++s) y += P[((int64_t)s * a.M + m) * N + n];
+    }
+    if (s1) y += DT<T>::ld(s1 + n);
+    if (s2) y += DT<T>::ld(s2 + n);
+    ys[n] = y;
+    sum += y;
+  }
+  if (a.out) {
+    T* o = (T*)a.out + (int64_t)m * N;
+    for (int n = tid; n < N; n += 256) DT<T>::st(o + n, ys[n]);
+  }
+  if (a.out_scatter.base) {
+    T* o = (T*)a.out_scatter.base + (int64_t)a.out_scatter.idx[m] * a.out_scatter.stride;
+    for (int n = tid; n < N; n += 256) DT<T>::st(o + n, ys[n]);
+  }
+  if (!a.out_norm) return;
+  // mean (LayerNorm) then mean square of (y - mean)
+  sum = wave_sum(sum);
+  if ((tid & 63) == 0) red[0][tid >> 6] = sum;
+  __syncthreads();
+  const float mean = a.layer_norm ? (red[0][0] + red[0][1] + red[0][2] + red[0][3]) / N : 0.f;
+  float sq = 0.f;
+  for (int n = tid; n < N; n += 256) {
+    float v = ys[n] - mean;
+    sq += v * v;
+  }
+  sq = wave_sum(sq);
+  if ((tid & 63) == 0) red[1][tid >> 6] = sq;
+  __syncthreads();
+  const float var = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / N;
+  const float inv = 1.0f / sqrtf(var + a.eps);
+  const T* gg = (const T*)a.gain;
+  const T* bb = (const T*)a.bias;
+  T* o = (T*)a.out_norm + (int64_t)m * N;
+  for (int n = tid; n < N; n += 256) {
+    float v = (ys[n] - mean) * inv * DT<T>::ld(gg + n);
+    if (bb) v += DT<T>::ld(bb + n);
+    DT<T>::st(o + n, v);
+  }
+}
+
+void launch_reduce_rows(int dtype, const ReduceArgs& a, hipStream_t st) {
+  size_t shm = (size_t)a.N * sizeof(float);
+  if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_reduce_rows<bf16s>, dim3(a.M), dim3(256), shm, st, a);
+  else hipLaunchKernelGGL(k_reduce_rows<float>, dim3(a.M), dim3(256), shm, st, a);
+}
+
+// RoPE + scatter of the fused q|k|v projection.  One thread per (row, head,
+// pair i) rotates elements (i, i + hd/2) by pos * theta^(-2i/hd); the angle
+// is formed and reduced in double precision.
+template <typename T>
+__global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
+  const int half = a.hd / 2;
+  const int heads = a.Hq + 2 * a.Hkv;
+  const int64_t total = (int64_t)a.M * heads * half;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int i = (int)(t % half);
+  const int h = (int)((t / half) % heads);
+  const int m = (int)(t / ((int64_t)half * heads));
+  const int N = heads * a.hd;
+  float x1 = 0.f, x2 = 0.f;
+  const int c1 = h * a.hd + i, c2 = c1 + half;
+  for (int s = 0; s < a.S; ++s) {
+    const float* row = a.P + ((int64_t)s * a.M + m) * N;
+    x1 += row[c1];
+    x2 += row[c2];
+  }
+  int pos;
+  if (a.pos) pos = a.pos[m];
+  else {  // packed context rows: position inside the request
+    int b = 0;
+    while (b + 1 < a.B && a.cu_n[b + 1] <= m) ++b;
+    pos = m - a.cu_n[b];
+  }
+  const bool is_v = h >= a.Hq + a.Hkv;
+  if (!is_v && a.theta > 0.f) {
+    double inv = exp2(-(2.0 * i / a.hd) * log2((double)a.theta));
+    double ang = (double)pos * inv;
+    ang -= 6.283185307179586 * rint(ang / 6.283185307179586);
+    float cs, sn;
+    sincosf((float)ang, &sn, &cs);
+    float y1 = x1 * cs - x2 * sn;
+    float y2 = x2 * cs + x1 * sn;
+    x1 = y1;
+    x2 = y2;
+  }
+  T* dst;
+  if (h < a.Hq) {
+    dst = (T*)a.q + ((int64_t)m * a.Hq + h) * a.hd;
+  } else {
+    const int kh = is_v ? h - a.Hq - a.Hkv : h - a.Hq;
+    const int64_t r = a.kv_idx ? (int64_t)a.kv_idx[m] : (int64_t)m;
+    dst = (T*)(is_v ? a.v : a.k) + (r * a.Hkv + kh) * a.hd;
+  }
+  DT<T>::st(dst + i, x1);
+  DT<T>::st(dst + i + half, x2);
+}
+
+void launch_epi_qkv(int dtype, const QkvArgs& a, hipStream_t st) {
+  const int64_t total = (int64_t)a.M * (a.Hq + 2 * a.Hkv) * (a.hd / 2);
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_qkv<bf16s>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_epi_qkv<float>, grid, dim3(256), 0, st, a);
+}
+
+// act = silu(gate) * up (SwiGLU) or gelu(up) (exact erf form)
+template <typename T>
+__global__ __launch_bounds__(256) void k_epi_act(ActArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)a.M * a.F) return;
+  const int m = (int)(t / a.F), j = (int)(t % a.F);
+  const int N = a.swiglu ? 2 * a.F : a.F;
+  float gsum = 0.f, usum = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const float* row = a.P + ((int64_t)s * a.M + m) * N;
+    if (a.swiglu) {
+      gsum += row[j];
+      usum += row[a.F + j];
+    } else {
+      usum += row[j];
+    }
+  }
+  float y;
+  if (a.swiglu) y = gsum / (1.0f + expf(-gsum)) * usum;
+  else y = 0.5f * usum * (1.0f + erff(usum * 0.70710678118654752f));
+  DT<T>::st((T*)a.out + t, y);
+}
+
+void launch_epi_act(int dtype, const ActArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(((int64_t)a.M * a.F + 255) / 256));
+  if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_act<bf16s>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_epi_act<float>, grid, dim3(256), 0, st, a);
+}
+
+}  // namespace eagle

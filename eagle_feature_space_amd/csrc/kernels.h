@@ -1,0 +1,164 @@
+// Kernel argument blocks and host launchers of the EAGLE HIP library.
+#pragma once
+#include "common.h"
+
+namespace eagle {
+
+// ---------------------------------------------------------------- GEMM
+// P[z][m][n] = sum_{k in split z} X[m][k] * W[n][k]
+// X row m = xs[0] for k < ksplit_x, else xs[1] (column k - ksplit_x);
+// W = rows [0, nseg1) of w[0], [nseg1, nseg2) of w[1], [nseg2, N) of w[2].
+struct GemmArgs {
+  RowSrc xs[2];
+  int ksplit_x;
+  int M, N, K;
+  const void* w[3];
+  int nseg1, nseg2;
+  float* P;
+  int kps;
+};
+struct GemmShape {
+  int MB, NB, mtiles, ntiles, S, kps;
+};
+GemmShape plan_gemm(int dtype, int M, int N, int K);
+void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st);
+
+// y = sum_s P + src1 + src2 ; out / out_scatter = y ; out_norm = Norm(y)
+struct ReduceArgs {
+  const float* P;
+  int S, M, N;
+  RowSrc src1, src2;
+  void* out;
+  RowSrc out_scatter;  // base/idx/stride used for writing (base non-null to enable)
+  void* out_norm;
+  const void* gain;
+  const void* bias;
+  int layer_norm;
+  float eps;
+};
+void launch_reduce_rows(int dtype, const ReduceArgs& a, hipStream_t st);
+
+struct QkvArgs {
+  const float* P;
+  int S, M, Hq, Hkv, hd;
+  float theta;
+  const int32_t* pos;   // per-row position, or null: packed context rows
+  const int32_t* cu_n;
+  int B;
+  void* q;              // [M][Hq][hd] (may be null when Hq == 0)
+  void* k;              // rows kv_idx[m] (or m) of [..][Hkv][hd]
+  void* v;
+  const int32_t* kv_idx;
+};
+void launch_epi_qkv(int dtype, const QkvArgs& a, hipStream_t st);
+
+struct ActArgs {
+  const float* P;
+  int S, M, F;
+  int swiglu;
+  void* out;            // [M][F]
+};
+void launch_epi_act(int dtype, const ActArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+// Rows of request b are m = b*W .. b*W+W-1; query row (m, head h) reads kv
+// head h / G.  Keys: the request's context [0, n_b) split into pieces of
+// `split_len`, plus (last split) up to 64 extra keys (tree slots) gated per
+// row by a 64-bit mask.
+struct AttnArgs {
+  const void* q;          // [M][Hq][hd]
+  int B, W, Hq, Hkv, hd;
+  const int32_t* n;       // [B]
+  const int32_t* cu_n;    // [B+1]
+  const void* k_ctx;      // [total][Hkv][hd]
+  const void* v_ctx;
+  const void* k_ex;       // [B*64][Hkv][hd]
+  const void* v_ex;
+  const uint64_t* mask;   // [M]
+  int split_len;          // multiple of 64
+  int nsplit;             // context splits (the extra split is index nsplit)
+  int rowgroups;          // ceil(W*G / 64)
+  float scale_log2;       // log2(e) / sqrt(hd)
+  float* part_o;          // [nsplit+1][M][Hq][hd]
+  float* part_ml;         // [nsplit+1][M][Hq][2] (running max in log2 units, sum)
+};
+void launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  int nparts, M, Hq, hd;
+  void* out;              // [M][Hq*hd]
+};
+void launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- LM head
+struct LmArgs {
+  RowSrc x;               // [M][d]
+  int M, K, V;
+  const void* w;          // [V][K]
+  int top_k;
+  float inv_temp;
+  float* logits;          // optional [M][V]
+  float* part_max;        // [ntiles][M]
+  float* part_sum;        // [ntiles][M]
+  int* part_id;           // [ntiles][M][top_k]
+  float* part_val;        // [ntiles][M][top_k]
+};
+struct LmShape {
+  int MB, mtiles, ntiles, cols;
+};
+LmShape plan_lmhead(int dtype, int M, int V);
+void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st);
+
+struct MergeArgs {
+  const float* part_max;
+  const float* part_sum;
+  const int* part_id;
+  const float* part_val;
+  int ntiles, M, top_k;
+  float inv_temp;
+  int* topk_id;           // [M][top_k]
+  float* topk_conf;       // [M][top_k]
+  float* lse;             // [M]
+  int vocab;              // ids are clamped to [0, vocab)
+};
+void launch_topk_merge(const MergeArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- tree
+struct TreeDev {          // device pointers into eagle_tree.state
+  int32_t *pool_tok, *pool_parent, *pool_depth, *pool_slot;
+  float *pool_conf, *pool_value;
+  int32_t *pool_count, *slot_count, *root_pos;
+  uint64_t* slot_mask;
+  int32_t *row_node, *row_tok, *row_pos, *row_slot, *row_pidx;
+  uint64_t* row_mask;
+  int32_t* topk_id;
+  float* topk_conf;
+  float* lse;
+  int32_t *f_node, *f_tok, *f_parent, *f_depth, *f_pos;
+  uint64_t* f_mask;
+  int32_t* f_count;
+  int32_t* choice;
+  int pool_cap, max_rows, positions;
+};
+
+struct StaticPlan {       // children created by one static / chain step
+  int nchild;             // per request
+  int nnext;              // rows of the next step per request
+  uint8_t row[64], rank[64], expand[64];
+};
+
+void launch_tree_init(const TreeDev& t, int B, int eagle3, int vocab, const int32_t* root_tok,
+                      const int32_t* n, const int32_t* cu_n, hipStream_t st);
+void launch_tree_expand(const TreeDev& t, int B, int kind, int step, int gamma,
+                        int rows, int top_k, int top_m, int final_step,
+                        const StaticPlan& plan, hipStream_t st);
+void launch_verify(const TreeDev& t, int B, const void* logits, int positions,
+                   int vocab, int dtype, int gamma, int32_t* accept_len,
+                   int32_t* accept_path, int32_t* out_tokens, hipStream_t st);
+void launch_tree_rows_final(const TreeDev& t, int B, int32_t* tok_idx,
+                            int32_t* kv_idx, int32_t* pos, uint64_t* mask,
+                            hipStream_t st);
+
+}  // namespace eagle

@@ -1,0 +1,262 @@
+// Frozen LM head with a fused softmax / top-k epilogue ("The recurrence,
+// written out": the next token comes from softmax(LM_head(f')); "EAGLE-2":
+// the confidences c are the softmax probabilities of the drafted tokens).
+//
+// logits = X W_LM^T with W_LM [V][d] is the largest byte mover of a draft step
+// (|V| = 128256 rows of d bf16), and the logits themselves never need to
+// reach HBM: each workgroup streams 256 vocabulary rows once (same register
+// blocking as the weight-streaming GEMM), keeps its 256 x M logit tile on
+// chip and emits, per row, the tile maximum, the tile sum of
+// exp(s * (logit - max)) and the tile's top-k (logit desc, id asc).  A second
+// kernel merges the ~|V|/256 tile partials of every row into the log-partition,
+// the top-k ids and their confidences softmax(s * logits)[id].
+#include "kernels.h"
+
+namespace eagle {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int MB>
+__global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
+  constexpr int NB = 4;
+  constexpr int VEC = DT<T>::VEC;
+  constexpr int KC = 32 * VEC;
+  constexpr int MT = 16 * MB;
+  constexpr int ROWB = KC * (int)sizeof(T) + 16;
+  constexpr int XBYTES = MT * ROWB;
+  constexpr int TROW = 256 + 4;                      // fp32 logit tile row (padded)
+  constexpr int TBYTES = 16 * TROW * 4;
+  constexpr int LBYTES = XBYTES > TBYTES ? XBYTES : TBYTES;
+  __shared__ __attribute__((aligned(16))) char lds[LBYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int tile = blockIdx.x;
+  const int n_base = tile * 256 + wave * 64;
+  const int m0 = blockIdx.y * MT;
+
+  const T* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = min(n_base + nb * 16 + c, a.V - 1);
+    wrow[nb] = (const T*)a.w + (int64_t)n * a.K;
+  }
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < a.K; k0 += KC) {
+    const int L = min(KC, a.K - k0);
+    const int U = L / (4 * VEC);
+    u32x4 wv[NB][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        if (u < U) wv[nb][u] = ld16(wrow[nb] + k0 + u * 4 * VEC + g * VEC);
+    __syncthreads();
+    const int pieces = L / VEC;
+    for (int p = tid; p < MT * pieces; p += 256) {
+      const int r = p / pieces, j = p - r * pieces;
+      const int m = m0 + r;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (m < a.M) v = ld16(row_ptr<T>(a.x, m) + k0 + j * VEC);
+      st16(lds + r * ROWB + j * 16, v);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < U) {
+        u32x4 xf[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xf[mb] = ld16(lds + (mb * 16 + c) * ROWB + (u * 4 * VEC + g * VEC) * (int)sizeof(T));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = DT<T>::mma(wv[nb][u], xf[mb], acc[nb][mb]);
+      }
+    }
+  }
+
+  // optional raw logits (parity checks)
+  if (a.logits) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + mb * 16 + c;
+        const int n = n_base + nb * 16 + 4 * g;
+        if (m >= a.M) continue;
+        float* dst = a.logits + (int64_t)m * a.V + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < a.V) dst[i] = acc[nb][mb][i];
+      }
+  }
+
+  // epilogue, one 16-row block at a time through LDS
+  float* tl = reinterpret_cast<float*>(lds);
+  const float sl = a.inv_temp * kLog2e;
+  const int ntiles = gridDim.x;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wave * 64 + nb * 16 + 4 * g;
+      f32x4 v = acc[nb][mb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tile * 256 + col + i >= a.V) v[i] = -INFINITY;
+      *reinterpret_cast<f32x4*>(tl + c * TROW + col) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = wave * 4 + rr;
+      const int m = m0 + mb * 16 + r;
+      if (m >= a.M) continue;
+      float v[4];
+      int id[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = tl[r * TROW + lane + 64 * j];
+        id[j] = tile * 256 + lane + 64 * j;
+      }
+      float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      mx = wave_max(mx);
+      float se = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) se += exp2f((v[j] - mx) * sl);
+      se = wave_sum(se);
+      const int64_t pi = (int64_t)tile * a.M + m;
+      if (lane == 0) {
+        a.part_max[pi] = mx;
+        a.part_sum[pi] = se;
+      }
+      // top-k: round k takes the best entry strictly worse than round k-1's
+      float pv = INFINITY;
+      int pid = -1;
+      for (int k = 0; k < a.top_k; ++k) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool below = better(pv, pid, v[j], id[j]);
+          if (below && better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
+        }
+        wave_best(bv, bi);
+        if (lane == 0) {
+          a.part_val[pi * a.top_k + k] = bv;
+          a.part_id[pi * a.top_k + k] = bi;
+        }
+        pv = bv;
+        pid = bi;
+      }
+    }
+  }
+  (void)ntiles;
+}
+
+LmShape plan_lmhead(int dtype, int M, int V) {
+  (void)dtype;
+  LmShape s;
+  s.MB = M >= 80 ? 5 : (M + 15) / 16;
+  if (s.MB < 1) s.MB = 1;
+  s.mtiles = (M + 16 * s.MB - 1) / (16 * s.MB);
+  s.cols = 256;
+  s.ntiles = (V + 255) / 256;
+  return s;
+}
+
+template <typename T>
+static void launch_lm_t(const LmArgs& a, const LmShape& s, hipStream_t st) {
+  dim3 grid(s.ntiles, s.mtiles), block(256);
+  switch (s.MB) {
+    case 1: hipLaunchKernelGGL((k_lmhead<T, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_lmhead<T, 2>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_lmhead<T, 3>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_lmhead<T, 4>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_lmhead<T, 5>), grid, block, 0, st, a); break;
+  }
+}
+
+void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st) {
+  if (dtype == EAGLE_BF16) launch_lm_t<bf16s>(a, s, st);
+  else launch_lm_t<float>(a, s, st);
+}
+
+// ---------------------------------------------------------------- merge
+__device__ __forceinline__ void block_best(float& v, int& i, float* sv, int* si) {
+  wave_best(v, i);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { sv[w] = v; si[w] = i; }
+  __syncthreads();
+  v = sv[0];
+  i = si[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k)
+    if (better(sv[k], si[k], v, i)) { v = sv[k]; i = si[k]; }
+}
+
+__global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float sl = a.inv_temp * kLog2e;
+  // log-partition of s * logits
+  float mx = -INFINITY;
+  for (int t = tid; t < a.ntiles; t += 256) mx = fmaxf(mx, a.part_max[(int64_t)t * a.M + m]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float z = 0.f;
+  for (int t = tid; t < a.ntiles; t += 256) {
+    const int64_t i = (int64_t)t * a.M + m;
+    z += a.part_sum[i] * exp2f((a.part_max[i] - mx) * sl);
+  }
+  z = wave_sum(z);
+  if ((tid & 63) == 0) red[tid >> 6] = z;
+  __syncthreads();
+  z = red[0] + red[1] + red[2] + red[3];
+  const float lse = a.inv_temp * mx + logf(z);
+  // top-k over the tiles' candidates
+  const int ncand = a.ntiles * a.top_k;
+  float pv = INFINITY;
+  int pid = -1;
+  for (int k = 0; k < a.top_k; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int q = tid; q < ncand; q += 256) {
+      const int t = q / a.top_k, j = q - t * a.top_k;
+      const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
+      const float v = a.part_val[i];
+      const int id = a.part_id[i];
+      if (better(pv, pid, v, id) && better(v, id, bv, bi)) { bv = v; bi = id; }
+    }
+    block_best(bv, bi, sv, si);
+    if (tid == 0) {
+      // a NaN row leaves no candidate: keep ids inside the vocabulary
+      a.topk_id[(int64_t)m * a.top_k + k] = bi < 0 ? 0 : (bi >= a.vocab ? a.vocab - 1 : bi);
+      a.topk_conf[(int64_t)m * a.top_k + k] = expf(a.inv_temp * bv - lse);
+    }
+    pv = bv;
+    pid = bi;
+  }
+  if (tid == 0) a.lse[m] = lse;
+}
+
+void launch_topk_merge(const MergeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_topk_merge, dim3(a.M), dim3(256), 0, st, a);
+}
+
+}  // namespace eagle

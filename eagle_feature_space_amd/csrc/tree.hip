@@ -1,0 +1,321 @@
+// Draft-tree bookkeeping and greedy verification.
+//
+//   init    node 0 = anchor token, value 1; the step-0 rows are the roots.
+//   expand  ("EAGLE-2: expand and rerank") children of every row of the step
+//           get value = value(parent) * conf; the next frontier is chosen
+//           (chain: the child; static: the template's expanded children;
+//           dynamic: the top_k newest nodes by (value desc, index asc)), each
+//           frontier node gets a slot and the 64-bit mask of its
+//           ancestor-or-self slots.  The last step reranks (dynamic: top_m
+//           of the pool by (value desc, depth asc, index asc)) and writes the
+//           verify tree in creation order with ancestor-or-self masks over
+//           positions and position ids root_pos + depth ("Tree attention in
+//           one verification pass").
+//   verify  (explainer steps 3-4) target choice per position = argmax of its
+//           logits, lowest id on ties; walk from the root along children whose
+//           token equals the choice; emit the accepted tokens and the choice at
+//           the deepest accepted node.
+// One workgroup serves one request; the pool holds at most 1024 nodes.
+#include "kernels.h"
+
+namespace eagle {
+
+constexpr int kPoolMax = 1024;
+
+__global__ void k_tree_init(TreeDev t, int B, int eagle3, int vocab, const int32_t* root_tok,
+                            const int32_t* n, const int32_t* cu_n) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int P = t.pool_cap;
+  const int tok = min(max(root_tok[b], 0), vocab - 1);
+  t.pool_tok[b * P] = tok;
+  t.pool_parent[b * P] = -1;
+  t.pool_depth[b * P] = 0;
+  t.pool_slot[b * P] = 0;
+  t.pool_conf[b * P] = 1.0f;
+  t.pool_value[b * P] = 1.0f;
+  t.pool_count[b] = 1;
+  t.slot_count[b] = 1;
+  const int rp = eagle3 ? n[b] - 1 : n[b];
+  t.root_pos[b] = rp;
+  const uint64_t m0 = eagle3 ? 0ull : 1ull;
+  t.slot_mask[b * kSlots] = m0;
+  t.row_node[b] = 0;
+  t.row_tok[b] = tok;
+  t.row_pos[b] = rp;
+  t.row_slot[b] = b * kSlots;
+  t.row_pidx[b] = eagle3 ? max(cu_n[b + 1] - 1, 0) : b;
+  t.row_mask[b] = m0;
+  t.f_count[b] = 0;
+}
+
+void launch_tree_init(const TreeDev& t, int B, int eagle3, int vocab, const int32_t* root_tok,
+                      const int32_t* n, const int32_t* cu_n, hipStream_t st) {
+  hipLaunchKernelGGL(k_tree_init, dim3((B + 63) / 64), dim3(64), 0, st, t, B, eagle3, vocab,
+                     root_tok, n, cu_n);
+}
+
+// key order: value desc, depth asc, index asc
+__device__ __forceinline__ bool before(float va, int da, int ia, float vb, int db, int ib) {
+  if (va != vb) return va > vb;
+  if (da != db) return da < db;
+  return ia < ib;
+}
+
+__global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, int kind, int step, int gamma,
+                                                     int W, int top_k, int top_m, int final_step,
+                                                     StaticPlan plan) {
+  __shared__ float sval[kPoolMax];
+  __shared__ int sdep[kPoolMax];
+  __shared__ int spar[kPoolMax];
+  __shared__ int spos[kPoolMax];
+  __shared__ int skeep[kPoolMax];
+  __shared__ int snext[256];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int P = t.pool_cap;
+  const int p0 = t.pool_count[b];
+  const int nchild = kind == EAGLE_TREE_DYNAMIC ? W * top_k : plan.nchild;
+  const int rp = t.root_pos[b];
+  const int64_t pb = (int64_t)b * P;
+  // a call out of order (pool or slots already full) must not write past them
+  if (p0 < 1 || p0 + nchild > P) return;
+  if (!final_step && t.slot_count[b] + (kind == EAGLE_TREE_DYNAMIC ? min(top_k, nchild) : plan.nnext) > kSlots)
+    return;
+
+  // 1. append the children of this step's rows
+  for (int cidx = tid; cidx < nchild; cidx += 256) {
+    int row, rank;
+    if (kind == EAGLE_TREE_DYNAMIC) { row = cidx / top_k; rank = cidx % top_k; }
+    else { row = plan.row[cidx]; rank = plan.rank[cidx]; }
+    const int r = b * W + row;
+    const int parent = t.row_node[r];
+    const float conf = t.topk_conf[(int64_t)r * top_k + rank];
+    const int node = p0 + cidx;
+    t.pool_tok[pb + node] = t.topk_id[(int64_t)r * top_k + rank];
+    t.pool_parent[pb + node] = parent;
+    t.pool_depth[pb + node] = t.pool_depth[pb + parent] + 1;
+    t.pool_slot[pb + node] = -1;
+    t.pool_conf[pb + node] = conf;
+    t.pool_value[pb + node] = __fmul_rn(t.pool_value[pb + parent], conf);
+  }
+  __syncthreads();
+  __threadfence_block();
+  const int pn = p0 + nchild;
+
+  if (!final_step) {
+    // 2. next frontier
+    int nnext;
+    if (kind == EAGLE_TREE_DYNAMIC) {
+      nnext = min(top_k, nchild);
+      for (int cidx = tid; cidx < nchild; cidx += 256) {
+        const int u = p0 + cidx;
+        const float vu = t.pool_value[pb + u];
+        int rank = 0;
+        for (int j = 0; j < nchild; ++j) {
+          const int v = p0 + j;
+          const float vv = t.pool_value[pb + v];
+          if (vv > vu || (vv == vu && v < u)) ++rank;
+        }
+        if (rank < nnext) snext[rank] = u;
+      }
+    } else {
+      nnext = plan.nnext;
+      if (tid == 0) {
+        int k = 0;
+        for (int cidx = 0; cidx < nchild; ++cidx)
+          if (plan.expand[cidx]) snext[k++] = p0 + cidx;
+      }
+    }
+    __syncthreads();
+    const int s0 = t.slot_count[b];
+    if (tid < nnext) {
+      const int u = snext[tid];
+      const int slot = s0 + tid;
+      const int parent = t.pool_parent[pb + u];
+      const int pslot = max(t.pool_slot[pb + parent], 0);
+      const uint64_t msk = t.slot_mask[b * kSlots + pslot] | (1ull << slot);
+      t.pool_slot[pb + u] = slot;
+      t.slot_mask[b * kSlots + slot] = msk;
+      const int r = b * nnext + tid;
+      t.row_node[r] = u;
+      t.row_tok[r] = t.pool_tok[pb + u];
+      t.row_pos[r] = rp + t.pool_depth[pb + u];
+      t.row_slot[r] = b * kSlots + slot;
+      t.row_pidx[r] = b * kSlots + pslot;
+      t.row_mask[r] = msk;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      t.pool_count[b] = pn;
+      t.slot_count[b] = s0 + nnext;
+    }
+    return;
+  }
+
+  // 3. rerank and verify tree
+  for (int u = tid; u < pn; u += 256) {
+    sval[u] = t.pool_value[pb + u];
+    sdep[u] = t.pool_depth[pb + u];
+    spar[u] = t.pool_parent[pb + u];
+  }
+  __syncthreads();
+  for (int u = tid; u < pn; u += 256) {
+    int keep;
+    if (u == 0) keep = 1;
+    else if (kind != EAGLE_TREE_DYNAMIC) keep = 1;
+    else {
+      int rank = 0;
+      for (int v = 1; v < pn; ++v)
+        if (before(sval[v], sdep[v], v, sval[u], sdep[u], u)) ++rank;
+      keep = rank < top_m;
+    }
+    skeep[u] = keep;
+  }
+  __syncthreads();
+  if (tid == 0) {   // positions in creation order
+    int k = 0;
+    for (int u = 0; u < pn; ++u) spos[u] = skeep[u] ? k++ : -1;
+    t.f_count[b] = k;
+    t.pool_count[b] = pn;
+  }
+  __syncthreads();
+  for (int u = tid; u < pn; u += 256) {
+    const int p = spos[u];
+    if (p < 0) continue;
+    const int fb = b * kMaxPos;
+    uint64_t msk = 0;
+    // kept sets are ancestor-closed (confidences are <= 1, so values never
+    // grow along a path and a parent ranks before its child)
+    for (int w = u; w >= 0; w = spar[w])
+      if (spos[w] >= 0) msk |= 1ull << spos[w];
+    t.f_node[fb + p] = u;
+    t.f_tok[fb + p] = t.pool_tok[pb + u];
+    t.f_parent[fb + p] = u == 0 ? -1 : spos[spar[u]];
+    t.f_depth[fb + p] = sdep[u];
+    t.f_pos[fb + p] = rp + sdep[u];
+    t.f_mask[fb + p] = msk;
+  }
+}
+
+void launch_tree_expand(const TreeDev& t, int B, int kind, int step, int gamma, int rows,
+                        int top_k, int top_m, int final_step, const StaticPlan& plan,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(k_tree_expand, dim3(B), dim3(256), 0, st, t, kind, step, gamma, rows, top_k,
+                     top_m, final_step, plan);
+}
+
+// ---------------------------------------------------------------- verify
+template <typename T>
+__device__ __forceinline__ void argmax_row(const T* row, int V, float& bv, int& bi) {
+  for (int j = threadIdx.x; j < V; j += 256) {
+    const float v = DT<T>::ld(row + j);
+    if (better(v, j, bv, bi)) { bv = v; bi = j; }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_verify_argmax(TreeDev t, const T* logits, int positions,
+                                                       int V) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int u = blockIdx.x, b = blockIdx.y;
+  if (u >= t.f_count[b]) return;
+  const T* row = logits + ((int64_t)b * positions + u) * V;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  constexpr int VEC = DT<T>::VEC;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+  if ((addr & 15) == 0) {
+    const int nvec = V / VEC;
+    for (int q = threadIdx.x; q < nvec; q += 256) {
+      const u32x4 x = ld16(row + q * VEC);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float v = DT<T>::elem(x, e);
+        const int j = q * VEC + e;
+        if (better(v, j, bv, bi)) { bv = v; bi = j; }
+      }
+    }
+    for (int j = nvec * VEC + threadIdx.x; j < V; j += 256) {
+      const float v = DT<T>::ld(row + j);
+      if (better(v, j, bv, bi)) { bv = v; bi = j; }
+    }
+  } else {
+    argmax_row(row, V, bv, bi);
+  }
+  wave_best(bv, bi);
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v0 = sv[0];
+    int i0 = si[0];
+    for (int k = 1; k < 4; ++k)
+      if (better(sv[k], si[k], v0, i0)) { v0 = sv[k]; i0 = si[k]; }
+    t.choice[b * kMaxPos + u] = i0;
+  }
+}
+
+__global__ void k_verify_walk(TreeDev t, int B, int gamma, int32_t* accept_len,
+                              int32_t* accept_path, int32_t* out_tokens) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int T = t.f_count[b];
+  const int fb = b * kMaxPos;
+  int32_t* path = accept_path + (int64_t)b * (gamma + 1);
+  int32_t* out = out_tokens + (int64_t)b * (gamma + 1);
+  for (int i = 0; i <= gamma; ++i) { path[i] = -1; out[i] = -1; }
+  int u = 0, acc = 0;
+  path[0] = 0;
+  while (true) {
+    const int choice = t.choice[fb + u];
+    int nxt = -1;
+    for (int v = u + 1; v < T; ++v)
+      if (t.f_parent[fb + v] == u && t.f_tok[fb + v] == choice) { nxt = v; break; }
+    if (nxt < 0 || acc >= gamma) {
+      out[acc] = choice;
+      break;
+    }
+    out[acc] = choice;
+    ++acc;
+    path[acc] = nxt;
+    u = nxt;
+  }
+  accept_len[b] = acc;
+}
+
+void launch_verify(const TreeDev& t, int B, const void* logits, int positions, int vocab,
+                   int dtype, int gamma, int32_t* accept_len, int32_t* accept_path,
+                   int32_t* out_tokens, hipStream_t st) {
+  dim3 grid(kMaxPos, B);
+  if (dtype == EAGLE_BF16)
+    hipLaunchKernelGGL(k_verify_argmax<bf16s>, grid, dim3(256), 0, st, t, (const bf16s*)logits,
+                       positions, vocab);
+  else
+    hipLaunchKernelGGL(k_verify_argmax<float>, grid, dim3(256), 0, st, t, (const float*)logits,
+                       positions, vocab);
+  hipLaunchKernelGGL(k_verify_walk, dim3((B + 63) / 64), dim3(64), 0, st, t, B, gamma, accept_len,
+                     accept_path, out_tokens);
+}
+
+// dense rows of the verify tree (row m = b * positions + u)
+__global__ void k_tree_rows_final(TreeDev t, int B, int32_t* tok_idx, int32_t* kv_idx,
+                                  int32_t* pos, uint64_t* mask) {
+  const int u = threadIdx.x, b = blockIdx.x;
+  const int T = t.positions;
+  if (u >= T) return;
+  const int m = b * T + u;
+  const int fb = b * kMaxPos + u;
+  const bool live = u < t.f_count[b];
+  tok_idx[m] = live ? t.f_tok[fb] : 0;
+  kv_idx[m] = b * kSlots + u;
+  pos[m] = live ? t.f_pos[fb] : 0;
+  mask[m] = live ? t.f_mask[fb] : 0ull;
+}
+
+void launch_tree_rows_final(const TreeDev& t, int B, int32_t* tok_idx, int32_t* kv_idx,
+                            int32_t* pos, uint64_t* mask, hipStream_t st) {
+  hipLaunchKernelGGL(k_tree_rows_final, dim3(B), dim3(64), 0, st, t, B, tok_idx, kv_idx, pos, mask);
+}
+
+}  // namespace eagle

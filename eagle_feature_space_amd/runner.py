@@ -1,0 +1,198 @@
+"""Device-side setup of one draft-and-verify round through the C-ABI.
+
+Uploads a head's weights and a round's inputs into torch device tensors, fills
+the C structs and calls the library entry points in order:
+  eagle_tree_init, then per step eagle_draft_step + eagle_tree_expand_rerank,
+  optionally eagle_tree_attend, then eagle_tree_verify.
+All arithmetic of the round happens in libeagle's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import binding as E
+from .configs import DTYPE_BF16, MODE_EAGLE3, TREE_STATIC, RoundCfg
+
+
+def to_dev(a: np.ndarray, device) -> torch.Tensor:
+    """numpy (bf16 bits as uint16, float32 or int32) -> device tensor."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+@dataclass
+class StepSnapshot:
+    rows: Dict[str, np.ndarray]        # this step's row descriptors
+    topk_id: np.ndarray
+    topk_conf: np.ndarray
+    lse: np.ndarray
+    logits: Optional[np.ndarray] = None
+    feat: Optional[np.ndarray] = None
+    feat_slot: Optional[np.ndarray] = None   # after the step (fp32)
+    k_slot: Optional[np.ndarray] = None
+    v_slot: Optional[np.ndarray] = None
+
+
+class GpuRound:
+    def __init__(self, cfg: RoundCfg, weights: Dict[str, np.ndarray], inputs, device="cuda:0"):
+        self.cfg = cfg
+        h = cfg.head
+        self.dev = torch.device(device)
+        self.dt = torch.bfloat16 if h.dtype == DTYPE_BF16 else torch.float32
+        self.w = {k: to_dev(v, self.dev) for k, v in weights.items()}
+        hd = E.eagle_head()
+        for f in ("d", "vocab", "ffn", "act", "norm", "dtype", "mode", "eps", "rope_theta"):
+            setattr(hd, f, getattr(h, f))
+        hd.n_q_heads, hd.n_kv_heads, hd.head_dim = h.n_q, h.n_kv, h.head_dim
+        for k, t in self.w.items():
+            setattr(hd, k, t.data_ptr())
+        self.head = hd
+
+        B = cfg.B
+        self.n = to_dev(inputs.n.astype(np.int32), self.dev)
+        self.cu_n = to_dev(inputs.cu_n.astype(np.int32), self.dev)
+        total = int(inputs.cu_n[-1])
+        if h.mode == MODE_EAGLE3:
+            self.k_ctx = torch.zeros((max(total, 1), h.n_kv, h.head_dim), dtype=self.dt, device=self.dev)
+            self.v_ctx = torch.zeros_like(self.k_ctx)
+            self.lmh = to_dev(inputs.lmh, self.dev)
+            self.ctx_tokens = to_dev(inputs.ctx_tokens.astype(np.int32), self.dev)
+            self.f_root = None
+        else:
+            self.k_ctx = to_dev(inputs.k_ctx, self.dev) if total else None
+            self.v_ctx = to_dev(inputs.v_ctx, self.dev) if total else None
+            self.f_root = to_dev(inputs.f_root, self.dev)
+            self.lmh = self.ctx_tokens = None
+        self.k_slot = torch.zeros((B * E.MAX_SLOTS, h.n_kv, h.head_dim), dtype=self.dt, device=self.dev)
+        self.v_slot = torch.zeros_like(self.k_slot)
+        self.feat_slot = torch.zeros((B * E.MAX_SLOTS, h.d), dtype=self.dt, device=self.dev)
+        kv = E.eagle_kv()
+        kv.B, kv.max_n, kv.total_n = B, int(inputs.n.max()), total
+        kv.n, kv.cu_n = self.n.data_ptr(), self.cu_n.data_ptr()
+        kv.k_ctx = self.k_ctx.data_ptr() if self.k_ctx is not None else None
+        kv.v_ctx = self.v_ctx.data_ptr() if self.v_ctx is not None else None
+        kv.k_slot, kv.v_slot = self.k_slot.data_ptr(), self.v_slot.data_ptr()
+        kv.feat_slot = self.feat_slot.data_ptr()
+        self.kv = kv
+
+        tr = E.eagle_tree()
+        tr.kind, tr.B, tr.gamma, tr.top_k, tr.top_m = cfg.tree, B, cfg.gamma, cfg.top_k, cfg.top_m
+        self._tmpl = (ctypes.c_int32 * max(1, len(cfg.template)))(*cfg.template)
+        tr.n_template = len(cfg.template) if cfg.tree == TREE_STATIC else 0
+        tr.template_parent = ctypes.cast(self._tmpl, ctypes.POINTER(ctypes.c_int32))
+        tr.inv_temp = cfg.inv_temp
+        nbytes = E.eagle_tree_state_bytes(tr)
+        if nbytes == 0:
+            raise E.EagleError(E.EAGLE_EINVAL, "eagle_tree_state_bytes")
+        self.state = torch.zeros(nbytes, dtype=torch.uint8, device=self.dev)
+        tr.state, tr.state_bytes = self.state.data_ptr(), nbytes
+        self.tree = tr
+        self.layout = E.eagle_tree_layout_of(tr)
+        wsb = E.eagle_workspace_bytes(hd, kv, tr)
+        if wsb == 0:
+            raise E.EagleError(E.EAGLE_EINVAL, "eagle_workspace_bytes")
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
+        self.root_tok = to_dev(inputs.t_root.astype(np.int32), self.dev)
+        self.rows = [E.eagle_step_rows(tr, s) for s in range(cfg.gamma)]
+        P = self.layout.positions
+        self.accept_len = torch.zeros(B, dtype=torch.int32, device=self.dev)
+        self.accept_path = torch.zeros((B, cfg.gamma + 1), dtype=torch.int32, device=self.dev)
+        self.out_tokens = torch.zeros((B, cfg.gamma + 1), dtype=torch.int32, device=self.dev)
+        self.attn_out = None
+
+    # ------------------------------------------------------------ state views
+    def view(self, name, dtype, shape):
+        off = getattr(self.layout, name)
+        nb = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        return self.state[off:off + nb].view(dtype).view(*shape)
+
+    def rows_view(self, W):
+        B = self.cfg.B
+        M = B * W
+        return dict(node=self.view("row_node", torch.int32, (M,)),
+                    tok=self.view("row_tok", torch.int32, (M,)),
+                    pos=self.view("row_pos", torch.int32, (M,)),
+                    slot=self.view("row_slot", torch.int32, (M,)),
+                    pidx=self.view("row_pidx", torch.int32, (M,)),
+                    mask=self.view("row_mask", torch.int64, (M,)))
+
+    def final_view(self):
+        B = self.cfg.B
+        fv = {k: self.view("f_" + k, torch.int32, (B, E.MAX_POSITIONS))
+              for k in ("node", "tok", "parent", "depth", "pos")}
+        fv["mask"] = self.view("f_mask", torch.int64, (B, E.MAX_POSITIONS))
+        fv["count"] = self.view("f_count", torch.int32, (B,))
+        return fv
+
+    def pool_view(self):
+        B, P = self.cfg.B, self.layout.pool_cap
+        pv = {k: self.view("pool_" + k, torch.int32, (B, P)) for k in ("tok", "parent", "depth", "slot")}
+        pv["conf"] = self.view("pool_conf", torch.float32, (B, P))
+        pv["value"] = self.view("pool_value", torch.float32, (B, P))
+        pv["count"] = self.view("pool_count", torch.int32, (B,))
+        return pv
+
+    # ------------------------------------------------------------ round
+    def init(self, stream=None):
+        E.eagle_tree_init(self.head, self.kv, self.tree, self.root_tok, stream)
+
+    def step(self, s, logits_out=None, feat_out=None, stream=None):
+        E.eagle_draft_step(self.head, self.kv, self.tree, s, f_root=self.f_root, lmh=self.lmh,
+                           ctx_tokens=self.ctx_tokens, logits_out=logits_out, feat_out=feat_out,
+                           ws=self.ws, stream=stream)
+
+    def expand(self, s, stream=None):
+        E.eagle_tree_expand_rerank(self.tree, s, stream)
+
+    def attend(self, stream=None):
+        h = self.cfg.head
+        if self.attn_out is None:
+            self.attn_out = torch.zeros((self.cfg.B * self.layout.positions, h.q_dim),
+                                        dtype=self.dt, device=self.dev)
+        E.eagle_tree_attend(self.head, self.kv, self.tree, self.attn_out, self.ws, stream=stream)
+
+    def verify(self, target: torch.Tensor, stream=None):
+        dtype = 0 if target.dtype == torch.bfloat16 else 1
+        E.eagle_tree_verify(self.tree, target, target.shape[1], target.shape[2], dtype,
+                            self.accept_len, self.accept_path, self.out_tokens, stream)
+
+    def run(self, target=None, snapshots=False, attend=False) -> List[StepSnapshot]:
+        """One round; with snapshots=True the state after every draft step is
+        copied to the host (for parity checks; synchronises)."""
+        cfg = self.cfg
+        snaps = []
+        self.init()
+        for s in range(cfg.gamma):
+            M = cfg.B * self.rows[s]
+            logits = feat = None
+            if snapshots:
+                rows = {k: v.cpu().numpy() for k, v in self.rows_view(self.rows[s]).items()}
+                logits = torch.empty((M, cfg.head.vocab), dtype=torch.float32, device=self.dev)
+                feat = torch.empty((M, cfg.head.d), dtype=self.dt, device=self.dev)
+            self.step(s, logits_out=logits, feat_out=feat)
+            if snapshots:
+                K = cfg.top_k
+                snaps.append(StepSnapshot(
+                    rows=rows,
+                    topk_id=self.view("topk_id", torch.int32, (M, K)).cpu().numpy(),
+                    topk_conf=self.view("topk_conf", torch.float32, (M, K)).cpu().numpy(),
+                    lse=self.view("lse", torch.float32, (M,)).cpu().numpy(),
+                    logits=logits.cpu().numpy(), feat=to_f32(feat),
+                    feat_slot=to_f32(self.feat_slot), k_slot=to_f32(self.k_slot),
+                    v_slot=to_f32(self.v_slot)))
+            self.expand(s)
+        if attend:
+            self.attend()
+        if target is not None:
+            self.verify(target)
+        return snaps

@@ -1,0 +1,262 @@
+/*
+ * eagle.h -- C-ABI of the MI355X (gfx950) EAGLE draft-and-verify library.
+ *
+ * One draft-and-verify round of EAGLE speculative decoding:
+ *
+ *   eagle_tree_init           root of every request's draft tree
+ *   eagle_draft_step  x gamma one pass of the draft head over the rows of a step
+ *   eagle_tree_expand_rerank  x gamma grow the tree from that step's top-k; the
+ *                             last call also reranks and builds the verify tree
+ *   eagle_tree_attend         (optional) tree-masked attention over the verify tree
+ *   eagle_tree_verify         accept the longest root path matching the target
+ *
+ * The method is the one described on the pages
+ *   "transformer_math / tm_eagle_deep" (aicassindra.com), sections "The
+ *     recurrence, written out", "What is actually in the head", "EAGLE-2: expand
+ *     and rerank" and "Tree attention in one verification pass";
+ *   "Speculative Decoding Deep Dive III: EAGLE, DFlash" (zackli.ai), sections
+ *     "EAGLE-1", "EAGLE-2" and "EAGLE-3";
+ *   "EAGLE / DFlash / DSpark" explainer (kaushalya.io), "How speculative
+ *     decoding works" steps 3-4;
+ *   "EAGLE: Drafting in Feature Space" (stable-lab.github.io), sections "The
+ *     Mechanism" and "Drafting a Tree, Not a Chain".
+ *
+ * Conventions (all entry points):
+ *   - Every pointer named "device" is a device (HBM) address owned by the
+ *     caller.  The library never allocates or frees device memory and keeps no
+ *     pointer after a call returns.  Scratch space comes from the caller's
+ *     workspace (eagle_workspace_bytes) and tree state (eagle_tree_state_bytes).
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *     enqueue work on it and return; nothing synchronises inside the library.
+ *   - Matrices are row-major [out][in] (the input dimension contiguous), in the
+ *     head's dtype (bf16 or fp32).  Activations between kernels are stored in
+ *     that dtype; accumulation, softmax and confidences are fp32.
+ *   - Every argument is validated on the host before anything is launched; on
+ *     any error nothing is enqueued.  A failed launch returns EAGLE_EHIP.
+ *   - Calls that share a workspace or tree state must be ordered on one stream.
+ */
+#ifndef EAGLE_H
+#define EAGLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EAGLE_OK = 0,
+  EAGLE_EINVAL = -1,       /* null pointer, bad size or step out of range   */
+  EAGLE_EUNSUPPORTED = -2, /* shape outside what the kernels implement      */
+  EAGLE_ECAPACITY = -3,    /* workspace / state / tree larger than allowed  */
+  EAGLE_EHIP = -4          /* a HIP launch or runtime call failed           */
+} eagle_status;
+
+enum { EAGLE_BF16 = 0, EAGLE_F32 = 1 };
+enum { EAGLE_ACT_SWIGLU = 0, EAGLE_ACT_GELU = 1 };
+enum { EAGLE_NORM_RMS = 0, EAGLE_NORM_LAYER = 1 };
+enum { EAGLE_MODE_1 = 1, EAGLE_MODE_3 = 3 };
+enum { EAGLE_TREE_CHAIN = 0, EAGLE_TREE_STATIC = 1, EAGLE_TREE_DYNAMIC = 2 };
+
+#define EAGLE_MAX_SLOTS 64      /* expanded nodes per request (64-bit masks)   */
+#define EAGLE_MAX_POSITIONS 64  /* verify-tree positions per request (root+m)  */
+#define EAGLE_MAX_TOPK 16
+
+/*
+ * The draft head ("What is actually in the head": an fc of shape [2d, d], one
+ * decoder layer of width d, and the target's shared embedding and LM head).
+ *
+ *   EAGLE-1 (mode 1):  h = x W_fc^T with x = [f ; emb(t)]           w_fc [d][2d]
+ *   EAGLE-3 (mode 3):  g = [l ; m ; h] W_fuse^T, x = g + emb(t)     w_fuse [d][3d]
+ *                      at verified positions; a + emb(t) afterwards (no fc)
+ *   layer (pre-norm):  h1 = h + Attn(N1(h)) W_o^T,  out = h1 + MLP(N2(h1))
+ *                      w_q [Hq*hd][d], w_k, w_v [Hkv*hd][d], w_o [d][Hq*hd]
+ *                      SwiGLU: w_gate, w_up [ffn][d], w_down [d][ffn]
+ *                      GELU:   w_up [ffn][d], w_down [d][ffn] (w_gate unused)
+ *                      N1, N2: RMSNorm (gain) or LayerNorm (gain, bias), eps
+ *                      RoPE rotate-half, inv_freq = theta^(-2i/hd); theta 0 = off
+ *   LM head:           logits = W_LM out, lm_head [V][d]; emb [V][d]
+ * Constraints: d % 64 == 0, ffn % 32 == 0, head_dim in {64, 128},
+ * n_q_heads % n_kv_heads == 0, V >= 16.
+ */
+typedef struct eagle_head {
+  int32_t d, vocab, n_q_heads, n_kv_heads, head_dim, ffn;
+  int32_t act;    /* EAGLE_ACT_*  */
+  int32_t norm;   /* EAGLE_NORM_* */
+  int32_t dtype;  /* EAGLE_BF16 or EAGLE_F32: weights, caches, activations */
+  int32_t mode;   /* EAGLE_MODE_1 or EAGLE_MODE_3 */
+  float eps, rope_theta;
+  const void *w_fc, *w_fuse;                 /* device; the one of the mode  */
+  const void *w_q, *w_k, *w_v, *w_o;         /* device */
+  const void *w_gate, *w_up, *w_down;        /* device */
+  const void *norm1_g, *norm1_b, *norm2_g, *norm2_b;  /* device [d]; b: LN only */
+  const void *emb, *lm_head;                 /* device [V][d] */
+} eagle_head;
+
+/*
+ * Key/value caches of the draft layer ("The recurrence, written out": the
+ * layer runs over a cache).  Requests are packed without padding (explainer,
+ * "Serving batch": variable-length blocks may be packed).
+ *   k_ctx, v_ctx  [total_n][Hkv][hd]  context K/V (rotated); read by the
+ *                                     attention, written by the EAGLE-3 ingest
+ *   k_slot,v_slot [B][64][Hkv][hd]    K/V of every expanded tree node (slot)
+ *   feat_slot     [B][64][d]          layer output of every expanded node
+ */
+typedef struct eagle_kv {
+  int32_t B;
+  int32_t max_n;       /* host copy of max_b n[b]  (sizes launch grids)  */
+  int64_t total_n;     /* host copy of sum_b n[b]                         */
+  const int32_t *n;    /* device [B]   */
+  const int32_t *cu_n; /* device [B+1] */
+  void *k_ctx, *v_ctx, *k_slot, *v_slot, *feat_slot; /* device */
+} eagle_kv;
+
+/*
+ * Draft tree of every request.
+ *   CHAIN    gamma steps of top-1
+ *   STATIC   fixed template (EAGLE-1, "Drafting a Tree, Not a Chain"):
+ *            template_parent[i] is the parent of template node i+1 (node 0 is
+ *            the root, parents precede children, siblings in rank order); a
+ *            node's token is the rank-th best of its parent's top-k
+ *   DYNAMIC  EAGLE-2 ("EAGLE-2: expand and rerank"): value = product of the
+ *            confidences on the root path; at every step the top_k nodes of
+ *            the newest depth by value are expanded to their top_k children;
+ *            after gamma steps the top_m nodes by value are kept
+ * Ordering: top-k by (logit desc, id asc); frontier and rerank by (value
+ * desc, depth asc, creation index asc); creation index = (step, frontier rank
+ * of the parent, child rank).  value(child) = fp32(value(parent) * conf).
+ * Position id of a node = root position + depth (root at n_b for EAGLE-1, at
+ * n_b - 1, the last verified position, for EAGLE-3).
+ * `state` (device, eagle_tree_state_bytes) holds the node pool, the rows of
+ * the next step, this step's top-k and the verify tree; its layout is given by
+ * eagle_tree_layout.
+ */
+typedef struct eagle_tree {
+  int32_t kind;          /* EAGLE_TREE_* */
+  int32_t B, gamma, top_k, top_m;
+  int32_t n_template;            /* STATIC: number of non-root nodes      */
+  const int32_t *template_parent;/* STATIC: HOST array [n_template]       */
+  float inv_temp;                /* s in conf = softmax(s * logits)       */
+  void *state;                   /* device */
+  size_t state_bytes;
+} eagle_tree;
+
+/* Byte offsets of the arrays inside eagle_tree.state (all per request b).
+ *   pool_* [B][pool_cap]: tok, parent (pool index, -1 root), depth, slot
+ *     (-1 if never expanded) int32; conf, value fp32
+ *   pool_count [B], slot_count [B], root_pos [B] int32; slot_mask [B][64] u64
+ *   rows of the NEXT draft step, request-major, row = b * W + i, [B*max_rows]:
+ *     row_node, row_tok, row_pos, row_slot, row_pidx int32, row_mask u64
+ *     (row_pidx = index of the input feature: b for the root row, else
+ *      b*64 + parent slot)
+ *   topk_id [B*max_rows][top_k] int32, topk_conf [..][top_k] fp32,
+ *   lse [B*max_rows] fp32 (log-partition of s * logits)
+ *   verify tree [B][64]: f_node, f_tok, f_parent (position), f_depth, f_pos
+ *     int32, f_mask u64 (ancestor-or-self over positions); f_count [B]
+ *   choice [B][64] int32: target's greedy token per verify position
+ */
+typedef struct eagle_tree_layout {
+  int32_t pool_cap, max_rows, positions;
+  size_t pool_tok, pool_parent, pool_depth, pool_slot, pool_conf, pool_value;
+  size_t pool_count, slot_count, root_pos, slot_mask;
+  size_t row_node, row_tok, row_pos, row_slot, row_pidx, row_mask;
+  size_t topk_id, topk_conf, lse;
+  size_t f_node, f_tok, f_parent, f_depth, f_pos, f_mask, f_count;
+  size_t choice;
+  size_t total;
+} eagle_tree_layout;
+
+/* Fill *out for this tree.  Returns EAGLE_OK or EAGLE_EINVAL/EUNSUPPORTED. */
+int eagle_tree_layout_of(const eagle_tree *tree, eagle_tree_layout *out);
+/* Bytes needed for tree->state (0 on invalid arguments). */
+size_t eagle_tree_state_bytes(const eagle_tree *tree);
+/* Rows per request processed by draft step `step` (0 on invalid arguments). */
+int eagle_step_rows(const eagle_tree *tree, int step);
+/* Workspace bytes eagle_draft_step / eagle_tree_attend need (0 on error). */
+size_t eagle_workspace_bytes(const eagle_head *head, const eagle_kv *kv,
+                             const eagle_tree *tree);
+
+/*
+ * Start the round: node 0 of every request is the anchor token root_tokens[b]
+ * (device [B]) with value 1; the rows of step 0 are the B roots.
+ */
+int eagle_tree_init(const eagle_head *head, const eagle_kv *kv,
+                    const eagle_tree *tree, const int32_t *root_tokens,
+                    void *stream);
+
+/*
+ * One draft step ("The recurrence, written out"): for every row of the step
+ * (node u of request b at depth `step`):
+ *   EAGLE-1: x = [f ; emb(tok(u))] with f = f_root[b] for the root, else the
+ *            layer output stored in the parent's slot; h = x W_fc^T
+ *   EAGLE-3: step 0 ingests every verified position j of every request:
+ *            g_j = lmh_j W_fuse^T, x_j = g_j + emb(ctx_tokens[j]); K/V of each
+ *            position are written to k_ctx/v_ctx; the root row is each
+ *            request's last position.  Later steps: h = a_parent + emb(tok(u)).
+ *   then the decoder layer at position root_pos + depth; attention sees the
+ *   request's context plus the ancestor-or-self slots (row_mask); K/V and the
+ *   output go to the row's slot; logits = W_LM out; top_k ids, their
+ *   confidences softmax(inv_temp * logits)[id] and the log-partition go to
+ *   the tree state.
+ * f_root:     device [B][d]           (EAGLE-1, step 0; else unused)
+ * lmh:        device [total_n][3d]    (EAGLE-3, step 0; l, m, h concatenated)
+ * ctx_tokens: device [total_n] int32  (EAGLE-3, step 0; token after each
+ *             verified position, the anchor token last)
+ * logits_out: optional device [M][V] fp32 (M = B * eagle_step_rows)
+ * feat_out:   optional device [M][d] in the head dtype (layer outputs)
+ * ws:         device workspace of at least eagle_workspace_bytes
+ */
+int eagle_draft_step(const eagle_head *head, const eagle_kv *kv,
+                     const eagle_tree *tree, int step, const void *f_root,
+                     const void *lmh, const int32_t *ctx_tokens,
+                     float *logits_out, void *feat_out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
+ * Grow the tree from draft step `step`'s top-k ("EAGLE-2: expand and
+ * rerank"; chain and static trees follow their shape).  Writes the rows of
+ * step+1.  When step == gamma-1 it also reranks (dynamic: keep top_m by
+ * value; chain/static: keep every node) and writes the verify tree: the kept
+ * nodes in creation order, root at position 0, parent positions, depth,
+ * position ids and ancestor-or-self masks ("Tree attention in one
+ * verification pass").
+ */
+int eagle_tree_expand_rerank(const eagle_tree *tree, int step, void *stream);
+
+/*
+ * Tree-masked attention over the verify tree, standing in for one target
+ * layer's verification pass ("Tree attention in one verification pass"): row
+ * u of request b has x = emb(f_tok[u]); q, k, v = N1(x) W^T with RoPE at
+ * f_pos[u]; it attends to the whole context plus the tree positions in
+ * f_mask[u].  out: device [B*positions][Hq*hd] in the head dtype.
+ */
+int eagle_tree_attend(const eagle_head *head, const eagle_kv *kv,
+                      const eagle_tree *tree, void *out, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/*
+ * Greedy verification (explainer steps 3-4): the target's choice at verify
+ * position u is argmax_v target_logits[b][u][v] (lowest id on ties); starting
+ * at the root, move to the child whose token equals the choice while one
+ * exists.
+ * target_logits: device [B][positions][vocab], dtype EAGLE_BF16 or EAGLE_F32
+ *   (positions >= the verify tree's position count, vocab >= 1)
+ * accept_len:  device [B]          accepted draft tokens (0..gamma)
+ * accept_path: device [B][gamma+1] verify positions, root first, -1 padded
+ * out_tokens:  device [B][gamma+1] accepted tokens then the target's token at
+ *              the deepest accepted node, -1 padded
+ */
+int eagle_tree_verify(const eagle_tree *tree, const void *target_logits,
+                      int positions, int vocab, int dtype, int32_t *accept_len,
+                      int32_t *accept_path, int32_t *out_tokens, void *stream);
+
+/* Text for a status code. */
+const char *eagle_strerror(int status);
+/* Library version string. */
+const char *eagle_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_H */

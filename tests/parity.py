@@ -1,0 +1,321 @@
+"""Parity of the HIP path (through the C-ABI) against the CPU oracle.
+
+Protocol
+  P1 draft step, teacher-forced: for every checked row the oracle gets the
+     GPU's inputs of that step (tokens, positions, masks, parent features and
+     ancestor K/V from the GPU's slots) and recomputes the row.  Logits must
+     satisfy max|g - o| / max|o| <= 2e-2 per row; top-k ids must match at
+     every rank up to which each oracle gap l(i) - l(i+1) exceeds that
+     tolerance; confidences agree in the log domain within 2 s (max logit
+     error); the fused softmax/top-k must also equal, exactly, the top-k of
+     the GPU's own logits.
+  P2 tree logic: the oracle's tree code driven by the GPU's (ids, conf) must
+     reproduce the GPU's pool, next-step rows and verify tree bit for bit.
+  P3 verify: the oracle's verify on the GPU's verify tree and the same target
+     logits gives the same accept_len / path / out_tokens, bit for bit, for
+     the synthetic logits and for logits with a planted accepted path.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from eagle_feature_space_amd import configs as C
+from eagle_feature_space_amd import synth
+from oracle import tree as OT
+from oracle import verify as OV
+from oracle.head import DraftHead
+from oracle.head import attend as o_attend
+from oracle.round import ingest, row_forward
+
+TOL = 2e-2          # logits: max relative error (bf16 inputs, fp32 accumulation)
+U64 = (1 << 64) - 1
+
+
+def rel_err(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    den = np.max(np.abs(o))
+    return float(np.max(np.abs(g - o)) / den) if den > 0 else float(np.max(np.abs(g)))
+
+
+def _bits(mask):
+    m = int(mask) & U64
+    return [j for j in range(64) if (m >> j) & 1]
+
+
+class Case:
+    """Seeded weights, inputs and target logits of one configuration."""
+
+    def __init__(self, cfg: C.RoundCfg, with_oracle=True):
+        self.cfg = cfg
+        self.w = synth.head_weights(cfg.head, cfg.seed_w)
+        self.inp = synth.round_inputs(cfg)
+        self.target = synth.target_logits(cfg)
+        self.head = DraftHead(cfg.head, {k: synth.f32(v) for k, v in self.w.items()}) if with_oracle else None
+        self._ctx = None
+
+    def gpu(self, device="cuda:0"):
+        from eagle_feature_space_amd.runner import GpuRound
+        return GpuRound(self.cfg, self.w, self.inp, device)
+
+    def target_dev(self, device="cuda:0", target=None):
+        from eagle_feature_space_amd.runner import to_dev
+        return to_dev(self.target if target is None else target, device)
+
+    def ctx(self, gr=None):
+        """Per-request context K/V (fp32) the attention reads."""
+        cu = self.inp.cu_n
+        if self.cfg.head.mode == C.MODE_EAGLE3:
+            from eagle_feature_space_amd.runner import to_f32
+            K, V = to_f32(gr.k_ctx), to_f32(gr.v_ctx)
+        else:
+            if self._ctx is None:
+                self._ctx = (synth.f32(self.inp.k_ctx), synth.f32(self.inp.v_ctx))
+            K, V = self._ctx
+        return [(K[cu[b]:cu[b + 1]], V[cu[b]:cu[b + 1]]) for b in range(self.cfg.B)]
+
+
+# ------------------------------------------------------------------ P1
+def check_step(case: Case, gr, snaps, s, rows=None, report=None):
+    cfg, hd = case.cfg, case.head
+    snap = snaps[s]
+    B = cfg.B
+    M = len(snap.rows["node"])
+    W = M // B
+    e3 = cfg.head.mode == C.MODE_EAGLE3
+    inp = case.inp
+    cu = inp.cu_n
+    ctx = case.ctx(gr)
+    f_root = synth.f32(inp.f_root) if not e3 else None
+    sel = range(M) if rows is None else rows
+    worst = dict(logit=0.0, feat=0.0, kv=0.0, ctxkv=0.0, conf=0.0)
+    ingested = {}
+    for m in sel:
+        b = m // W
+        pidx = int(snap.rows["pidx"][m])
+        tok = int(snap.rows["tok"][m])
+        pos = int(snap.rows["pos"][m])
+        slot = int(snap.rows["slot"][m])
+        mask = int(snap.rows["mask"][m]) & U64
+        sl = slot - b * 64
+        ck, cv = ctx[b]
+        if e3 and s == 0:
+            if b not in ingested:
+                K, V, hl = ingest(hd, synth.f32(inp.lmh[cu[b]:cu[b + 1]]), inp.ctx_tokens[cu[b]:cu[b + 1]])
+                worst["ctxkv"] = max(worst["ctxkv"], rel_err(ck, K), rel_err(cv, V))
+                ingested[b] = hl
+            h = ingested[b]
+            q, _, _ = hd.qkv(h[None], np.array([pos]))
+            out = hd.finish(h[None], o_attend(q[0], ck, cv, hd.group)[None])[0]
+        else:
+            if e3:
+                h = hd.latent_input(snap.feat_slot[pidx], tok)
+            else:
+                feat = f_root[b] if s == 0 else snap.feat_slot[pidx]
+                h = hd.fc_input(feat[None], np.array([tok]))[0]
+            anc = [b * 64 + j for j in _bits(mask) if j != sl]
+            out, k, v = row_forward(hd, h, pos, ck, cv, snap.k_slot[anc], snap.v_slot[anc])
+            worst["kv"] = max(worst["kv"], rel_err(snap.k_slot[slot], k), rel_err(snap.v_slot[slot], v))
+        worst["feat"] = max(worst["feat"], rel_err(snap.feat[m], out))
+        lo = hd.lm_head(out[None])[0]
+        lg = snap.logits[m]
+        e = rel_err(lg, lo)
+        worst["logit"] = max(worst["logit"], e)
+        assert e <= TOL, f"step {s} row {m}: logit rel err {e:.3g}"
+        _check_topk(cfg, lg, lo, snap.topk_id[m], snap.topk_conf[m], snap.lse[m], s, m, worst)
+    assert worst["feat"] <= TOL, worst
+    assert worst["kv"] <= TOL, worst
+    assert worst["ctxkv"] <= TOL, worst
+    if report is not None:
+        for k, v in worst.items():
+            report[k] = max(report.get(k, 0.0), v)
+    return worst
+
+
+def _check_topk(cfg, lg, lo, ids, conf, lse, s, m, worst):
+    K = cfg.top_k
+    st = cfg.inv_temp
+    # the fused kernel equals the top-k / softmax of the GPU's own logits
+    own = np.lexsort((np.arange(lg.size), -lg))[:K]
+    assert list(ids) == list(own), f"step {s} row {m}: fused top-k {ids} != top-k of GPU logits {own}"
+    z = st * lg.astype(np.float64)
+    zmax = z.max()
+    ref_lse = zmax + np.log(np.exp(z - zmax).sum())
+    assert abs(lse - ref_lse) <= 1e-5 * max(1.0, abs(ref_lse)) + 1e-5, (lse, ref_lse)
+    np.testing.assert_allclose(conf, np.exp(z[ids] - ref_lse), rtol=1e-4, atol=1e-12)
+    # against the oracle: ids fixed wherever every gap up to the rank is clear
+    tol = TOL * np.max(np.abs(lo))
+    order = np.lexsort((np.arange(lo.size), -lo))
+    srt = lo[order]
+    clear = True
+    for i in range(K):
+        clear = clear and (srt[i] - srt[i + 1] > tol)
+        if clear:
+            assert ids[i] == order[i], f"step {s} row {m} rank {i}: {ids[i]} != {order[i]}"
+    err = np.max(np.abs(lg.astype(np.float64) - lo))
+    zo = st * lo.astype(np.float64)
+    lse_o = zo.max() + np.log(np.exp(zo - zo.max()).sum())
+    for i in range(K):
+        c_o = np.exp(zo[ids[i]] - lse_o)
+        d = abs(np.log(max(conf[i], 1e-300)) - np.log(c_o))
+        worst["conf"] = max(worst["conf"], d)
+        assert d <= 2 * st * err + 1e-5, f"step {s} row {m}: log-conf diff {d:.3g} > {2 * st * err:.3g}"
+
+
+# ------------------------------------------------------------------ P2
+def check_tree_logic(case: Case, gr, snaps):
+    cfg = case.cfg
+    B = cfg.B
+    e3 = cfg.head.mode == C.MODE_EAGLE3
+    n = case.inp.n
+    top_k = 1 if cfg.tree == C.TREE_CHAIN else cfg.top_k
+    trees = [OT.RequestTree.start(cfg.tree, int(case.inp.t_root[b]),
+                                  int(n[b]) - 1 if e3 else int(n[b]), cfg.gamma, top_k,
+                                  cfg.top_m, cfg.template, e3) for b in range(B)]
+    for s in range(cfg.gamma):
+        snap = snaps[s]
+        M = len(snap.rows["node"])
+        W = M // B
+        for b in range(B):
+            ort = trees[b].rows()
+            assert len(ort) == W
+            for i, (u, ps, tok, pos, slot, mask) in enumerate(ort):
+                r = b * W + i
+                got = (int(snap.rows["node"][r]), int(snap.rows["tok"][r]), int(snap.rows["pos"][r]),
+                       int(snap.rows["slot"][r]), int(snap.rows["mask"][r]) & U64)
+                assert got == (u, tok, pos, b * 64 + slot, mask), (s, b, i, got, (u, tok, pos, slot, mask))
+                if s > 0:
+                    assert int(snap.rows["pidx"][r]) == b * 64 + ps
+            ids = snap.topk_id[b * W:(b + 1) * W, :cfg.top_k]
+            conf = snap.topk_conf[b * W:(b + 1) * W, :cfg.top_k]
+            trees[b].expand(s, ids, conf)
+    pv = {k: v.cpu().numpy() for k, v in gr.pool_view().items()}
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    for b in range(B):
+        t = trees[b]
+        P = len(t.tok)
+        assert int(pv["count"][b]) == P
+        assert list(pv["tok"][b, :P]) == t.tok
+        assert list(pv["parent"][b, :P]) == t.parent
+        assert list(pv["depth"][b, :P]) == t.depth
+        assert list(pv["slot"][b, :P]) == t.slot
+        np.testing.assert_array_equal(pv["conf"][b, :P], np.array(t.conf, np.float32))
+        np.testing.assert_array_equal(pv["value"][b, :P], np.array(t.value, np.float32))
+        f = t.final_tree()
+        T = len(f["tok"])
+        assert int(fv["count"][b]) == T
+        for k in ("node", "tok", "parent", "depth", "pos"):
+            assert list(fv[k][b, :T]) == list(f[k]), (b, k)
+        assert [int(x) & U64 for x in fv["mask"][b, :T]] == [int(x) for x in f["mask"]]
+    return trees
+
+
+# ------------------------------------------------------------------ P3
+def check_verify(case: Case, gr, target_np, gamma):
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    acc = gr.accept_len.cpu().numpy()
+    path = gr.accept_path.cpu().numpy()
+    out = gr.out_tokens.cpu().numpy()
+    tgt = synth.f32(target_np)
+    for b in range(case.cfg.B):
+        T = int(fv["count"][b])
+        a, p, o = OV.verify(fv["tok"][b, :T], fv["parent"][b, :T], tgt[b, :T], gamma)
+        assert int(acc[b]) == a, (b, int(acc[b]), a)
+        assert list(path[b]) == list(p), (b, path[b], p)
+        assert list(out[b]) == list(o), (b, out[b], o)
+    return acc
+
+
+def planted_target(case: Case, gr, seed=0):
+    """Target logits whose greedy choice follows a random root path of the
+    GPU's verify tree for a random number of steps (then leaves it)."""
+    rng = np.random.default_rng(seed)
+    tgt = synth.f32(case.target).copy()
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    V = tgt.shape[-1]
+    want = []
+    for b in range(case.cfg.B):
+        T = int(fv["count"][b])
+        par, tok = fv["parent"][b, :T], fv["tok"][b, :T]
+        u, depth = 0, 0
+        goal = int(rng.integers(0, case.cfg.gamma + 1))
+        while depth < goal:
+            kids = [v for v in range(T) if par[v] == u]
+            if not kids:
+                break
+            v = kids[int(rng.integers(len(kids)))]
+            tgt[b, u, tok[v]] = tgt[b, u].max() + 1.0
+            u, depth = v, depth + 1
+        # at the stopping node pick a token that is not a child
+        kid_toks = {int(tok[v]) for v in range(T) if par[v] == u}
+        c = int(rng.integers(V))
+        while c in kid_toks:
+            c = (c + 1) % V
+        tgt[b, u, c] = tgt[b, u].max() + 1.0
+        want.append(depth)
+    if case.cfg.head.dtype == C.DTYPE_BF16:
+        return synth.bf16_bits(tgt), want
+    return tgt, want
+
+
+# ------------------------------------------------------------------ tree attention
+def check_tree_attend(case: Case, gr):
+    cfg, hd = case.cfg, case.head
+    from eagle_feature_space_amd.runner import to_f32
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    out = to_f32(gr.attn_out)
+    T = gr.layout.positions
+    emb = hd.w["emb"]
+    ctx = case.ctx(gr)
+    worst = 0.0
+    for b in range(cfg.B):
+        cnt = int(fv["count"][b])
+        tok = fv["tok"][b, :cnt]
+        pos = fv["pos"][b, :cnt]
+        q, k, v = hd.qkv(emb[tok], pos)
+        ck, cv = ctx[b]
+        for u in range(cnt):
+            sel = _bits(fv["mask"][b, u])
+            K = np.concatenate([ck, k[sel]])
+            V = np.concatenate([cv, v[sel]])
+            ref = o_attend(q[u], K, V, hd.group).reshape(-1)
+            e = rel_err(out[b * T + u], ref)
+            worst = max(worst, e)
+    assert worst <= TOL, worst
+    return worst
+
+
+# ------------------------------------------------------------------ whole round
+def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:0"):
+    """Run one round on the GPU and check P1 (all or sampled rows), P2, P3."""
+    case = Case(cfg)
+    gr = case.gpu(device)
+    tgt = case.target_dev(device)
+    attend = cfg.tree == C.TREE_DYNAMIC if attend is None else attend
+    snaps = gr.run(target=tgt, snapshots=True, attend=attend)
+    report = {}
+    for s in range(cfg.gamma):
+        rows = None
+        if rows_per_step is not None:
+            M = len(snaps[s].rows["node"])
+            rows = sorted(set(np.linspace(0, M - 1, min(M, rows_per_step)).astype(int).tolist()))
+        check_step(case, gr, snaps, s, rows=rows, report=report)
+    check_tree_logic(case, gr, snaps)
+    check_verify(case, gr, case.target, cfg.gamma)
+    if attend:
+        report["attend"] = check_tree_attend(case, gr)
+    if planted:
+        pt, want = planted_target(case, gr)
+        gr.verify(case.target_dev(device, pt))
+        acc = check_verify(case, gr, pt, cfg.gamma)
+        assert list(acc) == want, (list(acc), want)
+        report["planted_accept"] = list(map(int, acc))
+    return report
+
+
+def smoke_round():
+    """Tiny fp32 chain on cuda:0, fully checked against the oracle."""
+    import torch
+    assert torch.cuda.is_available(), "smoke needs a GPU"
+    rep = full_check(C.CONFIGS["c0_tiny_chain"])
+    print("smoke c0_tiny_chain ok:", {k: (round(v, 6) if isinstance(v, float) else v) for k, v in rep.items()})

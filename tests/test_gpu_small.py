@@ -1,0 +1,42 @@
+"""GPU parity of whole rounds at sizes the oracle finishes in seconds: every
+tree mode, fp32 and bf16, GQA, RoPE, ragged vocab / MLP / context sizes and an
+empty context.  Checked through the C-ABI against the CPU oracle (P1-P3)."""
+import numpy as np
+import pytest
+
+from eagle_feature_space_amd import configs as C
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["c0_tiny_chain", "c0r_tiny_chain_rope", "s1_static", "s2_dynamic", "s3_eagle3",
+         "s4_dynamic_wide"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_round_parity(name):
+    from tests.parity import full_check
+    print(f"\n[parity] {name}", flush=True)
+    rep = full_check(C.ALL_CONFIGS[name])
+    print(f"[parity] {name}: {rep}", flush=True)
+
+
+def test_round_is_deterministic():
+    """Two runs with the same inputs give bit-identical logits, features and trees."""
+    import torch
+    from tests.parity import Case
+    case = Case(C.SMALL_CONFIGS["s2_dynamic"], with_oracle=False)
+    outs = []
+    for _ in range(2):
+        gr = case.gpu()
+        snaps = gr.run(target=case.target_dev(), snapshots=True, attend=True)
+        outs.append((snaps, {k: v.clone() for k, v in gr.final_view().items()},
+                     gr.attn_out.clone(), gr.accept_len.clone()))
+    (s1, f1, a1, c1), (s2, f2, a2, c2) = outs
+    for x, y in zip(s1, s2):
+        np.testing.assert_array_equal(x.logits, y.logits)
+        np.testing.assert_array_equal(x.feat, y.feat)
+        np.testing.assert_array_equal(x.topk_id, y.topk_id)
+        np.testing.assert_array_equal(x.topk_conf, y.topk_conf)
+    for k in f1:
+        assert torch.equal(f1[k], f2[k]), k
+    assert torch.equal(a1, a2) and torch.equal(c1, c2)
