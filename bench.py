@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Draft-and-verify throughput of the EAGLE hot path on one MI355X.
+
+One "step" is one full round on resident inputs: tree init, gamma draft steps
+(fc, decoder layer with tree-masked attention, LM head + softmax/top-k), the
+tree expand/rerank after each, and greedy verification against synthetic
+target logits.  The metric is draft-tree nodes per second (nodes of the
+verify tree, root excluded, summed over the batch).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  Besides the contract fields it carries
+  roofline      the dominant kernel (the LM head with its fused top-k):
+                algorithmic bytes per launch / mean launch time from HIP events
+                recorded on the launch stream inside the timed region
+  cpu_baseline  the CPU oracle timed on this host on whole rounds of the same
+                workload (a bounded sample of ~15 s)
+  breakdown     per kernel family: launches per round, mean us, GB/s, TFLOP/s
+                (a separate profiled pass, outside the timed region)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"lmhead": ["eagle_feature_space_amd/csrc/lmhead.hip",
+                             "eagle_feature_space_amd/csrc/common.h"]}
+
+
+def source_hash(family):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(family, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the kernel source as it is now."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        e = t[workload][family]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("source_sha256_16") != source_hash(family):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, weights, inp, target, seconds):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from eagle_feature_space_amd import synth
+    from oracle.head import DraftHead
+    from oracle.round import run_round
+
+    head = DraftHead(cfg.head, {k: synth.f32(v) for k, v in weights.items()})
+    kw = dict(n=inp.n, t_root=inp.t_root, target=synth.f32(target))
+    if inp.k_ctx is not None:
+        kw.update(k_ctx=synth.f32(inp.k_ctx), v_ctx=synth.f32(inp.v_ctx), f_root=synth.f32(inp.f_root))
+    else:
+        kw.update(lmh=synth.f32(inp.lmh), ctx_tokens=inp.ctx_tokens)
+    rounds = 0
+    t0 = time.perf_counter()
+    while True:
+        run_round(cfg, head, **kw)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    nodes = cfg.B * cfg.n_final
+    return {"value": nodes * rounds / el, "unit": "nodes/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rounds} full rounds of {cfg.name} (numpy fp32, {nodes} nodes each) in {el:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c1_8b_static")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requests shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from eagle_feature_space_amd import binding as E
+    from eagle_feature_space_amd import configs as C
+    from eagle_feature_space_amd import synth
+    from eagle_feature_space_amd.runner import GpuRound, to_dev
+
+    if not os.path.exists(E.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no CPU fallback)", file=sys.stderr)
+        sys.exit(3)
+
+    cfg = C.ALL_CONFIGS[args.workload]
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    weights = synth.head_weights(cfg.head, cfg.seed_w)
+    inp = synth.round_inputs(cfg)
+    target = synth.target_logits(cfg)
+    gr = GpuRound(cfg, weights, inp)
+    tgt = to_dev(target, gr.dev)
+    torch.cuda.synchronize()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        gr.run(target=tgt)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K rounds; HIP events bracket the LM-head launches only
+    E.eagle_profile_reset()
+    E.eagle_profile_enable(1 << E.PROF_FAMILIES["lmhead"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        gr.run(target=tgt)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    E.eagle_profile_enable(False)
+    lm = E.eagle_profile_read("lmhead")
+
+    nodes = cfg.B * cfg.n_final
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = nodes * args.steps / elapsed
+    avg_ms = lm["ms"] / max(1, lm["timed"])
+    bytes_per_launch = lm["bytes"] / max(1, lm["launches"])
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic("lmhead", cfg.name)
+    roofline = {"kernel": "k_lmhead (LM head + fused softmax/top-k partials)",
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "bytes_per_launch": bytes_per_launch,
+                "mean_launch_us": round(avg_ms * 1e3, 2), "launches_timed": lm["timed"]}
+
+    # ---- per-family breakdown (separate profiled pass)
+    breakdown = None
+    if not args.no_breakdown:
+        R = max(5, min(20, args.steps))
+        E.eagle_profile_reset()
+        E.eagle_profile_enable(True)
+        for _ in range(R):
+            gr.run(target=tgt)
+        torch.cuda.synchronize()
+        E.eagle_profile_enable(False)
+        breakdown = {}
+        tot_ms = tot_bytes = 0.0
+        for fam in E.PROF_FAMILIES:
+            p = E.eagle_profile_read(fam)
+            if p["launches"] == 0:
+                continue
+            ms = p["ms"] * p["launches"] / max(1, p["timed"])
+            tot_ms += ms
+            tot_bytes += p["bytes"]
+            breakdown[fam] = {"launches_per_round": p["launches"] / R,
+                              "us_per_round": round(ms * 1e3 / R, 2),
+                              "GB_per_round": round(p["bytes"] / R / 1e9, 4),
+                              "GBps": round(p["bytes"] / (ms * 1e-3) / 1e9, 1) if ms > 0 and p["bytes"] else None,
+                              "TFLOPps": round(p["flops"] / (ms * 1e-3) / 1e12, 2) if ms > 0 and p["flops"] else None}
+        breakdown["kernels_us_per_round"] = round(tot_ms * 1e3 / R, 2)
+        breakdown["round_bytes_GB"] = round(tot_bytes / R / 1e9, 4)
+        breakdown["round_hbm_roofline_us"] = round(tot_bytes / R / (HBM_PEAK_GBS * 1e9) * 1e6, 2)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, weights, inp, target, args.cpu_seconds)
+
+    h = cfg.head
+    out = {
+        "metric": "draft-tree nodes/sec (draft+verify) at d=4096,|V|=128256; % MFMA/HBM roofline",
+        "value": round(value, 2), "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if h.dtype == C.DTYPE_BF16 else "f32",
+        "data": "synthetic: seeded random-init head weights, inputs and target logits",
+        "config": {"workload": cfg.name, "B": cfg.B, "d": h.d, "vocab": h.vocab,
+                   "heads": f"{h.n_q}q/{h.n_kv}kv x {h.head_dim}", "ffn": h.ffn,
+                   "n": int(inp.n.max()), "tree": {0: "chain", 1: "static", 2: "dynamic"}[cfg.tree],
+                   "gamma": cfg.gamma, "top_k": cfg.top_k, "top_m": cfg.top_m,
+                   "nodes_per_round": nodes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

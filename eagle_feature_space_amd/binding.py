@@ -87,6 +87,10 @@ def lib():
                                c_size_t, c_void_p], ctypes.c_int),
         "eagle_tree_verify": ([P(eagle_tree), c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                c_void_p, c_void_p, c_void_p, c_void_p], ctypes.c_int),
+        "eagle_profile_enable": ([ctypes.c_int], ctypes.c_int),
+        "eagle_profile_reset": ([], ctypes.c_int),
+        "eagle_profile_read": ([ctypes.c_int, P(c_int64), P(c_int64), P(ctypes.c_double),
+                                P(ctypes.c_double), P(ctypes.c_double)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -98,7 +102,10 @@ def lib():
 
 EXPORTED = ("eagle_version", "eagle_strerror", "eagle_tree_layout_of", "eagle_tree_state_bytes",
             "eagle_step_rows", "eagle_workspace_bytes", "eagle_tree_init", "eagle_draft_step",
-            "eagle_tree_expand_rerank", "eagle_tree_attend", "eagle_tree_verify")
+            "eagle_tree_expand_rerank", "eagle_tree_attend", "eagle_tree_verify",
+            "eagle_profile_enable", "eagle_profile_reset", "eagle_profile_read")
+
+PROF_FAMILIES = {"lmhead": 0, "gemm": 1, "attn": 2, "verify": 3, "other": 4}
 
 
 class EagleError(RuntimeError):
@@ -180,3 +187,23 @@ def eagle_tree_verify(tree, target_logits, positions, vocab, dtype, accept_len, 
     return _check(lib().eagle_tree_verify(ctypes.byref(tree), _ptr(target_logits), positions, vocab,
                                           dtype, _ptr(accept_len), _ptr(accept_path),
                                           _ptr(out_tokens), _stream(stream)), "eagle_tree_verify")
+
+
+def eagle_profile_enable(on=True):
+    """on: True (every family), False, or a family bitmask."""
+    mask = (1 << len(PROF_FAMILIES)) - 1 if on is True else (0 if on is False else int(on))
+    return _check(lib().eagle_profile_enable(mask), "eagle_profile_enable")
+
+
+def eagle_profile_reset():
+    return _check(lib().eagle_profile_reset(), "eagle_profile_reset")
+
+
+def eagle_profile_read(family):
+    """-> dict(launches, timed, ms, bytes, flops) for a kernel family."""
+    fam = PROF_FAMILIES[family] if isinstance(family, str) else family
+    n, t = c_int64(), c_int64()
+    ms, by, fl = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().eagle_profile_read(fam, ctypes.byref(n), ctypes.byref(t), ctypes.byref(ms),
+                                    ctypes.byref(by), ctypes.byref(fl)), "eagle_profile_read")
+    return dict(launches=n.value, timed=t.value, ms=ms.value, bytes=by.value, flops=fl.value)

@@ -105,7 +105,7 @@ HEAD_70B = HeadCfg(d=8192, vocab=128256, n_q=64, n_kv=8, head_dim=128, ffn=28672
 # Inverse temperature for the EAGLE-2 dynamic tree at the 8B shape.  The random
 # head's draft logits are rescaled so that the mean top-1 confidence of the
 # first draft step is close to 0.6 (calibrated by oracle/calibrate_inv_temp.py).
-C2_INV_TEMP = 1.0
+C2_INV_TEMP = 1.39494
 
 CONFIGS = {
     "c0_tiny_chain": RoundCfg(

@@ -235,6 +235,47 @@ int check_kv(const eagle_kv* kv, int B) {
   return EAGLE_OK;
 }
 
+// ---------------------------------------------------------------- profiling
+constexpr size_t kMaxTimed = 16384;
+struct ProfFamily {
+  int64_t launches = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  size_t used = 0;
+  double bytes = 0, flops = 0;
+};
+struct Prof {
+  unsigned mask = 0;          // bit f set: family f is profiled
+  ProfFamily fam[EAGLE_PROF_FAMILIES];
+};
+Prof g_prof;
+
+// Brackets one launch with events on its stream when profiling is enabled.
+struct ProfScope {
+  ProfFamily* f = nullptr;
+  hipStream_t st = nullptr;
+  bool timed = false;
+  ProfScope(int family, double bytes, double flops, hipStream_t s) {
+    if (!(g_prof.mask >> family & 1u)) return;
+    f = &g_prof.fam[family];
+    st = s;
+    f->launches += 1;
+    f->bytes += bytes;
+    f->flops += flops;
+    if (f->used >= kMaxTimed) return;
+    if (f->used == f->ev.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      f->ev.push_back({a, b});
+    }
+    timed = hipEventRecord(f->ev[f->used].first, st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!timed) return;
+    if (hipEventRecord(f->ev[f->used].second, st) == hipSuccess) f->used += 1;
+  }
+};
+
 // ---------------------------------------------------------------- workspace
 struct AttnPlan {
   int split_len, nsplit;
@@ -343,6 +384,8 @@ void gemm(const eagle_head* h, RowSrc x0, RowSrc x1, int ksplit, int M, int N, i
   a.P = P;
   a.kps = 0;
   *shape = plan_gemm(h->dtype, M, N, K);
+  ProfScope ps(EAGLE_PROF_GEMM, (double)esz(h) * ((double)N * K + (double)M * K),
+               2.0 * M * (double)N * K, st);
   launch_gemm(h->dtype, a, *shape, st);
 }
 
@@ -362,6 +405,7 @@ void reduce(const eagle_head* h, const float* P, int S, int M, int N, RowSrc s1,
   a.bias = h->norm == EAGLE_NORM_LAYER ? (which_norm == 1 ? h->norm1_b : h->norm2_b) : nullptr;
   a.layer_norm = h->norm == EAGLE_NORM_LAYER;
   a.eps = h->eps;
+  ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
   launch_reduce_rows(h->dtype, a, st);
 }
 
@@ -390,6 +434,7 @@ void qkv_rope(const eagle_head* h, const char* ws, const Ws& w, const void* hn, 
   q.k = kdst;
   q.v = vdst;
   q.kv_idx = kv_idx;
+  ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
   launch_epi_qkv(h->dtype, q, st);
 }
 
@@ -415,7 +460,14 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)h->head_dim);
   a.part_o = (float*)(ws + w.att_o);
   a.part_ml = (float*)(ws + w.att_ml);
-  launch_attention(h->dtype, a, st);
+  {
+    // context K and V of every request once, plus the queries
+    const double kvd = (double)h->n_kv_heads * h->head_dim;
+    const double bytes = esz(h) * (2.0 * kv->total_n * kvd + (double)kv->B * W * h->n_q_heads * h->head_dim);
+    const double flops = 4.0 * h->head_dim * (double)h->n_q_heads * W * (double)kv->total_n;
+    ProfScope ps(EAGLE_PROF_ATTN, bytes, flops, st);
+    launch_attention(h->dtype, a, st);
+  }
   CombineArgs c;
   c.part_o = a.part_o;
   c.part_ml = a.part_ml;
@@ -424,6 +476,7 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
   c.Hq = h->n_q_heads;
   c.hd = h->head_dim;
   c.out = out;
+  ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
   launch_attn_combine(h->dtype, c, st);
 }
 
@@ -438,6 +491,39 @@ int finish(int status) {
 extern "C" {
 
 const char* eagle_version(void) { return "eagle-mi355x 0.1 (gfx950)"; }
+
+int eagle_profile_enable(int family_mask) {
+  g_prof.mask = (unsigned)family_mask & ((1u << EAGLE_PROF_FAMILIES) - 1u);
+  return EAGLE_OK;
+}
+
+int eagle_profile_reset(void) {
+  for (auto& f : g_prof.fam) {
+    f.launches = 0;
+    f.used = 0;
+    f.bytes = f.flops = 0;
+  }
+  return EAGLE_OK;
+}
+
+int eagle_profile_read(int family, int64_t* launches, int64_t* timed_launches, double* total_ms,
+                       double* bytes, double* flops) {
+  if (family < 0 || family >= EAGLE_PROF_FAMILIES) return EAGLE_EINVAL;
+  ProfFamily& f = g_prof.fam[family];
+  double ms = 0;
+  for (size_t i = 0; i < f.used; ++i) {
+    if (hipEventSynchronize(f.ev[i].second) != hipSuccess) return EAGLE_EHIP;
+    float t = 0;
+    if (hipEventElapsedTime(&t, f.ev[i].first, f.ev[i].second) != hipSuccess) return EAGLE_EHIP;
+    ms += t;
+  }
+  if (launches) *launches = f.launches;
+  if (timed_launches) *timed_launches = (int64_t)f.used;
+  if (total_ms) *total_ms = ms;
+  if (bytes) *bytes = f.bytes;
+  if (flops) *flops = f.flops;
+  return EAGLE_OK;
+}
 
 const char* eagle_strerror(int s) {
   switch (s) {
@@ -556,6 +642,7 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
     q.k = kv->k_ctx;
     q.v = kv->v_ctx;
     q.kv_idx = nullptr;
+    ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
     launch_epi_qkv(h->dtype, q, st);
     // root rows = each request's last verified position
     reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, kv->total_n), kNone, hbuf, kNone, hn, 1, st);
@@ -582,7 +669,10 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   aa.F = ffn;
   aa.swiglu = swiglu;
   aa.out = ws + w.act;
-  launch_epi_act(h->dtype, aa, st);
+  {
+    ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
+    launch_epi_act(h->dtype, aa, st);
+  }
   gemm(h, rs(ws + w.act, nullptr, ffn), kNone, ffn, M, d, ffn, h->w_down, nullptr, nullptr, d, d,
        P, &sh, st);
   void* fout = feat_out ? feat_out : (void*)(ws + w.f);
@@ -604,7 +694,11 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   la.part_sum = (float*)(ws + w.lm_sum);
   la.part_id = (int*)(ws + w.lm_id);
   la.part_val = (float*)(ws + w.lm_val);
-  launch_lmhead(h->dtype, la, ls, st);
+  {
+    ProfScope ps(EAGLE_PROF_LMHEAD, (double)esz(h) * ((double)h->vocab * d + (double)M * d),
+                 2.0 * M * (double)h->vocab * d, st);
+    launch_lmhead(h->dtype, la, ls, st);
+  }
   MergeArgs ma;
   ma.part_max = la.part_max;
   ma.part_sum = la.part_sum;
@@ -618,7 +712,10 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   ma.topk_conf = td.topk_conf;
   ma.lse = td.lse;
   ma.vocab = h->vocab;
-  launch_topk_merge(ma, st);
+  {
+    ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
+    launch_topk_merge(ma, st);
+  }
   return finish(EAGLE_OK);
 }
 
@@ -629,6 +726,7 @@ int eagle_tree_expand_rerank(const eagle_tree* tree, int step, void* stream) {
   if ((s = check_tree_state(tree, g))) return s;
   if (step < 0 || step >= g.gamma) return EAGLE_EINVAL;
   const bool fin = step == g.gamma - 1;
+  ProfScope ps(EAGLE_PROF_OTHER, 0, 0, (hipStream_t)stream);
   launch_tree_expand(tree_dev(tree, g), g.B, g.kind, step, g.gamma, g.rows[step], g.top_k,
                      g.top_m, fin, g.plans[step], (hipStream_t)stream);
   return finish(EAGLE_OK);
@@ -670,8 +768,12 @@ int eagle_tree_verify(const eagle_tree* tree, const void* target_logits, int pos
   if (!target_logits || !accept_len || !accept_path || !out_tokens) return EAGLE_EINVAL;
   if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_EINVAL;
   if (vocab < 1 || positions < g.positions) return EAGLE_EINVAL;
-  launch_verify(tree_dev(tree, g), g.B, target_logits, positions, vocab, dtype, g.gamma,
-                accept_len, accept_path, out_tokens, (hipStream_t)stream);
+  {
+    ProfScope ps(EAGLE_PROF_VERIFY, (double)g.B * g.positions * vocab * (dtype == EAGLE_BF16 ? 2 : 4),
+                 0, (hipStream_t)stream);
+    launch_verify(tree_dev(tree, g), g.B, target_logits, positions, vocab, dtype, g.gamma,
+                  accept_len, accept_path, out_tokens, (hipStream_t)stream);
+  }
   return finish(EAGLE_OK);
 }
 

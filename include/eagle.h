@@ -251,6 +251,31 @@ int eagle_tree_verify(const eagle_tree *tree, const void *target_logits,
                       int positions, int vocab, int dtype, int32_t *accept_len,
                       int32_t *accept_path, int32_t *out_tokens, void *stream);
 
+/*
+ * Kernel timing for benchmarks (off by default).  While enabled, every launch
+ * of a kernel family is bracketed by HIP events recorded on the launch stream,
+ * and the algorithmic bytes and flops of that launch (each weight, cache and
+ * logit byte counted once) are added up.  eagle_profile_read waits for the
+ * recorded events and returns, since the last reset, the launch count, the
+ * summed kernel time in milliseconds and the summed bytes / flops.  Up to
+ * 16384 launches per family are timed; later ones are counted but not timed
+ * (timed_launches tells how many were).  Not thread-safe across concurrent
+ * callers.
+ */
+enum {
+  EAGLE_PROF_LMHEAD = 0,  /* LM head + fused softmax/top-k partials      */
+  EAGLE_PROF_GEMM = 1,    /* weight-streaming GEMMs of the draft layer    */
+  EAGLE_PROF_ATTN = 2,    /* tree-masked attention (split-KV partials)    */
+  EAGLE_PROF_VERIFY = 3,  /* target-logit argmax of the verifier          */
+  EAGLE_PROF_OTHER = 4,   /* epilogues, merges, tree bookkeeping          */
+  EAGLE_PROF_FAMILIES = 5
+};
+/* family_mask: bit (1 << EAGLE_PROF_x) enables family x; 0 disables all. */
+int eagle_profile_enable(int family_mask);
+int eagle_profile_reset(void);
+int eagle_profile_read(int family, int64_t *launches, int64_t *timed_launches,
+                       double *total_ms, double *bytes, double *flops);
+
 /* Text for a status code. */
 const char *eagle_strerror(int status);
 /* Library version string. */
