@@ -233,33 +233,50 @@ void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
 }
 
 // out[m][h][d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// One workgroup per (head, row); split weights are formed once in LDS, then
+// every thread folds its d over the splits in split order.
+constexpr int kMaxParts = 1024;
 template <typename T>
-__global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
-  const int m = blockIdx.x;
-  const int HD = a.hd;
-  for (int idx = threadIdx.x; idx < a.Hq * HD; idx += 256) {
-    const int h = idx / HD, d = idx % HD;
+__global__ __launch_bounds__(128) void k_attn_combine(CombineArgs a) {
+  __shared__ float wts[kMaxParts];
+  __shared__ float red[2];
+  const int h = blockIdx.x, m = blockIdx.y;
+  const int np = a.nparts;
+  const int64_t stride = (int64_t)a.M * a.Hq;
+  const int64_t base = (int64_t)m * a.Hq + h;
+  if (threadIdx.x == 0) {
     float mx = -INFINITY;
-    for (int s = 0; s < a.nparts; ++s)
-      mx = fmaxf(mx, a.part_ml[2 * (((int64_t)s * a.M + m) * a.Hq + h)]);
-    float L = 0.f, O = 0.f;
-    if (mx != -INFINITY) {
-      for (int s = 0; s < a.nparts; ++s) {
-        const int64_t i = ((int64_t)s * a.M + m) * a.Hq + h;
-        const float ms = a.part_ml[2 * i];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - mx);
-        L += f * a.part_ml[2 * i + 1];
-        O += f * a.part_o[i * HD + d];
-      }
+    for (int s = 0; s < np; ++s) mx = fmaxf(mx, a.part_ml[2 * (s * stride + base)]);
+    float L = 0.f;
+    for (int s = 0; s < np; ++s) {
+      const float ms = a.part_ml[2 * (s * stride + base)];
+      const float f = (mx == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+      wts[s] = f;
+      L += f * a.part_ml[2 * (s * stride + base) + 1];
     }
-    DT<T>::st((T*)a.out + (int64_t)m * a.Hq * HD + idx, L > 0.f ? O / L : 0.f);
+    red[0] = L > 0.f ? 1.0f / L : 0.f;
+  }
+  __syncthreads();
+  const float inv = red[0];
+  for (int d = threadIdx.x; d < a.hd; d += blockDim.x) {
+    float O = 0.f;
+    int s = 0;
+    for (; s + 4 <= np; s += 4) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = a.part_o[((s + q) * stride + base) * a.hd + d];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) O += wts[s + q] * v[q];
+    }
+    for (; s < np; ++s) O += wts[s] * a.part_o[(s * stride + base) * a.hd + d];
+    DT<T>::st((T*)a.out + base * a.hd + d, O * inv);
   }
 }
 
 void launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t st) {
-  if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_attn_combine<bf16s>, dim3(a.M), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_attn_combine<float>, dim3(a.M), dim3(256), 0, st, a);
+  dim3 grid(a.Hq, a.M);
+  if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_attn_combine<bf16s>, grid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(128), 0, st, a);
 }
 
 }  // namespace eagle

@@ -134,12 +134,12 @@ void layout_of(const Geo& g, eagle_tree_layout* L) {
   L->slot_count = bp.take(B * 4);
   L->root_pos = bp.take(B * 4);
   L->slot_mask = bp.take(B * kSlots * 8);
-  L->row_node = bp.take(R * 4);
-  L->row_tok = bp.take(R * 4);
-  L->row_pos = bp.take(R * 4);
-  L->row_slot = bp.take(R * 4);
-  L->row_pidx = bp.take(R * 4);
-  L->row_mask = bp.take(R * 8);
+  L->row_node = bp.take(2 * R * 4);
+  L->row_tok = bp.take(2 * R * 4);
+  L->row_pos = bp.take(2 * R * 4);
+  L->row_slot = bp.take(2 * R * 4);
+  L->row_pidx = bp.take(2 * R * 4);
+  L->row_mask = bp.take(2 * R * 8);
   L->topk_id = bp.take(R * K * 4);
   L->topk_conf = bp.take(R * K * 4);
   L->lse = bp.take(R * 4);
@@ -154,7 +154,23 @@ void layout_of(const Geo& g, eagle_tree_layout* L) {
   L->total = bp.off;
 }
 
-TreeDev tree_dev(const eagle_tree* t, const Geo& g) {
+// Row arrays of step `step` (double buffer by step parity).
+RowsDev rows_dev(const eagle_tree* t, const Geo& g, int step) {
+  eagle_tree_layout L;
+  layout_of(g, &L);
+  char* s = (char*)t->state;
+  const size_t R = (size_t)g.B * g.max_rows, h = (size_t)(step & 1) * R;
+  RowsDev r;
+  r.node = (int32_t*)(s + L.row_node) + h;
+  r.tok = (int32_t*)(s + L.row_tok) + h;
+  r.pos = (int32_t*)(s + L.row_pos) + h;
+  r.slot = (int32_t*)(s + L.row_slot) + h;
+  r.pidx = (int32_t*)(s + L.row_pidx) + h;
+  r.mask = (uint64_t*)(s + L.row_mask) + h;
+  return r;
+}
+
+TreeDev tree_dev(const eagle_tree* t, const Geo& g, int step = 0) {
   eagle_tree_layout L;
   layout_of(g, &L);
   char* s = (char*)t->state;
@@ -189,6 +205,13 @@ TreeDev tree_dev(const eagle_tree* t, const Geo& g) {
   d.pool_cap = g.pool_cap;
   d.max_rows = g.max_rows;
   d.positions = g.positions;
+  const RowsDev r = rows_dev(t, g, step);
+  d.row_node = r.node;
+  d.row_tok = r.tok;
+  d.row_pos = r.pos;
+  d.row_slot = r.slot;
+  d.row_pidx = r.pidx;
+  d.row_mask = r.mask;
   return d;
 }
 
@@ -234,6 +257,8 @@ int check_kv(const eagle_kv* kv, int B) {
   if (kv->total_n > INT32_MAX || kv->max_n > kv->total_n) return EAGLE_EINVAL;
   return EAGLE_OK;
 }
+
+int check_attn_plan(const eagle_head* h, const eagle_kv* kv);
 
 // ---------------------------------------------------------------- profiling
 constexpr size_t kMaxTimed = 16384;
@@ -282,16 +307,17 @@ struct AttnPlan {
 };
 AttnPlan plan_attn(const eagle_head* h, const eagle_kv* kv) {
   AttnPlan p;
+  // about 1024 (request, kv head, split) units, splits of at least 256 keys
   const int64_t work = (int64_t)std::max(kv->max_n, 1) * kv->B * h->n_kv_heads;
   int64_t units = (work + 64 * 1024 - 1) / (64 * 1024);
-  if (units < 1) units = 1;
+  if (units < 4) units = 4;
   p.split_len = (int)(64 * units);
   p.nsplit = (std::max(kv->max_n, 1) + p.split_len - 1) / p.split_len;
   return p;
 }
 
 struct Ws {
-  size_t h, hn, h1, h1n, f, q, o, act, P;
+  size_t h, hn, h1, h1n, f, q, o, act, P, y32, stats;
   size_t att_o, att_ml, lm_max, lm_sum, lm_id, lm_val;
   size_t tk, tv, t_tok, t_kv, t_pos, t_mask;
   size_t x_in, xn_in, P_in;
@@ -303,6 +329,11 @@ size_t gemm_bytes(int dtype, int M, int N, int K) {
   if (M <= 0) return 0;
   GemmShape s = plan_gemm(dtype, M, N, K);
   return (size_t)s.S * M * N * 4;
+}
+
+int check_attn_plan(const eagle_head* h, const eagle_kv* kv) {
+  // the combine folds at most 1024 split partials per row
+  return plan_attn(h, kv).nsplit + 1 <= 1024 ? EAGLE_OK : EAGLE_EUNSUPPORTED;
 }
 
 Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
@@ -332,6 +363,9 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
     P = std::max(P, gemm_bytes(h->dtype, M, d, h->ffn));
   }
   w.P = bp.take(P);
+  const int Mrow = std::max(Mr, h->mode == EAGLE_MODE_3 ? (int)kv->total_n : 0);
+  w.y32 = bp.take((size_t)Mrow * d * 4);
+  w.stats = bp.take((size_t)Mrow * ((d + 255) / 256) * 2 * 4);
   w.ap = plan_attn(h, kv);
   const size_t nparts = (size_t)w.ap.nsplit + 1;
   w.att_o = bp.take(nparts * Mr * h->n_q_heads * h->head_dim * 4);
@@ -389,9 +423,15 @@ void gemm(const eagle_head* h, RowSrc x0, RowSrc x1, int ksplit, int M, int N, i
   launch_gemm(h->dtype, a, *shape, st);
 }
 
+// scratch of the row-norm epilogue, set per call by the entry points
+float* g_y32 = nullptr;
+float* g_stats = nullptr;
+
 void reduce(const eagle_head* h, const float* P, int S, int M, int N, RowSrc s1, RowSrc s2,
             void* out, RowSrc scatter, void* out_norm, int which_norm, hipStream_t st) {
   ReduceArgs a;
+  a.y32 = g_y32;
+  a.stats = g_stats;
   a.P = P;
   a.S = S;
   a.M = M;
@@ -587,6 +627,7 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   if ((s = check_head(h))) return s;
   if ((s = build_geo(tree, &g))) return s;
   if ((s = check_kv(kv, g.B))) return s;
+  if ((s = check_attn_plan(h, kv))) return s;
   if ((s = check_tree_state(tree, g))) return s;
   if (step < 0 || step >= g.gamma) return EAGLE_EINVAL;
   if (g.top_k > h->vocab) return EAGLE_EINVAL;
@@ -599,7 +640,9 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
 
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)ws_v;
-  const TreeDev td = tree_dev(tree, g);
+  g_y32 = (float*)(ws + w.y32);
+  g_stats = (float*)(ws + w.stats);
+  const TreeDev td = tree_dev(tree, g, step);
   const int B = g.B, W = g.rows[step], M = B * W;
   const int d = h->d, qd = h->n_q_heads * h->head_dim, ffn = h->ffn;
   const bool swiglu = h->act == EAGLE_ACT_SWIGLU;
@@ -727,8 +770,9 @@ int eagle_tree_expand_rerank(const eagle_tree* tree, int step, void* stream) {
   if (step < 0 || step >= g.gamma) return EAGLE_EINVAL;
   const bool fin = step == g.gamma - 1;
   ProfScope ps(EAGLE_PROF_OTHER, 0, 0, (hipStream_t)stream);
-  launch_tree_expand(tree_dev(tree, g), g.B, g.kind, step, g.gamma, g.rows[step], g.top_k,
-                     g.top_m, fin, g.plans[step], (hipStream_t)stream);
+  launch_tree_expand(tree_dev(tree, g, step), rows_dev(tree, g, step + 1), g.B, g.kind, step,
+                     g.gamma, g.rows[step], g.top_k, g.top_m, fin, g.plans[step],
+                     (hipStream_t)stream);
   return finish(EAGLE_OK);
 }
 
@@ -739,12 +783,15 @@ int eagle_tree_attend(const eagle_head* h, const eagle_kv* kv, const eagle_tree*
   if ((s = check_head(h))) return s;
   if ((s = build_geo(tree, &g))) return s;
   if ((s = check_kv(kv, g.B))) return s;
+  if ((s = check_attn_plan(h, kv))) return s;
   if ((s = check_tree_state(tree, g))) return s;
   if (!out || !ws_v) return EAGLE_EINVAL;
   const Ws w = plan_ws(h, kv, g);
   if (ws_bytes < w.total) return EAGLE_ECAPACITY;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)ws_v;
+  g_y32 = (float*)(ws + w.y32);
+  g_stats = (float*)(ws + w.stats);
   const TreeDev td = tree_dev(tree, g);
   const int Wt = g.positions, M = g.B * Wt, d = h->d;
   int32_t* t_tok = (int32_t*)(ws + w.t_tok);

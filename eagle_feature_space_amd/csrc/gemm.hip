@@ -12,6 +12,7 @@
 // gives the launch enough waves; partial sums go to an fp32 workspace that
 // the epilogue kernels reduce in a fixed order (bit-reproducible).
 #include "kernels.h"
+#include "stream.h"
 
 namespace eagle {
 
@@ -103,11 +104,70 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
+template <typename T, int MB, int NB>
+__global__ __launch_bounds__(256) void k_gemm_direct(GemmArgs a) {
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int n_base = (blockIdx.x * 4 + wave) * (16 * NB);
+  if (n_base >= a.N) return;
+  const int k_begin = blockIdx.z * a.kps;
+  const int k_end = min(a.K, k_begin + a.kps);
+  const T* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = min(n_base + nb * 16 + c, a.N - 1);
+    const T* base;
+    int off;
+    if (n < a.nseg1) { base = (const T*)a.w[0]; off = 0; }
+    else if (n < a.nseg2) { base = (const T*)a.w[1]; off = a.nseg1; }
+    else { base = (const T*)a.w[2]; off = a.nseg2; }
+    wrow[nb] = base + (int64_t)(n - off) * a.K;
+  }
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  direct_mainloop<T, MB, NB, U>(a, wrow, k_begin, k_end, g, c, acc);
+  float* P = a.P + (int64_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n_base + nb * 16 + 4 * g;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + c;
+      if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
+    }
+  }
+}
+
 // ----------------------------------------------------------------- planning
 static int kc_of(int dtype) { return dtype == EAGLE_BF16 ? 256 : 128; }
 
 GemmShape plan_gemm(int dtype, int M, int N, int K) {
   GemmShape s;
+  if (M <= 32) {
+    // direct kernel: waves of 2 n-blocks (32 columns); ~2048 waves, K spans
+    // that are whole multiples of the 4-step unroll
+    s.direct = 1;
+    s.MB = (M + 15) / 16;
+    s.mtiles = 1;
+    s.NB = 2;
+    const int wcols = (N + 31) / 32;
+    s.ntiles = (wcols + 3) / 4;
+    const int step = dtype == EAGLE_BF16 ? 128 : 64;
+    const int ksteps = (K + step - 1) / step;
+    int S = (2048 + wcols - 1) / wcols;
+    if (S > ksteps) S = ksteps;
+    if (S < 1) S = 1;
+    const int sps = (ksteps + S - 1) / S;
+    s.kps = sps * step;
+    s.S = (K + s.kps - 1) / s.kps;
+    return s;
+  }
+  s.direct = 0;
   s.MB = M >= 80 ? 5 : (M + 15) / 16;
   if (s.MB < 1) s.MB = 1;
   s.mtiles = (M + 16 * s.MB - 1) / (16 * s.MB);
@@ -143,6 +203,17 @@ static void launch_mb(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
 
 void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st) {
   a.kps = s.kps;
+  if (s.direct) {
+    dim3 grid(s.ntiles, 1, s.S), block(256);
+    if (dtype == EAGLE_BF16) {
+      if (s.MB == 1) hipLaunchKernelGGL((k_gemm_direct<bf16s, 1, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k_gemm_direct<bf16s, 2, 2>), grid, block, 0, st, a);
+    } else {
+      if (s.MB == 1) hipLaunchKernelGGL((k_gemm_direct<float, 1, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k_gemm_direct<float, 2, 2>), grid, block, 0, st, a);
+    }
+    return;
+  }
   if (dtype == EAGLE_BF16) {
     if (s.NB == 2) launch_mb<bf16s, 2>(a, s, st); else launch_mb<bf16s, 1>(a, s, st);
   } else {
@@ -151,67 +222,95 @@ void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st) {
 }
 
 // ----------------------------------------------------------------- epilogues
-// y = sum_s P[s][m] + src1[m] + src2[m] (fp32), one workgroup per row; writes
-// y (dense and/or scattered) in T and, optionally, yn = Norm(y).
+// Row epilogue, column-parallel (one thread per column, grid = column blocks x
+// rows, so even a single row spreads over many workgroups):
+//   y = sum_s P[s][m] + src1[m] + src2[m]            (fp32, fixed order)
+//   out / out_scatter = y (T); if a norm follows, y is kept in fp32 and each
+//   block writes its partial (sum y, sum y^2) for the row statistics.
 template <typename T>
-__global__ __launch_bounds__(256) void k_reduce_rows(ReduceArgs a) {
-  extern __shared__ float ys[];
+__global__ __launch_bounds__(256) void k_rows_sum(ReduceArgs a) {
   __shared__ float red[2][4];
-  const int m = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int N = a.N;
-  const float* P = a.P;
-  const T* s1 = a.src1.base ? row_ptr<T>(a.src1, m) : nullptr;
-  const T* s2 = a.src2.base ? row_ptr<T>(a.src2, m) : nullptr;
-  float sum = 0.f;
-  for (int n = tid; n < N; n += 256) {
-    float y = 0.f;
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const bool live = n < a.N;
+  float y = 0.f;
+  if (live) {
+    const float* P = a.P;
     if (P) {
-      for (int s = 0; s < a.S; ++s) y += P[((int64_t)s * a.M + m) * N + n];
+      const int64_t st = (int64_t)a.M * a.N;
+      const float* p = P + (int64_t)m * a.N + n;
+      int s = 0;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (; s + 4 <= a.S; s += 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = p[(int64_t)(s + q) * st];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y += acc[q];
+      }
+      for (; s < a.S; ++s) y += p[(int64_t)s * st];
     }
-    if (s1) y += DT<T>::ld(s1 + n);
-    if (s2) y += DT<T>::ld(s2 + n);
-    ys[n] = y;
-    sum += y;
+    if (a.src1.base) y += DT<T>::ld(row_ptr<T>(a.src1, m) + n);
+    if (a.src2.base) y += DT<T>::ld(row_ptr<T>(a.src2, m) + n);
+    if (a.out) DT<T>::st((T*)a.out + (int64_t)m * a.N + n, y);
+    if (a.out_scatter.base)
+      DT<T>::st((T*)a.out_scatter.base + (int64_t)a.out_scatter.idx[m] * a.out_scatter.stride + n, y);
+    if (a.y32) a.y32[(int64_t)m * a.N + n] = y;
   }
-  if (a.out) {
-    T* o = (T*)a.out + (int64_t)m * N;
-    for (int n = tid; n < N; n += 256) DT<T>::st(o + n, ys[n]);
+  if (!a.stats) return;
+  float s1 = live ? y : 0.f, s2 = live ? y * y : 0.f;
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = s1;
+    red[1][threadIdx.x >> 6] = s2;
   }
-  if (a.out_scatter.base) {
-    T* o = (T*)a.out_scatter.base + (int64_t)a.out_scatter.idx[m] * a.out_scatter.stride;
-    for (int n = tid; n < N; n += 256) DT<T>::st(o + n, ys[n]);
-  }
-  if (!a.out_norm) return;
-  // mean (LayerNorm) then mean square of (y - mean)
-  sum = wave_sum(sum);
-  if ((tid & 63) == 0) red[0][tid >> 6] = sum;
   __syncthreads();
-  const float mean = a.layer_norm ? (red[0][0] + red[0][1] + red[0][2] + red[0][3]) / N : 0.f;
-  float sq = 0.f;
-  for (int n = tid; n < N; n += 256) {
-    float v = ys[n] - mean;
-    sq += v * v;
-  }
-  sq = wave_sum(sq);
-  if ((tid & 63) == 0) red[1][tid >> 6] = sq;
-  __syncthreads();
-  const float var = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / N;
-  const float inv = 1.0f / sqrtf(var + a.eps);
-  const T* gg = (const T*)a.gain;
-  const T* bb = (const T*)a.bias;
-  T* o = (T*)a.out_norm + (int64_t)m * N;
-  for (int n = tid; n < N; n += 256) {
-    float v = (ys[n] - mean) * inv * DT<T>::ld(gg + n);
-    if (bb) v += DT<T>::ld(bb + n);
-    DT<T>::st(o + n, v);
+  if (threadIdx.x == 0) {
+    float* st = a.stats + ((int64_t)m * gridDim.x + blockIdx.x) * 2;
+    st[0] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    st[1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
   }
 }
 
-void launch_reduce_rows(int dtype, const ReduceArgs& a, hipStream_t st) {
-  size_t shm = (size_t)a.N * sizeof(float);
-  if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_reduce_rows<bf16s>, dim3(a.M), dim3(256), shm, st, a);
-  else hipLaunchKernelGGL(k_reduce_rows<float>, dim3(a.M), dim3(256), shm, st, a);
+// out_norm = Norm(y) from the fp32 row and the per-block partial statistics
+// (summed in block order): RMSNorm y / sqrt(mean(y^2) + eps) * g, or
+// LayerNorm (y - mean) / sqrt(var + eps) * g + b with var = E[y^2] - mean^2.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rows_norm(ReduceArgs a) {
+  __shared__ float sh[2];
+  const int m = blockIdx.y;
+  const int nblk = gridDim.x;
+  if (threadIdx.x == 0) {
+    float s1 = 0.f, s2 = 0.f;
+    const float* st = a.stats + (int64_t)m * nblk * 2;
+    for (int b = 0; b < nblk; ++b) {
+      s1 += st[2 * b];
+      s2 += st[2 * b + 1];
+    }
+    const float mean = a.layer_norm ? s1 / a.N : 0.f;
+    const float var = s2 / a.N - mean * mean;
+    sh[0] = mean;
+    sh[1] = 1.0f / sqrtf(fmaxf(var, 0.f) + a.eps);
+  }
+  __syncthreads();
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  float v = (a.y32[(int64_t)m * a.N + n] - sh[0]) * sh[1] * DT<T>::ld((const T*)a.gain + n);
+  if (a.bias) v += DT<T>::ld((const T*)a.bias + n);
+  DT<T>::st((T*)a.out_norm + (int64_t)m * a.N + n, v);
+}
+
+void launch_reduce_rows(int dtype, const ReduceArgs& a0, hipStream_t st) {
+  ReduceArgs a = a0;
+  if (!a.out_norm) { a.y32 = nullptr; a.stats = nullptr; }
+  dim3 grid((a.N + 255) / 256, a.M);
+  if (dtype == EAGLE_BF16) {
+    hipLaunchKernelGGL(k_rows_sum<bf16s>, grid, dim3(256), 0, st, a);
+    if (a.out_norm) hipLaunchKernelGGL(k_rows_norm<bf16s>, grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_rows_sum<float>, grid, dim3(256), 0, st, a);
+    if (a.out_norm) hipLaunchKernelGGL(k_rows_norm<float>, grid, dim3(256), 0, st, a);
+  }
 }
 
 // RoPE + scatter of the fused q|k|v projection.  One thread per (row, head,

@@ -19,6 +19,7 @@ struct GemmArgs {
 };
 struct GemmShape {
   int MB, NB, mtiles, ntiles, S, kps;
+  int direct;          // barrier-free register-streaming kernel (M <= 32)
 };
 GemmShape plan_gemm(int dtype, int M, int N, int K);
 void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st);
@@ -35,6 +36,8 @@ struct ReduceArgs {
   const void* bias;
   int layer_norm;
   float eps;
+  float* y32;          // [M][N] fp32 scratch (needed when out_norm is set)
+  float* stats;        // [M][ceil(N/256)][2] scratch (needed when out_norm is set)
 };
 void launch_reduce_rows(int dtype, const ReduceArgs& a, hipStream_t st);
 
@@ -143,6 +146,11 @@ struct TreeDev {          // device pointers into eagle_tree.state
   int pool_cap, max_rows, positions;
 };
 
+struct RowsDev {          // one half of the double-buffered step rows
+  int32_t *node, *tok, *pos, *slot, *pidx;
+  uint64_t* mask;
+};
+
 struct StaticPlan {       // children created by one static / chain step
   int nchild;             // per request
   int nnext;              // rows of the next step per request
@@ -151,8 +159,8 @@ struct StaticPlan {       // children created by one static / chain step
 
 void launch_tree_init(const TreeDev& t, int B, int eagle3, int vocab, const int32_t* root_tok,
                       const int32_t* n, const int32_t* cu_n, hipStream_t st);
-void launch_tree_expand(const TreeDev& t, int B, int kind, int step, int gamma,
-                        int rows, int top_k, int top_m, int final_step,
+void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, int step,
+                        int gamma, int rows, int top_k, int top_m, int final_step,
                         const StaticPlan& plan, hipStream_t st);
 void launch_verify(const TreeDev& t, int B, const void* logits, int positions,
                    int vocab, int dtype, int gamma, int32_t* accept_len,

@@ -11,10 +11,14 @@
 // kernel merges the ~|V|/256 tile partials of every row into the log-partition,
 // the top-k ids and their confidences softmax(s * logits)[id].
 #include "kernels.h"
+#include "stream.h"
 
 namespace eagle {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int MB>
+__device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB], int m0, char* lds);
 
 template <typename T, int MB>
 __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
@@ -82,6 +86,20 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
     }
   }
 
+  lm_epilogue<T, MB>(a, acc, m0, lds);
+}
+
+// Epilogue shared by both LM-head kernels: optional raw logits, then per row
+// the tile max, tile sum of exp(s (l - max)) and the tile top-k.
+template <typename T, int MB>
+__device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB], int m0, char* lds) {
+  constexpr int NB = 4;
+  constexpr int TROW = 256 + 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int tile = blockIdx.x;
+  const int n_base = tile * 256 + wave * 64;
   // optional raw logits (parity checks)
   if (a.logits) {
 #pragma unroll
@@ -101,7 +119,6 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   // epilogue, one 16-row block at a time through LDS
   float* tl = reinterpret_cast<float*>(lds);
   const float sl = a.inv_temp * kLog2e;
-  const int ntiles = gridDim.x;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     __syncthreads();
@@ -159,7 +176,38 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
       }
     }
   }
-  (void)ntiles;
+}
+
+// M <= 32: barrier-free streaming main loop (see k_gemm_direct), full K per
+// wave, 64 vocabulary rows per wave, 256 per workgroup.
+template <typename T, int MB>
+__global__ __launch_bounds__(256) void k_lmhead_direct(LmArgs a) {
+  constexpr int NB = 4;
+  constexpr int TBYTES = 16 * (256 + 4) * 4;
+  __shared__ __attribute__((aligned(16))) char lds[TBYTES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int n_base = blockIdx.x * 256 + wave * 64;
+  const T* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = min(n_base + nb * 16 + c, a.V - 1);
+    wrow[nb] = (const T*)a.w + (int64_t)n * a.K;
+  }
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  GemmArgs ga;
+  ga.xs[0] = a.x;
+  ga.xs[1] = RowSrc{nullptr, nullptr, 0, 0};
+  ga.ksplit_x = a.K;
+  ga.M = a.M;
+  ga.N = a.V;
+  ga.K = a.K;
+  direct_mainloop<T, MB, NB, 2>(ga, wrow, 0, a.K, g, c, acc);
+  lm_epilogue<T, MB>(a, acc, 0, lds);
 }
 
 LmShape plan_lmhead(int dtype, int M, int V) {
@@ -186,6 +234,17 @@ static void launch_lm_t(const LmArgs& a, const LmShape& s, hipStream_t st) {
 }
 
 void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st) {
+  if (a.M <= 32) {
+    dim3 grid(s.ntiles, 1), block(256);
+    if (dtype == EAGLE_BF16) {
+      if (a.M <= 16) hipLaunchKernelGGL((k_lmhead_direct<bf16s, 1>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k_lmhead_direct<bf16s, 2>), grid, block, 0, st, a);
+    } else {
+      if (a.M <= 16) hipLaunchKernelGGL((k_lmhead_direct<float, 1>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k_lmhead_direct<float, 2>), grid, block, 0, st, a);
+    }
+    return;
+  }
   if (dtype == EAGLE_BF16) launch_lm_t<bf16s>(a, s, st);
   else launch_lm_t<float>(a, s, st);
 }

@@ -62,9 +62,13 @@ __device__ __forceinline__ bool before(float va, int da, int ia, float vb, int d
   return ia < ib;
 }
 
-__global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, int kind, int step, int gamma,
-                                                     int W, int top_k, int top_m, int final_step,
-                                                     StaticPlan plan) {
+// `t` points its row_* arrays at the rows of this step; `nx` holds the row
+// arrays of the next step (the other half of the double buffer): the two
+// steps have different row counts per request, so writing in place would
+// overwrite rows other workgroups have not read yet.
+__global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, RowsDev nx, int kind, int step,
+                                                     int gamma, int W, int top_k, int top_m,
+                                                     int final_step, StaticPlan plan) {
   __shared__ float sval[kPoolMax];
   __shared__ int sdep[kPoolMax];
   __shared__ int spar[kPoolMax];
@@ -89,7 +93,8 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, int kind, int st
     if (kind == EAGLE_TREE_DYNAMIC) { row = cidx / top_k; rank = cidx % top_k; }
     else { row = plan.row[cidx]; rank = plan.rank[cidx]; }
     const int r = b * W + row;
-    const int parent = t.row_node[r];
+    int parent = t.row_node[r];
+    if (parent < 0 || parent >= p0) parent = 0;   // never reached with a consistent state
     const float conf = t.topk_conf[(int64_t)r * top_k + rank];
     const int node = p0 + cidx;
     t.pool_tok[pb + node] = t.topk_id[(int64_t)r * top_k + rank];
@@ -138,12 +143,12 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, int kind, int st
       t.pool_slot[pb + u] = slot;
       t.slot_mask[b * kSlots + slot] = msk;
       const int r = b * nnext + tid;
-      t.row_node[r] = u;
-      t.row_tok[r] = t.pool_tok[pb + u];
-      t.row_pos[r] = rp + t.pool_depth[pb + u];
-      t.row_slot[r] = b * kSlots + slot;
-      t.row_pidx[r] = b * kSlots + pslot;
-      t.row_mask[r] = msk;
+      nx.node[r] = u;
+      nx.tok[r] = t.pool_tok[pb + u];
+      nx.pos[r] = rp + t.pool_depth[pb + u];
+      nx.slot[r] = b * kSlots + slot;
+      nx.pidx[r] = b * kSlots + pslot;
+      nx.mask[r] = msk;
     }
     __syncthreads();
     if (tid == 0) {
@@ -186,23 +191,24 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, int kind, int st
     const int fb = b * kMaxPos;
     uint64_t msk = 0;
     // kept sets are ancestor-closed (confidences are <= 1, so values never
-    // grow along a path and a parent ranks before its child)
-    for (int w = u; w >= 0; w = spar[w])
+    // grow along a path and a parent ranks before its child).  Parents precede
+    // children, so the walk strictly decreases and ends at the root.
+    for (int w = u, it = 0; w >= 0 && it < kPoolMax; w = (spar[w] < w ? spar[w] : -1), ++it)
       if (spos[w] >= 0) msk |= 1ull << spos[w];
     t.f_node[fb + p] = u;
     t.f_tok[fb + p] = t.pool_tok[pb + u];
-    t.f_parent[fb + p] = u == 0 ? -1 : spos[spar[u]];
+    t.f_parent[fb + p] = (u == 0 || spar[u] < 0) ? -1 : spos[spar[u]];
     t.f_depth[fb + p] = sdep[u];
     t.f_pos[fb + p] = rp + sdep[u];
     t.f_mask[fb + p] = msk;
   }
 }
 
-void launch_tree_expand(const TreeDev& t, int B, int kind, int step, int gamma, int rows,
-                        int top_k, int top_m, int final_step, const StaticPlan& plan,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(k_tree_expand, dim3(B), dim3(256), 0, st, t, kind, step, gamma, rows, top_k,
-                     top_m, final_step, plan);
+void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, int step,
+                        int gamma, int rows, int top_k, int top_m, int final_step,
+                        const StaticPlan& plan, hipStream_t st) {
+  hipLaunchKernelGGL(k_tree_expand, dim3(B), dim3(256), 0, st, t, next, kind, step, gamma, rows,
+                     top_k, top_m, final_step, plan);
 }
 
 // ---------------------------------------------------------------- verify
@@ -267,7 +273,7 @@ __global__ void k_verify_walk(TreeDev t, int B, int gamma, int32_t* accept_len,
   for (int i = 0; i <= gamma; ++i) { path[i] = -1; out[i] = -1; }
   int u = 0, acc = 0;
   path[0] = 0;
-  while (true) {
+  for (int it = 0; it <= gamma; ++it) {
     const int choice = t.choice[fb + u];
     int nxt = -1;
     for (int v = u + 1; v < T; ++v)

@@ -116,15 +116,17 @@ class GpuRound:
         nb = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
         return self.state[off:off + nb].view(dtype).view(*shape)
 
-    def rows_view(self, W):
+    def rows_view(self, step):
+        """Row descriptors of draft step `step` (double buffer by parity)."""
         B = self.cfg.B
-        M = B * W
-        return dict(node=self.view("row_node", torch.int32, (M,)),
-                    tok=self.view("row_tok", torch.int32, (M,)),
-                    pos=self.view("row_pos", torch.int32, (M,)),
-                    slot=self.view("row_slot", torch.int32, (M,)),
-                    pidx=self.view("row_pidx", torch.int32, (M,)),
-                    mask=self.view("row_mask", torch.int64, (M,)))
+        R = B * self.layout.max_rows
+        M = B * self.rows[step]
+        h = (step % 2) * R
+        out = {}
+        for k, dt in (("node", torch.int32), ("tok", torch.int32), ("pos", torch.int32),
+                      ("slot", torch.int32), ("pidx", torch.int32), ("mask", torch.int64)):
+            out[k] = self.view("row_" + k, dt, (2 * R,))[h:h + M]
+        return out
 
     def final_view(self):
         B = self.cfg.B
@@ -176,7 +178,7 @@ class GpuRound:
             M = cfg.B * self.rows[s]
             logits = feat = None
             if snapshots:
-                rows = {k: v.cpu().numpy() for k, v in self.rows_view(self.rows[s]).items()}
+                rows = {k: v.cpu().numpy() for k, v in self.rows_view(s).items()}
                 logits = torch.empty((M, cfg.head.vocab), dtype=torch.float32, device=self.dev)
                 feat = torch.empty((M, cfg.head.d), dtype=self.dt, device=self.dev)
             self.step(s, logits_out=logits, feat_out=feat)

@@ -146,10 +146,13 @@ typedef struct eagle_tree {
  *   pool_* [B][pool_cap]: tok, parent (pool index, -1 root), depth, slot
  *     (-1 if never expanded) int32; conf, value fp32
  *   pool_count [B], slot_count [B], root_pos [B] int32; slot_mask [B][64] u64
- *   rows of the NEXT draft step, request-major, row = b * W + i, [B*max_rows]:
- *     row_node, row_tok, row_pos, row_slot, row_pidx int32, row_mask u64
- *     (row_pidx = index of the input feature: b for the root row, else
- *      b*64 + parent slot)
+ *   rows of each draft step, double-buffered by step parity: the rows of
+ *   step s are entries (s % 2) * B*max_rows + b * W_s + i of
+ *     row_node, row_tok, row_pos int32, row_slot (b*64 + slot), row_pidx int32,
+ *     row_mask u64, each [2][B*max_rows]
+ *     (row_pidx = index of the input feature: b for the root row of an
+ *      EAGLE-1 round, the packed row of the last verified position for
+ *      EAGLE-3, else b*64 + parent slot)
  *   topk_id [B*max_rows][top_k] int32, topk_conf [..][top_k] fp32,
  *   lse [B*max_rows] fp32 (log-partition of s * logits)
  *   verify tree [B][64]: f_node, f_tok, f_parent (position), f_depth, f_pos

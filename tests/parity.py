@@ -155,9 +155,12 @@ def _check_topk(cfg, lg, lo, ids, conf, lse, s, m, worst):
     err = np.max(np.abs(lg.astype(np.float64) - lo))
     zo = st * lo.astype(np.float64)
     lse_o = zo.max() + np.log(np.exp(zo - zo.max()).sum())
+    # confidences that underflow fp32 (deep steps of a random-init head can put
+    # lower ranks > 100 logits below the top) compare at the floor
+    floor = 1e-30
     for i in range(K):
         c_o = np.exp(zo[ids[i]] - lse_o)
-        d = abs(np.log(max(conf[i], 1e-300)) - np.log(c_o))
+        d = abs(np.log(max(float(conf[i]), floor)) - np.log(max(c_o, floor)))
         worst["conf"] = max(worst["conf"], d)
         assert d <= 2 * st * err + 1e-5, f"step {s} row {m}: log-conf diff {d:.3g} > {2 * st * err:.3g}"
 
@@ -288,11 +291,22 @@ def check_tree_attend(case: Case, gr):
 # ------------------------------------------------------------------ whole round
 def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:0"):
     """Run one round on the GPU and check P1 (all or sampled rows), P2, P3."""
+    import time
+
+    import torch
+    t0 = time.time()
+
+    def say(msg):
+        print(f"  [{cfg.name} {time.time() - t0:6.1f}s] {msg}", flush=True)
+
     case = Case(cfg)
+    say("inputs ready")
     gr = case.gpu(device)
     tgt = case.target_dev(device)
     attend = cfg.tree == C.TREE_DYNAMIC if attend is None else attend
     snaps = gr.run(target=tgt, snapshots=True, attend=attend)
+    torch.cuda.synchronize()
+    say("GPU round done")
     report = {}
     for s in range(cfg.gamma):
         rows = None
@@ -300,6 +314,7 @@ def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:
             M = len(snaps[s].rows["node"])
             rows = sorted(set(np.linspace(0, M - 1, min(M, rows_per_step)).astype(int).tolist()))
         check_step(case, gr, snaps, s, rows=rows, report=report)
+        say(f"step {s} checked")
     check_tree_logic(case, gr, snaps)
     check_verify(case, gr, case.target, cfg.gamma)
     if attend:
@@ -310,6 +325,7 @@ def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:
         acc = check_verify(case, gr, pt, cfg.gamma)
         assert list(acc) == want, (list(acc), want)
         report["planted_accept"] = list(map(int, acc))
+    torch.cuda.synchronize()
     return report
 
 
