@@ -17,8 +17,8 @@ namespace eagle {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int MB>
-__device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB], int m0, char* lds);
+template <typename T, int MB, int NB>
+__device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB], int m0, char* lds);
 
 template <typename T, int MB>
 __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
@@ -86,20 +86,21 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
     }
   }
 
-  lm_epilogue<T, MB>(a, acc, m0, lds);
+  lm_epilogue<T, MB, NB>(a, acc, m0, lds);
 }
 
 // Epilogue shared by both LM-head kernels: optional raw logits, then per row
 // the tile max, tile sum of exp(s (l - max)) and the tile top-k.
-template <typename T, int MB>
-__device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB], int m0, char* lds) {
-  constexpr int NB = 4;
-  constexpr int TROW = 256 + 4;
+template <typename T, int MB, int NB>
+__device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB], int m0, char* lds) {
+  constexpr int TCOLS = 64 * NB;          // tile columns (4 waves x 16*NB)
+  constexpr int TROW = TCOLS + 4;
+  constexpr int PER = TCOLS / 64;         // tile columns per lane in the row pass
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int tile = blockIdx.x;
-  const int n_base = tile * 256 + wave * 64;
+  const int n_base = tile * TCOLS + wave * 16 * NB;
   // optional raw logits (parity checks)
   if (a.logits) {
 #pragma unroll
@@ -124,11 +125,11 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB]
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = wave * 64 + nb * 16 + 4 * g;
+      const int col = wave * 16 * NB + nb * 16 + 4 * g;
       f32x4 v = acc[nb][mb];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (tile * 256 + col + i >= a.V) v[i] = -INFINITY;
+        if (tile * TCOLS + col + i >= a.V) v[i] = -INFINITY;
       *reinterpret_cast<f32x4*>(tl + c * TROW + col) = v;
     }
     __syncthreads();
@@ -137,18 +138,19 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB]
       const int r = wave * 4 + rr;
       const int m = m0 + mb * 16 + r;
       if (m >= a.M) continue;
-      float v[4];
-      int id[4];
+      float v[PER];
+      int id[PER];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < PER; ++j) {
         v[j] = tl[r * TROW + lane + 64 * j];
-        id[j] = tile * 256 + lane + 64 * j;
+        id[j] = tile * TCOLS + lane + 64 * j;
+        mx = fmaxf(mx, v[j]);
       }
-      float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
       mx = wave_max(mx);
       float se = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) se += exp2f((v[j] - mx) * sl);
+      for (int j = 0; j < PER; ++j) se += exp2f((v[j] - mx) * sl);
       se = wave_sum(se);
       const int64_t pi = (int64_t)tile * a.M + m;
       if (lane == 0) {
@@ -162,7 +164,7 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB]
         float bv = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < PER; ++j) {
           const bool below = better(pv, pid, v[j], id[j]);
           if (below && better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
         }
@@ -179,15 +181,16 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[4][MB]
 }
 
 // M <= 32: barrier-free streaming main loop (see k_gemm_direct), full K per
-// wave, 64 vocabulary rows per wave, 256 per workgroup.
+// wave, 128 vocabulary rows per wave (eight 16-row MFMA blocks share each X
+// fragment and keep 32 KB of W loads in flight per wave), 512 per workgroup.
 template <typename T, int MB>
 __global__ __launch_bounds__(256) void k_lmhead_direct(LmArgs a) {
-  constexpr int NB = 4;
-  constexpr int TBYTES = 16 * (256 + 4) * 4;
+  constexpr int NB = 8;
+  constexpr int TBYTES = 16 * (512 + 4) * 4;
   __shared__ __attribute__((aligned(16))) char lds[TBYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int n_base = blockIdx.x * 256 + wave * 64;
+  const int n_base = blockIdx.x * 512 + wave * 128;
   const T* wrow[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(256) void k_lmhead_direct(LmArgs a) {
   ga.N = a.V;
   ga.K = a.K;
   direct_mainloop<T, MB, NB, 2>(ga, wrow, 0, a.K, g, c, acc);
-  lm_epilogue<T, MB>(a, acc, 0, lds);
+  lm_epilogue<T, MB, NB>(a, acc, 0, lds);
 }
 
 LmShape plan_lmhead(int dtype, int M, int V) {
@@ -216,8 +219,8 @@ LmShape plan_lmhead(int dtype, int M, int V) {
   s.MB = M >= 80 ? 5 : (M + 15) / 16;
   if (s.MB < 1) s.MB = 1;
   s.mtiles = (M + 16 * s.MB - 1) / (16 * s.MB);
-  s.cols = 256;
-  s.ntiles = (V + 255) / 256;
+  s.cols = M <= 32 ? 512 : 256;
+  s.ntiles = (V + s.cols - 1) / s.cols;
   return s;
 }
 

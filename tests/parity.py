@@ -282,10 +282,28 @@ def check_tree_attend(case: Case, gr):
             K = np.concatenate([ck, k[sel]])
             V = np.concatenate([cv, v[sel]])
             ref = o_attend(q[u], K, V, hd.group).reshape(-1)
-            e = rel_err(out[b * T + u], ref)
-            worst = max(worst, e)
-    assert worst <= TOL, worst
+            got = out[b * T + u]
+            err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+            allowed = TOL * float(np.max(np.abs(ref))) + 1.5 * attn_bf16_bound(q[u], K, V, hd.group)
+            assert err <= allowed, (b, u, err, allowed)
+            worst = max(worst, err / allowed)
     return worst
+
+
+def attn_bf16_bound(q, K, V, group):
+    """First-order bound on |O_gpu - O| from bf16 storage: rounding q and k
+    (relative 2^-9 each) moves a score by at most 2^-8 |q| |k_i| / sqrt(hd);
+    softmax turns score shifts d_i into output shifts of at most
+    2 max|d_i| max|v|; P and O are rounded to bf16 once more (2^-8 max|v|)."""
+    Hq, hd = q.shape
+    b = 0.0
+    kn = np.linalg.norm(K, axis=-1)              # [L, Hkv]
+    for h in range(Hq):
+        kv = h // group
+        ds = 2.0 ** -8 * np.linalg.norm(q[h]) * kn[:, kv].max() / np.sqrt(hd)
+        vmax = float(np.abs(V[:, kv]).max())
+        b = max(b, 2 * ds * vmax + 2.0 ** -8 * vmax)
+    return b
 
 
 # ------------------------------------------------------------------ whole round
