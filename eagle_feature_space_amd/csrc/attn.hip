@@ -239,20 +239,28 @@ constexpr int kMaxParts = 1024;
 template <typename T>
 __global__ __launch_bounds__(128) void k_attn_combine(CombineArgs a) {
   __shared__ float wts[kMaxParts];
+  __shared__ float ls[kMaxParts];
   __shared__ float red[2];
   const int h = blockIdx.x, m = blockIdx.y;
   const int np = a.nparts;
   const int64_t stride = (int64_t)a.M * a.Hq;
   const int64_t base = (int64_t)m * a.Hq + h;
+  // every thread fetches some splits' (max, sum) at once
+  for (int s = threadIdx.x; s < np; s += blockDim.x) {
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * (s * stride + base));
+    wts[s] = ml.x;
+    ls[s] = ml.y;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     float mx = -INFINITY;
-    for (int s = 0; s < np; ++s) mx = fmaxf(mx, a.part_ml[2 * (s * stride + base)]);
+    for (int s = 0; s < np; ++s) mx = fmaxf(mx, wts[s]);
     float L = 0.f;
     for (int s = 0; s < np; ++s) {
-      const float ms = a.part_ml[2 * (s * stride + base)];
+      const float ms = wts[s];
       const float f = (mx == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - mx);
       wts[s] = f;
-      L += f * a.part_ml[2 * (s * stride + base) + 1];
+      L += f * ls[s];
     }
     red[0] = L > 0.f ? 1.0f / L : 0.f;
   }

@@ -151,6 +151,7 @@ void layout_of(const Geo& g, eagle_tree_layout* L) {
   L->f_mask = bp.take(B * kMaxPos * 8);
   L->f_count = bp.take(B * 4);
   L->choice = bp.take(B * kMaxPos * 4);
+  L->choice_part = bp.take(B * kMaxPos * kVerifySplits * 8);
   L->total = bp.off;
 }
 
@@ -202,6 +203,7 @@ TreeDev tree_dev(const eagle_tree* t, const Geo& g, int step = 0) {
   d.f_mask = (uint64_t*)(s + L.f_mask);
   d.f_count = (int32_t*)(s + L.f_count);
   d.choice = (int32_t*)(s + L.choice);
+  d.choice_part = (float2*)(s + L.choice_part);
   d.pool_cap = g.pool_cap;
   d.max_rows = g.max_rows;
   d.positions = g.positions;
@@ -307,10 +309,10 @@ struct AttnPlan {
 };
 AttnPlan plan_attn(const eagle_head* h, const eagle_kv* kv) {
   AttnPlan p;
-  // about 1024 (request, kv head, split) units, splits of at least 256 keys
+  // about 2048 (request, kv head, split) units; splits are whole 64-key tiles
   const int64_t work = (int64_t)std::max(kv->max_n, 1) * kv->B * h->n_kv_heads;
-  int64_t units = (work + 64 * 1024 - 1) / (64 * 1024);
-  if (units < 4) units = 4;
+  int64_t units = (work + 64 * 2048 - 1) / (64 * 2048);
+  if (units < 1) units = 1;
   p.split_len = (int)(64 * units);
   p.nsplit = (std::max(kv->max_n, 1) + p.split_len - 1) / p.split_len;
   return p;

@@ -278,14 +278,17 @@ __global__ __launch_bounds__(256) void k_rows_sum(ReduceArgs a) {
 template <typename T>
 __global__ __launch_bounds__(256) void k_rows_norm(ReduceArgs a) {
   __shared__ float sh[2];
+  __shared__ float2 part[256];
   const int m = blockIdx.y;
-  const int nblk = gridDim.x;
+  const int nblk = gridDim.x;      // <= 256 (N <= 65536)
+  const float* st = a.stats + (int64_t)m * nblk * 2;
+  if (threadIdx.x < nblk) part[threadIdx.x] = *reinterpret_cast<const float2*>(st + 2 * threadIdx.x);
+  __syncthreads();
   if (threadIdx.x == 0) {
     float s1 = 0.f, s2 = 0.f;
-    const float* st = a.stats + (int64_t)m * nblk * 2;
     for (int b = 0; b < nblk; ++b) {
-      s1 += st[2 * b];
-      s2 += st[2 * b + 1];
+      s1 += part[b].x;
+      s2 += part[b].y;
     }
     const float mean = a.layer_norm ? s1 / a.N : 0.f;
     const float var = s2 / a.N - mean * mean;

@@ -129,6 +129,8 @@ struct MergeArgs {
 void launch_topk_merge(const MergeArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- tree
+constexpr int kVerifySplits = 16;   // workgroups per target-logit row
+
 struct TreeDev {          // device pointers into eagle_tree.state
   int32_t *pool_tok, *pool_parent, *pool_depth, *pool_slot;
   float *pool_conf, *pool_value;
@@ -143,6 +145,7 @@ struct TreeDev {          // device pointers into eagle_tree.state
   uint64_t* f_mask;
   int32_t* f_count;
   int32_t* choice;
+  float2* choice_part;    // [B][64][kVerifySplits] (max value, index as float bits)
   int pool_cap, max_rows, positions;
 };
 

@@ -266,7 +266,11 @@ __device__ __forceinline__ void block_best(float& v, int& i, float* sv, int* si)
     if (better(sv[k], si[k], v, i)) { v = sv[k]; i = si[k]; }
 }
 
+constexpr int kMergeLds = 6144;   // candidates staged in LDS (48 KB)
+
 __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
+  __shared__ float cval[kMergeLds];
+  __shared__ int cid[kMergeLds];
   __shared__ float sv[4];
   __shared__ int si[4];
   __shared__ float red[4];
@@ -291,18 +295,33 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
   __syncthreads();
   z = red[0] + red[1] + red[2] + red[3];
   const float lse = a.inv_temp * mx + logf(z);
-  // top-k over the tiles' candidates
+  // top-k over the tiles' candidates, staged once in LDS
   const int ncand = a.ntiles * a.top_k;
+  const bool staged = ncand <= kMergeLds;
+  if (staged) {
+    for (int q = tid; q < ncand; q += 256) {
+      const int t = q / a.top_k, j = q - t * a.top_k;
+      const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
+      cval[q] = a.part_val[i];
+      cid[q] = a.part_id[i];
+    }
+    __syncthreads();
+  }
   float pv = INFINITY;
   int pid = -1;
   for (int k = 0; k < a.top_k; ++k) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     for (int q = tid; q < ncand; q += 256) {
-      const int t = q / a.top_k, j = q - t * a.top_k;
-      const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
-      const float v = a.part_val[i];
-      const int id = a.part_id[i];
+      float v;
+      int id;
+      if (staged) { v = cval[q]; id = cid[q]; }
+      else {
+        const int t = q / a.top_k, j = q - t * a.top_k;
+        const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
+        v = a.part_val[i];
+        id = a.part_id[i];
+      }
       if (better(pv, pid, v, id) && better(v, id, bv, bi)) { bv = v; bi = id; }
     }
     block_best(bv, bi, sv, si);

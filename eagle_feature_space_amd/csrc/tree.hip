@@ -212,29 +212,26 @@ void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, 
 }
 
 // ---------------------------------------------------------------- verify
-template <typename T>
-__device__ __forceinline__ void argmax_row(const T* row, int V, float& bv, int& bi) {
-  for (int j = threadIdx.x; j < V; j += 256) {
-    const float v = DT<T>::ld(row + j);
-    if (better(v, j, bv, bi)) { bv = v; bi = j; }
-  }
-}
-
+// Argmax of one vocabulary slice of one verify position (value desc, lowest
+// index on ties); grid = (position, request, slice).
 template <typename T>
 __global__ __launch_bounds__(256) void k_verify_argmax(TreeDev t, const T* logits, int positions,
                                                        int V) {
   __shared__ float sv[4];
   __shared__ int si[4];
-  const int u = blockIdx.x, b = blockIdx.y;
+  const int u = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
   if (u >= t.f_count[b]) return;
+  constexpr int VEC = DT<T>::VEC;
   const T* row = logits + ((int64_t)b * positions + u) * V;
+  // slice boundaries on VEC-element granules
+  const int nvec = V / VEC;
+  const int per = (nvec + kVerifySplits - 1) / kVerifySplits;
+  const int q0 = sp * per, q1 = min(nvec, q0 + per);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  constexpr int VEC = DT<T>::VEC;
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
-  if ((addr & 15) == 0) {
-    const int nvec = V / VEC;
-    for (int q = threadIdx.x; q < nvec; q += 256) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  if (aligned) {
+    for (int q = q0 + threadIdx.x; q < q1; q += 256) {
       const u32x4 x = ld16(row + q * VEC);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -243,13 +240,17 @@ __global__ __launch_bounds__(256) void k_verify_argmax(TreeDev t, const T* logit
         if (better(v, j, bv, bi)) { bv = v; bi = j; }
       }
     }
+  } else {
+    for (int j = q0 * VEC + threadIdx.x; j < q1 * VEC; j += 256) {
+      const float v = DT<T>::ld(row + j);
+      if (better(v, j, bv, bi)) { bv = v; bi = j; }
+    }
+  }
+  if (sp == kVerifySplits - 1)   // ragged tail past the last whole granule
     for (int j = nvec * VEC + threadIdx.x; j < V; j += 256) {
       const float v = DT<T>::ld(row + j);
       if (better(v, j, bv, bi)) { bv = v; bi = j; }
     }
-  } else {
-    argmax_row(row, V, bv, bi);
-  }
   wave_best(bv, bi);
   if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
   __syncthreads();
@@ -258,8 +259,21 @@ __global__ __launch_bounds__(256) void k_verify_argmax(TreeDev t, const T* logit
     int i0 = si[0];
     for (int k = 1; k < 4; ++k)
       if (better(sv[k], si[k], v0, i0)) { v0 = sv[k]; i0 = si[k]; }
-    t.choice[b * kMaxPos + u] = i0;
+    t.choice_part[((int64_t)b * kMaxPos + u) * kVerifySplits + sp] = make_float2(v0, __int_as_float(i0));
   }
+}
+
+// target choice at a verify position: best of its slices, in slice order
+__device__ __forceinline__ int verify_choice(const TreeDev& t, int b, int u) {
+  const float2* p = t.choice_part + ((int64_t)b * kMaxPos + u) * kVerifySplits;
+  float bv = p[0].x;
+  int bi = __float_as_int(p[0].y);
+  for (int s = 1; s < kVerifySplits; ++s) {
+    const int i = __float_as_int(p[s].y);
+    if (better(p[s].x, i, bv, bi)) { bv = p[s].x; bi = i; }
+  }
+  t.choice[b * kMaxPos + u] = bi;
+  return bi;
 }
 
 __global__ void k_verify_walk(TreeDev t, int B, int gamma, int32_t* accept_len,
@@ -274,7 +288,7 @@ __global__ void k_verify_walk(TreeDev t, int B, int gamma, int32_t* accept_len,
   int u = 0, acc = 0;
   path[0] = 0;
   for (int it = 0; it <= gamma; ++it) {
-    const int choice = t.choice[fb + u];
+    const int choice = verify_choice(t, b, u);
     int nxt = -1;
     for (int v = u + 1; v < T; ++v)
       if (t.f_parent[fb + v] == u && t.f_tok[fb + v] == choice) { nxt = v; break; }
@@ -293,7 +307,7 @@ __global__ void k_verify_walk(TreeDev t, int B, int gamma, int32_t* accept_len,
 void launch_verify(const TreeDev& t, int B, const void* logits, int positions, int vocab,
                    int dtype, int gamma, int32_t* accept_len, int32_t* accept_path,
                    int32_t* out_tokens, hipStream_t st) {
-  dim3 grid(kMaxPos, B);
+  dim3 grid(kMaxPos, B, kVerifySplits);
   if (dtype == EAGLE_BF16)
     hipLaunchKernelGGL(k_verify_argmax<bf16s>, grid, dim3(256), 0, st, t, (const bf16s*)logits,
                        positions, vocab);

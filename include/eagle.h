@@ -158,6 +158,8 @@ typedef struct eagle_tree {
  *   verify tree [B][64]: f_node, f_tok, f_parent (position), f_depth, f_pos
  *     int32, f_mask u64 (ancestor-or-self over positions); f_count [B]
  *   choice [B][64] int32: target's greedy token per verify position
+ *   choice_part [B][64][16] (float max, int32 index): argmax of each of the
+ *     16 vocabulary slices of a verify position's target logits
  */
 typedef struct eagle_tree_layout {
   int32_t pool_cap, max_rows, positions;
@@ -166,7 +168,7 @@ typedef struct eagle_tree_layout {
   size_t row_node, row_tok, row_pos, row_slot, row_pidx, row_mask;
   size_t topk_id, topk_conf, lse;
   size_t f_node, f_tok, f_parent, f_depth, f_pos, f_mask, f_count;
-  size_t choice;
+  size_t choice, choice_part;
   size_t total;
 } eagle_tree_layout;
 
