@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="one 1 GiB device-to-device copy before warm-up (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -132,6 +135,12 @@ def main():
     tgt = to_dev(target, gr.dev)
     torch.cuda.synchronize()
 
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=gr.dev).fill_(7)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         gr.run(target=tgt)

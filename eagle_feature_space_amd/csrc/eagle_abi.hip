@@ -277,9 +277,11 @@ struct Prof {
 Prof g_prof;
 
 // Brackets one launch with events on its stream when profiling is enabled.
+// Each scope reserves its own event pair when it opens, so scopes may nest.
 struct ProfScope {
   ProfFamily* f = nullptr;
   hipStream_t st = nullptr;
+  size_t slot = 0;
   bool timed = false;
   ProfScope(int family, double bytes, double flops, hipStream_t s) {
     if (!(g_prof.mask >> family & 1u)) return;
@@ -295,11 +297,13 @@ struct ProfScope {
       if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
       f->ev.push_back({a, b});
     }
-    timed = hipEventRecord(f->ev[f->used].first, st) == hipSuccess;
+    slot = f->used;
+    if (hipEventRecord(f->ev[slot].first, st) != hipSuccess) return;
+    f->used += 1;
+    timed = true;
   }
   ~ProfScope() {
-    if (!timed) return;
-    if (hipEventRecord(f->ev[f->used].second, st) == hipSuccess) f->used += 1;
+    if (timed) (void)hipEventRecord(f->ev[slot].second, st);
   }
 };
 
@@ -687,8 +691,10 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
     q.k = kv->k_ctx;
     q.v = kv->v_ctx;
     q.kv_idx = nullptr;
-    ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
-    launch_epi_qkv(h->dtype, q, st);
+    {
+      ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
+      launch_epi_qkv(h->dtype, q, st);
+    }
     // root rows = each request's last verified position
     reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, kv->total_n), kNone, hbuf, kNone, hn, 1, st);
   }

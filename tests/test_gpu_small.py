@@ -40,3 +40,25 @@ def test_round_is_deterministic():
     for k in f1:
         assert torch.equal(f1[k], f2[k]), k
     assert torch.equal(a1, a2) and torch.equal(c1, c2)
+
+
+def test_profiling_every_family_eagle3():
+    """Kernel-family timing with every family on, across an EAGLE-3 round
+    (its ingest opens nested timing scopes)."""
+    from eagle_feature_space_amd import binding as E
+    from tests.parity import Case
+    case = Case(C.SMALL_CONFIGS["s3_eagle3"], with_oracle=False)
+    gr = case.gpu()
+    E.eagle_profile_reset()
+    E.eagle_profile_enable(True)
+    try:
+        for _ in range(2):
+            gr.run(target=case.target_dev())
+    finally:
+        E.eagle_profile_enable(False)
+    import torch
+    torch.cuda.synchronize()
+    for fam in ("lmhead", "gemm", "attn", "verify", "other"):
+        p = E.eagle_profile_read(fam)
+        assert p["launches"] > 0 and p["timed"] == p["launches"] and p["ms"] > 0, (fam, p)
+    E.eagle_profile_reset()
