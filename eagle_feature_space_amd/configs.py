@@ -160,6 +160,14 @@ SMALL_CONFIGS = {
                                              ffn=1024, vocab=5000),
         B=5, n=(300, 17, 0, 64, 129), tree=TREE_DYNAMIC, gamma=5, top_k=8,
         top_m=40, inv_temp=6.0, seed_w=1104, seed_in=2104, seed_t=3104),
+    # 160 rows per step after the root: the large-M tiled GEMM and LM head,
+    # with ragged row, column and vocabulary tiles
+    "s5_dynamic_many": RoundCfg(
+        name="s5_dynamic_many", head=replace(_HEAD_SMALL, vocab=6016),
+        B=20, n=tuple(int(x) for x in (5, 90, 33, 1, 64, 128, 7, 200, 0, 49,
+                                       12, 77, 150, 3, 65, 31, 100, 9, 256, 18)),
+        tree=TREE_DYNAMIC, gamma=4, top_k=8, top_m=24, inv_temp=5.0,
+        seed_w=1105, seed_in=2105, seed_t=3105),
 }
 
 ALL_CONFIGS = {**CONFIGS, **SMALL_CONFIGS}

@@ -323,7 +323,7 @@ AttnPlan plan_attn(const eagle_head* h, const eagle_kv* kv) {
 }
 
 struct Ws {
-  size_t h, hn, h1, h1n, f, q, o, act, P, y32, stats;
+  size_t h, hn, h1, h1n, f, q, o, act, P, y32, stats, logits;
   size_t att_o, att_ml, lm_max, lm_sum, lm_id, lm_val;
   size_t tk, tv, t_tok, t_kv, t_pos, t_mask;
   size_t x_in, xn_in, P_in;
@@ -377,6 +377,8 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
   w.att_o = bp.take(nparts * Mr * h->n_q_heads * h->head_dim * 4);
   w.att_ml = bp.take(nparts * Mr * h->n_q_heads * 2 * 4);
   LmShape ls = plan_lmhead(h->dtype, Mmax, h->vocab);
+  if (big_gemm_ok(h->dtype, Mmax, h->vocab, d)) ls.ntiles = std::max(ls.ntiles, logits_tiles(h->vocab));
+  w.logits = big_gemm_ok(h->dtype, Mmax, h->vocab, d) ? bp.take((size_t)Mmax * h->vocab * 4) : 0;
   w.lm_max = bp.take((size_t)ls.ntiles * Mmax * 4);
   w.lm_sum = bp.take((size_t)ls.ntiles * Mmax * 4);
   w.lm_id = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
@@ -745,7 +747,32 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   la.part_sum = (float*)(ws + w.lm_sum);
   la.part_id = (int*)(ws + w.lm_id);
   la.part_val = (float*)(ws + w.lm_val);
-  {
+  if (big_gemm_ok(h->dtype, M, h->vocab, d)) {
+    // MFMA-bound: tiled GEMM into fp32 logits, then tile partials
+    float* lg = logits_out ? logits_out : (float*)(ws + w.logits);
+    GemmArgs ga;
+    ga.xs[0] = rs(fout, nullptr, d);
+    ga.xs[1] = kNone;
+    ga.ksplit_x = d;
+    ga.M = M;
+    ga.N = h->vocab;
+    ga.K = d;
+    ga.w[0] = ga.w[1] = ga.w[2] = h->lm_head;
+    ga.nseg1 = ga.nseg2 = h->vocab;
+    ga.P = lg;
+    GemmShape gs = plan_gemm_big(M, h->vocab, d);
+    gs.S = 1;
+    gs.kps = d;
+    {
+      ProfScope ps(EAGLE_PROF_LMHEAD, (double)esz(h) * ((double)h->vocab * d + (double)M * d),
+                   2.0 * M * (double)h->vocab * d, st);
+      launch_gemm_big(ga, gs, st);
+    }
+    la.logits = nullptr;
+    ls.ntiles = logits_tiles(h->vocab);
+    ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
+    launch_logits_partials(la, lg, st);
+  } else {
     ProfScope ps(EAGLE_PROF_LMHEAD, (double)esz(h) * ((double)h->vocab * d + (double)M * d),
                  2.0 * M * (double)h->vocab * d, st);
     launch_lmhead(h->dtype, la, ls, st);

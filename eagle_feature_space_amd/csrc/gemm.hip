@@ -148,6 +148,7 @@ static int kc_of(int dtype) { return dtype == EAGLE_BF16 ? 256 : 128; }
 
 GemmShape plan_gemm(int dtype, int M, int N, int K) {
   GemmShape s;
+  if (big_gemm_ok(dtype, M, N, K)) return plan_gemm_big(M, N, K);
   if (M <= 32) {
     // direct kernel: waves of 2 n-blocks (32 columns); ~2048 waves, K spans
     // that are whole multiples of the 4-step unroll
@@ -203,6 +204,10 @@ static void launch_mb(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
 
 void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st) {
   a.kps = s.kps;
+  if (s.direct == 2) {
+    launch_gemm_big(a, s, st);
+    return;
+  }
   if (s.direct) {
     dim3 grid(s.ntiles, 1, s.S), block(256);
     if (dtype == EAGLE_BF16) {

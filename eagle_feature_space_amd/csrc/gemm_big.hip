@@ -1,0 +1,175 @@
+// Large-M GEMM (M >= 128 rows: the 70B-shaped head's 512-row draft steps, the
+// EAGLE-3 ingest over every verified position, the verify-tree projections).
+// There every weight byte is reused M times, so the contraction is MFMA-bound
+// and the kernel is a classic LDS-tiled one:
+//   workgroup tile 256 (n) x 128 (m), BK = 64, four waves of 128 x 64;
+//   each wave holds 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16 (W rows are
+//   the A operand, X rows the B operand, so a lane owns 4 consecutive n of one
+//   m and stores 16 contiguous bytes);
+//   W and X tiles are staged through LDS, double-buffered; the global loads of
+//   stage k+1 are issued into registers before the MFMAs of stage k and land
+//   in the other LDS buffer after them; LDS rows are padded by 16 bytes so the
+//   16-lane fragment reads hit 16 distinct 4-bank groups;
+//   workgroups are ordered so that the m-tiles sharing a W tile are dispatched
+//   back to back on the same XCD (workgroup i runs on XCD i mod 8) and share
+//   that XCD's L2.
+// The result goes to fp32 split-K partials P[z][m][n], consumed by the same
+// epilogue kernels as the weight-streaming GEMM.
+#include "kernels.h"
+
+namespace eagle {
+
+constexpr int kBN = 256, kBM = 128, kBK = 64;
+constexpr int kRowB = kBK * 2 + 16;                        // padded LDS row (bytes)
+constexpr int kStageB = (kBN + kBM) * kRowB;               // 55296
+constexpr int kBigLds = 2 * kStageB;                       // 110592
+
+__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, int nt, int mt, int S) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int wn = wave >> 1, wm = wave & 1;           // 2 x 2 waves
+
+  // XCD-aware order: XCD x (= wgid mod 8) walks a contiguous run of the
+  // (split, n-tile, m-tile) list, m fastest
+  const int total = nt * mt * S;
+  const int per = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int mtile = lin % mt;
+  const int ntile = (lin / mt) % nt;
+  const int z = lin / (mt * nt);
+  const int n0 = ntile * kBN, m0 = mtile * kBM;
+  const int k_begin = z * a.kps, k_end = min(a.K, k_begin + a.kps);
+
+  // global -> LDS mapping: 8 chunks of 16 B per row; W tile 2048 chunks (8
+  // per thread), X tile 1024 chunks (4 per thread)
+  const bf16s* wsrc[8];
+  const bf16s* xsrc[4];
+  const bf16s* xsrc1[4];      // second A segment (k >= ksplit_x), e.g. emb(t) of [f ; emb(t)]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = tid + 256 * i, r = q >> 3, ch = q & 7;
+    const int n = min(n0 + r, a.N - 1);
+    const bf16s* base;
+    int off;
+    if (n < a.nseg1) { base = (const bf16s*)a.w[0]; off = 0; }
+    else if (n < a.nseg2) { base = (const bf16s*)a.w[1]; off = a.nseg1; }
+    else { base = (const bf16s*)a.w[2]; off = a.nseg2; }
+    wsrc[i] = base + (int64_t)(n - off) * a.K + ch * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + 256 * i, r = q >> 3, ch = q & 7;
+    const int m = min(m0 + r, a.M - 1);
+    xsrc[i] = row_ptr<bf16s>(a.xs[0], m) + ch * 8;
+    xsrc1[i] = (a.xs[1].base ? row_ptr<bf16s>(a.xs[1], m) : xsrc[i] - ch * 8) + ch * 8;
+  }
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 wreg[8], xreg[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wreg[i] = ld16(wsrc[i] + k0);
+    const bool hi = k0 >= a.ksplit_x;      // a BK tile never straddles the split
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xreg[i] = hi ? ld16(xsrc1[i] + (k0 - a.ksplit_x)) : ld16(xsrc[i] + k0);
+  };
+  auto lstore = [&](int buf) {
+    char* base = lds + buf * kStageB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;
+      st16(base + (q >> 3) * kRowB + (q & 7) * 16, wreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      st16(base + (kBN + (q >> 3)) * kRowB + (q & 7) * 16, xreg[i]);
+    }
+  };
+
+  int buf = 0;
+  if (k_begin < k_end) {
+    gload(k_begin);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int k0 = k_begin; k0 < k_end; k0 += kBK) {
+    const bool more = k0 + kBK < k_end;
+    if (more) gload(k0 + kBK);
+    const char* wt = lds + buf * kStageB + (wn * 128) * kRowB;
+    const char* xt = lds + buf * kStageB + (kBN + wm * 64) * kRowB;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 32; ++kk) {
+      u32x4 xf[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) xf[mb] = ld16(xt + (mb * 16 + c) * kRowB + (kk * 32 + g * 8) * 2);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const u32x4 wf = ld16(wt + (nb * 16 + c) * kRowB + (kk * 32 + g * 8) * 2);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = DT<bf16s>::mma(wf, xf[mb], acc[nb][mb]);
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // acc[nb][mb]: lane holds out[m = m0 + 64 wm + 16 mb + c][n = n0 + 128 wn + 16 nb + 4 g + 0..3]
+  float* P = a.P + (int64_t)z * a.M * a.N;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const int n = n0 + wn * 128 + nb * 16 + 4 * g;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 64 + mb * 16 + c;
+      if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
+    }
+  }
+}
+
+bool big_gemm_ok(int dtype, int M, int N, int K) {
+  return dtype == EAGLE_BF16 && M >= 128 && K % kBK == 0 && N % 16 == 0;
+}
+
+GemmShape plan_gemm_big(int M, int N, int K) {
+  GemmShape s;
+  s.direct = 2;
+  s.MB = 0;
+  s.NB = 0;
+  s.ntiles = (N + kBN - 1) / kBN;
+  s.mtiles = (M + kBM - 1) / kBM;
+  const int tiles = s.ntiles * s.mtiles;
+  const int kst = K / kBK;
+  int S = (512 + tiles - 1) / tiles;      // at least two workgroups per CU
+  if (S > kst / 4) S = kst / 4 > 0 ? kst / 4 : 1;   // keep >= 256 K per split
+  if (S < 1) S = 1;
+  const int sps = (kst + S - 1) / S;
+  s.kps = sps * kBK;
+  s.S = (K + s.kps - 1) / s.kps;
+  return s;
+}
+
+void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_big),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kBigLds);
+    attr = true;
+  }
+  a.kps = s.kps;
+  const int total = s.ntiles * s.mtiles * s.S;
+  const int per = (total + 7) / 8;
+  hipLaunchKernelGGL(k_gemm_big, dim3(per * 8), dim3(256), kBigLds, st, a, s.ntiles, s.mtiles, s.S);
+}
+
+}  // namespace eagle

@@ -19,10 +19,16 @@ struct GemmArgs {
 };
 struct GemmShape {
   int MB, NB, mtiles, ntiles, S, kps;
-  int direct;          // barrier-free register-streaming kernel (M <= 32)
+  int direct;          // 1: barrier-free streaming (M <= 32), 2: MFMA-tiled big GEMM
 };
+// plan_gemm picks the kernel: direct streaming (M <= 32), LDS-staged
+// streaming (M < 128 or unsupported shape) or the MFMA-tiled big GEMM.
+// The A operand's split point (ksplit_x) must be a multiple of 64.
 GemmShape plan_gemm(int dtype, int M, int N, int K);
 void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st);
+bool big_gemm_ok(int dtype, int M, int N, int K);
+GemmShape plan_gemm_big(int M, int N, int K);
+void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st);
 
 // y = sum_s P + src1 + src2 ; out / out_scatter = y ; out_norm = Norm(y)
 struct ReduceArgs {
@@ -113,6 +119,9 @@ struct LmShape {
 };
 LmShape plan_lmhead(int dtype, int M, int V);
 void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st);
+// large M: logits from the MFMA-tiled GEMM, then per-(row, 2048-column tile) partials
+int logits_tiles(int V);
+void launch_logits_partials(const LmArgs& a, const float* logits, hipStream_t st);
 
 struct MergeArgs {
   const float* part_max;

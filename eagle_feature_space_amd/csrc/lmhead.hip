@@ -252,6 +252,63 @@ void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st)
   else launch_lm_t<float>(a, s, st);
 }
 
+// Tile partials from materialised logits (large M, after the MFMA-tiled GEMM):
+// one wave per (row, 2048-column tile), same partial format as the fused
+// epilogue: tile max, tile sum of exp(s (l - max)), tile top-k.
+constexpr int kLogitTile = 2048;
+__global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* logits) {
+  constexpr int PER = kLogitTile / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x;
+  const int m = blockIdx.y * 4 + wave;
+  if (m >= a.M) return;
+  const float* row = logits + (int64_t)m * a.V + tile * kLogitTile;
+  float v[PER];
+  int id[PER];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int n = tile * kLogitTile + lane + 64 * j;
+    v[j] = n < a.V ? row[lane + 64 * j] : -INFINITY;
+    id[j] = n;
+    mx = fmaxf(mx, v[j]);
+  }
+  mx = wave_max(mx);
+  const float sl = a.inv_temp * kLog2e;
+  float se = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) se += exp2f((v[j] - mx) * sl);
+  se = wave_sum(se);
+  const int64_t pi = (int64_t)tile * a.M + m;
+  if (lane == 0) {
+    a.part_max[pi] = mx;
+    a.part_sum[pi] = se;
+  }
+  float pv = INFINITY;
+  int pid = -1;
+  for (int k = 0; k < a.top_k; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (better(pv, pid, v[j], id[j]) && better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
+    wave_best(bv, bi);
+    if (lane == 0) {
+      a.part_val[pi * a.top_k + k] = bv;
+      a.part_id[pi * a.top_k + k] = bi;
+    }
+    pv = bv;
+    pid = bi;
+  }
+}
+
+int logits_tiles(int V) { return (V + kLogitTile - 1) / kLogitTile; }
+
+void launch_logits_partials(const LmArgs& a, const float* logits, hipStream_t st) {
+  dim3 grid(logits_tiles(a.V), (a.M + 3) / 4);
+  hipLaunchKernelGGL(k_logits_partials, grid, dim3(256), 0, st, a, logits);
+}
+
 // ---------------------------------------------------------------- merge
 __device__ __forceinline__ void block_best(float& v, int& i, float* sv, int* si) {
   wave_best(v, i);
