@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <vector>
 
+
 #include "kernels.h"
 
 using namespace eagle;
@@ -293,8 +294,12 @@ struct ProfScope {
     if (f->used >= kMaxTimed) return;
     if (f->used == f->ev.size()) {
       hipEvent_t a, b;
-      if (hipEventCreate(&a) != hipSuccess) return;
-      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      // device-scope release only: the timed kernels' results stay on the GPU
+      if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return;
+      if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return;
+      }
       f->ev.push_back({a, b});
     }
     slot = f->used;
@@ -324,6 +329,7 @@ AttnPlan plan_attn(const eagle_head* h, const eagle_kv* kv) {
 
 struct Ws {
   size_t h, hn, h1, h1n, f, q, o, act, P, y32, stats, logits;
+  size_t rs0, rs1;   // row-complete path (M <= 16): per-block row statistics
   size_t att_o, att_ml, lm_max, lm_sum, lm_id, lm_val;
   size_t tk, tv, t_tok, t_kv, t_pos, t_mask;
   size_t x_in, xn_in, P_in;
@@ -385,6 +391,11 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
   w.lm_val = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
   w.tk = bp.take((size_t)g.B * kSlots * kvd * e);
   w.tv = bp.take((size_t)g.B * kSlots * kvd * e);
+  {
+    const int R = std::min(Mmax, 16);
+    w.rs0 = bp.take((size_t)R * (d / 16) * 2 * 4);
+    w.rs1 = bp.take((size_t)R * (d / 16) * 2 * 4);
+  }
   w.t_tok = bp.take((size_t)Mt * 4);
   w.t_kv = bp.take((size_t)Mt * 4);
   w.t_pos = bp.take((size_t)Mt * 4);
@@ -436,8 +447,11 @@ float* g_y32 = nullptr;
 float* g_stats = nullptr;
 
 void reduce(const eagle_head* h, const float* P, int S, int M, int N, RowSrc s1, RowSrc s2,
-            void* out, RowSrc scatter, void* out_norm, int which_norm, hipStream_t st) {
+            void* out, RowSrc scatter, void* out_norm, int which_norm, hipStream_t st,
+            bool keep_stats = false, void* out_g = nullptr) {
   ReduceArgs a;
+  a.keep_stats = keep_stats;
+  a.out_g = out_g;
   a.y32 = g_y32;
   a.stats = g_stats;
   a.P = P;
@@ -526,6 +540,30 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
   c.out = out;
   ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
   launch_attn_combine(h->dtype, c, st);
+}
+
+// Row-complete GEMM launch (M <= 16): B-operand rows w0|w1|w2 split at
+// nseg1 / nseg2; A operand, row scale and epilogue fields set by the caller.
+RowsArgs rows_args(int M, int N, int K, const void* w0, const void* w1, const void* w2, int nseg1,
+                   int nseg2) {
+  RowsArgs r;
+  memset(&r, 0, sizeof(r));
+  r.g.M = M;
+  r.g.N = N;
+  r.g.K = K;
+  r.g.w[0] = w0;
+  r.g.w[1] = w1 ? w1 : w0;
+  r.g.w[2] = w2 ? w2 : (w1 ? w1 : w0);
+  r.g.nseg1 = nseg1;
+  r.g.nseg2 = nseg2;
+  r.g.ksplit_x = K;
+  return r;
+}
+
+void run_rows(const eagle_head* h, int ep, const RowsArgs& r, hipStream_t st) {
+  ProfScope ps(EAGLE_PROF_GEMM, (double)esz(h) * ((double)r.g.N * r.g.K + (double)r.g.M * r.g.K),
+               2.0 * r.g.M * (double)r.g.N * r.g.K, st);
+  launch_gemm_rows(h->dtype, ep, r, st);
 }
 
 int finish(int status) {
@@ -660,17 +698,39 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   GemmShape sh;
 
   // ---- layer input h and N1(h)
+  // Row-complete path (M <= 16, RMSNorm): every projection of the layer is
+  // one kernel with its epilogue fused; N1 / N2 are folded through the next
+  // projection (operand h * g, result rows scaled by rstd from the statistics).
+  const bool rows = rows_gemm_ok(M, d, 32) && h->norm == EAGLE_NORM_RMS;
+  const int kvd = h->n_kv_heads * h->head_dim;
+  const float* nst = g_stats;          // row statistics of h (row path)
+  int nblk = (d + 255) / 256;
   if (!e3) {
     const void* fsrc = step == 0 ? f_root : kv->feat_slot;
-    gemm(h, rs(fsrc, td.row_pidx, d, step == 0 ? (int64_t)B : (int64_t)B * kSlots), rs(h->emb, td.row_tok, d, h->vocab), d, M, d, 2 * d, h->w_fc,
-         nullptr, nullptr, d, d, P, &sh, st);
-    reduce(h, P, sh.S, M, d, kNone, kNone, hbuf, kNone, hn, 1, st);
+    const RowSrc xf = rs(fsrc, td.row_pidx, d, step == 0 ? (int64_t)B : (int64_t)B * kSlots);
+    const RowSrc xe = rs(h->emb, td.row_tok, d, h->vocab);
+    if (rows) {
+      RowsArgs r = rows_args(M, d, 2 * d, h->w_fc, nullptr, nullptr, d, d);
+      r.g.xs[0] = xf;
+      r.g.xs[1] = xe;
+      r.g.ksplit_x = d;
+      r.out = hbuf;
+      r.out_g = hn;
+      r.gain = h->norm1_g;
+      r.stats = (float*)(ws + w.rs0);
+      run_rows(h, EP_STORE, r, st);
+      nst = r.stats;
+      nblk = d / 16;
+    } else {
+      gemm(h, xf, xe, d, M, d, 2 * d, h->w_fc, nullptr, nullptr, d, d, P, &sh, st);
+      reduce(h, P, sh.S, M, d, kNone, kNone, hbuf, kNone, hn, 1, st);
+    }
   } else if (step > 0) {
     reduce(h, nullptr, 0, M, d, rs(kv->feat_slot, td.row_pidx, d, (int64_t)B * kSlots), rs(h->emb, td.row_tok, d, h->vocab),
-           hbuf, kNone, hn, 1, st);
+           hbuf, kNone, rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
   } else {
     // ingest of every verified position: g = [l;m;h] W_fuse^T, x = g + emb(t_next)
-    const int Tn = (int)kv->total_n, kvd = h->n_kv_heads * h->head_dim;
+    const int Tn = (int)kv->total_n;
     float* Pin = (float*)(ws + w.P_in);
     gemm(h, rs(lmh, nullptr, 3 * d), kNone, 3 * d, Tn, d, 3 * d, h->w_fuse, nullptr, nullptr, d,
          d, Pin, &sh, st);
@@ -698,39 +758,87 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
       launch_epi_qkv(h->dtype, q, st);
     }
     // root rows = each request's last verified position
-    reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, kv->total_n), kNone, hbuf, kNone, hn, 1, st);
+    reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, kv->total_n), kNone, hbuf, kNone,
+           rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
   }
 
   // ---- attention sub-layer
-  qkv_rope(h, ws, w, hn, M, td.row_pos, kv->k_slot, kv->v_slot, td.row_slot, st);
+  if (rows) {
+    RowsArgs r = rows_args(M, qd + 2 * kvd, d, h->w_q, h->w_k, h->w_v, qd, qd + kvd);
+    r.g.xs[0] = rs(hn, nullptr, d);
+    r.xstats = nst;
+    r.xnblk = nblk;
+    r.eps = h->eps;
+    r.Hq = h->n_q_heads;
+    r.Hkv = h->n_kv_heads;
+    r.hd = h->head_dim;
+    r.theta = h->rope_theta;
+    r.pos = td.row_pos;
+    r.q = ws + w.q;
+    r.k = kv->k_slot;
+    r.v = kv->v_slot;
+    r.kv_idx = td.row_slot;
+    run_rows(h, EP_ROPE, r, st);
+  } else {
+    qkv_rope(h, ws, w, hn, M, td.row_pos, kv->k_slot, kv->v_slot, td.row_slot, st);
+  }
   attend(h, kv, ws, w, W, kv->k_slot, kv->v_slot, td.row_mask, ws + w.o, st);
-  gemm(h, rs(ws + w.o, nullptr, qd), kNone, qd, M, d, qd, h->w_o, nullptr, nullptr, d, d, P, &sh,
-       st);
-  reduce(h, P, sh.S, M, d, rs(hbuf, nullptr, d), kNone, ws + w.h1, kNone, ws + w.h1n, 2, st);
+  if (rows) {
+    RowsArgs r = rows_args(M, d, qd, h->w_o, nullptr, nullptr, d, d);
+    r.g.xs[0] = rs(ws + w.o, nullptr, qd);
+    r.res = rs(hbuf, nullptr, d);
+    r.out = ws + w.h1;
+    r.out_g = ws + w.h1n;
+    r.gain = h->norm2_g;
+    r.stats = (float*)(ws + w.rs1);
+    run_rows(h, EP_STORE, r, st);
+  } else {
+    gemm(h, rs(ws + w.o, nullptr, qd), kNone, qd, M, d, qd, h->w_o, nullptr, nullptr, d, d, P, &sh,
+         st);
+    reduce(h, P, sh.S, M, d, rs(hbuf, nullptr, d), kNone, ws + w.h1, kNone, ws + w.h1n, 2, st);
+  }
 
   // ---- MLP sub-layer
-  if (swiglu)
-    gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, 2 * ffn, d, h->w_gate, h->w_up, nullptr, ffn,
-         2 * ffn, P, &sh, st);
-  else
-    gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn, P,
-         &sh, st);
-  ActArgs aa;
-  aa.P = P;
-  aa.S = sh.S;
-  aa.M = M;
-  aa.F = ffn;
-  aa.swiglu = swiglu;
-  aa.out = ws + w.act;
-  {
-    ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
-    launch_epi_act(h->dtype, aa, st);
-  }
-  gemm(h, rs(ws + w.act, nullptr, ffn), kNone, ffn, M, d, ffn, h->w_down, nullptr, nullptr, d, d,
-       P, &sh, st);
   void* fout = feat_out ? feat_out : (void*)(ws + w.f);
-  reduce(h, P, sh.S, M, d, rs(ws + w.h1, nullptr, d), kNone, fout,
-         rs(kv->feat_slot, td.row_slot, d), nullptr, 0, st);
+  if (rows) {
+    RowsArgs r = swiglu ? rows_args(M, 2 * ffn, d, h->w_gate, h->w_up, nullptr, ffn, 2 * ffn)
+                        : rows_args(M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn);
+    r.g.xs[0] = rs(ws + w.h1n, nullptr, d);
+    r.xstats = (const float*)(ws + w.rs1);
+    r.xnblk = d / 16;
+    r.eps = h->eps;
+    r.act_F = ffn;
+    r.out = ws + w.act;
+    run_rows(h, swiglu ? EP_SWIGLU : EP_GELU, r, st);
+    RowsArgs r2 = rows_args(M, d, ffn, h->w_down, nullptr, nullptr, d, d);
+    r2.g.xs[0] = rs(ws + w.act, nullptr, ffn);
+    r2.res = rs(ws + w.h1, nullptr, d);
+    r2.out = fout;
+    r2.scatter = rs(kv->feat_slot, td.row_slot, d);
+    run_rows(h, EP_STORE, r2, st);
+  } else {
+    if (swiglu)
+      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, 2 * ffn, d, h->w_gate, h->w_up, nullptr,
+           ffn, 2 * ffn, P, &sh, st);
+    else
+      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn,
+           P, &sh, st);
+    ActArgs aa;
+    aa.P = P;
+    aa.S = sh.S;
+    aa.M = M;
+    aa.F = ffn;
+    aa.swiglu = swiglu;
+    aa.out = ws + w.act;
+    {
+      ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
+      launch_epi_act(h->dtype, aa, st);
+    }
+    gemm(h, rs(ws + w.act, nullptr, ffn), kNone, ffn, M, d, ffn, h->w_down, nullptr, nullptr, d, d,
+         P, &sh, st);
+    reduce(h, P, sh.S, M, d, rs(ws + w.h1, nullptr, d), kNone, fout,
+           rs(kv->feat_slot, td.row_slot, d), nullptr, 0, st);
+  }
 
   // ---- LM head + softmax / top-k
   LmShape ls = plan_lmhead(h->dtype, M, h->vocab);

@@ -227,6 +227,23 @@ void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st) {
 }
 
 // ----------------------------------------------------------------- epilogues
+// sum_{s < S} p[s * stride], added in order s = 0, 1, ...; the loads of up to
+// 16 partials are issued together (indexes clamped into range, the clamped
+// duplicates replaced by 0 before they are added), so the epilogues pay one
+// memory latency instead of S.
+__device__ __forceinline__ float sum_parts(const float* p, int64_t stride, int S) {
+  float y = 0.f;
+  if (S <= 0) return y;
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = p[(int64_t)min(s0 + q, S - 1) * stride];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) y += s0 + q < S ? v[q] : 0.f;
+  }
+  return y;
+}
+
 // Row epilogue, column-parallel (one thread per column, grid = column blocks x
 // rows, so even a single row spreads over many workgroups):
 //   y = sum_s P[s][m] + src1[m] + src2[m]            (fp32, fixed order)
@@ -240,26 +257,14 @@ __global__ __launch_bounds__(256) void k_rows_sum(ReduceArgs a) {
   const bool live = n < a.N;
   float y = 0.f;
   if (live) {
-    const float* P = a.P;
-    if (P) {
-      const int64_t st = (int64_t)a.M * a.N;
-      const float* p = P + (int64_t)m * a.N + n;
-      int s = 0;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (; s + 4 <= a.S; s += 4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = p[(int64_t)(s + q) * st];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y += acc[q];
-      }
-      for (; s < a.S; ++s) y += p[(int64_t)s * st];
-    }
+    if (a.P) y = sum_parts(a.P + (int64_t)m * a.N + n, (int64_t)a.M * a.N, a.S);
     if (a.src1.base) y += DT<T>::ld(row_ptr<T>(a.src1, m) + n);
     if (a.src2.base) y += DT<T>::ld(row_ptr<T>(a.src2, m) + n);
     if (a.out) DT<T>::st((T*)a.out + (int64_t)m * a.N + n, y);
     if (a.out_scatter.base)
       DT<T>::st((T*)a.out_scatter.base + (int64_t)a.out_scatter.idx[m] * a.out_scatter.stride + n, y);
     if (a.y32) a.y32[(int64_t)m * a.N + n] = y;
+    if (a.out_g) DT<T>::st((T*)a.out_g + (int64_t)m * a.N + n, y * DT<T>::ld((const T*)a.gain + n));
   }
   if (!a.stats) return;
   float s1 = live ? y : 0.f, s2 = live ? y * y : 0.f;
@@ -287,6 +292,14 @@ __global__ __launch_bounds__(256) void k_rows_norm(ReduceArgs a) {
   const int m = blockIdx.y;
   const int nblk = gridDim.x;      // <= 256 (N <= 65536)
   const float* st = a.stats + (int64_t)m * nblk * 2;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const bool live = n < a.N;
+  float y = 0.f, gn = 0.f, bs = 0.f;
+  if (live) {
+    y = a.y32[(int64_t)m * a.N + n];
+    gn = DT<T>::ld((const T*)a.gain + n);
+    if (a.bias) bs = DT<T>::ld((const T*)a.bias + n);
+  }
   if (threadIdx.x < nblk) part[threadIdx.x] = *reinterpret_cast<const float2*>(st + 2 * threadIdx.x);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -301,16 +314,15 @@ __global__ __launch_bounds__(256) void k_rows_norm(ReduceArgs a) {
     sh[1] = 1.0f / sqrtf(fmaxf(var, 0.f) + a.eps);
   }
   __syncthreads();
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= a.N) return;
-  float v = (a.y32[(int64_t)m * a.N + n] - sh[0]) * sh[1] * DT<T>::ld((const T*)a.gain + n);
-  if (a.bias) v += DT<T>::ld((const T*)a.bias + n);
+  if (!live) return;
+  float v = (y - sh[0]) * sh[1] * gn;
+  if (a.bias) v += bs;
   DT<T>::st((T*)a.out_norm + (int64_t)m * a.N + n, v);
 }
 
 void launch_reduce_rows(int dtype, const ReduceArgs& a0, hipStream_t st) {
   ReduceArgs a = a0;
-  if (!a.out_norm) { a.y32 = nullptr; a.stats = nullptr; }
+  if (!a.out_norm && !a.keep_stats) { a.y32 = nullptr; a.stats = nullptr; }
   dim3 grid((a.N + 255) / 256, a.M);
   if (dtype == EAGLE_BF16) {
     hipLaunchKernelGGL(k_rows_sum<bf16s>, grid, dim3(256), 0, st, a);
@@ -335,13 +347,10 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
   const int h = (int)((t / half) % heads);
   const int m = (int)(t / ((int64_t)half * heads));
   const int N = heads * a.hd;
-  float x1 = 0.f, x2 = 0.f;
   const int c1 = h * a.hd + i, c2 = c1 + half;
-  for (int s = 0; s < a.S; ++s) {
-    const float* row = a.P + ((int64_t)s * a.M + m) * N;
-    x1 += row[c1];
-    x2 += row[c2];
-  }
+  const int64_t pst = (int64_t)a.M * N;
+  float x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S);
+  float x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S);
   int pos;
   if (a.pos) pos = a.pos[m];
   else {  // packed context rows: position inside the request
@@ -387,16 +396,10 @@ __global__ __launch_bounds__(256) void k_epi_act(ActArgs a) {
   if (t >= (int64_t)a.M * a.F) return;
   const int m = (int)(t / a.F), j = (int)(t % a.F);
   const int N = a.swiglu ? 2 * a.F : a.F;
-  float gsum = 0.f, usum = 0.f;
-  for (int s = 0; s < a.S; ++s) {
-    const float* row = a.P + ((int64_t)s * a.M + m) * N;
-    if (a.swiglu) {
-      gsum += row[j];
-      usum += row[a.F + j];
-    } else {
-      usum += row[j];
-    }
-  }
+  const int64_t pst = (int64_t)a.M * N;
+  const float* row = a.P + (int64_t)m * N;
+  const float usum = sum_parts(row + (a.swiglu ? a.F : 0) + j, pst, a.S);
+  const float gsum = a.swiglu ? sum_parts(row + j, pst, a.S) : 0.f;
   float y;
   if (a.swiglu) y = gsum / (1.0f + expf(-gsum)) * usum;
   else y = 0.5f * usum * (1.0f + erff(usum * 0.70710678118654752f));

@@ -44,8 +44,44 @@ struct ReduceArgs {
   float eps;
   float* y32;          // [M][N] fp32 scratch (needed when out_norm is set)
   float* stats;        // [M][ceil(N/256)][2] scratch (needed when out_norm is set)
+  int keep_stats;      // write y32 / stats even without out_norm (a later kernel normalises)
+  void* out_g;         // optional: y * gain (T), the operand of a folded RMSNorm
 };
 void launch_reduce_rows(int dtype, const ReduceArgs& a, hipStream_t st);
+
+// Row-complete streaming GEMM for M <= 16 rows: each workgroup owns one
+// 16-row block of W over the whole K (its waves split K and reduce through
+// LDS), so the row epilogue runs in the same kernel.  RMSNorm is folded
+// through the projection: the producer stores bf16(y * g) and per-block sums
+// of y^2, the consumer scales its result rows by rstd.
+enum { EP_STORE = 0, EP_ROPE = 1, EP_SWIGLU = 2, EP_GELU = 3 };
+struct RowsArgs {
+  GemmArgs g;              // xs / ksplit_x (A operand), M, N, K, w / nseg (B operand rows)
+  const float* xstats;     // optional: [M][xnblk] (sum, sum of squares) of the rows the
+  int xnblk;               //   A operand was formed from; result rows scaled by rstd
+  float eps;
+  // EP_STORE: y = acc + res ; out / scatter = y, out_g = y * gain (T), stats [M][N/16]
+  RowSrc res;
+  void* out;
+  RowSrc scatter;
+  void* out_g;
+  const void* gain;
+  float* stats;
+  // EP_SWIGLU: act [M][act_F] = silu(gate) * up, gate rows [0, F), up rows [F, 2F)
+  // EP_GELU: act [M][N] = gelu(acc)
+  int act_F;
+  // EP_ROPE: fused q|k|v columns; rotate q and k heads, scatter k / v rows
+  int Hq, Hkv, hd;
+  float theta;
+  const int32_t* pos;
+  void* q;
+  void* k;
+  void* v;
+  const int32_t* kv_idx;
+};
+// shapes the row-complete path takes (M <= 16, N % 16 == 0, K % 32 == 0)
+bool rows_gemm_ok(int M, int N, int K);
+void launch_gemm_rows(int dtype, int ep, const RowsArgs& a, hipStream_t st);
 
 struct QkvArgs {
   const float* P;
