@@ -5,7 +5,7 @@
 // kernel boundaries (each drains the GPU and writes back its caches).  The
 // split-K streaming kernel needs separate reduction, norm, RoPE and activation
 // kernels after it; this one does not:
-//   * a workgroup of 16 waves owns one 16-row block of W over the WHOLE of K;
+//   * a workgroup of 8 waves owns one 16-row block of W over the WHOLE of K;
 //     its waves stream disjoint K ranges of those rows, double-buffered in
 //     registers, and reduce their accumulators through LDS in wave order
 //     (deterministic), so the epilogue sees final values;
@@ -28,7 +28,7 @@
 namespace eagle {
 
 constexpr int kRowsU = 4;       // MFMA steps per register batch
-constexpr int kRowsWaves = 16;
+constexpr int kRowsWaves = 8;   // two workgroups per CU hide each other's reduction barrier
 constexpr int kRowsStats = 16;  // statistics partials per lane (K <= 16384: <= 1024 blocks)
 
 template <typename T>
@@ -45,11 +45,9 @@ __device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
-template <typename T, int EP>
-__global__ __launch_bounds__(64 * kRowsWaves) void k_gemm_rows(RowsArgs a) {
-  constexpr int WAVES = kRowsWaves;
+template <typename T, int EP, int WAVES = kRowsWaves, int U = kRowsU>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_rows(RowsArgs a) {
   constexpr int VEC = DT<T>::VEC;
-  constexpr int U = kRowsU;
   constexpr int KS = 4 * VEC;            // K of one MFMA step
   constexpr int STEP = U * KS;
   __shared__ f32x4 red[WAVES][64];
@@ -173,6 +171,15 @@ __global__ __launch_bounds__(64 * kRowsWaves) void k_gemm_rows(RowsArgs a) {
     for (int j = 0; j < kRowsStats; ++j) s2 += lane + 64 * j < a.xnblk ? sp[j] : 0.f;
     s2 = wave_sum(s2);
     if (lane == 0) s_rstd[wave] = 1.0f / sqrtf(s2 / K + a.eps);
+    // rows past the wave count (fewer than 16 waves): same order, not prefetched
+    for (int r = wave + WAVES; r < M; r += WAVES) {
+      const float* st = a.xstats + (int64_t)r * a.xnblk * 2;
+      float t2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < kRowsStats; ++j) t2 += lane + 64 * j < a.xnblk ? st[2 * min(lane + 64 * j, a.xnblk - 1) + 1] : 0.f;
+      t2 = wave_sum(t2);
+      if (lane == 0) s_rstd[r] = 1.0f / sqrtf(t2 / K + a.eps);
+    }
   }
   // reduce the waves' partial sums in wave order
   red[wave][lane] = acc;

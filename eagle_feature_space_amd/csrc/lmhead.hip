@@ -183,14 +183,14 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
 // M <= 32: barrier-free streaming main loop (see k_gemm_direct), full K per
 // wave, 128 vocabulary rows per wave (eight 16-row MFMA blocks share each X
 // fragment and keep 32 KB of W loads in flight per wave), 512 per workgroup.
-template <typename T, int MB>
+template <typename T, int MB, int NB = 8, int U = 2>
 __global__ __launch_bounds__(256) void k_lmhead_direct(LmArgs a) {
-  constexpr int NB = 8;
-  constexpr int TBYTES = 16 * (512 + 4) * 4;
+  constexpr int TCOLS = 64 * NB;
+  constexpr int TBYTES = 16 * (TCOLS + 4) * 4;
   __shared__ __attribute__((aligned(16))) char lds[TBYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int n_base = blockIdx.x * 512 + wave * 128;
+  const int n_base = blockIdx.x * TCOLS + wave * 16 * NB;
   const T* wrow[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void k_lmhead_direct(LmArgs a) {
   ga.M = a.M;
   ga.N = a.V;
   ga.K = a.K;
-  direct_mainloop<T, MB, NB, 2>(ga, wrow, 0, a.K, g, c, acc);
+  direct_mainloop<T, MB, NB, U>(ga, wrow, 0, a.K, g, c, acc);
   lm_epilogue<T, MB, NB>(a, acc, 0, lds);
 }
 
