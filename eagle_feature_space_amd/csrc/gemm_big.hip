@@ -1,7 +1,8 @@
-// Large-M GEMM (M >= 128 rows: the 70B-shaped head's 512-row draft steps, the
-// EAGLE-3 ingest over every verified position, the verify-tree projections).
-// There every weight byte is reused M times, so the contraction is MFMA-bound
-// and the kernel is a classic LDS-tiled one:
+// Large-M GEMM (M >= 64 rows: the 80-row EAGLE-2 steps, the 70B-shaped head's
+// 64- and 512-row draft steps, the EAGLE-3 ingest over every verified
+// position, the verify-tree projections).  Every weight byte is reused M
+// times, so W is read once per 128-row tile and the kernel is a classic
+// LDS-tiled one:
 //   workgroup tile 256 (n) x 128 (m), BK = 64, four waves of 128 x 64;
 //   each wave holds 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16 (W rows are
 //   the A operand, X rows the B operand, so a lane owns 4 consecutive n of one
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, int nt, int mt, in
 }
 
 bool big_gemm_ok(int dtype, int M, int N, int K) {
-  return dtype == EAGLE_BF16 && M >= 128 && K % kBK == 0 && N % 16 == 0;
+  return dtype == EAGLE_BF16 && M >= 64 && K % kBK == 0 && N % 16 == 0;
 }
 
 GemmShape plan_gemm_big(int M, int N, int K) {

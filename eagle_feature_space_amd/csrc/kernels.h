@@ -22,7 +22,7 @@ struct GemmShape {
   int direct;          // 1: barrier-free streaming (M <= 32), 2: MFMA-tiled big GEMM
 };
 // plan_gemm picks the kernel: direct streaming (M <= 32), LDS-staged
-// streaming (M < 128 or unsupported shape) or the MFMA-tiled big GEMM.
+// streaming (M < 64 or unsupported shape) or the MFMA-tiled big GEMM.
 // The A operand's split point (ksplit_x) must be a multiple of 64.
 GemmShape plan_gemm(int dtype, int M, int N, int K);
 void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st);
