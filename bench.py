@@ -36,6 +36,7 @@ FP32_PEAK_TFLOPS = 157.3
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"lmhead": ["eagle_feature_space_amd/csrc/lmhead.hip",
+                             "eagle_feature_space_amd/csrc/stream.h",
                              "eagle_feature_space_amd/csrc/common.h"]}
 
 
