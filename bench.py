@@ -144,7 +144,7 @@ def main():
         del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        gr.run(target=tgt)
+        gr.run(target=tgt, attend=cfg.tree_attend)
     torch.cuda.synchronize()
 
     # ---- timed region: K rounds; HIP events bracket the LM-head launches only
@@ -153,7 +153,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        gr.run(target=tgt)
+        gr.run(target=tgt, attend=cfg.tree_attend)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     E.eagle_profile_enable(False)
@@ -179,7 +179,7 @@ def main():
         E.eagle_profile_reset()
         E.eagle_profile_enable(True)
         for _ in range(R):
-            gr.run(target=tgt)
+            gr.run(target=tgt, attend=cfg.tree_attend)
         torch.cuda.synchronize()
         E.eagle_profile_enable(False)
         breakdown = {}
@@ -199,6 +199,32 @@ def main():
         breakdown["kernels_us_per_round"] = round(tot_ms * 1e3 / R, 2)
         breakdown["round_bytes_GB"] = round(tot_bytes / R / 1e9, 4)
         breakdown["round_hbm_roofline_us"] = round(tot_bytes / R / (HBM_PEAK_GBS * 1e9) * 1e6, 2)
+
+    # ---- per-round distribution (separate pass, events at round start, end of
+    # drafting and end of verify; the events add a few µs to each round)
+    round_stats = None
+    if not args.no_breakdown:
+        R = max(20, min(50, args.steps))
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(R)]
+        for r in range(R):
+            ev[r][0].record()
+            gr.init()
+            for st in range(cfg.gamma):
+                gr.step(st)
+                gr.expand(st)
+            if cfg.tree_attend:
+                gr.attend()
+            ev[r][1].record()
+            gr.verify(tgt)
+            ev[r][2].record()
+        torch.cuda.synchronize()
+        tot = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in ev)
+        drf = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+        ver = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
+        q = lambda v, f: round(v[min(len(v) - 1, int(f * len(v)))], 2)
+        round_stats = {"rounds": R, "round_us_p10": q(tot, 0.1), "round_us_p50": q(tot, 0.5),
+                       "round_us_p90": q(tot, 0.9), "draft_us_p50": q(drf, 0.5),
+                       "verify_us_p50": q(ver, 0.5)}
 
     cpu = None
     if not args.no_cpu:
@@ -221,6 +247,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "round_stats": round_stats,
     }
     print(json.dumps(out))
 

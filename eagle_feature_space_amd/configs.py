@@ -66,6 +66,7 @@ class RoundCfg:
     top_m: int = 0                    # nodes kept by rerank (dynamic trees)
     template: Tuple[int, ...] = ()    # static tree: parent of template node i+1
     inv_temp: float = 1.0             # s in conf = softmax(s * logits)
+    tree_attend: bool = False         # the round includes the verify-side tree attention
     seed_w: int = 0
     seed_in: int = 0
     seed_t: int = 0
@@ -119,7 +120,7 @@ CONFIGS = {
         note="Llama-3-8B-shaped head, bf16, B=1, n=2048, static 25-node tree"),
     "c2_8b_dynamic": RoundCfg(
         name="c2_8b_dynamic", head=HEAD_8B, B=8, n=(4096,) * 8, tree=TREE_DYNAMIC,
-        gamma=6, top_k=10, top_m=60, inv_temp=C2_INV_TEMP, seed_w=1002,
+        gamma=6, top_k=10, top_m=60, inv_temp=C2_INV_TEMP, tree_attend=True, seed_w=1002,
         seed_in=2002, seed_t=3002,
         note="EAGLE-2 dynamic tree on the 8B head, B=8, n=4096, top-k 10, depth 6, top-m 60"),
     "c3_8b_eagle3": RoundCfg(
@@ -175,5 +176,15 @@ SMALL_CONFIGS = {
         B=2, n=(40, 9), tree=TREE_DYNAMIC, gamma=3, top_k=3, top_m=6, inv_temp=3.0,
         seed_w=1106, seed_in=2106, seed_t=3106),
 }
+
+# Chains whose row count sits on either side of every kernel-dispatch boundary:
+# 16 / 17 (row-complete vs split-K streaming), 32 / 33 (streaming vs LDS-staged),
+# 63 / 64 (LDS-staged vs tiled GEMM, and the tiled LM head: |V| = 3008 is a
+# multiple of 16).  Mixed context lengths including empty ones.
+for _i, _b in enumerate((16, 17, 32, 33, 63, 64)):
+    SMALL_CONFIGS[f"s7_chain_b{_b}"] = RoundCfg(
+        name=f"s7_chain_b{_b}", head=replace(_HEAD_SMALL, vocab=3008), B=_b,
+        n=tuple((7 * j + 3 * _b) % 41 for j in range(_b)), tree=TREE_CHAIN, gamma=2,
+        top_k=1, seed_w=1107 + _i, seed_in=2107 + _i, seed_t=3107 + _i)
 
 ALL_CONFIGS = {**CONFIGS, **SMALL_CONFIGS}
