@@ -169,11 +169,12 @@ SMALL_CONFIGS = {
                                        12, 77, 150, 3, 65, 31, 100, 9, 256, 18)),
         tree=TREE_DYNAMIC, gamma=4, top_k=8, top_m=24, inv_temp=5.0,
         seed_w=1105, seed_in=2105, seed_t=3105),
-    # fp32 head with RMSNorm and GELU: the row-complete fp32 kernels, GELU epilogue
+    # fp32 head with RMSNorm and GELU: the row-complete fp32 kernels (2 rows),
+    # the GELU epilogue, and 18 rows x 2 heads per kv head (workgroup attention)
     "s6_f32_rms_gelu": RoundCfg(
         name="s6_f32_rms_gelu", head=replace(HEAD_TINY_F32, norm=NORM_RMS, n_kv=2,
                                              rope_theta=10000.0),
-        B=2, n=(40, 9), tree=TREE_DYNAMIC, gamma=3, top_k=3, top_m=6, inv_temp=3.0,
+        B=2, n=(40, 9), tree=TREE_DYNAMIC, gamma=3, top_k=9, top_m=14, inv_temp=3.0,
         seed_w=1106, seed_in=2106, seed_t=3106),
 }
 

@@ -206,6 +206,239 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
   }
 }
 
+// Many query rows per (request, kv head) -- the wide EAGLE-2 trees, the
+// verify-side tree attention: a workgroup of NW waves serves 16 * NW query
+// rows (16 per wave) of one (request, kv head, key split).  Its threads load
+// each 64-key K / V tile once, cooperatively, into LDS (K as [key][d], V
+// transposed as [d][key] by 4-key quads), double-buffered: the next tile's
+// global loads are in flight in registers while the waves compute on the
+// current one, and one barrier per tile hands the buffers over.  Per wave the
+// arithmetic is that of k_attn with one 16-row block (same key permutation,
+// same online softmax, same partial format).
+template <typename T, int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
+  constexpr int VEC = DT<T>::VEC;
+  constexpr int DSTEPS = HD / (4 * VEC);
+  constexpr int DB = HD / 16;
+  constexpr int NV = 16 / VEC;
+  constexpr int NT = 64 * NW;                          // threads
+  constexpr int KROW = HD * (int)sizeof(T) + 16;       // K tile row (bytes, padded)
+  constexpr int VROW = 64 * (int)sizeof(T) + 16;       // V^T row (bytes, padded)
+  constexpr int BUF = 64 * KROW + HD * VROW;
+  constexpr int DG = HD / VEC;                         // 16-byte groups per key
+  constexpr int KCH = 64 * DG;                         // K chunks per tile
+  constexpr int VUN = 16 * DG;                         // V (key quad, d group) units per tile
+  constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VUN + NT - 1) / NT;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int kvh = blockIdx.y % a.Hkv;
+  const int rg = blockIdx.y / a.Hkv;
+  const int b = blockIdx.z;
+  const int split = blockIdx.x;
+  const int G = a.Hq / a.Hkv;
+  const int R = a.W * G;
+  const int M = a.B * a.W;
+
+  // this wave's 16 query rows
+  const int qrow = rg * 16 * NW + w * 16 + c;
+  const bool qok = qrow < R;
+  const bool wave_live = rg * 16 * NW + w * 16 < R;
+  const int rl = qok ? qrow / G : 0, gi = qok ? qrow % G : 0;
+  const int qm = qok ? b * a.W + rl : -1;
+  const int qh = kvh * G + gi;
+  const uint64_t msk = qok ? a.mask[b * a.W + rl] : 0ull;
+  u32x4 qf[DSTEPS];
+  {
+    const T* qp = (const T*)a.q + ((int64_t)(b * a.W + rl) * a.Hq + qh) * HD;
+#pragma unroll
+    for (int u = 0; u < DSTEPS; ++u)
+      qf[u] = qok ? ld16(qp + u * 4 * VEC + g * VEC) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const bool extra = split == a.nsplit;
+  int kbeg, kend;
+  const T *kb, *vb;
+  const int64_t kstride = (int64_t)a.Hkv * HD;
+  if (!extra) {
+    const int nb = a.n[b];
+    kbeg = split * a.split_len;
+    kend = min(kbeg + a.split_len, nb);
+    kb = (const T*)a.k_ctx + (int64_t)a.cu_n[b] * kstride + kvh * HD;
+    vb = (const T*)a.v_ctx + (int64_t)a.cu_n[b] * kstride + kvh * HD;
+  } else {
+    uint64_t any = 0;
+    for (int r = 0; r < a.W; ++r) any |= a.mask[b * a.W + r];
+    kbeg = 0;
+    kend = any ? 64 - __builtin_clzll(any) : 0;
+    kb = (const T*)a.k_ex + (int64_t)b * kSlots * kstride + kvh * HD;
+    vb = (const T*)a.v_ex + (int64_t)b * kSlots * kstride + kvh * HD;
+  }
+  const int ntiles = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+
+  // cooperative tile loads (keys past kend re-read key kend - 1; masked below)
+  u32x4 kr[KPT], vr[VPT][4];
+  auto gload = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int q = tid + i * NT;
+      if (q < KCH) {
+        const int key = min(t0 + q / DG, kend - 1);
+        kr[i] = ld16(kb + (int64_t)key * kstride + (q % DG) * VEC);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int q = tid + i * NT;
+      if (q < VUN) {
+        const int kq = q / DG, dg = q % DG;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int key = min(t0 + 4 * kq + kk, kend - 1);
+          vr[i][kk] = ld16(vb + (int64_t)key * kstride + dg * VEC);
+        }
+      }
+    }
+  };
+  auto lstore = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int q = tid + i * NT;
+      if (q < KCH) st16(buf + (q / DG) * KROW + (q % DG) * 16, kr[i]);
+    }
+    char* vt = buf + 64 * KROW;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int q = tid + i * NT;
+      if (q < VUN) {
+        const int kq = q / DG, dg = q % DG;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          char* dst = vt + (dg * VEC + e) * VROW + 4 * kq * (int)sizeof(T);
+          if constexpr (sizeof(T) == 2) {
+            const int sh = (e & 1) * 16;
+            const uint32_t w0 = ((vr[i][0][e >> 1] >> sh) & 0xffffu) | (((vr[i][1][e >> 1] >> sh) & 0xffffu) << 16);
+            const uint32_t w1 = ((vr[i][2][e >> 1] >> sh) & 0xffffu) | (((vr[i][3][e >> 1] >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+          } else {
+            st16(dst, u32x4{vr[i][0][e], vr[i][1][e], vr[i][2][e], vr[i][3][e]});
+          }
+        }
+      }
+    }
+  };
+
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) {
+    gload(kbeg);
+    lstore(lds);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = kbeg + it * 64;
+    const char* cur = lds + (it & 1) * BUF;
+    if (it + 1 < ntiles) gload(t0 + 64);
+    if (wave_live) {
+      // ---- S^T = K Q^T (key permutation as in k_attn)
+      f32x4 sc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kl = (c >> 2) * 16 + j * 4 + (c & 3);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < DSTEPS; ++u)
+          acc = DT<T>::mma(ld16(cur + kl * KROW + (u * 4 * VEC + g * VEC) * (int)sizeof(T)), qf[u], acc);
+        sc[j] = acc;
+      }
+      // ---- online softmax, O^T += V^T P^T
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = t0 + g * 16 + j * 4 + i;
+          bool valid = key < kend;
+          if (extra) valid = valid && ((msk >> key) & 1ull);
+          const float v = valid ? sc[j][i] * a.scale_log2 : -INFINITY;
+          sc[j][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun, tmax);
+      const bool empty = mnew == -INFINITY;
+      const float alpha = empty ? 1.f : exp2f(mrun - mnew);
+      float p[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = empty ? 0.f : exp2f(sc[j][i] - mnew);
+          p[4 * j + i] = e;
+          psum += e;
+        }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      const char* vt = cur + 64 * KROW;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const u32x4 pf = DT<T>::pack(p + v * VEC);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 vf = ld16(vt + (db * 16 + c) * VROW + (g * 16 + v * VEC) * (int)sizeof(T));
+          o[db] = DT<T>::mma(vf, pf, o[db]);
+        }
+      }
+    }
+    if (it + 1 < ntiles) lstore(lds + ((it + 1) & 1) * BUF);
+    __syncthreads();
+  }
+
+  // ---- partial (m, l, O) of this split
+  if (qm < 0) return;
+  const int64_t idx = ((int64_t)split * M + qm) * a.Hq + qh;
+  if (g == 0) {
+    a.part_ml[2 * idx] = mrun;
+    a.part_ml[2 * idx + 1] = lrun;
+  }
+  float* po = a.part_o + idx * HD;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * g) = o[db];
+}
+
+template <typename T, int HD, int NW>
+static void launch_wg(const AttnArgs& a, hipStream_t st) {
+  constexpr int KROW = HD * (int)sizeof(T) + 16, VROW = 64 * (int)sizeof(T) + 16;
+  constexpr int LDS = 2 * (64 * KROW + HD * VROW);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_wg<T, HD, NW>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    attr = true;
+  }
+  const int R = a.W * (a.Hq / a.Hkv);
+  const int rowgroups = (R + 16 * NW - 1) / (16 * NW);
+  dim3 grid(a.nsplit + 1, a.Hkv * rowgroups, a.B);
+  hipLaunchKernelGGL((k_attn_wg<T, HD, NW>), grid, dim3(64 * NW), LDS, st, a);
+}
+
+template <typename T, int HD>
+static void launch_wide(const AttnArgs& a, int R, hipStream_t st) {
+  if (R <= 32) launch_wg<T, HD, 2>(a, st);
+  else launch_wg<T, HD, 4>(a, st);
+}
+
 template <typename T, int HD>
 static void launch_rb(const AttnArgs& a, int RB, dim3 grid, hipStream_t st) {
   dim3 block(64 * kAttnWaves);
@@ -219,6 +452,17 @@ static void launch_rb(const AttnArgs& a, int RB, dim3 grid, hipStream_t st) {
 void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
   AttnArgs a = a0;
   const int R = a.W * (a.Hq / a.Hkv);
+  if (R > 16) {
+    // more than one 16-row block per (request, kv head): workgroup kernel
+    if (dtype == EAGLE_BF16) {
+      if (a.hd == 128) launch_wide<bf16s, 128>(a, R, st);
+      else launch_wide<bf16s, 64>(a, R, st);
+    } else {
+      if (a.hd == 128) launch_wide<float, 128>(a, R, st);
+      else launch_wide<float, 64>(a, R, st);
+    }
+    return;
+  }
   const int RB = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   a.rowgroups = (R + 16 * RB - 1) / (16 * RB);
   const int kvgroups = (a.Hkv + kAttnWaves - 1) / kAttnWaves;
