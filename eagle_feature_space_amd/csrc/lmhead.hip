@@ -17,7 +17,7 @@ namespace eagle {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int MB, int NB>
+template <typename T, int MB, int NB, int WAVES = 4>
 __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB], int m0, char* lds);
 
 template <typename T, int MB>
@@ -91,11 +91,12 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
 
 // Epilogue shared by both LM-head kernels: optional raw logits, then per row
 // the tile max, tile sum of exp(s (l - max)) and the tile top-k.
-template <typename T, int MB, int NB>
+template <typename T, int MB, int NB, int WAVES>
 __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB], int m0, char* lds) {
-  constexpr int TCOLS = 64 * NB;          // tile columns (4 waves x 16*NB)
+  constexpr int TCOLS = 16 * NB * WAVES;  // tile columns (WAVES waves x 16*NB)
   constexpr int TROW = TCOLS + 4;
   constexpr int PER = TCOLS / 64;         // tile columns per lane in the row pass
+  constexpr int RPW = 16 / WAVES;         // rows of a 16-row block per wave in the row pass
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -133,9 +134,10 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
       *reinterpret_cast<f32x4*>(tl + c * TROW + col) = v;
     }
     __syncthreads();
+    // rows dealt round-robin, so a few live rows still spread over the waves
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = wave * 4 + rr;
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int r = rr * WAVES + wave;
       const int m = m0 + mb * 16 + r;
       if (m >= a.M) continue;
       float v[PER];
@@ -183,9 +185,9 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
 // M <= 32: barrier-free streaming main loop (see k_gemm_direct), full K per
 // wave, 128 vocabulary rows per wave (eight 16-row MFMA blocks share each X
 // fragment and keep 32 KB of W loads in flight per wave), 512 per workgroup.
-template <typename T, int MB, int NB = 8, int U = 2>
-__global__ __launch_bounds__(256) void k_lmhead_direct(LmArgs a) {
-  constexpr int TCOLS = 64 * NB;
+template <typename T, int MB, int NB = 8, int U = 2, int WAVES = 4>
+__global__ __launch_bounds__(64 * WAVES) void k_lmhead_direct(LmArgs a) {
+  constexpr int TCOLS = 16 * NB * WAVES;
   constexpr int TBYTES = 16 * (TCOLS + 4) * 4;
   __shared__ __attribute__((aligned(16))) char lds[TBYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(256) void k_lmhead_direct(LmArgs a) {
   ga.N = a.V;
   ga.K = a.K;
   direct_mainloop<T, MB, NB, U>(ga, wrow, 0, a.K, g, c, acc);
-  lm_epilogue<T, MB, NB>(a, acc, 0, lds);
+  lm_epilogue<T, MB, NB, WAVES>(a, acc, 0, lds);
 }
 
 LmShape plan_lmhead(int dtype, int M, int V) {
