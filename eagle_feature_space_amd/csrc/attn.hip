@@ -483,44 +483,58 @@ constexpr int kMaxParts = 1024;
 template <typename T>
 __global__ __launch_bounds__(128) void k_attn_combine(CombineArgs a) {
   __shared__ float wts[kMaxParts];
-  __shared__ float ls[kMaxParts];
-  __shared__ float red[2];
+  __shared__ float red[2][2];
   const int h = blockIdx.x, m = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int np = a.nparts;
   const int64_t stride = (int64_t)a.M * a.Hq;
   const int64_t base = (int64_t)m * a.Hq + h;
-  // every thread fetches some splits' (max, sum) at once
-  for (int s = threadIdx.x; s < np; s += blockDim.x) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * (s * stride + base));
-    wts[s] = ml.x;
-    ls[s] = ml.y;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float mx = -INFINITY;
-    for (int s = 0; s < np; ++s) mx = fmaxf(mx, wts[s]);
-    float L = 0.f;
-    for (int s = 0; s < np; ++s) {
-      const float ms = wts[s];
-      const float f = (mx == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-      wts[s] = f;
-      L += f * ls[s];
+  // split maxima and sums: every thread holds the (max, sum) of its splits
+  constexpr int SPT = kMaxParts / 128;
+  float ms[SPT], lsum[SPT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int s = tid + 128 * i;
+    ms[i] = -INFINITY;
+    lsum[i] = 0.f;
+    if (s < np) {
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * (s * stride + base));
+      ms[i] = ml.x;
+      lsum[i] = ml.y;
     }
-    red[0] = L > 0.f ? 1.0f / L : 0.f;
+    mx = fmaxf(mx, ms[i]);
   }
+  mx = wave_max(mx);
+  if (lane == 0) red[0][w] = mx;
   __syncthreads();
-  const float inv = red[0];
-  for (int d = threadIdx.x; d < a.hd; d += blockDim.x) {
+  mx = fmaxf(red[0][0], red[0][1]);
+  // split weights 2^(m_s - max) and L = sum_s weight_s l_s
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int s = tid + 128 * i;
+    const float f = (mx == -INFINITY || ms[i] == -INFINITY) ? 0.f : exp2f(ms[i] - mx);
+    if (s < np) wts[s] = f;
+    L += f * lsum[i];
+  }
+  L = wave_sum(L);
+  if (lane == 0) red[1][w] = L;
+  __syncthreads();
+  L = red[1][0] + red[1][1];
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  // O = sum_s weight_s O_s in split order; up to 16 partial loads in flight
+  for (int d = tid; d < a.hd; d += 128) {
+    const float* po = a.part_o + base * a.hd + d;
     float O = 0.f;
-    int s = 0;
-    for (; s + 4 <= np; s += 4) {
-      float v[4];
+    for (int s0 = 0; s0 < np; s0 += 16) {
+      float v[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = a.part_o[((s + q) * stride + base) * a.hd + d];
+      for (int q = 0; q < 16; ++q) v[q] = po[(int64_t)min(s0 + q, np - 1) * stride * a.hd];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) O += wts[s + q] * v[q];
+      for (int q = 0; q < 16; ++q)
+        if (s0 + q < np) O += wts[s0 + q] * v[q];
     }
-    for (; s < np; ++s) O += wts[s] * a.part_o[(s * stride + base) * a.hd + d];
     DT<T>::st((T*)a.out + base * a.hd + d, O * inv);
   }
 }
