@@ -336,25 +336,8 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
   const float sl = a.inv_temp * kLog2e;
-  // log-partition of s * logits
-  float mx = -INFINITY;
-  for (int t = tid; t < a.ntiles; t += 256) mx = fmaxf(mx, a.part_max[(int64_t)t * a.M + m]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float z = 0.f;
-  for (int t = tid; t < a.ntiles; t += 256) {
-    const int64_t i = (int64_t)t * a.M + m;
-    z += a.part_sum[i] * exp2f((a.part_max[i] - mx) * sl);
-  }
-  z = wave_sum(z);
-  if ((tid & 63) == 0) red[tid >> 6] = z;
-  __syncthreads();
-  z = red[0] + red[1] + red[2] + red[3];
-  const float lse = a.inv_temp * mx + logf(z);
-  // top-k over the tiles' candidates, staged once in LDS
+  // all loads first: the tile (max, sum) partials of this thread's tiles and
+  // the candidates staged in LDS, so the row pays one memory latency
   const int ncand = a.ntiles * a.top_k;
   const bool staged = ncand <= kMergeLds;
   if (staged) {
@@ -364,8 +347,42 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
       cval[q] = a.part_val[i];
       cid[q] = a.part_id[i];
     }
-    __syncthreads();
   }
+  constexpr int TPT = 4;                  // tiles per thread held in registers
+  float tm[TPT], ts[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int t = tid + 256 * i;
+    tm[i] = -INFINITY;
+    ts[i] = 0.f;
+    if (t < a.ntiles) {
+      tm[i] = a.part_max[(int64_t)t * a.M + m];
+      ts[i] = a.part_sum[(int64_t)t * a.M + m];
+    }
+  }
+  // log-partition of s * logits
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) mx = fmaxf(mx, tm[i]);
+  for (int t = tid + 256 * TPT; t < a.ntiles; t += 256) mx = fmaxf(mx, a.part_max[(int64_t)t * a.M + m]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float z = 0.f;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+    if (tid + 256 * i < a.ntiles) z += ts[i] * exp2f((tm[i] - mx) * sl);
+  for (int t = tid + 256 * TPT; t < a.ntiles; t += 256) {
+    const int64_t i = (int64_t)t * a.M + m;
+    z += a.part_sum[i] * exp2f((a.part_max[i] - mx) * sl);
+  }
+  z = wave_sum(z);
+  if ((tid & 63) == 0) red[tid >> 6] = z;
+  __syncthreads();
+  z = red[0] + red[1] + red[2] + red[3];
+  const float lse = a.inv_temp * mx + logf(z);
   float pv = INFINITY;
   int pid = -1;
   for (int k = 0; k < a.top_k; ++k) {
