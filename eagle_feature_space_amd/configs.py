@@ -176,6 +176,12 @@ SMALL_CONFIGS = {
                                              rope_theta=10000.0),
         B=2, n=(40, 9), tree=TREE_DYNAMIC, gamma=3, top_k=9, top_m=14, inv_temp=3.0,
         seed_w=1106, seed_in=2106, seed_t=3106),
+    # the same with head_dim 128 (fp32 instantiations of both attention kernels)
+    "s8_f32_hd128": RoundCfg(
+        name="s8_f32_hd128", head=replace(HEAD_TINY_F32, norm=NORM_RMS, n_q=2, n_kv=1,
+                                          head_dim=128, rope_theta=10000.0),
+        B=2, n=(70, 0), tree=TREE_DYNAMIC, gamma=3, top_k=9, top_m=14, inv_temp=3.0,
+        seed_w=1108, seed_in=2108, seed_t=3108),
 }
 
 # Chains whose row count sits on either side of every kernel-dispatch boundary:

@@ -27,46 +27,21 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One key split of (request b, kv head): the context split `split` or, for
+// split == nsplit, the request's tree-node slots gated by the rows' masks.
+// Folds its tiles into the running (max, sum, O^T) state of the wave's rows.
 template <typename T, int HD, int RB>
-__global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
+__device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, int split,
+                                           const u32x4 (&qf)[RB][HD / (4 * DT<T>::VEC)],
+                                           const uint64_t (&msk)[RB], char* vt, float (&mrun)[RB],
+                                           float (&lrun)[RB], f32x4 (&o)[HD / 16][RB]) {
   constexpr int VEC = DT<T>::VEC;
-  constexpr int DSTEPS = HD / (4 * VEC);    // MFMA steps over the head dim
-  constexpr int DB = HD / 16;               // output d blocks
-  constexpr int NV = 16 / VEC;              // 16-byte vectors per lane group per tile
+  constexpr int DSTEPS = HD / (4 * VEC);
+  constexpr int DB = HD / 16;
+  constexpr int NV = 16 / VEC;
   constexpr int ROWB = 64 * (int)sizeof(T) + 16;
-  __shared__ __attribute__((aligned(16))) char vts[kAttnWaves][HD * ROWB];
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-  const int kvgroups = (a.Hkv + kAttnWaves - 1) / kAttnWaves;
-  const int kvh = (blockIdx.y % kvgroups) * kAttnWaves + w;
-  const int rg = blockIdx.y / kvgroups;
-  if (kvh >= a.Hkv) return;
-  const int b = blockIdx.z;
-  const int split = blockIdx.x;
-  const int G = a.Hq / a.Hkv;
-  const int R = a.W * G;
-  const int M = a.B * a.W;
-  char* vt = vts[w];
-
-  // query fragments
-  u32x4 qf[RB][DSTEPS];
-  uint64_t msk[RB];
-  int qm[RB], qh[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int qrow = rg * 16 * RB + rb * 16 + c;
-    const bool ok = qrow < R;
-    const int rl = ok ? qrow / G : 0, gi = ok ? qrow % G : 0;
-    qm[rb] = ok ? b * a.W + rl : -1;
-    qh[rb] = kvh * G + gi;
-    msk[rb] = ok ? a.mask[b * a.W + rl] : 0ull;
-    const T* qp = (const T*)a.q + ((int64_t)(b * a.W + rl) * a.Hq + qh[rb]) * HD;
-#pragma unroll
-    for (int u = 0; u < DSTEPS; ++u)
-      qf[rb][u] = ok ? ld16(qp + u * 4 * VEC + g * VEC) : u32x4{0u, 0u, 0u, 0u};
-  }
-
   const bool extra = split == a.nsplit;
   int kbeg, kend;
   const T *kb, *vb;
@@ -84,16 +59,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
     kend = any ? 64 - __builtin_clzll(any) : 0;
     kb = (const T*)a.k_ex + (int64_t)b * kSlots * kstride + kvh * HD;
     vb = (const T*)a.v_ex + (int64_t)b * kSlots * kstride + kvh * HD;
-  }
-
-  float mrun[RB], lrun[RB];
-  f32x4 o[DB][RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    mrun[rb] = -INFINITY;
-    lrun[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   for (int t0 = kbeg; t0 < kend; t0 += 64) {
@@ -190,6 +155,58 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
       }
     }
   }
+}
+
+template <typename T, int HD, int RB>
+__global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
+  constexpr int VEC = DT<T>::VEC;
+  constexpr int DSTEPS = HD / (4 * VEC);    // MFMA steps over the head dim
+  constexpr int DB = HD / 16;               // output d blocks
+  constexpr int ROWB = 64 * (int)sizeof(T) + 16;
+  __shared__ __attribute__((aligned(16))) char vts[kAttnWaves][HD * ROWB];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int kvgroups = (a.Hkv + kAttnWaves - 1) / kAttnWaves;
+  const int kvh = (blockIdx.y % kvgroups) * kAttnWaves + w;
+  const int rg = blockIdx.y / kvgroups;
+  if (kvh >= a.Hkv) return;
+  const int b = blockIdx.z;
+  const int split = blockIdx.x;
+  const int G = a.Hq / a.Hkv;
+  const int R = a.W * G;
+  const int M = a.B * a.W;
+  char* vt = vts[w];
+
+  // query fragments
+  u32x4 qf[RB][DSTEPS];
+  uint64_t msk[RB];
+  int qm[RB], qh[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qrow = rg * 16 * RB + rb * 16 + c;
+    const bool ok = qrow < R;
+    const int rl = ok ? qrow / G : 0, gi = ok ? qrow % G : 0;
+    qm[rb] = ok ? b * a.W + rl : -1;
+    qh[rb] = kvh * G + gi;
+    msk[rb] = ok ? a.mask[b * a.W + rl] : 0ull;
+    const T* qp = (const T*)a.q + ((int64_t)(b * a.W + rl) * a.Hq + qh[rb]) * HD;
+#pragma unroll
+    for (int u = 0; u < DSTEPS; ++u)
+      qf[rb][u] = ok ? ld16(qp + u * 4 * VEC + g * VEC) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  float mrun[RB], lrun[RB];
+  f32x4 o[DB][RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    mrun[rb] = -INFINITY;
+    lrun[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  attn_split<T, HD, RB>(a, b, kvh, split, qf, msk, vt, mrun, lrun, o);
 
   // ---- partial (m, l, O) of this split
 #pragma unroll
@@ -439,16 +456,6 @@ static void launch_wide(const AttnArgs& a, int R, hipStream_t st) {
   else launch_wg<T, HD, 4>(a, st);
 }
 
-template <typename T, int HD>
-static void launch_rb(const AttnArgs& a, int RB, dim3 grid, hipStream_t st) {
-  dim3 block(64 * kAttnWaves);
-  switch (RB) {
-    case 1: hipLaunchKernelGGL((k_attn<T, HD, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn<T, HD, 2>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_attn<T, HD, 4>), grid, block, 0, st, a); break;
-  }
-}
-
 void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
   AttnArgs a = a0;
   const int R = a.W * (a.Hq / a.Hkv);
@@ -463,16 +470,16 @@ void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
     }
     return;
   }
-  const int RB = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
-  a.rowgroups = (R + 16 * RB - 1) / (16 * RB);
+  // at most 16 query rows per (request, kv head): one 16-row block per wave
+  a.rowgroups = 1;
   const int kvgroups = (a.Hkv + kAttnWaves - 1) / kAttnWaves;
-  dim3 grid(a.nsplit + 1, kvgroups * a.rowgroups, a.B);
+  const dim3 grid(a.nsplit + 1, kvgroups, a.B), block(64 * kAttnWaves);
   if (dtype == EAGLE_BF16) {
-    if (a.hd == 128) launch_rb<bf16s, 128>(a, RB, grid, st);
-    else launch_rb<bf16s, 64>(a, RB, grid, st);
+    if (a.hd == 128) hipLaunchKernelGGL((k_attn<bf16s, 128, 1>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn<bf16s, 64, 1>), grid, block, 0, st, a);
   } else {
-    if (a.hd == 128) launch_rb<float, 128>(a, RB, grid, st);
-    else launch_rb<float, 64>(a, RB, grid, st);
+    if (a.hd == 128) hipLaunchKernelGGL((k_attn<float, 128, 1>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn<float, 64, 1>), grid, block, 0, st, a);
   }
 }
 

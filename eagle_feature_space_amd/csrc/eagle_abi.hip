@@ -522,12 +522,12 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)h->head_dim);
   a.part_o = (float*)(ws + w.att_o);
   a.part_ml = (float*)(ws + w.att_ml);
+  const double kvd = (double)h->n_kv_heads * h->head_dim;
+  const double att_bytes = esz(h) * (2.0 * kv->total_n * kvd + (double)kv->B * W * h->n_q_heads * h->head_dim);
+  const double att_flops = 4.0 * h->head_dim * (double)h->n_q_heads * W * (double)kv->total_n;
   {
     // context K and V of every request once, plus the queries
-    const double kvd = (double)h->n_kv_heads * h->head_dim;
-    const double bytes = esz(h) * (2.0 * kv->total_n * kvd + (double)kv->B * W * h->n_q_heads * h->head_dim);
-    const double flops = 4.0 * h->head_dim * (double)h->n_q_heads * W * (double)kv->total_n;
-    ProfScope ps(EAGLE_PROF_ATTN, bytes, flops, st);
+    ProfScope ps(EAGLE_PROF_ATTN, att_bytes, att_flops, st);
     launch_attention(h->dtype, a, st);
   }
   CombineArgs c;
