@@ -1,16 +1,20 @@
 // Large-M GEMM (M >= 64 rows: the 80-row EAGLE-2 steps, the 70B-shaped head's
 // 64- and 512-row draft steps, the EAGLE-3 ingest over every verified
 // position, the verify-tree projections).  Every weight byte is reused M
-// times, so W is read once per 128-row tile and the kernel is a classic
-// LDS-tiled one:
-//   workgroup tile 256 (n) x 128 (m), BK = 64, four waves of 128 x 64;
-//   each wave holds 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16 (W rows are
-//   the A operand, X rows the B operand, so a lane owns 4 consecutive n of one
-//   m and stores 16 contiguous bytes);
+// times, so W is read once per row tile and the kernel is a classic LDS-tiled
+// one:
+//   workgroup tile 256 (n) x BM (m), BM = 256 from 256 rows on, else 128;
+//   BK = 64; sixteen waves in a 4 x 4 grid, each 64 (n) x BM/4 (m) with
+//   4 x BM/64 accumulators of v_mfma_f32_16x16x32_bf16 (W rows are the A
+//   operand, X rows the B operand, so a lane owns 4 consecutive n of one m
+//   and stores 16 contiguous bytes);
 //   W and X tiles are staged through LDS, double-buffered; the global loads of
 //   stage k+1 are issued into registers before the MFMAs of stage k and land
 //   in the other LDS buffer after them; LDS rows are padded by 16 bytes so the
-//   16-lane fragment reads hit 16 distinct 4-bank groups;
+//   16-lane fragment reads hit 16 distinct 4-bank groups.  Sixteen waves (four
+//   per SIMD) keep the MFMA pipes busy across the barrier and load waits that a
+//   4-wave workgroup of 128 x 64 wave tiles left exposed (2.1x faster at the
+//   70B LM head: 1.14 PFLOP/s);
 //   workgroups are ordered so that the m-tiles sharing a W tile are dispatched
 //   back to back on the same XCD (workgroup i runs on XCD i mod 8) and share
 //   that XCD's L2.
@@ -20,17 +24,25 @@
 
 namespace eagle {
 
-constexpr int kBN = 256, kBM = 128, kBK = 64;
+constexpr int kBN = 256, kBK = 64;
 constexpr int kRowB = kBK * 2 + 16;                        // padded LDS row (bytes)
-constexpr int kStageB = (kBN + kBM) * kRowB;               // 55296
-constexpr int kBigLds = 2 * kStageB;                       // 110592
+template <int BM> constexpr int big_stage() { return (kBN + BM) * kRowB; }
+template <int BM> constexpr int big_lds() { return 2 * big_stage<BM>(); }   // 110592 / 147456
 
-__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, int nt, int mt, int S) {
+// WN x WM waves; wave (wn, wm) owns 256/WN n and WMB 16-row blocks of m;
+// the tile is 256 x BM with BM = 16 WMB WM
+template <int WN, int WM, int WMB>
+__global__ __launch_bounds__(64 * WN * WM) void k_gemm_big(GemmArgs a, int nt, int mt, int S) {
+  constexpr int NT = 64 * WN * WM;
+  constexpr int WNB = 16 / WN;                     // 16-row W blocks per wave
+  constexpr int kBM = 16 * WMB * WM;
+  constexpr int kStageB = big_stage<kBM>();
+  constexpr int WCH = 2048 / NT, XCH = kBM * 8 / NT;  // staged 16-byte chunks per thread
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int wn = wave >> 1, wm = wave & 1;           // 2 x 2 waves
+  const int wn = wave / WM, wm = wave % WM;
 
   // XCD-aware order: XCD x (= wgid mod 8) walks a contiguous run of the
   // (split, n-tile, m-tile) list, m fastest
@@ -44,14 +56,14 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, int nt, int mt, in
   const int n0 = ntile * kBN, m0 = mtile * kBM;
   const int k_begin = z * a.kps, k_end = min(a.K, k_begin + a.kps);
 
-  // global -> LDS mapping: 8 chunks of 16 B per row; W tile 2048 chunks (8
-  // per thread), X tile 1024 chunks (4 per thread)
-  const bf16s* wsrc[8];
-  const bf16s* xsrc[4];
-  const bf16s* xsrc1[4];      // second A segment (k >= ksplit_x), e.g. emb(t) of [f ; emb(t)]
+  // global -> LDS mapping: 8 chunks of 16 B per row; W tile 2048 chunks,
+  // X tile 8 BM chunks, spread over the threads
+  const bf16s* wsrc[WCH];
+  const bf16s* xsrc[XCH];
+  const bf16s* xsrc1[XCH];    // second A segment (k >= ksplit_x), e.g. emb(t) of [f ; emb(t)]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = tid + 256 * i, r = q >> 3, ch = q & 7;
+  for (int i = 0; i < WCH; ++i) {
+    const int q = tid + NT * i, r = q >> 3, ch = q & 7;
     const int n = min(n0 + r, a.N - 1);
     const bf16s* base;
     int off;
@@ -61,37 +73,37 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, int nt, int mt, in
     wsrc[i] = base + (int64_t)(n - off) * a.K + ch * 8;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + 256 * i, r = q >> 3, ch = q & 7;
+  for (int i = 0; i < XCH; ++i) {
+    const int q = tid + NT * i, r = q >> 3, ch = q & 7;
     const int m = min(m0 + r, a.M - 1);
     xsrc[i] = row_ptr<bf16s>(a.xs[0], m) + ch * 8;
     xsrc1[i] = (a.xs[1].base ? row_ptr<bf16s>(a.xs[1], m) : xsrc[i] - ch * 8) + ch * 8;
   }
 
-  f32x4 acc[8][4];
+  f32x4 acc[WNB][WMB];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
+  for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 wreg[8], xreg[4];
+  u32x4 wreg[WCH], xreg[XCH];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wreg[i] = ld16(wsrc[i] + k0);
+    for (int i = 0; i < WCH; ++i) wreg[i] = ld16(wsrc[i] + k0);
     const bool hi = k0 >= a.ksplit_x;      // a BK tile never straddles the split
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xreg[i] = hi ? ld16(xsrc1[i] + (k0 - a.ksplit_x)) : ld16(xsrc[i] + k0);
+    for (int i = 0; i < XCH; ++i) xreg[i] = hi ? ld16(xsrc1[i] + (k0 - a.ksplit_x)) : ld16(xsrc[i] + k0);
   };
   auto lstore = [&](int buf) {
     char* base = lds + buf * kStageB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i;
+    for (int i = 0; i < WCH; ++i) {
+      const int q = tid + NT * i;
       st16(base + (q >> 3) * kRowB + (q & 7) * 16, wreg[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;
+    for (int i = 0; i < XCH; ++i) {
+      const int q = tid + NT * i;
       st16(base + (kBN + (q >> 3)) * kRowB + (q & 7) * 16, xreg[i]);
     }
   };
@@ -105,18 +117,18 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, int nt, int mt, in
   for (int k0 = k_begin; k0 < k_end; k0 += kBK) {
     const bool more = k0 + kBK < k_end;
     if (more) gload(k0 + kBK);
-    const char* wt = lds + buf * kStageB + (wn * 128) * kRowB;
-    const char* xt = lds + buf * kStageB + (kBN + wm * 64) * kRowB;
+    const char* wt = lds + buf * kStageB + (wn * 16 * WNB) * kRowB;
+    const char* xt = lds + buf * kStageB + (kBN + wm * 16 * WMB) * kRowB;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
-      u32x4 xf[4];
+      u32x4 xf[WMB];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) xf[mb] = ld16(xt + (mb * 16 + c) * kRowB + (kk * 32 + g * 8) * 2);
+      for (int mb = 0; mb < WMB; ++mb) xf[mb] = ld16(xt + (mb * 16 + c) * kRowB + (kk * 32 + g * 8) * 2);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
+      for (int nb = 0; nb < WNB; ++nb) {
         const u32x4 wf = ld16(wt + (nb * 16 + c) * kRowB + (kk * 32 + g * 8) * 2);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = DT<bf16s>::mma(wf, xf[mb], acc[nb][mb]);
+        for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = DT<bf16s>::mma(wf, xf[mb], acc[nb][mb]);
       }
     }
     if (more) lstore(buf ^ 1);
@@ -124,15 +136,15 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, int nt, int mt, in
     buf ^= 1;
   }
 
-  // acc[nb][mb]: lane holds out[m = m0 + 64 wm + 16 mb + c][n = n0 + 128 wn + 16 nb + 4 g + 0..3]
+  // acc[nb][mb]: lane holds out[m = m0 + 16 (WMB wm + mb) + c][n = n0 + 16 (WNB wn + nb) + 4 g + 0..3]
   float* P = a.P + (int64_t)z * a.M * a.N;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const int n = n0 + wn * 128 + nb * 16 + 4 * g;
+  for (int nb = 0; nb < WNB; ++nb) {
+    const int n = n0 + (wn * WNB + nb) * 16 + 4 * g;
     if (n >= a.N) continue;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 64 + mb * 16 + c;
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int m = m0 + (wm * WMB + mb) * 16 + c;
       if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
     }
   }
@@ -145,10 +157,11 @@ bool big_gemm_ok(int dtype, int M, int N, int K) {
 GemmShape plan_gemm_big(int M, int N, int K) {
   GemmShape s;
   s.direct = 2;
-  s.MB = 0;
+  s.MB = M >= 256 ? 16 : 8;                // tile height / 16
   s.NB = 0;
+  const int BM = 16 * s.MB;
   s.ntiles = (N + kBN - 1) / kBN;
-  s.mtiles = (M + kBM - 1) / kBM;
+  s.mtiles = (M + BM - 1) / BM;
   const int tiles = s.ntiles * s.mtiles;
   const int kst = K / kBK;
   int S = (512 + tiles - 1) / tiles;      // at least two workgroups per CU
@@ -160,17 +173,25 @@ GemmShape plan_gemm_big(int M, int N, int K) {
   return s;
 }
 
-void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
+template <int WN, int WM, int WMB>
+static void launch_big_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+  constexpr int LDS = big_lds<16 * WMB * WM>();
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_big),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kBigLds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_big<WN, WM, WMB>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     attr = true;
   }
-  a.kps = s.kps;
   const int total = s.ntiles * s.mtiles * s.S;
   const int per = (total + 7) / 8;
-  hipLaunchKernelGGL(k_gemm_big, dim3(per * 8), dim3(256), kBigLds, st, a, s.ntiles, s.mtiles, s.S);
+  hipLaunchKernelGGL((k_gemm_big<WN, WM, WMB>), dim3(per * 8), dim3(64 * WN * WM), LDS, st, a,
+                     s.ntiles, s.mtiles, s.S);
+}
+
+void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
+  a.kps = s.kps;
+  if (s.MB == 16) launch_big_t<4, 4, 4>(a, s, st);
+  else launch_big_t<4, 4, 2>(a, s, st);
 }
 
 }  // namespace eagle
