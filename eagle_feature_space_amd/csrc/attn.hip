@@ -296,14 +296,17 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
   const int ntiles = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
 
   // cooperative tile loads (keys past kend re-read key kend - 1; masked below)
-  u32x4 kr[KPT], vr[VPT][4];
-  auto gload = [&](int t0) {
+  struct Stage {
+    u32x4 kr[KPT];
+    u32x4 vr[VPT][4];
+  };
+  auto gload = [&](Stage& r, int t0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int q = tid + i * NT;
       if (q < KCH) {
         const int key = min(t0 + q / DG, kend - 1);
-        kr[i] = ld16(kb + (int64_t)key * kstride + (q % DG) * VEC);
+        r.kr[i] = ld16(kb + (int64_t)key * kstride + (q % DG) * VEC);
       }
     }
 #pragma unroll
@@ -314,16 +317,16 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int key = min(t0 + 4 * kq + kk, kend - 1);
-          vr[i][kk] = ld16(vb + (int64_t)key * kstride + dg * VEC);
+          r.vr[i][kk] = ld16(vb + (int64_t)key * kstride + dg * VEC);
         }
       }
     }
   };
-  auto lstore = [&](char* buf) {
+  auto lstore = [&](const Stage& r, char* buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int q = tid + i * NT;
-      if (q < KCH) st16(buf + (q / DG) * KROW + (q % DG) * 16, kr[i]);
+      if (q < KCH) st16(buf + (q / DG) * KROW + (q % DG) * 16, r.kr[i]);
     }
     char* vt = buf + 64 * KROW;
 #pragma unroll
@@ -336,11 +339,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
           char* dst = vt + (dg * VEC + e) * VROW + 4 * kq * (int)sizeof(T);
           if constexpr (sizeof(T) == 2) {
             const int sh = (e & 1) * 16;
-            const uint32_t w0 = ((vr[i][0][e >> 1] >> sh) & 0xffffu) | (((vr[i][1][e >> 1] >> sh) & 0xffffu) << 16);
-            const uint32_t w1 = ((vr[i][2][e >> 1] >> sh) & 0xffffu) | (((vr[i][3][e >> 1] >> sh) & 0xffffu) << 16);
+            const uint32_t w0 = ((r.vr[i][0][e >> 1] >> sh) & 0xffffu) | (((r.vr[i][1][e >> 1] >> sh) & 0xffffu) << 16);
+            const uint32_t w1 = ((r.vr[i][2][e >> 1] >> sh) & 0xffffu) | (((r.vr[i][3][e >> 1] >> sh) & 0xffffu) << 16);
             *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
           } else {
-            st16(dst, u32x4{vr[i][0][e], vr[i][1][e], vr[i][2][e], vr[i][3][e]});
+            st16(dst, u32x4{r.vr[i][0][e], r.vr[i][1][e], r.vr[i][2][e], r.vr[i][3][e]});
           }
         }
       }
@@ -352,15 +355,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (ntiles > 0) {
-    gload(kbeg);
-    lstore(lds);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int t0 = kbeg + it * 64;
-    const char* cur = lds + (it & 1) * BUF;
-    if (it + 1 < ntiles) gload(t0 + 64);
+  auto compute = [&](const char* cur, int t0) {
     if (wave_live) {
       // ---- S^T = K Q^T (key permutation as in k_attn)
       f32x4 sc[4];
@@ -418,8 +413,34 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
         }
       }
     }
-    if (it + 1 < ntiles) lstore(lds + ((it + 1) & 1) * BUF);
-    __syncthreads();
+  };
+
+  // two register stages in flight: while the waves compute tile i from one LDS
+  // buffer, tile i+1 waits in registers for the other buffer and the loads of
+  // tile i+2 are issued (unrolled by two so every stage index is static)
+  Stage ra, rb;
+  if (ntiles > 0) {
+    gload(ra, kbeg);
+    if (ntiles > 1) gload(rb, kbeg + 64);
+    lstore(ra, lds);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    {
+      const int t0 = kbeg + it * 64;
+      if (it + 2 < ntiles) gload(ra, t0 + 128);
+      compute(lds, t0);
+      if (it + 1 < ntiles) lstore(rb, lds + BUF);
+      __syncthreads();
+    }
+    if (it + 1 >= ntiles) break;
+    {
+      const int t0 = kbeg + (it + 1) * 64;
+      if (it + 3 < ntiles) gload(rb, t0 + 128);
+      compute(lds + BUF, t0);
+      if (it + 2 < ntiles) lstore(ra, lds);
+      __syncthreads();
+    }
   }
 
   // ---- partial (m, l, O) of this split
