@@ -2,7 +2,7 @@
 // every node attends only to its ancestors, position ids from the depth) over
 // a request's context cache plus the K/V of its expanded tree nodes.
 //
-// One wave owns (request b, kv head, key split, group of <= 16*RB query rows).
+// k_attn: one wave owns (request b, kv head, key split) and its <= 16 query rows.
 // Query rows of a request are (row, head-in-group) pairs, so all G = Hq/Hkv
 // heads that share a kv head are served by one pass over its keys (GQA).
 // Per 64-key tile:

@@ -227,21 +227,29 @@ void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st) {
 }
 
 // ----------------------------------------------------------------- epilogues
-// sum_{s < S} p[s * stride], added in order s = 0, 1, ...; the loads of up to
-// 16 partials are issued together (indexes clamped into range, the clamped
-// duplicates replaced by 0 before they are added), so the epilogues pay one
-// memory latency instead of S.
-__device__ __forceinline__ float sum_parts(const float* p, int64_t stride, int S) {
+// sum_{s < S} p[s * stride], added in order s = 0, 1, ...; the loads of a
+// batch (sized to S: 2, 4, 8 or 16 partials) are issued together (indexes
+// clamped into range, the clamped duplicates replaced by 0 before they are
+// added), so the epilogues pay about one memory latency instead of S, without
+// re-issuing loads when S is small.
+template <int NB>
+__device__ __forceinline__ float sum_parts_n(const float* p, int64_t stride, int S) {
   float y = 0.f;
-  if (S <= 0) return y;
-  for (int s0 = 0; s0 < S; s0 += 16) {
-    float v[16];
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    float v[NB];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = p[(int64_t)min(s0 + q, S - 1) * stride];
+    for (int q = 0; q < NB; ++q) v[q] = p[(int64_t)min(s0 + q, S - 1) * stride];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) y += s0 + q < S ? v[q] : 0.f;
+    for (int q = 0; q < NB; ++q) y += s0 + q < S ? v[q] : 0.f;
   }
   return y;
+}
+__device__ __forceinline__ float sum_parts(const float* p, int64_t stride, int S) {
+  if (S <= 0) return 0.f;
+  if (S <= 2) return sum_parts_n<2>(p, stride, S);
+  if (S <= 4) return sum_parts_n<4>(p, stride, S);
+  if (S <= 8) return sum_parts_n<8>(p, stride, S);
+  return sum_parts_n<16>(p, stride, S);
 }
 
 // Row epilogue, column-parallel (one thread per column, grid = column blocks x

@@ -259,27 +259,34 @@ void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st)
 // epilogue: tile max, tile sum of exp(s (l - max)), tile top-k.
 constexpr int kLogitTile = 2048;
 __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* logits) {
-  constexpr int PER = kLogitTile / 64;
+  // lane owns columns 4 lane + 256 j + 0..3 (16-byte loads; V % 4 == 0 on this path)
+  constexpr int PER = kLogitTile / 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int m = blockIdx.y * 4 + wave;
   if (m >= a.M) return;
-  const float* row = logits + (int64_t)m * a.V + tile * kLogitTile;
-  float v[PER];
-  int id[PER];
+  const int c0 = tile * kLogitTile;
+  const float* row = logits + (int64_t)m * a.V + c0;
+  float v[PER][4];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int n = tile * kLogitTile + lane + 64 * j;
-    v[j] = n < a.V ? row[lane + 64 * j] : -INFINITY;
-    id[j] = n;
-    mx = fmaxf(mx, v[j]);
+    const int n = c0 + 256 * j + 4 * lane;
+    f32x4 t = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (n < a.V) t = *reinterpret_cast<const f32x4*>(row + 256 * j + 4 * lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[j][e] = t[e];
+      mx = fmaxf(mx, t[e]);
+    }
   }
   mx = wave_max(mx);
   const float sl = a.inv_temp * kLog2e;
   float se = 0.f;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) se += exp2f((v[j] - mx) * sl);
+  for (int j = 0; j < PER; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) se += exp2f((v[j][e] - mx) * sl);
   se = wave_sum(se);
   const int64_t pi = (int64_t)tile * a.M + m;
   if (lane == 0) {
@@ -293,7 +300,11 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
     int bi = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      if (better(pv, pid, v[j], id[j]) && better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = c0 + 256 * j + 4 * lane + e;
+        if (better(pv, pid, v[j][e], id) && better(v[j][e], id, bv, bi)) { bv = v[j][e]; bi = id; }
+      }
     wave_best(bv, bi);
     if (lane == 0) {
       a.part_val[pi * a.top_k + k] = bv;
