@@ -21,6 +21,17 @@ namespace eagle {
 
 constexpr int kAttnWaves = 2;   // kv heads per workgroup
 
+// LDS byte offset of V^T[d][key] (64 keys per row of `rowb` bytes).  bf16 rows
+// hold 8 chunks of 8 keys and chunk j of row d sits at position
+// j ^ ((d >> 3) & 7): the 4-key stores of 16 consecutive d-groups (rows 8
+// apart, which would otherwise share two bank groups) spread over the banks,
+// and an 8-key fragment read stays one contiguous 16-byte chunk.
+template <typename T>
+__device__ __forceinline__ int vt_off(int d, int key, int rowb) {
+  if constexpr (sizeof(T) == 2) return d * rowb + 16 * ((key >> 3) ^ ((d >> 3) & 7)) + 2 * (key & 7);
+  else return d * rowb + 4 * key;
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -78,7 +89,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
         }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          char* dst = vt + (dg * VEC + e) * ROWB + 4 * kq * (int)sizeof(T);
+          char* dst = vt + vt_off<T>(dg * VEC + e, 4 * kq, ROWB);
           if constexpr (sizeof(T) == 2) {
             const int sh = (e & 1) * 16;
             uint32_t w0 = ((v4[0][e >> 1] >> sh) & 0xffffu) | (((v4[1][e >> 1] >> sh) & 0xffffu) << 16);
@@ -149,7 +160,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
         const u32x4 pf = DT<T>::pack(p + v * VEC);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = ld16(vt + (db * 16 + c) * ROWB + (g * 16 + v * VEC) * (int)sizeof(T));
+          const u32x4 vf = ld16(vt + vt_off<T>(db * 16 + c, g * 16 + v * VEC, ROWB));
           o[db][rb] = DT<T>::mma(vf, pf, o[db][rb]);
         }
       }
@@ -239,7 +250,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
   constexpr int DB = HD / 16;
   constexpr int NV = 16 / VEC;
   constexpr int NT = 64 * NW;                          // threads
-  constexpr int KROW = HD * (int)sizeof(T) + 16;       // K tile row (bytes, padded)
+  // K tile rows: bf16 x 128 rows are 16 chunks of 16 bytes, stored unpadded with
+  // chunk j of key row r at position j ^ (((r >> 4) & 3) | ((r & 3) << 2)), so
+  // the 16 keys of one fragment read (4 apart in r & 3, 16 apart in r >> 4)
+  // hit 16 different chunks; other shapes use padded rows
+  constexpr bool KSW = sizeof(T) == 2 && HD == 128;
+  constexpr int KROW = KSW ? HD * 2 : HD * (int)sizeof(T) + 16;
   constexpr int VROW = 64 * (int)sizeof(T) + 16;       // V^T row (bytes, padded)
   constexpr int BUF = 64 * KROW + HD * VROW;
   constexpr int DG = HD / VEC;                         // 16-byte groups per key
@@ -326,7 +342,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int q = tid + i * NT;
-      if (q < KCH) st16(buf + (q / DG) * KROW + (q % DG) * 16, r.kr[i]);
+      if (q < KCH) {
+        const int key = q / DG, ch = q % DG;
+        const int pc = KSW ? ch ^ (((key >> 4) & 3) | ((key & 3) << 2)) : ch;
+        st16(buf + key * KROW + pc * 16, r.kr[i]);
+      }
     }
     char* vt = buf + 64 * KROW;
 #pragma unroll
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
         const int kq = q / DG, dg = q % DG;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          char* dst = vt + (dg * VEC + e) * VROW + 4 * kq * (int)sizeof(T);
+          char* dst = vt + vt_off<T>(dg * VEC + e, 4 * kq, VROW);
           if constexpr (sizeof(T) == 2) {
             const int sh = (e & 1) * 16;
             const uint32_t w0 = ((r.vr[i][0][e >> 1] >> sh) & 0xffffu) | (((r.vr[i][1][e >> 1] >> sh) & 0xffffu) << 16);
@@ -364,8 +384,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
         const int kl = (c >> 2) * 16 + j * 4 + (c & 3);
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < DSTEPS; ++u)
-          acc = DT<T>::mma(ld16(cur + kl * KROW + (u * 4 * VEC + g * VEC) * (int)sizeof(T)), qf[u], acc);
+        for (int u = 0; u < DSTEPS; ++u) {
+          const int ch = 4 * u + g;
+          const int pc = KSW ? ch ^ (((kl >> 4) & 3) | ((kl & 3) << 2)) : ch;
+          acc = DT<T>::mma(ld16(cur + kl * KROW + pc * 16), qf[u], acc);
+        }
         sc[j] = acc;
       }
       // ---- online softmax, O^T += V^T P^T
@@ -408,7 +431,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
         const u32x4 pf = DT<T>::pack(p + v * VEC);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = ld16(vt + (db * 16 + c) * VROW + (g * 16 + v * VEC) * (int)sizeof(T));
+          const u32x4 vf = ld16(vt + vt_off<T>(db * 16 + c, g * 16 + v * VEC, VROW));
           o[db] = DT<T>::mma(vf, pf, o[db]);
         }
       }
@@ -457,7 +480,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
 
 template <typename T, int HD, int NW>
 static void launch_wg(const AttnArgs& a, hipStream_t st) {
-  constexpr int KROW = HD * (int)sizeof(T) + 16, VROW = 64 * (int)sizeof(T) + 16;
+  constexpr bool KSW = sizeof(T) == 2 && HD == 128;
+  constexpr int KROW = KSW ? HD * 2 : HD * (int)sizeof(T) + 16, VROW = 64 * (int)sizeof(T) + 16;
   constexpr int LDS = 2 * (64 * KROW + HD * VROW);
   static bool attr = false;
   if (!attr) {
