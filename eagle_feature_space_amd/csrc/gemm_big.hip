@@ -10,8 +10,9 @@
 //   and stores 16 contiguous bytes);
 //   W and X tiles are staged through LDS, double-buffered; the global loads of
 //   stage k+1 are issued into registers before the MFMAs of stage k and land
-//   in the other LDS buffer after them; LDS rows are padded by 16 bytes so the
-//   16-lane fragment reads hit 16 distinct 4-bank groups.  Sixteen waves (four
+//   in the other LDS buffer after them; the 16-byte chunks of an LDS row are
+//   XOR-swizzled by the row index, so the tile stores and the 16-lane fragment
+//   reads are free of bank conflicts.  Sixteen waves (four
 //   per SIMD) keep the MFMA pipes busy across the barrier and load waits that a
 //   4-wave workgroup of 128 x 64 wave tiles left exposed (2.1x faster at the
 //   70B LM head: 1.14 PFLOP/s);
@@ -25,7 +26,12 @@
 namespace eagle {
 
 constexpr int kBN = 256, kBK = 64;
-constexpr int kRowB = kBK * 2 + 16;                        // padded LDS row (bytes)
+constexpr int kRowB = kBK * 2;                             // LDS row (bytes): 8 chunks of 16 B
+
+// LDS byte offset of 16-byte chunk j of tile row r: chunk j sits at position
+// j ^ ((r >> 1) & 7).  A store pass (16 lanes: two rows x 8 chunks) and a
+// fragment read (16 rows, one chunk each) both touch every bank once.
+__device__ __forceinline__ int big_off(int r, int j) { return r * kRowB + 16 * (j ^ ((r >> 1) & 7)); }
 template <int BM> constexpr int big_stage() { return (kBN + BM) * kRowB; }
 template <int BM> constexpr int big_lds() { return 2 * big_stage<BM>(); }   // 110592 / 147456
 
@@ -99,12 +105,12 @@ __global__ __launch_bounds__(64 * WN * WM) void k_gemm_big(GemmArgs a, int nt, i
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int q = tid + NT * i;
-      st16(base + (q >> 3) * kRowB + (q & 7) * 16, wreg[i]);
+      st16(base + big_off(q >> 3, q & 7), wreg[i]);
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int q = tid + NT * i;
-      st16(base + (kBN + (q >> 3)) * kRowB + (q & 7) * 16, xreg[i]);
+      st16(base + big_off(kBN + (q >> 3), q & 7), xreg[i]);
     }
   };
 
@@ -117,16 +123,16 @@ __global__ __launch_bounds__(64 * WN * WM) void k_gemm_big(GemmArgs a, int nt, i
   for (int k0 = k_begin; k0 < k_end; k0 += kBK) {
     const bool more = k0 + kBK < k_end;
     if (more) gload(k0 + kBK);
-    const char* wt = lds + buf * kStageB + (wn * 16 * WNB) * kRowB;
-    const char* xt = lds + buf * kStageB + (kBN + wm * 16 * WMB) * kRowB;
+    const char* st = lds + buf * kStageB;
+    const int wr0 = wn * 16 * WNB, xr0 = kBN + wm * 16 * WMB;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
       u32x4 xf[WMB];
 #pragma unroll
-      for (int mb = 0; mb < WMB; ++mb) xf[mb] = ld16(xt + (mb * 16 + c) * kRowB + (kk * 32 + g * 8) * 2);
+      for (int mb = 0; mb < WMB; ++mb) xf[mb] = ld16(st + big_off(xr0 + mb * 16 + c, kk * 4 + g));
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
-        const u32x4 wf = ld16(wt + (nb * 16 + c) * kRowB + (kk * 32 + g * 8) * 2);
+        const u32x4 wf = ld16(st + big_off(wr0 + nb * 16 + c, kk * 4 + g));
 #pragma unroll
         for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = DT<bf16s>::mma(wf, xf[mb], acc[nb][mb]);
       }
