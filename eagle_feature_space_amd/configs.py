@@ -184,6 +184,15 @@ SMALL_CONFIGS = {
         seed_w=1108, seed_in=2108, seed_t=3108),
 }
 
+# The maxima of the boundary: top-k 16 with a 64-position verify tree, and a
+# chain of 63 steps (positions 0..63 use every bit of the 64-bit masks).
+SMALL_CONFIGS["s9_dynamic_topk16"] = RoundCfg(
+    name="s9_dynamic_topk16", head=_HEAD_SMALL, B=2, n=(50, 300), tree=TREE_DYNAMIC,
+    gamma=3, top_k=16, top_m=63, inv_temp=4.0, seed_w=1109, seed_in=2109, seed_t=3109)
+SMALL_CONFIGS["s10_chain_63"] = RoundCfg(
+    name="s10_chain_63", head=_HEAD_SMALL, B=1, n=(33,), tree=TREE_CHAIN, gamma=63,
+    top_k=1, seed_w=1110, seed_in=2110, seed_t=3110)
+
 # Chains whose row count sits on either side of every kernel-dispatch boundary:
 # 16 / 17 (row-complete vs split-K streaming), 32 / 33 (streaming vs LDS-staged),
 # 63 / 64 (LDS-staged vs tiled GEMM, and the tiled LM head: |V| = 3008 is a
