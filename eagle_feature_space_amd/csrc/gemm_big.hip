@@ -170,7 +170,7 @@ GemmShape plan_gemm_big(int M, int N, int K) {
   s.mtiles = (M + BM - 1) / BM;
   const int tiles = s.ntiles * s.mtiles;
   const int kst = K / kBK;
-  int S = (512 + tiles - 1) / tiles;      // at least two workgroups per CU
+  int S = (256 + tiles - 1) / tiles;      // one workgroup per CU (LDS-bound): fewer fp32 partials
   if (S > kst / 4) S = kst / 4 > 0 ? kst / 4 : 1;   // keep >= 256 K per split
   if (S < 1) S = 1;
   const int sps = (kst + S - 1) / S;
