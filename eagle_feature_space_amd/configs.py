@@ -60,6 +60,10 @@ class RoundCfg:
     B: int
     n: Tuple[int, ...] = ()           # fixed per-request context lengths (len B) ...
     n_range: Optional[Tuple[int, int]] = None   # ... or uniform integers in [lo, hi]
+    # EAGLE-3 steady-state round: each request already holds n (above) context
+    # positions and ingests tau ~ U{lo..hi} newly verified ones (the previous
+    # round's accepted path and corrected token) instead of all of them
+    new_range: Optional[Tuple[int, int]] = None
     tree: int = TREE_CHAIN
     gamma: int = 4                    # draft depth = number of draft steps
     top_k: int = 1

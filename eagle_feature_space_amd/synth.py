@@ -88,7 +88,7 @@ def f32(a: np.ndarray) -> np.ndarray:
 _T = {name: i for i, name in enumerate([
     "w_fc", "w_fuse", "w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down",
     "norm1_g", "norm1_b", "norm2_g", "norm2_b", "emb", "lm_head",
-    "n", "k_ctx", "v_ctx", "f_root", "t_root", "lmh", "ctx_tokens", "target"])}
+    "n", "k_ctx", "v_ctx", "f_root", "t_root", "lmh", "ctx_tokens", "target", "n_new"])}
 
 
 def head_weights(h: HeadCfg, seed: int) -> Dict[str, np.ndarray]:
@@ -126,8 +126,13 @@ class RoundInputs:
     k_ctx: Optional[np.ndarray] = None  # [sum n, Hkv, hd] (EAGLE-1 rounds)
     v_ctx: Optional[np.ndarray] = None
     f_root: Optional[np.ndarray] = None  # [B, d] (EAGLE-1 rounds)
-    lmh: Optional[np.ndarray] = None     # [sum n, 3d] (EAGLE-3 rounds)
-    ctx_tokens: Optional[np.ndarray] = None  # int32 [sum n] shifted tokens (EAGLE-3)
+    lmh: Optional[np.ndarray] = None     # [sum n, 3d] (EAGLE-3 rounds; new rows only when steady)
+    ctx_tokens: Optional[np.ndarray] = None  # int32 [sum n] shifted tokens (EAGLE-3; likewise)
+    # EAGLE-3 steady state: n counts old + new positions; request b's newest
+    # n_new[b] positions are ingested (packed by cu_new); k_ctx / v_ctx hold the
+    # old positions' K/V in each request's segment (new rows zero)
+    n_new: Optional[np.ndarray] = None   # int32 [B]
+    cu_new: Optional[np.ndarray] = None  # int32 [B+1]
 
 
 def context_lengths(r: RoundCfg) -> np.ndarray:
@@ -152,6 +157,25 @@ def round_inputs(r: RoundCfg) -> RoundInputs:
             k_ctx=normal(s, _T["k_ctx"], (total, h.n_kv, h.head_dim), bf16=bf),
             v_ctx=normal(s, _T["v_ctx"], (total, h.n_kv, h.head_dim), bf16=bf),
             f_root=normal(s, _T["f_root"], (r.B, h.d), bf16=bf))
+    if r.new_range is not None:
+        # steady state: n above is the old context; tau new positions follow
+        tau = integers(s, _T["n_new"], (r.B,), r.new_range[0], r.new_range[1])
+        n_old = n
+        n = (n_old + tau).astype(np.int32)
+        cu[1:] = np.cumsum(n)
+        total = int(cu[-1])
+        cun = np.zeros(r.B + 1, dtype=np.int32)
+        cun[1:] = np.cumsum(tau)
+        k = normal(s, _T["k_ctx"], (total, h.n_kv, h.head_dim), bf16=bf)
+        v = normal(s, _T["v_ctx"], (total, h.n_kv, h.head_dim), bf16=bf)
+        for b in range(r.B):
+            k[cu[b] + n_old[b]:cu[b + 1]] = 0
+            v[cu[b] + n_old[b]:cu[b + 1]] = 0
+        ctx = integers(s, _T["ctx_tokens"], (int(cun[-1]),), 0, h.vocab - 1)
+        ctx[cun[1:] - 1] = t_root
+        return RoundInputs(n=n, cu_n=cu, t_root=t_root, k_ctx=k, v_ctx=v,
+                           lmh=normal(s, _T["lmh"], (int(cun[-1]), 3 * h.d), bf16=bf),
+                           ctx_tokens=ctx, n_new=tau.astype(np.int32), cu_new=cun)
     assert (n >= 1).all(), "EAGLE-3 rounds need at least the anchor position"
     ctx = integers(s, _T["ctx_tokens"], (total,), 0, h.vocab - 1)
     # the shifted token of each request's last position is the anchor token

@@ -22,7 +22,11 @@ Readings (listed in the design notes):
     read), so the full layer runs for that row alone, attending to all
     verified positions of its request;
   * a row attends to its request's whole context plus its ancestor-or-self
-    slots; the root row of an EAGLE-1 round sits at position n_b.
+    slots; the root row of an EAGLE-1 round sits at position n_b;
+  * EAGLE-3 steady state (the next round after a verification, "Speculative
+    Decoding Deep Dive III", EAGLE-3 example: each round feeds the fused
+    features of the verified tokens): only the positions verified since the
+    last round are ingested; their K/V join the cache after the old ones.
 """
 from __future__ import annotations
 
@@ -51,16 +55,16 @@ def row_forward(head: DraftHead, h, pos, ctx_k, ctx_v, anc_k, anc_v):
     return head.finish(h[None, :], att[None])[0], k[0], v[0]
 
 
-def ingest(head: DraftHead, lmh, ctx_tokens):
-    """EAGLE-3 verified positions of ONE request.
+def ingest(head: DraftHead, lmh, ctx_tokens, pos0=0):
+    """EAGLE-3 verified positions pos0 .. pos0 + n - 1 of ONE request.
 
     lmh [n, 3d] (the target's low/mid/high features), ctx_tokens [n] (token
     t_{j+1} following position j; the last is the anchor token).
-    Returns (K [n, Hkv, hd], V [n, Hkv, hd], h_last [d], q-side input of the
-    last row) where K/V hold every position's rotated key/value."""
+    Returns (K [n, Hkv, hd], V [n, Hkv, hd], h_last [d]): every position's
+    rotated key/value and the layer input of the last one."""
     n = lmh.shape[0]
     x = head.latent_input(head.fuse(lmh), ctx_tokens)        # g_j + emb(t_{j+1})
-    _, K, V = head.qkv(x, np.arange(n))
+    _, K, V = head.qkv(x, np.arange(pos0, pos0 + n))
     return K, V, x[-1]
 
 
@@ -87,13 +91,16 @@ class RoundResult:
 
 def run_round(cfg, head: DraftHead, n, t_root, k_ctx=None, v_ctx=None,
               f_root=None, lmh=None, ctx_tokens=None, target=None,
-              teacher=None):
+              teacher=None, n_new=None):
     """One round for all B requests.
 
     n [B] context lengths; EAGLE-1 rounds take packed k_ctx/v_ctx
     [sum n, Hkv, hd] and f_root [B, d]; EAGLE-3 rounds take packed lmh
-    [sum n, 3d] and ctx_tokens [sum n].  target [B, T, |V|] are the
-    verification logits (verify is skipped when None).
+    [sum n, 3d] and ctx_tokens [sum n] -- or, in the steady state (n_new
+    given), the K/V of each request's first n - n_new positions in k_ctx /
+    v_ctx (segments of n rows) and lmh / ctx_tokens for its newest n_new
+    positions only, packed.  target [B, T, |V|] are the verification logits
+    (verify is skipped when None).
     teacher(step) -> (ids, conf) makes the tree follow someone else's
     discrete choices (teacher forcing); the oracle's own logits are still
     computed and recorded.
@@ -103,10 +110,19 @@ def run_round(cfg, head: DraftHead, n, t_root, k_ctx=None, v_ctx=None,
     B = cfg.B
     e3 = c.mode == 3
     cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    cun = None if n_new is None else np.concatenate([[0], np.cumsum(n_new)]).astype(np.int64)
     ctxK, ctxV, root_h = [], [], []
     for b in range(B):
         lo, hi = cu[b], cu[b + 1]
-        if e3:
+        if e3 and cun is not None:
+            # steady state: the old positions' K/V are given, the newest
+            # n_new[b] positions are ingested at positions n_old .. n - 1
+            n_old = int(n[b]) - int(n_new[b])
+            K, V, hl = ingest(head, lmh[cun[b]:cun[b + 1]], ctx_tokens[cun[b]:cun[b + 1]], n_old)
+            ctxK.append(np.concatenate([k_ctx[lo:lo + n_old], K]))
+            ctxV.append(np.concatenate([v_ctx[lo:lo + n_old], V]))
+            root_h.append(hl)
+        elif e3:
             K, V, hl = ingest(head, lmh[lo:hi], ctx_tokens[lo:hi])
             ctxK.append(K)
             ctxV.append(V)

@@ -496,6 +496,51 @@ def test_eagle3_chain_equals_full_causal_recompute():
         assert res.final[b]["pos"][0] == n - 1
 
 
+def test_eagle3_steady_state_equals_full_causal_recompute():
+    """EAGLE-3 steady state: with the first n - tau positions already in the
+    cache (their K/V written out here from the definition, position by
+    position) and only the newest tau positions ingested, a top-1 chain drafts
+    exactly what a full causal recompute of the whole sequence drafts; and it
+    equals the round that ingests all n positions."""
+    cfg = _round_cfg(T.CHAIN, TINY_E3, B=2, n=(7, 4), gamma=3, top_k=1)
+    hd = _head(TINY_E3, np.float64)
+    inp = _inputs64(cfg)
+    full = run_round(cfg, hd, **inp)
+    tau = np.array([3, 1], np.int32)
+    cu = np.concatenate([[0], np.cumsum(inp["n"])])
+    k_old = np.zeros((cu[-1], TINY_E3.n_kv, TINY_E3.head_dim))
+    v_old = np.zeros_like(k_old)
+    lmh_new, tok_new = [], []
+    for b in range(cfg.B):
+        lmh = inp["lmh"][cu[b]:cu[b + 1]]
+        tk = inp["ctx_tokens"][cu[b]:cu[b + 1]]
+        n_old = len(tk) - tau[b]
+        for j in range(n_old):
+            x = hd.fuse(lmh[j:j + 1]) + hd.w["emb"][tk[j:j + 1]]
+            _, k, v = hd.qkv(x, np.array([j]))
+            k_old[cu[b] + j], v_old[cu[b] + j] = k[0], v[0]
+        lmh_new.append(lmh[n_old:])
+        tok_new.append(tk[n_old:])
+    steady = run_round(cfg, hd, n=inp["n"], t_root=inp["t_root"], k_ctx=k_old, v_ctx=v_old,
+                       lmh=np.concatenate(lmh_new), ctx_tokens=np.concatenate(tok_new), n_new=tau)
+    for s in range(cfg.gamma):
+        np.testing.assert_allclose(steady.steps[s].feat, full.steps[s].feat, rtol=1e-10, atol=1e-10)
+    for b in range(cfg.B):
+        assert list(steady.final[b]["tok"]) == list(full.final[b]["tok"])
+        assert list(steady.final[b]["pos"]) == list(full.final[b]["pos"])
+        # and the whole chain against a causal recompute from scratch
+        lmh = inp["lmh"][cu[b]:cu[b + 1]]
+        tk = inp["ctx_tokens"][cu[b]:cu[b + 1]]
+        xs = list(hd.fuse(lmh) + hd.w["emb"][tk])
+        for s in range(cfg.gamma):
+            X = np.stack(xs)
+            q, k, v = hd.qkv(X, np.arange(len(xs)))
+            a = hd.finish(X[-1:], H.attend(q[-1], k, v, hd.group)[None])[0]
+            t = int(np.argmax(hd.lm_head(a[None])[0]))
+            assert steady.final[b]["tok"][s + 1] == t
+            xs.append(a + hd.w["emb"][t])
+
+
 def test_oracle_float32_tracks_float64():
     cfg = C.CONFIGS["c0_tiny_chain"]
     w = synth.head_weights(cfg.head, cfg.seed_w)
