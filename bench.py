@@ -73,9 +73,11 @@ def cpu_baseline(cfg, weights, inp, target, seconds):
     head = DraftHead(cfg.head, {k: synth.f32(v) for k, v in weights.items()})
     kw = dict(n=inp.n, t_root=inp.t_root, target=synth.f32(target))
     if inp.k_ctx is not None:
-        kw.update(k_ctx=synth.f32(inp.k_ctx), v_ctx=synth.f32(inp.v_ctx), f_root=synth.f32(inp.f_root))
-    else:
-        kw.update(lmh=synth.f32(inp.lmh), ctx_tokens=inp.ctx_tokens)
+        kw.update(k_ctx=synth.f32(inp.k_ctx), v_ctx=synth.f32(inp.v_ctx))
+    if inp.f_root is not None:
+        kw.update(f_root=synth.f32(inp.f_root))
+    if inp.lmh is not None:
+        kw.update(lmh=synth.f32(inp.lmh), ctx_tokens=inp.ctx_tokens, n_new=inp.n_new)
     rounds = 0
     t0 = time.perf_counter()
     while True:

@@ -34,7 +34,8 @@ class eagle_head(ctypes.Structure):
 class eagle_kv(ctypes.Structure):
     _fields_ = [("B", c_int32), ("max_n", c_int32), ("total_n", c_int64),
                 ("n", c_void_p), ("cu_n", c_void_p), ("k_ctx", c_void_p), ("v_ctx", c_void_p),
-                ("k_slot", c_void_p), ("v_slot", c_void_p), ("feat_slot", c_void_p)]
+                ("k_slot", c_void_p), ("v_slot", c_void_p), ("feat_slot", c_void_p),
+                ("total_new", c_int64), ("n_new", c_void_p), ("cu_new", c_void_p)]
 
 
 class eagle_tree(ctypes.Structure):

@@ -131,6 +131,13 @@ CONFIGS = {
         name="c3_8b_eagle3", head=HEAD_8B_E3, B=32, n_range=(256, 1024),
         tree=TREE_CHAIN, gamma=7, top_k=1, seed_w=1003, seed_in=2003, seed_t=3003,
         note="EAGLE-3 fused-feature chain, B=32, packed n in [256,1024], gamma=7"),
+    # the round after c3_8b_eagle3's: the cache holds n in [256, 1024] positions
+    # and each request ingests only the tau in [1, 8] it has just verified
+    "c5_8b_eagle3_steady": RoundCfg(
+        name="c5_8b_eagle3_steady", head=HEAD_8B_E3, B=32, n_range=(256, 1024),
+        new_range=(1, 8), tree=TREE_CHAIN, gamma=7, top_k=1, seed_w=1003,
+        seed_in=2005, seed_t=3005,
+        note="EAGLE-3 steady-state chain, B=32, cached n in [256,1024] + tau in [1,8] new, gamma=7"),
     "c4_70b_dynamic": RoundCfg(
         name="c4_70b_dynamic", head=HEAD_70B, B=64, n=(8192,) * 64,
         tree=TREE_DYNAMIC, gamma=6, top_k=8, top_m=60, seed_w=1004,
@@ -196,6 +203,18 @@ SMALL_CONFIGS["s9_dynamic_topk16"] = RoundCfg(
 SMALL_CONFIGS["s10_chain_63"] = RoundCfg(
     name="s10_chain_63", head=_HEAD_SMALL, B=1, n=(33,), tree=TREE_CHAIN, gamma=63,
     top_k=1, seed_w=1110, seed_in=2110, seed_t=3110)
+
+# EAGLE-3 steady state: cached contexts (one empty) plus 1..8 newly verified
+# positions; a dynamic tree at 3 requests (row-complete kernels) and a chain
+# at 20 (split-K kernels at step 0)
+SMALL_CONFIGS["s11_eagle3_steady_dynamic"] = RoundCfg(
+    name="s11_eagle3_steady_dynamic", head=replace(_HEAD_SMALL, mode=MODE_EAGLE3), B=3,
+    n=(0, 40, 120), new_range=(1, 8), tree=TREE_DYNAMIC, gamma=4, top_k=4, top_m=12,
+    inv_temp=4.0, seed_w=1111, seed_in=2111, seed_t=3111)
+SMALL_CONFIGS["s12_eagle3_steady_chain"] = RoundCfg(
+    name="s12_eagle3_steady_chain", head=replace(_HEAD_SMALL, mode=MODE_EAGLE3), B=20,
+    n_range=(0, 60), new_range=(1, 8), tree=TREE_CHAIN, gamma=3, top_k=1,
+    seed_w=1112, seed_in=2112, seed_t=3112)
 
 # Chains whose row count sits on either side of every kernel-dispatch boundary:
 # 16 / 17 (row-complete vs split-K streaming), 32 / 33 (streaming vs LDS-staged),

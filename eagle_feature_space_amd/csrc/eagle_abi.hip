@@ -258,8 +258,17 @@ int check_kv(const eagle_kv* kv, int B) {
   if (!kv->n || !kv->cu_n || !kv->k_slot || !kv->v_slot || !kv->feat_slot) return EAGLE_EINVAL;
   if (kv->total_n > 0 && (!kv->k_ctx || !kv->v_ctx)) return EAGLE_EINVAL;
   if (kv->total_n > INT32_MAX || kv->max_n > kv->total_n) return EAGLE_EINVAL;
+  if (kv->n_new) {
+    if (!kv->cu_new || kv->total_new < B || kv->total_new > kv->total_n) return EAGLE_EINVAL;
+  } else if (kv->cu_new || kv->total_new != 0) {
+    return EAGLE_EINVAL;
+  }
   return EAGLE_OK;
 }
+
+// Rows the EAGLE-3 ingest processes: every context position, or only each
+// request's newest ones in the steady state.
+int64_t ingest_rows(const eagle_kv* kv) { return kv->n_new ? kv->total_new : kv->total_n; }
 
 int check_attn_plan(const eagle_head* h, const eagle_kv* kv);
 
@@ -375,7 +384,7 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
     P = std::max(P, gemm_bytes(h->dtype, M, d, h->ffn));
   }
   w.P = bp.take(P);
-  const int Mrow = std::max(Mr, h->mode == EAGLE_MODE_3 ? (int)kv->total_n : 0);
+  const int Mrow = std::max(Mr, h->mode == EAGLE_MODE_3 ? (int)ingest_rows(kv) : 0);
   w.y32 = bp.take((size_t)Mrow * d * 4);
   w.stats = bp.take((size_t)Mrow * ((d + 255) / 256) * 2 * 4);
   w.ap = plan_attn(h, kv);
@@ -401,7 +410,7 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
   w.t_pos = bp.take((size_t)Mt * 4);
   w.t_mask = bp.take((size_t)Mt * 8);
   if (h->mode == EAGLE_MODE_3) {
-    const int Tn = (int)kv->total_n;
+    const int Tn = (int)ingest_rows(kv);
     w.x_in = bp.take((size_t)Tn * d * e);
     w.xn_in = bp.take((size_t)Tn * d * e);
     w.P_in = bp.take(std::max(gemm_bytes(h->dtype, Tn, d, 3 * d),
@@ -490,8 +499,6 @@ void qkv_rope(const eagle_head* h, const char* ws, const Ws& w, const void* hn, 
   q.hd = h->head_dim;
   q.theta = h->rope_theta;
   q.pos = pos;
-  q.cu_n = nullptr;
-  q.B = 0;
   q.q = (void*)(ws + w.q);
   q.k = kdst;
   q.v = vdst;
@@ -658,9 +665,11 @@ int eagle_tree_init(const eagle_head* head, const eagle_kv* kv, const eagle_tree
   if ((s = check_kv(kv, g.B))) return s;
   if ((s = check_tree_state(tree, g))) return s;
   if (!root_tokens) return EAGLE_EINVAL;
-  if (head->mode == EAGLE_MODE_3 && kv->total_n < kv->B) return EAGLE_EINVAL;
+  if (head->mode == EAGLE_MODE_3 && ingest_rows(kv) < kv->B) return EAGLE_EINVAL;
+  if (head->mode != EAGLE_MODE_3 && kv->n_new) return EAGLE_EINVAL;
+  // EAGLE-3 root rows: the last ingested row of each request
   launch_tree_init(tree_dev(tree, g), g.B, head->mode == EAGLE_MODE_3, head->vocab, root_tokens,
-                   kv->n, kv->cu_n, (hipStream_t)stream);
+                   kv->n, kv->n_new ? kv->cu_new : kv->cu_n, (hipStream_t)stream);
   return finish(EAGLE_OK);
 }
 
@@ -679,7 +688,8 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   if (g.top_k > h->vocab) return EAGLE_EINVAL;
   const bool e3 = h->mode == EAGLE_MODE_3;
   if (step == 0 && !e3 && !f_root) return EAGLE_EINVAL;
-  if (step == 0 && e3 && (!lmh || !ctx_tokens || kv->total_n < 1)) return EAGLE_EINVAL;
+  if (step == 0 && e3 && (!lmh || !ctx_tokens || ingest_rows(kv) < kv->B)) return EAGLE_EINVAL;
+  if (!e3 && kv->n_new) return EAGLE_EINVAL;
   if (!ws_v) return EAGLE_EINVAL;
   const Ws w = plan_ws(h, kv, g);
   if (ws_bytes < w.total) return EAGLE_ECAPACITY;
@@ -729,8 +739,8 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
     reduce(h, nullptr, 0, M, d, rs(kv->feat_slot, td.row_pidx, d, (int64_t)B * kSlots), rs(h->emb, td.row_tok, d, h->vocab),
            hbuf, kNone, rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
   } else {
-    // ingest of every verified position: g = [l;m;h] W_fuse^T, x = g + emb(t_next)
-    const int Tn = (int)kv->total_n;
+    // ingest of the new verified positions: g = [l;m;h] W_fuse^T, x = g + emb(t_next)
+    const int Tn = (int)ingest_rows(kv);
     float* Pin = (float*)(ws + w.P_in);
     gemm(h, rs(lmh, nullptr, 3 * d), kNone, 3 * d, Tn, d, 3 * d, h->w_fuse, nullptr, nullptr, d,
          d, Pin, &sh, st);
@@ -746,19 +756,20 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
     q.Hkv = h->n_kv_heads;
     q.hd = h->head_dim;
     q.theta = h->rope_theta;
-    q.pos = nullptr;
+    q.cu_row = kv->n_new ? kv->cu_new : kv->cu_n;
+    q.n = kv->n;
+    q.n_new = kv->n_new;
     q.cu_n = kv->cu_n;
+    q.total_rows = kv->total_n;
     q.B = B;
-    q.q = nullptr;
     q.k = kv->k_ctx;
     q.v = kv->v_ctx;
-    q.kv_idx = nullptr;
     {
       ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
       launch_epi_qkv(h->dtype, q, st);
     }
     // root rows = each request's last verified position
-    reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, kv->total_n), kNone, hbuf, kNone,
+    reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, Tn), kNone, hbuf, kNone,
            rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
   }
 

@@ -360,11 +360,18 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
   float x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S);
   float x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S);
   int pos;
+  int64_t row = m;
   if (a.pos) pos = a.pos[m];
   else {  // packed context rows: position inside the request
     int b = 0;
-    while (b + 1 < a.B && a.cu_n[b + 1] <= m) ++b;
-    pos = m - a.cu_n[b];
+    while (b + 1 < a.B && a.cu_row[b + 1] <= m) ++b;
+    pos = m - a.cu_row[b];
+    if (a.n_new) {
+      const int nb = a.n[b];
+      pos += nb - a.n_new[b];
+      row = (int64_t)a.cu_n[b] + pos;
+      if (pos < 0 || pos >= nb || row >= a.total_rows) return;
+    }
   }
   const bool is_v = h >= a.Hq + a.Hkv;
   if (!is_v && a.theta > 0.f) {
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
     dst = (T*)a.q + ((int64_t)m * a.Hq + h) * a.hd;
   } else {
     const int kh = is_v ? h - a.Hq - a.Hkv : h - a.Hq;
-    const int64_t r = a.kv_idx ? (int64_t)a.kv_idx[m] : (int64_t)m;
+    const int64_t r = a.kv_idx ? (int64_t)a.kv_idx[m] : row;
     dst = (T*)(is_v ? a.v : a.k) + (r * a.Hkv + kh) * a.hd;
   }
   DT<T>::st(dst + i, x1);

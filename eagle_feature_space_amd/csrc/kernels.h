@@ -84,16 +84,25 @@ bool rows_gemm_ok(int M, int N, int K);
 void launch_gemm_rows(int dtype, int ep, const RowsArgs& a, hipStream_t st);
 
 struct QkvArgs {
-  const float* P;
-  int S, M, Hq, Hkv, hd;
-  float theta;
-  const int32_t* pos;   // per-row position, or null: packed context rows
-  const int32_t* cu_n;
-  int B;
-  void* q;              // [M][Hq][hd] (may be null when Hq == 0)
-  void* k;              // rows kv_idx[m] (or m) of [..][Hkv][hd]
-  void* v;
-  const int32_t* kv_idx;
+  const float* P = nullptr;
+  int S = 0, M = 0, Hq = 0, Hkv = 0, hd = 0;
+  float theta = 0.f;
+  const int32_t* pos = nullptr;    // per-row position, or null: packed context rows
+  // packed context rows: row m belongs to request b with cu_row[b] <= m <
+  // cu_row[b+1].  n_new null: its position is m - cu_row[b] and K/V go to row
+  // m.  n_new set (rows are each request's newest positions): the position is
+  // n[b] - n_new[b] + (m - cu_row[b]) and K/V go to row cu_n[b] + position;
+  // rows whose position falls outside [0, n[b]) or past total_rows are skipped.
+  const int32_t* cu_row = nullptr;
+  const int32_t* n = nullptr;
+  const int32_t* n_new = nullptr;
+  const int32_t* cu_n = nullptr;
+  int64_t total_rows = 0;
+  int B = 0;
+  void* q = nullptr;               // [M][Hq][hd] (may be null when Hq == 0)
+  void* k = nullptr;               // rows kv_idx[m] (or as above) of [..][Hkv][hd]
+  void* v = nullptr;
+  const int32_t* kv_idx = nullptr;
 };
 void launch_epi_qkv(int dtype, const QkvArgs& a, hipStream_t st);
 

@@ -62,9 +62,14 @@ class GpuRound:
         self.n = to_dev(inputs.n.astype(np.int32), self.dev)
         self.cu_n = to_dev(inputs.cu_n.astype(np.int32), self.dev)
         total = int(inputs.cu_n[-1])
+        steady = inputs.n_new is not None
         if h.mode == MODE_EAGLE3:
-            self.k_ctx = torch.zeros((max(total, 1), h.n_kv, h.head_dim), dtype=self.dt, device=self.dev)
-            self.v_ctx = torch.zeros_like(self.k_ctx)
+            if steady:  # the old positions' K/V are already cached
+                self.k_ctx = to_dev(inputs.k_ctx, self.dev)
+                self.v_ctx = to_dev(inputs.v_ctx, self.dev)
+            else:
+                self.k_ctx = torch.zeros((max(total, 1), h.n_kv, h.head_dim), dtype=self.dt, device=self.dev)
+                self.v_ctx = torch.zeros_like(self.k_ctx)
             self.lmh = to_dev(inputs.lmh, self.dev)
             self.ctx_tokens = to_dev(inputs.ctx_tokens.astype(np.int32), self.dev)
             self.f_root = None
@@ -83,6 +88,11 @@ class GpuRound:
         kv.v_ctx = self.v_ctx.data_ptr() if self.v_ctx is not None else None
         kv.k_slot, kv.v_slot = self.k_slot.data_ptr(), self.v_slot.data_ptr()
         kv.feat_slot = self.feat_slot.data_ptr()
+        if steady:
+            self.n_new = to_dev(inputs.n_new.astype(np.int32), self.dev)
+            self.cu_new = to_dev(inputs.cu_new.astype(np.int32), self.dev)
+            kv.total_new = int(inputs.cu_new[-1])
+            kv.n_new, kv.cu_new = self.n_new.data_ptr(), self.cu_new.data_ptr()
         self.kv = kv
 
         tr = E.eagle_tree()

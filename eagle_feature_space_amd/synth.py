@@ -159,6 +159,7 @@ def round_inputs(r: RoundCfg) -> RoundInputs:
             f_root=normal(s, _T["f_root"], (r.B, h.d), bf16=bf))
     if r.new_range is not None:
         # steady state: n above is the old context; tau new positions follow
+        assert r.new_range[0] >= 1, "every request ingests at least its anchor position"
         tau = integers(s, _T["n_new"], (r.B,), r.new_range[0], r.new_range[1])
         n_old = n
         n = (n_old + tau).astype(np.int32)

@@ -102,6 +102,15 @@ typedef struct eagle_head {
  *                                     attention, written by the EAGLE-3 ingest
  *   k_slot,v_slot [B][64][Hkv][hd]    K/V of every expanded tree node (slot)
  *   feat_slot     [B][64][d]          layer output of every expanded node
+ * EAGLE-3 steady state ("Speculative Decoding Deep Dive III", EAGLE-3
+ * example: each round feeds the fused features of the tokens the target has
+ * just verified; the draft cache of older positions is kept).  With n_new set, request b already holds the K/V of its first
+ * n[b] - n_new[b] positions in k_ctx/v_ctx, and step 0 ingests only its last
+ * n_new[b] >= 1 positions (the accepted path and the target's token).  With
+ * n_new NULL every one of the n[b] positions is ingested (a first round).
+ * The caller keeps 1 <= n_new[b] <= n[b] and cu_new the prefix sum of n_new;
+ * rows that break this are skipped on the device, never written outside
+ * k_ctx/v_ctx.
  */
 typedef struct eagle_kv {
   int32_t B;
@@ -110,6 +119,9 @@ typedef struct eagle_kv {
   const int32_t *n;    /* device [B]   */
   const int32_t *cu_n; /* device [B+1] */
   void *k_ctx, *v_ctx, *k_slot, *v_slot, *feat_slot; /* device */
+  int64_t total_new;      /* host copy of sum_b n_new[b] (0 when n_new NULL) */
+  const int32_t *n_new;   /* device [B] or NULL (EAGLE-3 only)              */
+  const int32_t *cu_new;  /* device [B+1] or NULL; required with n_new      */
 } eagle_kv;
 
 /*
@@ -195,19 +207,23 @@ int eagle_tree_init(const eagle_head *head, const eagle_kv *kv,
  * (node u of request b at depth `step`):
  *   EAGLE-1: x = [f ; emb(tok(u))] with f = f_root[b] for the root, else the
  *            layer output stored in the parent's slot; h = x W_fc^T
- *   EAGLE-3: step 0 ingests every verified position j of every request:
+ *   EAGLE-3: step 0 ingests every new verified position j of every request
+ *            (all n[b] of them, or the last n_new[b] in the steady state):
  *            g_j = lmh_j W_fuse^T, x_j = g_j + emb(ctx_tokens[j]); K/V of each
- *            position are written to k_ctx/v_ctx; the root row is each
- *            request's last position.  Later steps: h = a_parent + emb(tok(u)).
+ *            are written to k_ctx/v_ctx at the position's own row of the
+ *            request's segment; the root row is each request's last position.
+ *            Later steps: h = a_parent + emb(tok(u)).
  *   then the decoder layer at position root_pos + depth; attention sees the
  *   request's context plus the ancestor-or-self slots (row_mask); K/V and the
  *   output go to the row's slot; logits = W_LM out; top_k ids, their
  *   confidences softmax(inv_temp * logits)[id] and the log-partition go to
  *   the tree state.
  * f_root:     device [B][d]           (EAGLE-1, step 0; else unused)
- * lmh:        device [total_n][3d]    (EAGLE-3, step 0; l, m, h concatenated)
- * ctx_tokens: device [total_n] int32  (EAGLE-3, step 0; token after each
- *             verified position, the anchor token last)
+ * lmh:        device [T][3d]          (EAGLE-3, step 0; l, m, h concatenated;
+ *             T = total_new in the steady state, else total_n; packed by
+ *             cu_new, else cu_n)
+ * ctx_tokens: device [T] int32        (EAGLE-3, step 0; token after each
+ *             ingested position, the anchor token last)
  * logits_out: optional device [M][V] fp32 (M = B * eagle_step_rows)
  * feat_out:   optional device [M][d] in the head dtype (layer outputs)
  * ws:         device workspace of at least eagle_workspace_bytes

@@ -101,8 +101,17 @@ def check_step(case: Case, gr, snaps, s, rows=None, report=None):
         ck, cv = ctx[b]
         if e3 and s == 0:
             if b not in ingested:
-                K, V, hl = ingest(hd, synth.f32(inp.lmh[cu[b]:cu[b + 1]]), inp.ctx_tokens[cu[b]:cu[b + 1]])
-                worst["ctxkv"] = max(worst["ctxkv"], rel_err(ck, K), rel_err(cv, V))
+                if inp.n_new is None:
+                    lo, hi, n_old = cu[b], cu[b + 1], 0
+                else:  # steady state: only the newest n_new[b] positions are ingested
+                    lo, hi = inp.cu_new[b], inp.cu_new[b + 1]
+                    n_old = int(inp.n[b]) - int(inp.n_new[b])
+                    # the cached positions are left exactly as they were
+                    old = slice(cu[b], cu[b] + n_old)
+                    assert np.array_equal(ck[:n_old], synth.f32(inp.k_ctx[old])), f"request {b}: old K changed"
+                    assert np.array_equal(cv[:n_old], synth.f32(inp.v_ctx[old])), f"request {b}: old V changed"
+                K, V, hl = ingest(hd, synth.f32(inp.lmh[lo:hi]), inp.ctx_tokens[lo:hi], n_old)
+                worst["ctxkv"] = max(worst["ctxkv"], rel_err(ck[n_old:], K), rel_err(cv[n_old:], V))
                 ingested[b] = hl
             h = ingested[b]
             q, _, _ = hd.qkv(h[None], np.array([pos]))

@@ -3,6 +3,7 @@ symbol include/eagle.h declares, sizes its buffers consistently with the tree
 shapes, and rejects bad arguments before launching anything.  No GPU needed:
 every call here returns before the first HIP call."""
 import ctypes
+from dataclasses import replace
 import os
 import re
 
@@ -157,3 +158,28 @@ def test_rejects_bad_arguments_before_launch(lib):
     assert lib.eagle_tree_verify(t, 1, 2, 100, 0, 1, 1, 1, None) == E.EAGLE_EINVAL
     assert lib.eagle_tree_verify(t, 1, 64, 100, 5, 1, 1, 1, None) == E.EAGLE_EINVAL
     assert lib.eagle_strerror(E.EAGLE_ECAPACITY).startswith(b"capacity")
+
+
+def test_steady_state_kv_is_validated(lib):
+    """EAGLE-3 steady state: n_new needs cu_new and 1 <= total_new / B; an
+    EAGLE-1 head refuses it; its workspace is sized by the new rows only."""
+    cfg = C.CONFIGS["c5_8b_eagle3_steady"]
+    n = [600] * cfg.B
+    h, t = _head(cfg.head), _tree(cfg)
+    full = E.eagle_workspace_bytes(h, _kv(cfg, n), t)
+    kv = _kv(cfg, n)
+    kv.n_new, kv.cu_new, kv.total_new = 1 << 20, 1 << 20, 4 * cfg.B
+    steady = E.eagle_workspace_bytes(h, kv, t)
+    assert 0 < steady < full
+    for f, v in [("cu_new", None), ("total_new", cfg.B - 1), ("total_new", sum(n) + 1)]:
+        kb = _kv(cfg, n)
+        kb.n_new, kb.cu_new, kb.total_new = 1 << 20, 1 << 20, 4 * cfg.B
+        setattr(kb, f, v)
+        assert E.eagle_workspace_bytes(h, kb, t) == 0, (f, v)
+    kb = _kv(cfg, n)
+    kb.cu_new = 1 << 20           # cu_new without n_new
+    assert E.eagle_workspace_bytes(h, kb, t) == 0
+    ts = _tree(cfg, state=1 << 20, nbytes=1 << 30)
+    h1 = _head(replace(cfg.head, mode=C.MODE_EAGLE1))
+    assert lib.eagle_draft_step(h1, kv, ts, 0, 1, None, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
+    assert lib.eagle_tree_init(h1, kv, ts, 1, None) == E.EAGLE_EINVAL
