@@ -496,6 +496,101 @@ def test_eagle3_chain_equals_full_causal_recompute():
         assert res.final[b]["pos"][0] == n - 1
 
 
+# ------------------------------------------------- stochastic verification
+@pytest.mark.parametrize("seed", range(8))
+def test_verify_sample_with_one_hot_target_is_greedy(seed):
+    """A target with all its mass on the argmax (inv_temp -> infinity) makes
+    multi-round speculative sampling deterministic: it must return exactly
+    what greedy verification returns, on random dynamic trees."""
+    rng = np.random.default_rng(300 + seed)
+    t = _random_tree(rng, T.DYNAMIC, 4, 3, 10, V=12)
+    f = t.final_tree()
+    Tn = len(f["tok"])
+    logits = rng.standard_normal((Tn, 12))
+    # plant some accepted children so paths of every length occur
+    for u in range(Tn):
+        kids = [v for v in range(Tn) if f["parent"][v] == u]
+        if kids and rng.random() < 0.7:
+            logits[u, f["tok"][kids[int(rng.integers(len(kids)))]]] = 4.0
+    draws = rng.random((Tn, VF.N_DRAWS)) * (1 - 1e-9)
+    g = VF.verify(f["tok"], f["parent"], logits.astype(np.float32), 4)
+    s_ = VF.verify_sample(f["tok"], f["parent"], logits.astype(np.float32), 1e6, draws, 4)
+    assert g[0] == s_[0]
+    assert list(g[1]) == list(s_[1]) and list(g[2]) == list(s_[2])
+
+
+def _sampled(tok, parent, logits, inv_temp, gamma, n, seed):
+    rng = np.random.default_rng(seed)
+    res = []
+    for _ in range(n):
+        res.append(VF.verify_sample(tok, parent, logits, inv_temp, rng.random((len(tok), VF.N_DRAWS)), gamma))
+    return res
+
+
+def _close(freq, p, n, z=5.0):
+    return np.all(np.abs(freq - p) <= z * np.sqrt(p * (1 - p) / n) + 1.0 / n)
+
+
+def test_verify_sample_is_lossless():
+    """The emitted tokens follow the target: the first ~ p(root), and after an
+    accepted child the next ~ p(that child's position), whatever the tree
+    proposed (Monte Carlo, fixed seed, 5-sigma bounds per token)."""
+    V = 6
+    tok = np.array([5, 3, 1, 4, 0])          # root; children 3, 1, 4; 3 -> 0
+    parent = np.array([-1, 0, 0, 0, 1])
+    rng = np.random.default_rng(7)
+    logits = rng.standard_normal((5, V)).astype(np.float32)
+    s = 1.3
+    n = 30000
+    res = _sampled(tok, parent, logits, s, 2, n, 8)
+    first = np.array([o[2][0] for o in res])
+    p0 = VF.target_probs(logits[0], s)
+    assert _close(np.bincount(first, minlength=V) / n, p0, n)
+    for child in (1, 2):                     # token 3 (has a child), token 1 (leaf)
+        sel = [o for o in res if o[0] >= 1 and o[1][1] == child]
+        second = np.array([o[2][1] for o in sel])
+        pc = VF.target_probs(logits[child], s)
+        assert _close(np.bincount(second, minlength=V) / len(sel), pc, len(sel))
+    # a token drawn from the residual is never one the node's children offered
+    for acc, path, out in res:
+        u = path[acc]
+        offered = {int(tok[v]) for v in range(5) if parent[v] == u}
+        assert out[acc] not in offered
+
+
+def test_verify_sample_chain_acceptance_matches_page():
+    """Chain whose every drafted token has target probability alpha = 0.7:
+    P(reach depth 2) = 0.49 and E[tokens per pass] = (1 - a^(g+1)) / (1 - a)
+    ("transformer_math / tm_eagle_deep", Acceptance length under a tree)."""
+    g = json.load(open(os.path.join(GOLD, "tree_acceptance_examples.json")))
+    V, gamma, a = 10, 3, 0.7
+    tok = np.array([9, 1, 2, 3])
+    parent = np.array([-1, 0, 1, 2])
+    logits = np.zeros((4, V), np.float32)
+    for u in range(3):
+        logits[u, tok[u + 1]] = np.log(a * (V - 1) / (1 - a))
+    n = 20000
+    acc = np.array([r[0] for r in _sampled(tok, parent, logits, 1.0, gamma, n, 9)])
+    reach2 = (acc >= 2).mean()
+    assert abs(reach2 - g["reach_depth2_alpha07_chain"]) <= 5 * np.sqrt(0.49 * 0.51 / n)
+    expect = (1 - a ** (gamma + 1)) / (1 - a)
+    assert abs((acc + 1).mean() - expect) <= 5 * (acc + 1).std() / np.sqrt(n)
+
+
+def test_verify_sample_residual_is_inverse_cdf():
+    """Brute force on a tiny vocabulary: the residual draw is the token whose
+    cumulative-mass interval (rejected tokens removed) contains u."""
+    p = np.array([0.1, 0.25, 0.05, 0.3, 0.2, 0.1])
+    excl = [3, 0]
+    r = p.copy()
+    r[excl] = 0
+    r /= r.sum()
+    edges = np.concatenate([[0], np.cumsum(r)])
+    for u in np.linspace(0, 1, 101)[:-1]:
+        x = VF.residual_draw(p, excl, u)
+        assert x not in excl and edges[x] <= u < edges[x + 1] + 1e-12
+
+
 def test_eagle3_steady_state_equals_full_causal_recompute():
     """EAGLE-3 steady state: with the first n - tau positions already in the
     cache (their K/V written out here from the definition, position by
