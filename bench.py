@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--workload", default="c1_8b_static")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--verify", choices=("greedy", "sample"), default="greedy",
+                    help="greedy verification (default) or lossless speculative sampling "
+                         "(inverse temperature 1, seeded uniforms)")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="one 1 GiB device-to-device copy before warm-up (a known-size kernel for "
@@ -138,6 +141,9 @@ def main():
     tgt = to_dev(target, gr.dev)
     torch.cuda.synchronize()
 
+    sample = None
+    if args.verify == "sample":
+        sample = (1.0, to_dev(synth.verify_draws(cfg, tgt.shape[1]), gr.dev))
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=gr.dev).fill_(7)
         dst = torch.empty_like(src)
@@ -146,7 +152,7 @@ def main():
         del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        gr.run(target=tgt, attend=cfg.tree_attend)
+        gr.run(target=tgt, attend=cfg.tree_attend, sample=sample)
     torch.cuda.synchronize()
 
     # ---- timed region: K rounds; HIP events bracket the LM-head launches only
@@ -155,7 +161,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        gr.run(target=tgt, attend=cfg.tree_attend)
+        gr.run(target=tgt, attend=cfg.tree_attend, sample=sample)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     E.eagle_profile_enable(False)
@@ -181,7 +187,7 @@ def main():
         E.eagle_profile_reset()
         E.eagle_profile_enable(True)
         for _ in range(R):
-            gr.run(target=tgt, attend=cfg.tree_attend)
+            gr.run(target=tgt, attend=cfg.tree_attend, sample=sample)
         torch.cuda.synchronize()
         E.eagle_profile_enable(False)
         breakdown = {}
@@ -217,7 +223,10 @@ def main():
             if cfg.tree_attend:
                 gr.attend()
             ev[r][1].record()
-            gr.verify(tgt)
+            if sample is None:
+                gr.verify(tgt)
+            else:
+                gr.verify_sample(tgt, *sample)
             ev[r][2].record()
         torch.cuda.synchronize()
         tot = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in ev)
@@ -245,7 +254,7 @@ def main():
                    "heads": f"{h.n_q}q/{h.n_kv}kv x {h.head_dim}", "ffn": h.ffn,
                    "n": int(inp.n.max()), "tree": {0: "chain", 1: "static", 2: "dynamic"}[cfg.tree],
                    "gamma": cfg.gamma, "top_k": cfg.top_k, "top_m": cfg.top_m,
-                   "nodes_per_round": nodes},
+                   "nodes_per_round": nodes, "verify": args.verify},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown": breakdown,

@@ -20,6 +20,7 @@ c_int32, c_int64, c_float, c_size_t, c_void_p = (ctypes.c_int32, ctypes.c_int64,
 EAGLE_OK, EAGLE_EINVAL, EAGLE_EUNSUPPORTED, EAGLE_ECAPACITY, EAGLE_EHIP = 0, -1, -2, -3, -4
 MAX_SLOTS = 64
 MAX_POSITIONS = 64
+VERIFY_DRAWS = 17
 
 
 class eagle_head(ctypes.Structure):
@@ -88,6 +89,9 @@ def lib():
                                c_size_t, c_void_p], ctypes.c_int),
         "eagle_tree_verify": ([P(eagle_tree), c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                c_void_p, c_void_p, c_void_p, c_void_p], ctypes.c_int),
+        "eagle_tree_verify_sample": ([P(eagle_tree), c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_float, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p], ctypes.c_int),
         "eagle_profile_enable": ([ctypes.c_int], ctypes.c_int),
         "eagle_profile_reset": ([], ctypes.c_int),
         "eagle_profile_read": ([ctypes.c_int, P(c_int64), P(c_int64), P(ctypes.c_double),
@@ -104,6 +108,7 @@ def lib():
 EXPORTED = ("eagle_version", "eagle_strerror", "eagle_tree_layout_of", "eagle_tree_state_bytes",
             "eagle_step_rows", "eagle_workspace_bytes", "eagle_tree_init", "eagle_draft_step",
             "eagle_tree_expand_rerank", "eagle_tree_attend", "eagle_tree_verify",
+            "eagle_tree_verify_sample",
             "eagle_profile_enable", "eagle_profile_reset", "eagle_profile_read")
 
 PROF_FAMILIES = {"lmhead": 0, "gemm": 1, "attn": 2, "verify": 3, "other": 4}
@@ -188,6 +193,14 @@ def eagle_tree_verify(tree, target_logits, positions, vocab, dtype, accept_len, 
     return _check(lib().eagle_tree_verify(ctypes.byref(tree), _ptr(target_logits), positions, vocab,
                                           dtype, _ptr(accept_len), _ptr(accept_path),
                                           _ptr(out_tokens), _stream(stream)), "eagle_tree_verify")
+
+
+def eagle_tree_verify_sample(tree, target_logits, positions, vocab, dtype, inv_temp, draws,
+                             accept_len, accept_path, out_tokens, stream=None):
+    return _check(lib().eagle_tree_verify_sample(ctypes.byref(tree), _ptr(target_logits), positions,
+                                                 vocab, dtype, inv_temp, _ptr(draws), _ptr(accept_len),
+                                                 _ptr(accept_path), _ptr(out_tokens), _stream(stream)),
+                  "eagle_tree_verify_sample")
 
 
 def eagle_profile_enable(on=True):

@@ -978,4 +978,24 @@ int eagle_tree_verify(const eagle_tree* tree, const void* target_logits, int pos
   return finish(EAGLE_OK);
 }
 
+int eagle_tree_verify_sample(const eagle_tree* tree, const void* target_logits, int positions,
+                             int vocab, int dtype, float inv_temp, const float* draws,
+                             int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                             void* stream) {
+  Geo g;
+  int s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (!target_logits || !draws || !accept_len || !accept_path || !out_tokens) return EAGLE_EINVAL;
+  if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_EINVAL;
+  if (vocab < 1 || positions < g.positions) return EAGLE_EINVAL;
+  if (!(inv_temp > 0.f) || !std::isfinite(inv_temp)) return EAGLE_EINVAL;
+  {
+    ProfScope ps(EAGLE_PROF_VERIFY, 0, 0, (hipStream_t)stream);
+    launch_verify_sample(tree_dev(tree, g), g.B, target_logits, positions, vocab, dtype, inv_temp,
+                         draws, g.gamma, accept_len, accept_path, out_tokens, (hipStream_t)stream);
+  }
+  return finish(EAGLE_OK);
+}
+
 }  // extern "C"

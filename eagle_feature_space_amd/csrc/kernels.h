@@ -222,6 +222,10 @@ void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, 
 void launch_verify(const TreeDev& t, int B, const void* logits, int positions,
                    int vocab, int dtype, int gamma, int32_t* accept_len,
                    int32_t* accept_path, int32_t* out_tokens, hipStream_t st);
+void launch_verify_sample(const TreeDev& t, int B, const void* logits, int positions, int vocab,
+                          int dtype, float inv_temp, const float* draws, int gamma,
+                          int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                          hipStream_t st);
 void launch_tree_rows_final(const TreeDev& t, int B, int32_t* tok_idx,
                             int32_t* kv_idx, int32_t* pos, uint64_t* mask,
                             hipStream_t st);

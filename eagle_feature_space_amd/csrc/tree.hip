@@ -318,6 +318,187 @@ void launch_verify(const TreeDev& t, int B, const void* logits, int positions, i
                      accept_path, out_tokens);
 }
 
+// ------------------------------------------------- stochastic verification
+// Multi-round speculative sampling over the verify tree, one workgroup per
+// request (the walk is sequential; only the rows it visits are read).  At a
+// visited node u the target distribution is p(y) = e_y / S with
+// v_y = fp32(s * z_y), M = max_y v_y, e_y = expf(v_y - M) and S the fp64 sum of
+// the e_y.  Children of u are tried in verify-tree order: child i (token x) is
+// kept iff draw[u][i] < e_x / (S - sum of e over the children rejected before
+// it).  When none is kept (or u has no child, or u is at depth gamma) one
+// token is drawn from p with the rejected tokens removed, by inverse CDF over
+// token ids: the smallest x whose cumulative fp64 mass exceeds
+// draw[u][16] * (total residual mass).  Each thread owns one contiguous range
+// of token ids, so the cumulative sums follow id order: per-thread sums, a
+// workgroup exclusive scan in thread order, then the one thread whose range
+// holds the target walks it.  Every sum has a fixed order (deterministic).
+constexpr int kSampleThreads = 512;
+constexpr int kDraws = EAGLE_VERIFY_DRAWS;
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSampleThreads) void k_verify_sample(
+    TreeDev t, const T* logits, int positions, int V, float s, const float* draws, int gamma,
+    int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens) {
+  constexpr int NW = kSampleThreads / 64;
+  constexpr int VEC = DT<T>::VEC;
+  __shared__ float s_max[NW];
+  __shared__ double s_sum[NW];
+  __shared__ double s_pre[NW];
+  __shared__ int s_excl[kMaxTopK];
+  __shared__ int s_nexcl, s_next, s_pick;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T_ = t.f_count[b];
+  const int fb = b * kMaxPos;
+  int32_t* path = accept_path + (int64_t)b * (gamma + 1);
+  int32_t* out = out_tokens + (int64_t)b * (gamma + 1);
+  if (tid <= gamma) { path[tid] = tid == 0 ? 0 : -1; out[tid] = -1; }
+  // this thread's token ids [lo, hi), whole granules except at the row's end
+  const int per = ((V + kSampleThreads - 1) / kSampleThreads + VEC - 1) / VEC * VEC;
+  const int lo = min(V, tid * per), hi = min(V, lo + per);
+
+  int u = 0, acc = 0;
+  while (true) {
+    const T* row = logits + ((int64_t)b * positions + u) * V;
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    // visit this thread's values: f(y, v) for y in [lo, hi)
+    auto each = [&](auto&& f) {
+      int y = lo;
+      if (aligned) {
+        for (; y + VEC <= hi; y += VEC) {
+          const u32x4 x = ld16(row + y);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) f(y + e, s * DT<T>::elem(x, e));
+        }
+      }
+      for (; y < hi; ++y) f(y, s * DT<T>::ld(row + y));
+    };
+    // M = max v
+    float m = -INFINITY;
+    each([&](int, float v) { m = fmaxf(m, v); });
+    m = wave_max(m);
+    if (lane == 0) s_max[wave] = m;
+    __syncthreads();
+    float M = s_max[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_max[w]);
+    // S = sum e (thread ranges, then waves, in order)
+    double sm = 0.0;
+    each([&](int, float v) { sm += (double)expf(v - M); });
+    sm = wave_sum_d(sm);
+    if (lane == 0) s_sum[wave] = sm;
+    __syncthreads();
+    if (tid == 0) {
+      double S = 0.0;
+      for (int w = 0; w < NW; ++w) S += s_sum[w];
+      const float* dr = draws + ((int64_t)b * positions + u) * kDraws;
+      double rem = S;
+      int nex = 0, nxt = -1;
+      if (acc < gamma) {
+        for (int v = u + 1; v < T_ && nex < kMaxTopK; ++v) {
+          if (t.f_parent[fb + v] != u) continue;
+          const int x = t.f_tok[fb + v];
+          // a token outside the target's vocabulary has no target mass
+          const double e = x >= 0 && x < V ? (double)expf(s * DT<T>::ld(row + x) - M) : 0.0;
+          if ((double)dr[nex] < e / rem) { nxt = v; break; }
+          rem -= e;
+          s_excl[nex++] = x;
+        }
+      }
+      s_nexcl = nex;
+      s_next = nxt;
+      s_pick = -1;
+    }
+    __syncthreads();
+    const int nxt = s_next;
+    if (nxt >= 0) {   // every thread follows the walk
+      if (tid == 0) {
+        out[acc] = t.f_tok[fb + nxt];
+        path[acc + 1] = nxt;
+      }
+      ++acc;
+      u = nxt;
+      __syncthreads();
+      continue;
+    }
+    // residual draw at u: the rejected tokens carry no mass
+    const int nex = s_nexcl;
+    auto mass = [&](int y, float v) -> double {
+      for (int i = 0; i < nex; ++i)
+        if (s_excl[i] == y) return 0.0;
+      return (double)expf(v - M);
+    };
+    double part = 0.0;
+    each([&](int y, float v) { part += mass(y, v); });
+    // prefix sums of the per-thread masses in thread order; thread t's
+    // interval is [end of thread t-1, end of thread t), so the intervals tile
+    // [0, total) exactly and one thread at most holds the target
+    double inc = part;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double x = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += x;
+    }
+    if (lane == 63) s_pre[wave] = inc;
+    __syncthreads();
+    double before = 0.0, total = 0.0;
+    for (int w = 0; w < NW; ++w) {
+      if (w == wave) before = total;
+      total += s_pre[w];
+    }
+    const double end = before + inc;
+    double start = __shfl_up(end, 1, 64);
+    if (lane == 0) start = before;
+    const double target =
+        (double)draws[((int64_t)b * positions + u) * kDraws + kDraws - 1] * total;
+    if (part > 0.0 && start <= target && target < end) {
+      double c = start;
+      int pick = -1, last = -1;
+      each([&](int y, float v) {
+        if (pick >= 0) return;
+        const double e = mass(y, v);
+        if (e > 0.0) last = y;
+        c += e;
+        if (c > target && e > 0.0) pick = y;
+      });
+      s_pick = pick >= 0 ? pick : last;   // rounding at the range's end
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int pick = s_pick;
+      if (pick < 0) {  // target at or past the total (rounding): last token with mass
+        for (int y = V - 1; y >= 0 && pick < 0; --y) {
+          bool ex = false;
+          for (int i = 0; i < nex; ++i) ex |= s_excl[i] == y;
+          if (!ex) pick = y;
+        }
+      }
+      out[acc] = pick;
+      accept_len[b] = acc;
+    }
+    return;
+  }
+}
+
+void launch_verify_sample(const TreeDev& t, int B, const void* logits, int positions, int vocab,
+                          int dtype, float inv_temp, const float* draws, int gamma,
+                          int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                          hipStream_t st) {
+  if (dtype == EAGLE_BF16)
+    hipLaunchKernelGGL(k_verify_sample<bf16s>, dim3(B), dim3(kSampleThreads), 0, st, t,
+                       (const bf16s*)logits, positions, vocab, inv_temp, draws, gamma, accept_len,
+                       accept_path, out_tokens);
+  else
+    hipLaunchKernelGGL(k_verify_sample<float>, dim3(B), dim3(kSampleThreads), 0, st, t,
+                       (const float*)logits, positions, vocab, inv_temp, draws, gamma, accept_len,
+                       accept_path, out_tokens);
+}
+
 // dense rows of the verify tree (row m = b * positions + u)
 __global__ void k_tree_rows_final(TreeDev t, int B, int32_t* tok_idx, int32_t* kv_idx,
                                   int32_t* pos, uint64_t* mask) {

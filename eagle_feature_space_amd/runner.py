@@ -178,9 +178,19 @@ class GpuRound:
         E.eagle_tree_verify(self.tree, target, target.shape[1], target.shape[2], dtype,
                             self.accept_len, self.accept_path, self.out_tokens, stream)
 
-    def run(self, target=None, snapshots=False, attend=False) -> List[StepSnapshot]:
+    def verify_sample(self, target: torch.Tensor, inv_temp: float, draws: torch.Tensor, stream=None):
+        """Stochastic (lossless) verification; draws [B, positions, 17] fp32 on the device."""
+        dtype = 0 if target.dtype == torch.bfloat16 else 1
+        assert draws.dtype == torch.float32 and draws.is_contiguous()
+        assert tuple(draws.shape) == (self.cfg.B, target.shape[1], E.VERIFY_DRAWS)
+        E.eagle_tree_verify_sample(self.tree, target, target.shape[1], target.shape[2], dtype,
+                                   inv_temp, draws, self.accept_len, self.accept_path,
+                                   self.out_tokens, stream)
+
+    def run(self, target=None, snapshots=False, attend=False, sample=None) -> List[StepSnapshot]:
         """One round; with snapshots=True the state after every draft step is
-        copied to the host (for parity checks; synchronises)."""
+        copied to the host (for parity checks; synchronises).  sample =
+        (inv_temp, draws) verifies by speculative sampling instead of greedily."""
         cfg = self.cfg
         snaps = []
         self.init()
@@ -206,5 +216,8 @@ class GpuRound:
         if attend:
             self.attend()
         if target is not None:
-            self.verify(target)
+            if sample is None:
+                self.verify(target)
+            else:
+                self.verify_sample(target, *sample)
         return snaps

@@ -12,7 +12,9 @@ none of that is available or needed here, only the shapes):
   * norm gains 1 + 0.1 N(0,1), LayerNorm biases 0.1 N(0,1);
   * features f (or EAGLE-3's l, m, h) ~ N(0, 1); token ids uniform in [0, |V|);
   * synthetic context K/V ~ N(0, 1) (already rotated) for EAGLE-1 rounds;
-  * synthetic target logits ~ N(0, 1), one row per verify-tree position.
+  * synthetic target logits ~ N(0, 1), one row per verify-tree position;
+  * the uniforms of stochastic verification ~ U[0, 1) in float32, 17 per
+    verify-tree position.
 """
 from __future__ import annotations
 
@@ -88,7 +90,8 @@ def f32(a: np.ndarray) -> np.ndarray:
 _T = {name: i for i, name in enumerate([
     "w_fc", "w_fuse", "w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down",
     "norm1_g", "norm1_b", "norm2_g", "norm2_b", "emb", "lm_head",
-    "n", "k_ctx", "v_ctx", "f_root", "t_root", "lmh", "ctx_tokens", "target", "n_new"])}
+    "n", "k_ctx", "v_ctx", "f_root", "t_root", "lmh", "ctx_tokens", "target", "n_new",
+    "draws"])}
 
 
 def head_weights(h: HeadCfg, seed: int) -> Dict[str, np.ndarray]:
@@ -191,3 +194,13 @@ def target_logits(r: RoundCfg, positions: Optional[int] = None) -> np.ndarray:
     T = r.positions if positions is None else positions
     return normal(r.seed_t, _T["target"], (r.B, T, r.head.vocab),
                   bf16=r.head.dtype == DTYPE_BF16)
+
+
+N_DRAWS = 17
+
+
+def verify_draws(r: RoundCfg, positions: Optional[int] = None, k: int = 0) -> np.ndarray:
+    """Uniforms in [0, 1) for stochastic verification, float32 [B, positions, 17];
+    k selects an independent set."""
+    T = r.positions if positions is None else positions
+    return _stream(r.seed_t, _T["draws"], k).random((r.B, T, N_DRAWS), dtype=np.float32)

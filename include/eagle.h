@@ -9,6 +9,7 @@
  *                             last call also reranks and builds the verify tree
  *   eagle_tree_attend         (optional) tree-masked attention over the verify tree
  *   eagle_tree_verify         accept the longest root path matching the target
+ *   (or eagle_tree_verify_sample: lossless multi-round speculative sampling)
  *
  * The method is the one described on the pages
  *   "transformer_math / tm_eagle_deep" (aicassindra.com), sections "The
@@ -62,6 +63,7 @@ enum { EAGLE_TREE_CHAIN = 0, EAGLE_TREE_STATIC = 1, EAGLE_TREE_DYNAMIC = 2 };
 #define EAGLE_MAX_SLOTS 64      /* expanded nodes per request (64-bit masks)   */
 #define EAGLE_MAX_POSITIONS 64  /* verify-tree positions per request (root+m)  */
 #define EAGLE_MAX_TOPK 16
+#define EAGLE_VERIFY_DRAWS 17   /* uniforms per verify position: 16 child tests + 1 residual draw */
 
 /*
  * The draft head ("What is actually in the head": an fc of shape [2d, d], one
@@ -271,6 +273,34 @@ int eagle_tree_attend(const eagle_head *head, const eagle_kv *kv,
 int eagle_tree_verify(const eagle_tree *tree, const void *target_logits,
                       int positions, int vocab, int dtype, int32_t *accept_len,
                       int32_t *accept_path, int32_t *out_tokens, void *stream);
+
+/*
+ * Lossless verification by multi-round speculative sampling over the verify
+ * tree ("Speculative Decoding Deep Dive III", EAGLE-1 "Inference": one
+ * target pass checks the tree and keeps the target's distribution;
+ * "transformer_math / tm_eagle_deep", "Why draft confidence is a usable
+ * acceptance proxy": keep a drafted token with probability
+ * min(1, p_target / p_draft)).  Top-k drafting proposes each child with
+ * certainty (p_draft = 1), so at verify position u, with the target
+ * distribution p = softmax(inv_temp * target_logits[b][u]), the children of
+ * u are tried in verify-tree order and child i (token x) is accepted iff
+ *   draws[b][u][i] < p(x) / (1 - sum of p over the children rejected before it);
+ * the walk moves to the first accepted child.  Where no child is accepted
+ * (or u has none, or is at depth gamma) one token is drawn from p with the
+ * rejected tokens removed and renormalised: the smallest token id whose
+ * cumulative mass exceeds draws[b][u][16] times the residual mass.
+ * Arithmetic: scaled logits and exponentials exp(v - max v) in fp32, every
+ * sum in fp64, in a fixed order (bit-reproducible).
+ * draws:   device [B][positions][EAGLE_VERIFY_DRAWS] fp32 uniforms in [0, 1)
+ *          (the caller's random numbers; the library draws none)
+ * inv_temp: > 0 and finite.  Other arguments and outputs as eagle_tree_verify;
+ * one workgroup per request reads only the rows the walk visits.
+ */
+int eagle_tree_verify_sample(const eagle_tree *tree, const void *target_logits,
+                             int positions, int vocab, int dtype, float inv_temp,
+                             const float *draws, int32_t *accept_len,
+                             int32_t *accept_path, int32_t *out_tokens,
+                             void *stream);
 
 /*
  * Kernel timing for benchmarks (off by default).  While enabled, every launch

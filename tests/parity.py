@@ -270,6 +270,112 @@ def planted_target(case: Case, gr, seed=0):
     return tgt, want
 
 
+# ------------------------------------------------------------------ P3s: stochastic verify
+# Margins: the kernel forms p in fp32 exponentials with fp64 sums, the oracle in
+# fp64, so a decision is fixed wherever the uniform sits clear of its threshold:
+# relative 1e-5 for an acceptance test (q = p(x) / residual mass), 1.5e-7 of the
+# residual mass for the inverse-CDF draw (at most ~1e-7 relative systematic
+# error of fp32 exponentials summed over the row).  Inside a margin either
+# outcome is valid and the walk follows the GPU.
+ACC_MARGIN = 1e-5
+CDF_MARGIN = 1.5e-7
+
+
+def check_verify_sample(case: Case, gr, target_np, draws, inv_temp):
+    gamma = case.cfg.gamma
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    acc_g = gr.accept_len.cpu().numpy()
+    path_g = gr.accept_path.cpu().numpy()
+    out_g = gr.out_tokens.cpu().numpy()
+    V = target_np.shape[-1]
+    stats = dict(tests=0, draws=0, ambiguous=0, accepted=[])
+    for b in range(case.cfg.B):
+        T = int(fv["count"][b])
+        tok, par = fv["tok"][b, :T], fv["parent"][b, :T]
+        kids = [[v for v in range(T) if par[v] == u] for u in range(T)]
+        a = int(acc_g[b])
+        assert 0 <= a <= gamma and path_g[b, 0] == 0, (b, a, path_g[b])
+        u = 0
+        for depth in range(a + 1):
+            p = OV.target_probs(synth.f32(target_np[b, u]), inv_temp)
+            resid = p.copy()
+            take = int(path_g[b, depth + 1]) if depth < a else -1
+            tried = []
+            cand = kids[u] if depth < gamma else []
+            if take >= 0:
+                assert take in cand, (b, depth, take, cand)
+            for i, v in enumerate(cand):
+                x = int(tok[v])
+                q = resid[x] / resid.sum()
+                d = float(draws[b, u, i])
+                stats["tests"] += 1
+                if abs(d - q) > ACC_MARGIN * q + 1e-12:
+                    assert (d < q) == (v == take), (b, u, i, d, q, take)
+                else:
+                    stats["ambiguous"] += 1
+                if v == take:
+                    break
+                resid[x] = 0.0
+                tried.append(x)
+            if take >= 0:
+                assert out_g[b, depth] == tok[take], (b, depth)
+                u = take
+                continue
+            # the walk stopped at u: residual draw by inverse CDF
+            x = int(out_g[b, a])
+            assert 0 <= x < V and x not in tried and resid[x] > 0, (b, x, tried)
+            c = np.cumsum(resid)
+            total = c[-1]
+            target = float(draws[b, u, OV.N_DRAWS - 1]) * total
+            lo_e = c[x - 1] if x > 0 else 0.0
+            tol = CDF_MARGIN * total
+            assert lo_e - tol <= target < c[x] + tol, (b, x, lo_e, target, c[x])
+            stats["draws"] += 1
+            if not (target - lo_e > tol and c[x] - target > tol):
+                stats["ambiguous"] += 1
+        assert all(o == -1 for o in out_g[b, a + 1:]) and all(pp == -1 for pp in path_g[b, a + 1:])
+        stats["accepted"].append(a)
+    return stats
+
+
+def planted_sampling_target(case: Case, gr, seed=0):
+    """Target logits that give every drafted child a real chance: at each
+    node, each child's token gets a logit about log(1.65 |V|) + U(-2, 3), so a
+    lone child's target probability lies in ~(0.1, 0.95) against the N(0, 1)
+    background."""
+    rng = np.random.default_rng(1000 + seed)
+    tgt = case.target.copy()          # stored form (bf16 bits or float32)
+    bf = tgt.dtype == np.uint16
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    V = tgt.shape[-1]
+    base = np.log(1.65 * V)
+    for b in range(case.cfg.B):
+        T = int(fv["count"][b])
+        par, tok = fv["parent"][b, :T], fv["tok"][b, :T]
+        for v in range(1, T):
+            val = np.float32(base + rng.uniform(-2.0, 3.0))
+            tgt[b, par[v], tok[v]] = synth.bf16_bits(np.array([val]))[0] if bf else val
+    return tgt
+
+
+def sampling_checks(case: Case, gr, device, seeds=(0, 1, 2), inv_temps=(1.0, 0.7)):
+    """P3s on the synthetic target and on planted targets, several draw sets."""
+    import torch
+    out = dict(tests=0, draws=0, ambiguous=0, accepted=[])
+    T = case.target.shape[1]
+    for k in seeds:
+        draws = synth.verify_draws(case.cfg, T, k)
+        dd = torch.from_numpy(draws).to(device)
+        tnp = case.target if k == 0 else planted_sampling_target(case, gr, k)
+        s_ = inv_temps[k % len(inv_temps)]
+        gr.verify_sample(case.target_dev(device, tnp), s_, dd)
+        st = check_verify_sample(case, gr, tnp, draws, s_)
+        for key in ("tests", "draws", "ambiguous"):
+            out[key] += st[key]
+        out["accepted"] += st["accepted"]
+    return out
+
+
 # ------------------------------------------------------------------ tree attention
 def check_tree_attend(case: Case, gr):
     cfg, hd = case.cfg, case.head
@@ -316,7 +422,7 @@ def attn_bf16_bound(q, K, V, group):
 
 
 # ------------------------------------------------------------------ whole round
-def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:0"):
+def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:0", sampling=True):
     """Run one round on the GPU and check P1 (all or sampled rows), P2, P3."""
     import time
 
@@ -352,6 +458,12 @@ def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:
         acc = check_verify(case, gr, pt, cfg.gamma)
         assert list(acc) == want, (list(acc), want)
         report["planted_accept"] = list(map(int, acc))
+    if sampling:
+        st = sampling_checks(case, gr, device)
+        say(f"stochastic verify checked: {st['tests']} tests, {st['draws']} draws, "
+            f"{st['ambiguous']} inside a margin")
+        report["sample_accept_hist"] = np.bincount(st["accepted"], minlength=cfg.gamma + 1).tolist()
+        report["sample_ambiguous"] = st["ambiguous"]
     torch.cuda.synchronize()
     return report
 

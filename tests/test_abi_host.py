@@ -157,6 +157,10 @@ def test_rejects_bad_arguments_before_launch(lib):
     # verify: positions smaller than the tree, bad dtype
     assert lib.eagle_tree_verify(t, 1, 2, 100, 0, 1, 1, 1, None) == E.EAGLE_EINVAL
     assert lib.eagle_tree_verify(t, 1, 64, 100, 5, 1, 1, 1, None) == E.EAGLE_EINVAL
+    # stochastic verify: null draws, non-positive or non-finite inv_temp, short positions
+    for pos, temp, draws in [(64, 1.0, None), (64, 0.0, 1), (64, -1.0, 1), (64, float("nan"), 1),
+                             (64, float("inf"), 1), (2, 1.0, 1)]:
+        assert lib.eagle_tree_verify_sample(t, 1, pos, 100, 0, temp, draws, 1, 1, 1, None) == E.EAGLE_EINVAL
     assert lib.eagle_strerror(E.EAGLE_ECAPACITY).startswith(b"capacity")
 
 
