@@ -990,6 +990,7 @@ int eagle_tree_verify_sample(const eagle_tree* tree, const void* target_logits, 
   if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_EINVAL;
   if (vocab < 1 || positions < g.positions) return EAGLE_EINVAL;
   if (!(inv_temp > 0.f) || !std::isfinite(inv_temp)) return EAGLE_EINVAL;
+  if (!verify_sample_ok(vocab, dtype)) return EAGLE_EUNSUPPORTED;
   {
     ProfScope ps(EAGLE_PROF_VERIFY, 0, 0, (hipStream_t)stream);
     launch_verify_sample(tree_dev(tree, g), g.B, target_logits, positions, vocab, dtype, inv_temp,

@@ -222,6 +222,7 @@ void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, 
 void launch_verify(const TreeDev& t, int B, const void* logits, int positions,
                    int vocab, int dtype, int gamma, int32_t* accept_len,
                    int32_t* accept_path, int32_t* out_tokens, hipStream_t st);
+bool verify_sample_ok(int vocab, int dtype);
 void launch_verify_sample(const TreeDev& t, int B, const void* logits, int positions, int vocab,
                           int dtype, float inv_temp, const float* draws, int gamma,
                           int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,

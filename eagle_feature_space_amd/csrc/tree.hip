@@ -319,20 +319,27 @@ void launch_verify(const TreeDev& t, int B, const void* logits, int positions, i
 }
 
 // ------------------------------------------------- stochastic verification
-// Multi-round speculative sampling over the verify tree, one workgroup per
-// request (the walk is sequential; only the rows it visits are read).  At a
-// visited node u the target distribution is p(y) = e_y / S with
-// v_y = fp32(s * z_y), M = max_y v_y, e_y = expf(v_y - M) and S the fp64 sum of
-// the e_y.  Children of u are tried in verify-tree order: child i (token x) is
-// kept iff draw[u][i] < e_x / (S - sum of e over the children rejected before
-// it).  When none is kept (or u has no child, or u is at depth gamma) one
-// token is drawn from p with the rejected tokens removed, by inverse CDF over
-// token ids: the smallest x whose cumulative fp64 mass exceeds
-// draw[u][16] * (total residual mass).  Each thread owns one contiguous range
-// of token ids, so the cumulative sums follow id order: per-thread sums, a
-// workgroup exclusive scan in thread order, then the one thread whose range
-// holds the target walks it.  Every sum has a fixed order (deterministic).
-constexpr int kSampleThreads = 512;
+// Multi-round speculative sampling over the verify tree: one workgroup per
+// request walks its tree and reads only the target rows the walk visits.
+// At a visited node u, with v_y = fp32(s * z_y) and M = max_y v_y, every
+// probability term is e_y = expf(v_y - M); S sums them, each granule (8 bf16 /
+// 4 fp32 ids) in fp32, everything above that in fp64.
+// Children of u are tried in verify-tree order: child i (token x) is kept iff
+// draw[u][i] < e_x / (S - sum of e over the children rejected before it).
+// When none is kept (or u has none, or is at depth gamma) one token is drawn
+// from the residual (rejected tokens carry no mass) by inverse CDF over token
+// ids.
+//
+// Row layout: granule q = 8 bf16 / 4 fp32 ids; round k = granules
+// [k * NT, (k + 1) * NT), granule k * NT + t read by thread t (coalesced);
+// a row's ids ascend with (round, thread, element).  A round's total is
+// summed in a fixed order (thread granule, wave butterfly, waves in order),
+// S is the sum of round totals in round order, and the residual draw finds
+// its round from the totals, then its thread from an exclusive scan of the
+// round's per-thread sums, then its id inside that thread's granule.
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleWaves = kSampleThreads / 64;
+constexpr int kMaxRounds = 64;   // rows of up to 64 * 1024 granules
 constexpr int kDraws = EAGLE_VERIFY_DRAWS;
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -341,84 +348,192 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// One granule's raw bits (ids past V read as -inf): a 16-byte load on rows on
+// 16-byte boundaries, element loads for the ragged last granule and for
+// unaligned rows.
 template <typename T>
+__device__ __forceinline__ u32x4 fetch_granule(const T* row, int q, int nvec, int V, bool aligned) {
+  constexpr int VEC = DT<T>::VEC;
+  if (aligned && q < nvec) return ld16(row + (int64_t)q * VEC);
+  float f[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    const int y = q * VEC + e;
+    f[e] = y < V ? DT<T>::ld(row + y) : -INFINITY;
+  }
+  return DT<T>::pack(f);
+}
+
+// rounds c0 .. c0 + H - 1 of thread tid, all loads in flight together
+template <typename T, int H>
+__device__ __forceinline__ void load_rounds(u32x4 (&raw)[H], const T* row, int c0, int G,
+                                            int NQ, int nvec, int V, bool aligned, int tid,
+                                            u32x4 ninf) {
+  constexpr int VEC = DT<T>::VEC;
+  constexpr int NT = kSampleThreads;
+  if (aligned && nvec > 0) {
+#pragma unroll
+    for (int k = 0; k < H; ++k)
+      raw[k] = ld16(row + (int64_t)min((c0 + k) * NT + tid, nvec - 1) * VEC);
+  }
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const int q = (c0 + k) * NT + tid;
+    if (c0 + k >= G || q >= NQ) raw[k] = ninf;
+    else if (!aligned || q >= nvec) raw[k] = fetch_granule<T>(row, q, nvec, V, aligned);
+  }
+}
+
+// Each pass streams the row in batches of H rounds (the second pass and the
+// residual draw find it in L2).
+template <typename T, int H>
 __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(
     TreeDev t, const T* logits, int positions, int V, float s, const float* draws, int gamma,
     int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens) {
-  constexpr int NW = kSampleThreads / 64;
   constexpr int VEC = DT<T>::VEC;
+  constexpr int NT = kSampleThreads, NW = kSampleWaves;
+  constexpr int RB = 4;             // round totals reduced together
+  __shared__ int s_tok[kMaxPos], s_par[kMaxPos];
   __shared__ float s_max[NW];
-  __shared__ double s_sum[NW];
-  __shared__ double s_pre[NW];
-  __shared__ int s_excl[kMaxTopK];
-  __shared__ int s_nexcl, s_next, s_pick;
+  __shared__ float s_dr[kDraws];
+  __shared__ double s_red[NW][RB];
+  __shared__ double s_rt[kMaxRounds];
+  __shared__ double s_e[kMaxTopK];
+  __shared__ int s_x[kMaxTopK], s_v[kMaxTopK], s_nk;
+  __shared__ int s_excl[kMaxTopK], s_nex, s_next, s_round, s_pick;
+  __shared__ double s_tgt, s_pre[NW];
+  __shared__ int s_last[NW];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T_ = t.f_count[b];
   const int fb = b * kMaxPos;
+  const int nvec = V / VEC;
+  const int NQ = (V + VEC - 1) / VEC;             // granules, the last one maybe partial
+  const int G = (NQ + NT - 1) / NT;               // rounds
   int32_t* path = accept_path + (int64_t)b * (gamma + 1);
   int32_t* out = out_tokens + (int64_t)b * (gamma + 1);
+  if (tid < kMaxPos) {
+    s_tok[tid] = tid < T_ ? t.f_tok[fb + tid] : -1;
+    s_par[tid] = tid < T_ ? t.f_parent[fb + tid] : -2;
+  }
   if (tid <= gamma) { path[tid] = tid == 0 ? 0 : -1; out[tid] = -1; }
-  // this thread's token ids [lo, hi), whole granules except at the row's end
-  const int per = ((V + kSampleThreads - 1) / kSampleThreads + VEC - 1) / VEC * VEC;
-  const int lo = min(V, tid * per), hi = min(V, lo + per);
+  __syncthreads();
 
+  u32x4 raw[H];
+  u32x4 ninf;
+  {
+    float f[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) f[e] = -INFINITY;
+    ninf = DT<T>::pack(f);
+  }
   int u = 0, acc = 0;
   while (true) {
     const T* row = logits + ((int64_t)b * positions + u) * V;
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-    // visit this thread's values: f(y, v) for y in [lo, hi)
-    auto each = [&](auto&& f) {
-      int y = lo;
-      if (aligned) {
-        for (; y + VEC <= hi; y += VEC) {
-          const u32x4 x = ld16(row + y);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) f(y + e, s * DT<T>::elem(x, e));
-        }
-      }
-      for (; y < hi; ++y) f(y, s * DT<T>::ld(row + y));
-    };
+    // this node's uniforms, fetched with the row
+    if (wave == 1 && lane < kDraws) s_dr[lane] = draws[((int64_t)b * positions + u) * kDraws + lane];
     // M = max v
     float m = -INFINITY;
-    each([&](int, float v) { m = fmaxf(m, v); });
+    for (int c0 = 0; c0 < G; c0 += H) {
+      load_rounds<T, H>(raw, row, c0, G, NQ, nvec, V, aligned, tid, ninf);
+#pragma unroll
+      for (int k = 0; k < H; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) m = fmaxf(m, s * DT<T>::elem(raw[k], e));
+    }
     m = wave_max(m);
     if (lane == 0) s_max[wave] = m;
     __syncthreads();
     float M = s_max[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_max[w]);
-    // S = sum e (thread ranges, then waves, in order)
-    double sm = 0.0;
-    each([&](int, float v) { sm += (double)expf(v - M); });
-    sm = wave_sum_d(sm);
-    if (lane == 0) s_sum[wave] = sm;
+    // round totals, RB rounds reduced at a time
+    for (int c0 = 0; c0 < G; c0 += H) {
+      load_rounds<T, H>(raw, row, c0, G, NQ, nvec, V, aligned, tid, ninf);
+#pragma unroll
+      for (int r0 = 0; r0 < H; r0 += RB) {
+        if (c0 + r0 >= G) break;
+        double pr[RB];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          // a granule's terms summed in fp32 (ids past V give expf(-inf) = 0)
+          float gs = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) gs += expf(s * DT<T>::elem(raw[r0 + j], e) - M);
+          pr[j] = (double)gs;
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) pr[j] = wave_sum_d(pr[j]);
+        if (lane == 0)
+#pragma unroll
+          for (int j = 0; j < RB; ++j) s_red[wave][j] = pr[j];
+        __syncthreads();
+        if (tid < RB && c0 + r0 + tid < G) {
+          double r = 0.0;
+          for (int w = 0; w < NW; ++w) r += s_red[w][tid];
+          s_rt[c0 + r0 + tid] = r;
+        }
+        __syncthreads();
+      }
+    }
+    // the node's children in order and their terms (wave 0)
+    if (wave == 0) {
+      const bool kid = acc < gamma && lane < T_ && lane > u && s_par[lane] == u;
+      const uint64_t km = __ballot(kid);
+      const int rank = __popcll(km & ((1ull << lane) - 1ull));
+      if (kid && rank < kMaxTopK) {
+        const int x = s_tok[lane];
+        s_e[rank] = x >= 0 && x < V ? (double)expf(s * DT<T>::ld(row + x) - M) : 0.0;
+        s_x[rank] = x;
+        s_v[rank] = lane;
+      }
+      if (lane == 0) s_nk = min(__popcll(km), kMaxTopK);
+    }
     __syncthreads();
     if (tid == 0) {
       double S = 0.0;
-      for (int w = 0; w < NW; ++w) S += s_sum[w];
-      const float* dr = draws + ((int64_t)b * positions + u) * kDraws;
+      for (int k = 0; k < G; ++k) S += s_rt[k];
       double rem = S;
       int nex = 0, nxt = -1;
-      if (acc < gamma) {
-        for (int v = u + 1; v < T_ && nex < kMaxTopK; ++v) {
-          if (t.f_parent[fb + v] != u) continue;
-          const int x = t.f_tok[fb + v];
-          // a token outside the target's vocabulary has no target mass
-          const double e = x >= 0 && x < V ? (double)expf(s * DT<T>::ld(row + x) - M) : 0.0;
-          if ((double)dr[nex] < e / rem) { nxt = v; break; }
-          rem -= e;
-          s_excl[nex++] = x;
-        }
+      for (int i = 0; i < s_nk; ++i) {
+        if ((double)s_dr[i] < s_e[i] / rem) { nxt = s_v[i]; break; }
+        rem -= s_e[i];
+        s_excl[nex++] = s_x[i];
       }
-      s_nexcl = nex;
+      s_nex = nex;
       s_next = nxt;
       s_pick = -1;
+      if (nxt < 0) {
+        // residual mass per round; the round holding the target
+        for (int i = 0; i < nex; ++i) {
+          const int x = s_excl[i];
+          if (x >= 0 && x < V) {
+            const int k = (x / VEC) / NT;
+            s_rt[k] = fmax(s_rt[k] - s_e[i], 0.0);
+          }
+        }
+        double tot = 0.0;
+        for (int k = 0; k < G; ++k) tot += s_rt[k];
+        const double target = (double)s_dr[kDraws - 1] * tot;
+        double pre = 0.0, pre_k = 0.0;
+        int kk = -1;
+        for (int k = 0; k < G; ++k) {
+          if (s_rt[k] > 0.0) {
+            kk = k;
+            pre_k = pre;
+            if (target < pre + s_rt[k]) break;   // else: rounding past the end
+          }
+          pre += s_rt[k];
+        }
+        s_round = kk;
+        s_tgt = target - pre_k;
+      }
     }
     __syncthreads();
     const int nxt = s_next;
     if (nxt >= 0) {   // every thread follows the walk
       if (tid == 0) {
-        out[acc] = t.f_tok[fb + nxt];
+        out[acc] = s_tok[nxt];
         path[acc + 1] = nxt;
       }
       ++acc;
@@ -426,58 +541,64 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(
       __syncthreads();
       continue;
     }
-    // residual draw at u: the rejected tokens carry no mass
-    const int nex = s_nexcl;
-    auto mass = [&](int y, float v) -> double {
-      for (int i = 0; i < nex; ++i)
-        if (s_excl[i] == y) return 0.0;
-      return (double)expf(v - M);
-    };
-    double part = 0.0;
-    each([&](int y, float v) { part += mass(y, v); });
-    // prefix sums of the per-thread masses in thread order; thread t's
-    // interval is [end of thread t-1, end of thread t), so the intervals tile
-    // [0, total) exactly and one thread at most holds the target
-    double inc = part;
+    // inverse CDF inside the chosen round
+    const int kk = s_round;
+    int pick = -1;
+    if (kk >= 0) {
+      const int nex = s_nex;
+      const int q = kk * NT + tid;
+      const u32x4 g = q < NQ ? fetch_granule<T>(row, q, nvec, V, aligned) : ninf;
+      double e[VEC];
+      double part = 0.0;
+      int last = -1;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double x = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += x;
-    }
-    if (lane == 63) s_pre[wave] = inc;
-    __syncthreads();
-    double before = 0.0, total = 0.0;
-    for (int w = 0; w < NW; ++w) {
-      if (w == wave) before = total;
-      total += s_pre[w];
-    }
-    const double end = before + inc;
-    double start = __shfl_up(end, 1, 64);
-    if (lane == 0) start = before;
-    const double target =
-        (double)draws[((int64_t)b * positions + u) * kDraws + kDraws - 1] * total;
-    if (part > 0.0 && start <= target && target < end) {
-      double c = start;
-      int pick = -1, last = -1;
-      each([&](int y, float v) {
-        if (pick >= 0) return;
-        const double e = mass(y, v);
-        if (e > 0.0) last = y;
-        c += e;
-        if (c > target && e > 0.0) pick = y;
-      });
-      s_pick = pick >= 0 ? pick : last;   // rounding at the range's end
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int pick = s_pick;
-      if (pick < 0) {  // target at or past the total (rounding): last token with mass
-        for (int y = V - 1; y >= 0 && pick < 0; --y) {
-          bool ex = false;
-          for (int i = 0; i < nex; ++i) ex |= s_excl[i] == y;
-          if (!ex) pick = y;
-        }
+      for (int j = 0; j < VEC; ++j) {
+        const int y = q * VEC + j;
+        const float v = s * DT<T>::elem(g, j);
+        bool ex = q >= NQ || v == -INFINITY;
+        for (int i = 0; i < nex; ++i) ex |= s_excl[i] == y;
+        e[j] = ex ? 0.0 : (double)expf(v - M);
+        part += e[j];
+        if (e[j] > 0.0) last = y;
       }
+      // intervals [end of thread t-1, end of thread t) tile [0, round total)
+      double inc = part;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double xo = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += xo;
+      }
+      int lastw = last;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) lastw = max(lastw, __shfl_xor(lastw, o, 64));
+      if (lane == 63) s_pre[wave] = inc;
+      if (lane == 0) s_last[wave] = lastw;
+      __syncthreads();
+      double before = 0.0, total = 0.0;
+      int lastb = -1;
+      for (int w = 0; w < NW; ++w) {
+        if (w == wave) before = total;
+        total += s_pre[w];
+        lastb = max(lastb, s_last[w]);
+      }
+      const double end = before + inc;
+      double start = __shfl_up(end, 1, 64);
+      if (lane == 0) start = before;
+      const double target = s_tgt;
+      if (part > 0.0 && start <= target && target < end) {
+        double c = start;
+        int pk = -1;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          c += e[j];
+          if (pk < 0 && e[j] > 0.0 && c > target) pk = q * VEC + j;
+        }
+        s_pick = pk >= 0 ? pk : last;
+      }
+      __syncthreads();
+      pick = s_pick >= 0 ? s_pick : lastb;   // target at or past the round total (rounding)
+    }
+    if (tid == 0) {
       out[acc] = pick;
       accept_len[b] = acc;
     }
@@ -485,18 +606,29 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(
   }
 }
 
+bool verify_sample_ok(int vocab, int dtype) {
+  const int vec = dtype == EAGLE_BF16 ? 8 : 4;
+  return vocab >= 1 && (int64_t)vocab <= (int64_t)kMaxRounds * kSampleThreads * vec;
+}
+
+template <typename T>
+static void launch_sample_t(const TreeDev& t, int B, const T* logits, int positions, int vocab,
+                            float inv_temp, const float* draws, int gamma, int32_t* accept_len,
+                            int32_t* accept_path, int32_t* out_tokens, hipStream_t st) {
+  hipLaunchKernelGGL((k_verify_sample<T, 4>), dim3(B), dim3(kSampleThreads), 0, st, t, logits,
+                     positions, vocab, inv_temp, draws, gamma, accept_len, accept_path, out_tokens);
+}
+
 void launch_verify_sample(const TreeDev& t, int B, const void* logits, int positions, int vocab,
                           int dtype, float inv_temp, const float* draws, int gamma,
                           int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
                           hipStream_t st) {
   if (dtype == EAGLE_BF16)
-    hipLaunchKernelGGL(k_verify_sample<bf16s>, dim3(B), dim3(kSampleThreads), 0, st, t,
-                       (const bf16s*)logits, positions, vocab, inv_temp, draws, gamma, accept_len,
-                       accept_path, out_tokens);
+    launch_sample_t(t, B, (const bf16s*)logits, positions, vocab, inv_temp, draws, gamma,
+                    accept_len, accept_path, out_tokens, st);
   else
-    hipLaunchKernelGGL(k_verify_sample<float>, dim3(B), dim3(kSampleThreads), 0, st, t,
-                       (const float*)logits, positions, vocab, inv_temp, draws, gamma, accept_len,
-                       accept_path, out_tokens);
+    launch_sample_t(t, B, (const float*)logits, positions, vocab, inv_temp, draws, gamma,
+                    accept_len, accept_path, out_tokens, st);
 }
 
 // dense rows of the verify tree (row m = b * positions + u)

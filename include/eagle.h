@@ -289,11 +289,13 @@ int eagle_tree_verify(const eagle_tree *tree, const void *target_logits,
  * (or u has none, or is at depth gamma) one token is drawn from p with the
  * rejected tokens removed and renormalised: the smallest token id whose
  * cumulative mass exceeds draws[b][u][16] times the residual mass.
- * Arithmetic: scaled logits and exponentials exp(v - max v) in fp32, every
- * sum in fp64, in a fixed order (bit-reproducible).
+ * Arithmetic: scaled logits and exponentials exp(v - max v) in fp32; sums of
+ * 8 (bf16) or 4 (fp32) consecutive ids in fp32, every sum above that in
+ * fp64, all in a fixed order (bit-reproducible).
  * draws:   device [B][positions][EAGLE_VERIFY_DRAWS] fp32 uniforms in [0, 1)
  *          (the caller's random numbers; the library draws none)
- * inv_temp: > 0 and finite.  Other arguments and outputs as eagle_tree_verify;
+ * inv_temp: > 0 and finite.  vocab <= 524288 (bf16) or 262144 (fp32), else
+ * EAGLE_EUNSUPPORTED.  Other arguments and outputs as eagle_tree_verify;
  * one workgroup per request reads only the rows the walk visits.
  */
 int eagle_tree_verify_sample(const eagle_tree *tree, const void *target_logits,
