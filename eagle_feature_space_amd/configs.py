@@ -64,6 +64,10 @@ class RoundCfg:
     # positions and ingests tau ~ U{lo..hi} newly verified ones (the previous
     # round's accepted path and corrected token) instead of all of them
     new_range: Optional[Tuple[int, int]] = None
+    # target verification pass: L decoder layers of the head's shape (sharing
+    # its embedding and LM head) produce the target logits (0: synthetic logits)
+    target_layers: int = 0
+    seed_tm: int = 0
     tree: int = TREE_CHAIN
     gamma: int = 4                    # draft depth = number of draft steps
     top_k: int = 1

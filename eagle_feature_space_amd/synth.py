@@ -14,7 +14,11 @@ none of that is available or needed here, only the shapes):
   * synthetic context K/V ~ N(0, 1) (already rotated) for EAGLE-1 rounds;
   * synthetic target logits ~ N(0, 1), one row per verify-tree position;
   * the uniforms of stochastic verification ~ U[0, 1) in float32, 17 per
-    verify-tree position.
+    verify-tree position;
+  * target layers drawn like the head's layer (matrices N(0, 0.02), gains
+    1 + 0.1 N(0, 1)), a final RMSNorm gain 1 + 0.1 N(0, 1), and a synthetic
+    context cache ~ N(0, 1) per layer; the embedding and LM head are the
+    head's.
 """
 from __future__ import annotations
 
@@ -91,7 +95,8 @@ _T = {name: i for i, name in enumerate([
     "w_fc", "w_fuse", "w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down",
     "norm1_g", "norm1_b", "norm2_g", "norm2_b", "emb", "lm_head",
     "n", "k_ctx", "v_ctx", "f_root", "t_root", "lmh", "ctx_tokens", "target", "n_new",
-    "draws"])}
+    "draws", "final_g"])}
+_LAYER_TAGS = 64     # tag stride of one target layer
 
 
 def head_weights(h: HeadCfg, seed: int) -> Dict[str, np.ndarray]:
@@ -204,3 +209,39 @@ def verify_draws(r: RoundCfg, positions: Optional[int] = None, k: int = 0) -> np
     k selects an independent set."""
     T = r.positions if positions is None else positions
     return _stream(r.seed_t, _T["draws"], k).random((r.B, T, N_DRAWS), dtype=np.float32)
+
+
+def target_layer_weights(h: HeadCfg, seed: int, layer: int) -> Dict[str, np.ndarray]:
+    """Decoder-layer weights of target layer `layer` (the head's layer shape)."""
+    bf = h.dtype == DTYPE_BF16
+    d = h.d
+    t = lambda name: _T[name] + _LAYER_TAGS * (layer + 1)
+    w: Dict[str, np.ndarray] = {}
+    w["w_q"] = normal(seed, t("w_q"), (h.q_dim, d), 0.02, bf16=bf)
+    w["w_k"] = normal(seed, t("w_k"), (h.kv_dim, d), 0.02, bf16=bf)
+    w["w_v"] = normal(seed, t("w_v"), (h.kv_dim, d), 0.02, bf16=bf)
+    w["w_o"] = normal(seed, t("w_o"), (d, h.q_dim), 0.02, bf16=bf)
+    if h.act == ACT_SWIGLU:
+        w["w_gate"] = normal(seed, t("w_gate"), (h.ffn, d), 0.02, bf16=bf)
+    w["w_up"] = normal(seed, t("w_up"), (h.ffn, d), 0.02, bf16=bf)
+    w["w_down"] = normal(seed, t("w_down"), (d, h.ffn), 0.02, bf16=bf)
+    w["norm1_g"] = normal(seed, t("norm1_g"), (d,), 0.1, 1.0, bf16=bf)
+    w["norm2_g"] = normal(seed, t("norm2_g"), (d,), 0.1, 1.0, bf16=bf)
+    if h.norm == NORM_LAYER:
+        w["norm1_b"] = normal(seed, t("norm1_b"), (d,), 0.1, bf16=bf)
+        w["norm2_b"] = normal(seed, t("norm2_b"), (d,), 0.1, bf16=bf)
+    return w
+
+
+def target_final_gain(h: HeadCfg, seed: int) -> np.ndarray:
+    return normal(seed, _T["final_g"], (h.d,), 0.1, 1.0, bf16=h.dtype == DTYPE_BF16)
+
+
+def target_context(r: RoundCfg, layer: int):
+    """Synthetic context cache (K, V) [sum n, Hkv, hd] of target layer `layer`."""
+    h = r.head
+    total = int(context_lengths(r).sum())
+    bf = h.dtype == DTYPE_BF16
+    t = _LAYER_TAGS * (layer + 1)
+    return (normal(r.seed_tm, _T["k_ctx"] + t, (total, h.n_kv, h.head_dim), bf16=bf),
+            normal(r.seed_tm, _T["v_ctx"] + t, (total, h.n_kv, h.head_dim), bf16=bf))

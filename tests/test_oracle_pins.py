@@ -15,6 +15,7 @@ from eagle_feature_space_amd import configs as C
 from eagle_feature_space_amd import synth
 from oracle import head as H
 from oracle import tree as T
+from oracle import target as TG
 from oracle import verify as VF
 from oracle.round import run_round
 
@@ -589,6 +590,64 @@ def test_verify_sample_residual_is_inverse_cdf():
     for u in np.linspace(0, 1, 101)[:-1]:
         x = VF.residual_draw(p, excl, u)
         assert x not in excl and edges[x] <= u < edges[x + 1] + 1e-12
+
+
+# ------------------------------------------------- target verification pass
+def _target(L=3, seed=31):
+    w = lambda l: {k: synth.f32(v).astype(np.float64)
+                   for k, v in synth.target_layer_weights(TINY, seed, l).items()}
+    layers = [H.DraftHead(TINY, w(l), np.float64) for l in range(L)]
+    hw = {k: synth.f32(v).astype(np.float64) for k, v in synth.head_weights(TINY, 77).items()}
+    g = synth.f32(synth.target_final_gain(TINY, seed)).astype(np.float64)
+    return layers, hw["emb"], g, hw["lm_head"]
+
+
+@pytest.mark.parametrize("kind", [T.DYNAMIC, T.STATIC])
+def test_target_tree_pass_equals_causal_decoding(kind):
+    """Tree attention over L target layers: the logits at every node equal
+    plain causal decoding of the node's root path after the context (fp64)."""
+    rng = np.random.default_rng(41 if kind == T.DYNAMIC else 42)
+    tmpl = C.STATIC_TREE_25 if kind == T.STATIC else ()
+    t = _random_tree(rng, kind, 4, 4 if kind == T.STATIC else 3, 9, V=TINY.vocab, template=tmpl)
+    f = t.final_tree()
+    layers, emb, g, lm = _target()
+    n = 6
+    ctx = [(rng.standard_normal((n, TINY.n_kv, TINY.head_dim)),
+            rng.standard_normal((n, TINY.n_kv, TINY.head_dim))) for _ in layers]
+    pos = np.asarray(f["pos"]) - 17 + n          # root at position n
+    logits, _ = TG.tree_forward(layers, emb, g, TINY.eps, lm, f["tok"], pos, f["mask"], ctx)
+    for u, path in enumerate(_all_root_paths(f["parent"])):
+        ref = TG.causal_forward(layers, emb, g, TINY.eps, lm, [f["tok"][w] for w in path], n, ctx)
+        np.testing.assert_allclose(logits[u], ref[-1], rtol=1e-10, atol=1e-10)
+
+
+def test_committed_path_extends_the_cache():
+    """After verification, the cache extended by the accepted path's keys and
+    values (root first) makes the next token's logits equal causal decoding
+    of the whole accepted sequence."""
+    rng = np.random.default_rng(43)
+    t = _random_tree(rng, T.DYNAMIC, 3, 3, 8, V=TINY.vocab)
+    f = t.final_tree()
+    layers, emb, g, lm = _target(L=2)
+    n = 5
+    ctx = [(rng.standard_normal((n, TINY.n_kv, TINY.head_dim)),
+            rng.standard_normal((n, TINY.n_kv, TINY.head_dim))) for _ in layers]
+    pos = np.asarray(f["pos"]) - 17 + n
+    logits, kv_tree = TG.tree_forward(layers, emb, g, TINY.eps, lm, f["tok"], pos, f["mask"], ctx)
+    # plant a path of depth 2 in the target's greedy choices
+    kid = [v for v in range(len(f["tok"])) if f["parent"][v] == 0][1]
+    kid2 = [v for v in range(len(f["tok"])) if f["parent"][v] == kid][0]
+    lg = np.array(logits)
+    lg[0, f["tok"][kid]] = lg[kid, f["tok"][kid2]] = 1e3
+    acc, path, out = VF.verify(f["tok"], f["parent"], lg, 3)
+    assert acc >= 2 and list(path[:3]) == [0, kid, kid2]
+    com = TG.commit_path(kv_tree, acc, path)
+    new_ctx = [(np.concatenate([ck, k]), np.concatenate([cv, v])) for (ck, cv), (k, v) in zip(ctx, com)]
+    nxt = int(out[acc])
+    one = TG.causal_forward(layers, emb, g, TINY.eps, lm, [nxt], n + acc + 1, new_ctx)
+    seq = [f["tok"][w] for w in path[:acc + 1]] + [nxt]
+    full = TG.causal_forward(layers, emb, g, TINY.eps, lm, seq, n, ctx)
+    np.testing.assert_allclose(one[0], full[-1], rtol=1e-10, atol=1e-10)
 
 
 def test_eagle3_steady_state_equals_full_causal_recompute():
