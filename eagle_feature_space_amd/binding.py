@@ -39,6 +39,17 @@ class eagle_kv(ctypes.Structure):
                 ("total_new", c_int64), ("n_new", c_void_p), ("cu_new", c_void_p)]
 
 
+class eagle_layer(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down",
+                                        "norm1_g", "norm1_b", "norm2_g", "norm2_b", "k_ctx",
+                                        "v_ctx")]
+
+
+class eagle_target(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("layers", ctypes.POINTER(eagle_layer)),
+                ("final_norm_g", c_void_p)]
+
+
 class eagle_tree(ctypes.Structure):
     _fields_ = [("kind", c_int32), ("B", c_int32), ("gamma", c_int32), ("top_k", c_int32),
                 ("top_m", c_int32), ("n_template", c_int32),
@@ -92,6 +103,14 @@ def lib():
         "eagle_tree_verify_sample": ([P(eagle_tree), c_void_p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_float, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p], ctypes.c_int),
+        "eagle_target_verify_logits": ([P(eagle_head), P(eagle_target), P(eagle_kv), P(eagle_tree),
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+                                       ctypes.c_int),
+        "eagle_target_workspace_bytes": ([P(eagle_head), P(eagle_target), P(eagle_kv),
+                                          P(eagle_tree)], c_size_t),
+        "eagle_kv_commit": ([P(eagle_tree), ctypes.c_int, ctypes.c_int, ctypes.c_int, c_void_p,
+                             c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                             c_void_p], ctypes.c_int),
         "eagle_profile_enable": ([ctypes.c_int], ctypes.c_int),
         "eagle_profile_reset": ([], ctypes.c_int),
         "eagle_profile_read": ([ctypes.c_int, P(c_int64), P(c_int64), P(ctypes.c_double),
@@ -108,7 +127,8 @@ def lib():
 EXPORTED = ("eagle_version", "eagle_strerror", "eagle_tree_layout_of", "eagle_tree_state_bytes",
             "eagle_step_rows", "eagle_workspace_bytes", "eagle_tree_init", "eagle_draft_step",
             "eagle_tree_expand_rerank", "eagle_tree_attend", "eagle_tree_verify",
-            "eagle_tree_verify_sample",
+            "eagle_tree_verify_sample", "eagle_target_verify_logits",
+            "eagle_target_workspace_bytes", "eagle_kv_commit",
             "eagle_profile_enable", "eagle_profile_reset", "eagle_profile_read")
 
 PROF_FAMILIES = {"lmhead": 0, "gemm": 1, "attn": 2, "verify": 3, "other": 4}
@@ -201,6 +221,27 @@ def eagle_tree_verify_sample(tree, target_logits, positions, vocab, dtype, inv_t
                                                  vocab, dtype, inv_temp, _ptr(draws), _ptr(accept_len),
                                                  _ptr(accept_path), _ptr(out_tokens), _stream(stream)),
                   "eagle_tree_verify_sample")
+
+
+def eagle_target_workspace_bytes(head, target, kv, tree):
+    return lib().eagle_target_workspace_bytes(ctypes.byref(head), ctypes.byref(target),
+                                              ctypes.byref(kv), ctypes.byref(tree))
+
+
+def eagle_target_verify_logits(head, target, kv, tree, logits_out, k_tree, v_tree, ws, ws_bytes,
+                               stream=None):
+    return _check(lib().eagle_target_verify_logits(
+        ctypes.byref(head), ctypes.byref(target), ctypes.byref(kv), ctypes.byref(tree),
+        _ptr(logits_out), _ptr(k_tree), _ptr(v_tree), _ptr(ws), ws_bytes, _stream(stream)),
+        "eagle_target_verify_logits")
+
+
+def eagle_kv_commit(tree, kv_heads, head_dim, dtype, accept_len, accept_path, k_tree, v_tree,
+                    dst_row, dst_rows, k_dst, v_dst, stream=None):
+    return _check(lib().eagle_kv_commit(
+        ctypes.byref(tree), kv_heads, head_dim, dtype, _ptr(accept_len), _ptr(accept_path),
+        _ptr(k_tree), _ptr(v_tree), _ptr(dst_row), dst_rows, _ptr(k_dst), _ptr(v_dst),
+        _stream(stream)), "eagle_kv_commit")
 
 
 def eagle_profile_enable(on=True):

@@ -137,6 +137,13 @@ CONFIGS = {
         note="EAGLE-3 fused-feature chain, B=32, packed n in [256,1024], gamma=7"),
     # the round after c3_8b_eagle3's: the cache holds n in [256, 1024] positions
     # and each request ingests only the tau in [1, 8] it has just verified
+    # the benchmark's round with a real verification pass: a 32-layer target
+    # of the 8B head's layer shape (sharing its embedding and LM head)
+    "c6_8b_target": RoundCfg(
+        name="c6_8b_target", head=HEAD_8B, B=1, n=(2048,), tree=TREE_STATIC,
+        gamma=4, top_k=4, template=STATIC_TREE_25, seed_w=1001, seed_in=2001,
+        seed_t=3001, target_layers=32, seed_tm=4006,
+        note="c1 with a 32-layer 8B-shaped target's tree-attention verification pass"),
     "c5_8b_eagle3_steady": RoundCfg(
         name="c5_8b_eagle3_steady", head=HEAD_8B_E3, B=32, n_range=(256, 1024),
         new_range=(1, 8), tree=TREE_CHAIN, gamma=7, top_k=1, seed_w=1003,
@@ -219,6 +226,24 @@ SMALL_CONFIGS["s12_eagle3_steady_chain"] = RoundCfg(
     name="s12_eagle3_steady_chain", head=replace(_HEAD_SMALL, mode=MODE_EAGLE3), B=20,
     n_range=(0, 60), new_range=(1, 8), tree=TREE_CHAIN, gamma=3, top_k=1,
     seed_w=1112, seed_in=2112, seed_t=3112)
+
+# The target's verification pass: a static tree (52 rows, tiled kernels), a
+# dynamic tree with an empty context, an fp32 LayerNorm / GELU head, and a
+# 12-row chain (row-complete kernels)
+SMALL_CONFIGS["s13_target_static"] = RoundCfg(
+    name="s13_target_static", head=_HEAD_SMALL, B=2, n=(40, 9), tree=TREE_STATIC, gamma=4,
+    top_k=4, template=STATIC_TREE_25, seed_w=1113, seed_in=2113, seed_t=3113,
+    target_layers=3, seed_tm=4113)
+SMALL_CONFIGS["s14_target_dynamic"] = RoundCfg(
+    name="s14_target_dynamic", head=_HEAD_SMALL, B=3, n=(0, 30, 70), tree=TREE_DYNAMIC,
+    gamma=3, top_k=4, top_m=12, inv_temp=4.0, seed_w=1114, seed_in=2114, seed_t=3114,
+    target_layers=2, seed_tm=4114)
+SMALL_CONFIGS["s15_target_f32"] = RoundCfg(
+    name="s15_target_f32", head=HEAD_TINY_F32, B=2, n=(33, 64), tree=TREE_DYNAMIC, gamma=3,
+    top_k=3, top_m=8, seed_w=1115, seed_in=2115, seed_t=3115, target_layers=2, seed_tm=4115)
+SMALL_CONFIGS["s16_target_chain_rows"] = RoundCfg(
+    name="s16_target_chain_rows", head=_HEAD_SMALL, B=3, n=(17, 5, 60), tree=TREE_CHAIN,
+    gamma=3, top_k=1, seed_w=1116, seed_in=2116, seed_t=3116, target_layers=3, seed_tm=4116)
 
 # Chains whose row count sits on either side of every kernel-dispatch boundary:
 # 16 / 17 (row-complete vs split-K streaming), 32 / 33 (streaming vs LDS-staged),

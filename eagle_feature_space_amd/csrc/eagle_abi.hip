@@ -357,14 +357,16 @@ int check_attn_plan(const eagle_head* h, const eagle_kv* kv) {
   return plan_attn(h, kv).nsplit + 1 <= 1024 ? EAGLE_OK : EAGLE_EUNSUPPORTED;
 }
 
-Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
+// target: sized for the target's verification pass as well (every buffer
+// holds the B * positions verify-tree rows)
+Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g, bool target = false) {
   Ws w;
   Bump bp;
   const int e = esz(h), d = h->d, qd = h->n_q_heads * h->head_dim,
             kvd = h->n_kv_heads * h->head_dim;
   const int nact = h->act == EAGLE_ACT_SWIGLU ? 2 * h->ffn : h->ffn;
-  const int Mmax = g.B * g.max_rows;
   const int Mt = g.B * g.positions;
+  const int Mmax = target ? std::max(g.B * g.max_rows, Mt) : g.B * g.max_rows;
   const int Mr = std::max(Mmax, Mt);
   w.h = bp.take((size_t)Mr * d * e);
   w.hn = bp.take((size_t)Mr * d * e);
@@ -375,6 +377,11 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
   w.o = bp.take((size_t)Mr * qd * e);
   w.act = bp.take((size_t)Mmax * h->ffn * e);
   size_t P = gemm_bytes(h->dtype, Mt, qd + 2 * kvd, d);
+  if (target) {
+    P = std::max(P, gemm_bytes(h->dtype, Mt, d, qd));
+    P = std::max(P, gemm_bytes(h->dtype, Mt, nact, d));
+    P = std::max(P, gemm_bytes(h->dtype, Mt, d, h->ffn));
+  }
   for (int s = 0; s < g.gamma; ++s) {
     const int M = g.B * g.rows[s];
     if (h->mode == EAGLE_MODE_1) P = std::max(P, gemm_bytes(h->dtype, M, d, 2 * d));
@@ -393,7 +400,9 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g) {
   w.att_ml = bp.take(nparts * Mr * h->n_q_heads * 2 * 4);
   LmShape ls = plan_lmhead(h->dtype, Mmax, h->vocab);
   if (big_gemm_ok(h->dtype, Mmax, h->vocab, d)) ls.ntiles = std::max(ls.ntiles, logits_tiles(h->vocab));
-  w.logits = big_gemm_ok(h->dtype, Mmax, h->vocab, d) ? bp.take((size_t)Mmax * h->vocab * 4) : 0;
+  // (the target pass writes its logits straight to the caller's buffer)
+  const int Mlg = g.B * g.max_rows;
+  w.logits = big_gemm_ok(h->dtype, Mlg, h->vocab, d) ? bp.take((size_t)Mlg * h->vocab * 4) : 0;
   w.lm_max = bp.take((size_t)ls.ntiles * Mmax * 4);
   w.lm_sum = bp.take((size_t)ls.ntiles * Mmax * 4);
   w.lm_id = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
@@ -573,6 +582,113 @@ void run_rows(const eagle_head* h, int ep, const RowsArgs& r, hipStream_t st) {
   launch_gemm_rows(h->dtype, ep, r, st);
 }
 
+// One pre-norm decoder layer over io.M rows (io.W per request), from the
+// attention sub-layer on.  Input rows io.x with N1(io.x) in io.xn (row path:
+// io.x * g1 with per-block statistics io.nst / io.nblk, or plain N1 rows when
+// io.nst is null); q|k|v with RoPE at io.pos, K/V rows written to io.kdst /
+// io.vdst rows io.kv_idx; attention over the request's context plus the rows
+// in io.mask; output rows to io.out (and to io.scatter rows when given).
+struct LayerIO {
+  int M = 0, W = 0;
+  const void* x = nullptr;
+  const void* xn = nullptr;
+  const float* nst = nullptr;
+  int nblk = 0;
+  const int32_t* pos = nullptr;
+  void* kdst = nullptr;
+  void* vdst = nullptr;
+  const int32_t* kv_idx = nullptr;
+  const uint64_t* mask = nullptr;
+  void* out = nullptr;
+  RowSrc scatter{nullptr, nullptr, 0, 0};
+};
+
+void layer_body(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, bool rows,
+                const LayerIO& io, hipStream_t st) {
+  const int d = h->d, qd = h->n_q_heads * h->head_dim, ffn = h->ffn;
+  const int kvd = h->n_kv_heads * h->head_dim;
+  const bool swiglu = h->act == EAGLE_ACT_SWIGLU;
+  float* P = (float*)(ws + w.P);
+  GemmShape sh;
+  // ---- attention sub-layer
+  if (rows) {
+    RowsArgs r = rows_args(io.M, qd + 2 * kvd, d, h->w_q, h->w_k, h->w_v, qd, qd + kvd);
+    r.g.xs[0] = rs(io.xn, nullptr, d);
+    r.xstats = io.nst;
+    r.xnblk = io.nblk;
+    r.eps = h->eps;
+    r.Hq = h->n_q_heads;
+    r.Hkv = h->n_kv_heads;
+    r.hd = h->head_dim;
+    r.theta = h->rope_theta;
+    r.pos = io.pos;
+    r.q = ws + w.q;
+    r.k = io.kdst;
+    r.v = io.vdst;
+    r.kv_idx = io.kv_idx;
+    run_rows(h, EP_ROPE, r, st);
+  } else {
+    qkv_rope(h, ws, w, io.xn, io.M, io.pos, io.kdst, io.vdst, io.kv_idx, st);
+  }
+  attend(h, kv, ws, w, io.W, io.kdst, io.vdst, io.mask, ws + w.o, st);
+  if (rows) {
+    RowsArgs r = rows_args(io.M, d, qd, h->w_o, nullptr, nullptr, d, d);
+    r.g.xs[0] = rs(ws + w.o, nullptr, qd);
+    r.res = rs(io.x, nullptr, d);
+    r.out = ws + w.h1;
+    r.out_g = ws + w.h1n;
+    r.gain = h->norm2_g;
+    r.stats = (float*)(ws + w.rs1);
+    run_rows(h, EP_STORE, r, st);
+  } else {
+    gemm(h, rs(ws + w.o, nullptr, qd), kNone, qd, io.M, d, qd, h->w_o, nullptr, nullptr, d, d, P, &sh,
+         st);
+    reduce(h, P, sh.S, io.M, d, rs(io.x, nullptr, d), kNone, ws + w.h1, kNone, ws + w.h1n, 2, st);
+  }
+
+  // ---- MLP sub-layer
+  if (rows) {
+    RowsArgs r = swiglu ? rows_args(io.M, 2 * ffn, d, h->w_gate, h->w_up, nullptr, ffn, 2 * ffn)
+                        : rows_args(io.M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn);
+    r.g.xs[0] = rs(ws + w.h1n, nullptr, d);
+    r.xstats = (const float*)(ws + w.rs1);
+    r.xnblk = d / 16;
+    r.eps = h->eps;
+    r.act_F = ffn;
+    r.out = ws + w.act;
+    run_rows(h, swiglu ? EP_SWIGLU : EP_GELU, r, st);
+    RowsArgs r2 = rows_args(io.M, d, ffn, h->w_down, nullptr, nullptr, d, d);
+    r2.g.xs[0] = rs(ws + w.act, nullptr, ffn);
+    r2.res = rs(ws + w.h1, nullptr, d);
+    r2.out = io.out;
+    r2.scatter = io.scatter;
+    run_rows(h, EP_STORE, r2, st);
+  } else {
+    if (swiglu)
+      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, io.M, 2 * ffn, d, h->w_gate, h->w_up, nullptr,
+           ffn, 2 * ffn, P, &sh, st);
+    else
+      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, io.M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn,
+           P, &sh, st);
+    ActArgs aa;
+    aa.P = P;
+    aa.S = sh.S;
+    aa.M = io.M;
+    aa.F = ffn;
+    aa.swiglu = swiglu;
+    aa.out = ws + w.act;
+    {
+      ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
+      launch_epi_act(h->dtype, aa, st);
+    }
+    gemm(h, rs(ws + w.act, nullptr, ffn), kNone, ffn, io.M, d, ffn, h->w_down, nullptr, nullptr, d, d,
+         P, &sh, st);
+    reduce(h, P, sh.S, io.M, d, rs(ws + w.h1, nullptr, d), kNone, io.out, io.scatter, nullptr, 0,
+           st);
+  }
+
+}
+
 int finish(int status) {
   if (status != EAGLE_OK) return status;
   return last_error() == hipSuccess ? EAGLE_OK : EAGLE_EHIP;
@@ -700,8 +816,7 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   g_stats = (float*)(ws + w.stats);
   const TreeDev td = tree_dev(tree, g, step);
   const int B = g.B, W = g.rows[step], M = B * W;
-  const int d = h->d, qd = h->n_q_heads * h->head_dim, ffn = h->ffn;
-  const bool swiglu = h->act == EAGLE_ACT_SWIGLU;
+  const int d = h->d;
   float* P = (float*)(ws + w.P);
   void* hbuf = ws + w.h;
   void* hn = ws + w.hn;
@@ -773,82 +888,24 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
            rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
   }
 
-  // ---- attention sub-layer
-  if (rows) {
-    RowsArgs r = rows_args(M, qd + 2 * kvd, d, h->w_q, h->w_k, h->w_v, qd, qd + kvd);
-    r.g.xs[0] = rs(hn, nullptr, d);
-    r.xstats = nst;
-    r.xnblk = nblk;
-    r.eps = h->eps;
-    r.Hq = h->n_q_heads;
-    r.Hkv = h->n_kv_heads;
-    r.hd = h->head_dim;
-    r.theta = h->rope_theta;
-    r.pos = td.row_pos;
-    r.q = ws + w.q;
-    r.k = kv->k_slot;
-    r.v = kv->v_slot;
-    r.kv_idx = td.row_slot;
-    run_rows(h, EP_ROPE, r, st);
-  } else {
-    qkv_rope(h, ws, w, hn, M, td.row_pos, kv->k_slot, kv->v_slot, td.row_slot, st);
-  }
-  attend(h, kv, ws, w, W, kv->k_slot, kv->v_slot, td.row_mask, ws + w.o, st);
-  if (rows) {
-    RowsArgs r = rows_args(M, d, qd, h->w_o, nullptr, nullptr, d, d);
-    r.g.xs[0] = rs(ws + w.o, nullptr, qd);
-    r.res = rs(hbuf, nullptr, d);
-    r.out = ws + w.h1;
-    r.out_g = ws + w.h1n;
-    r.gain = h->norm2_g;
-    r.stats = (float*)(ws + w.rs1);
-    run_rows(h, EP_STORE, r, st);
-  } else {
-    gemm(h, rs(ws + w.o, nullptr, qd), kNone, qd, M, d, qd, h->w_o, nullptr, nullptr, d, d, P, &sh,
-         st);
-    reduce(h, P, sh.S, M, d, rs(hbuf, nullptr, d), kNone, ws + w.h1, kNone, ws + w.h1n, 2, st);
-  }
-
-  // ---- MLP sub-layer
+  // ---- decoder layer from the attention sub-layer on
   void* fout = feat_out ? feat_out : (void*)(ws + w.f);
-  if (rows) {
-    RowsArgs r = swiglu ? rows_args(M, 2 * ffn, d, h->w_gate, h->w_up, nullptr, ffn, 2 * ffn)
-                        : rows_args(M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn);
-    r.g.xs[0] = rs(ws + w.h1n, nullptr, d);
-    r.xstats = (const float*)(ws + w.rs1);
-    r.xnblk = d / 16;
-    r.eps = h->eps;
-    r.act_F = ffn;
-    r.out = ws + w.act;
-    run_rows(h, swiglu ? EP_SWIGLU : EP_GELU, r, st);
-    RowsArgs r2 = rows_args(M, d, ffn, h->w_down, nullptr, nullptr, d, d);
-    r2.g.xs[0] = rs(ws + w.act, nullptr, ffn);
-    r2.res = rs(ws + w.h1, nullptr, d);
-    r2.out = fout;
-    r2.scatter = rs(kv->feat_slot, td.row_slot, d);
-    run_rows(h, EP_STORE, r2, st);
-  } else {
-    if (swiglu)
-      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, 2 * ffn, d, h->w_gate, h->w_up, nullptr,
-           ffn, 2 * ffn, P, &sh, st);
-    else
-      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn,
-           P, &sh, st);
-    ActArgs aa;
-    aa.P = P;
-    aa.S = sh.S;
-    aa.M = M;
-    aa.F = ffn;
-    aa.swiglu = swiglu;
-    aa.out = ws + w.act;
-    {
-      ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
-      launch_epi_act(h->dtype, aa, st);
-    }
-    gemm(h, rs(ws + w.act, nullptr, ffn), kNone, ffn, M, d, ffn, h->w_down, nullptr, nullptr, d, d,
-         P, &sh, st);
-    reduce(h, P, sh.S, M, d, rs(ws + w.h1, nullptr, d), kNone, fout,
-           rs(kv->feat_slot, td.row_slot, d), nullptr, 0, st);
+  {
+    LayerIO io;
+    io.M = M;
+    io.W = W;
+    io.x = hbuf;
+    io.xn = hn;
+    io.nst = nst;
+    io.nblk = nblk;
+    io.pos = td.row_pos;
+    io.kdst = kv->k_slot;
+    io.vdst = kv->v_slot;
+    io.kv_idx = td.row_slot;
+    io.mask = td.row_mask;
+    io.out = fout;
+    io.scatter = rs(kv->feat_slot, td.row_slot, d);
+    layer_body(h, kv, ws, w, rows, io, st);
   }
 
   // ---- LM head + softmax / top-k
@@ -956,6 +1013,165 @@ int eagle_tree_attend(const eagle_head* h, const eagle_kv* kv, const eagle_tree*
   reduce(h, nullptr, 0, M, d, rs(h->emb, t_tok, d, h->vocab), kNone, nullptr, kNone, ws + w.hn, 1, st);
   qkv_rope(h, ws, w, ws + w.hn, M, t_pos, ws + w.tk, ws + w.tv, t_kv, st);
   attend(h, kv, ws, w, Wt, ws + w.tk, ws + w.tv, t_mask, out, st);
+  return finish(EAGLE_OK);
+}
+
+int check_target(const eagle_head* h, const eagle_target* t) {
+  if (!t || t->n_layers < 1 || !t->layers || !t->final_norm_g) return EAGLE_EINVAL;
+  for (int l = 0; l < t->n_layers; ++l) {
+    const eagle_layer& L = t->layers[l];
+    if (!L.w_q || !L.w_k || !L.w_v || !L.w_o || !L.w_up || !L.w_down) return EAGLE_EINVAL;
+    if (h->act == EAGLE_ACT_SWIGLU && !L.w_gate) return EAGLE_EINVAL;
+    if (!L.norm1_g || !L.norm2_g) return EAGLE_EINVAL;
+    if (h->norm == EAGLE_NORM_LAYER && (!L.norm1_b || !L.norm2_b)) return EAGLE_EINVAL;
+  }
+  return EAGLE_OK;
+}
+
+size_t eagle_target_workspace_bytes(const eagle_head* head, const eagle_target* target,
+                                    const eagle_kv* kv, const eagle_tree* tree) {
+  Geo g;
+  if (check_head(head) || check_target(head, target) || build_geo(tree, &g) || check_kv(kv, g.B))
+    return 0;
+  return plan_ws(head, kv, g, true).total;
+}
+
+int eagle_target_verify_logits(const eagle_head* head, const eagle_target* target,
+                               const eagle_kv* kv, const eagle_tree* tree, float* logits_out,
+                               void* k_tree, void* v_tree, void* ws_v, size_t ws_bytes,
+                               void* stream) {
+  Geo g;
+  int s;
+  if ((s = check_head(head))) return s;
+  if ((s = check_target(head, target))) return s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_kv(kv, g.B))) return s;
+  if ((s = check_attn_plan(head, kv))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (!logits_out || !ws_v || (!k_tree) != (!v_tree)) return EAGLE_EINVAL;
+  const Ws w = plan_ws(head, kv, g, true);
+  if (ws_bytes < w.total) return EAGLE_ECAPACITY;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)ws_v;
+  g_y32 = (float*)(ws + w.y32);
+  g_stats = (float*)(ws + w.stats);
+  const TreeDev td = tree_dev(tree, g);
+  const int Wt = g.positions, M = g.B * Wt, d = head->d;
+  const int kvd = head->n_kv_heads * head->head_dim;
+  int32_t* t_tok = (int32_t*)(ws + w.t_tok);
+  int32_t* t_kv = (int32_t*)(ws + w.t_kv);
+  int32_t* t_pos = (int32_t*)(ws + w.t_pos);
+  uint64_t* t_mask = (uint64_t*)(ws + w.t_mask);
+  launch_tree_rows_final(td, g.B, t_tok, t_kv, t_pos, t_mask, st);
+  const bool rows = rows_gemm_ok(M, d, 32) && head->norm == EAGLE_NORM_RMS;
+  // layer inputs alternate between two row buffers; layer 0 reads the
+  // embeddings of the verify-tree tokens
+  void* xb[2] = {ws + w.h, ws + w.f};
+  const size_t tree_kv = (size_t)g.B * kSlots * kvd * esz(head);
+  for (int l = 0; l < target->n_layers; ++l) {
+    const eagle_layer& L = target->layers[l];
+    eagle_head hl = *head;
+    hl.w_q = L.w_q;
+    hl.w_k = L.w_k;
+    hl.w_v = L.w_v;
+    hl.w_o = L.w_o;
+    hl.w_gate = L.w_gate;
+    hl.w_up = L.w_up;
+    hl.w_down = L.w_down;
+    hl.norm1_g = L.norm1_g;
+    hl.norm1_b = L.norm1_b;
+    hl.norm2_g = L.norm2_g;
+    hl.norm2_b = L.norm2_b;
+    eagle_kv kl = *kv;
+    kl.k_ctx = const_cast<void*>(L.k_ctx);
+    kl.v_ctx = const_cast<void*>(L.v_ctx);
+    if (kl.total_n > 0 && (!kl.k_ctx || !kl.v_ctx)) return EAGLE_EINVAL;
+    void* x = xb[l & 1];
+    // N1 of the layer input (plain normalised rows; the row path takes them
+    // without a folded scale)
+    if (l == 0)
+      reduce(&hl, nullptr, 0, M, d, rs(head->emb, t_tok, d, head->vocab), kNone, x, kNone,
+             ws + w.hn, 1, st);
+    else
+      reduce(&hl, nullptr, 0, M, d, rs(x, nullptr, d), kNone, nullptr, kNone, ws + w.hn, 1, st);
+    LayerIO io;
+    io.M = M;
+    io.W = Wt;
+    io.x = x;
+    io.xn = ws + w.hn;
+    io.pos = t_pos;
+    io.kdst = k_tree ? (char*)k_tree + l * tree_kv : (void*)(ws + w.tk);
+    io.vdst = v_tree ? (char*)v_tree + l * tree_kv : (void*)(ws + w.tv);
+    io.kv_idx = t_kv;
+    io.mask = t_mask;
+    io.out = xb[(l + 1) & 1];
+    layer_body(&hl, &kl, ws, w, rows, io, st);
+  }
+  // final RMSNorm, then the shared LM head into fp32 logits
+  eagle_head hf = *head;
+  hf.norm = EAGLE_NORM_RMS;
+  hf.norm1_g = target->final_norm_g;
+  hf.norm1_b = nullptr;
+  reduce(&hf, nullptr, 0, M, d, rs(xb[target->n_layers & 1], nullptr, d), kNone, nullptr, kNone,
+         ws + w.hn, 1, st);
+  const double lm_bytes = (double)esz(head) * ((double)head->vocab * d + (double)M * d);
+  const double lm_flops = 2.0 * M * (double)head->vocab * d;
+  if (big_gemm_ok(head->dtype, M, head->vocab, d)) {
+    GemmArgs ga;
+    ga.xs[0] = rs(ws + w.hn, nullptr, d);
+    ga.xs[1] = kNone;
+    ga.ksplit_x = d;
+    ga.M = M;
+    ga.N = head->vocab;
+    ga.K = d;
+    ga.w[0] = ga.w[1] = ga.w[2] = head->lm_head;
+    ga.nseg1 = ga.nseg2 = head->vocab;
+    ga.P = logits_out;
+    GemmShape gs = plan_gemm_big(M, head->vocab, d);
+    gs.S = 1;
+    gs.kps = d;
+    ProfScope ps(EAGLE_PROF_LMHEAD, lm_bytes, lm_flops, st);
+    launch_gemm_big(ga, gs, st);
+  } else {
+    LmShape ls = plan_lmhead(head->dtype, M, head->vocab);
+    LmArgs la;
+    la.x = rs(ws + w.hn, nullptr, d);
+    la.M = M;
+    la.K = d;
+    la.V = head->vocab;
+    la.w = head->lm_head;
+    la.top_k = 1;
+    la.inv_temp = 1.0f;
+    la.logits = logits_out;
+    la.part_max = (float*)(ws + w.lm_max);
+    la.part_sum = (float*)(ws + w.lm_sum);
+    la.part_id = (int*)(ws + w.lm_id);
+    la.part_val = (float*)(ws + w.lm_val);
+    ProfScope ps(EAGLE_PROF_LMHEAD, lm_bytes, lm_flops, st);
+    launch_lmhead(head->dtype, la, ls, st);
+  }
+  return finish(EAGLE_OK);
+}
+
+int eagle_kv_commit(const eagle_tree* tree, int kv_heads, int head_dim, int dtype,
+                    const int32_t* accept_len, const int32_t* accept_path, const void* k_tree,
+                    const void* v_tree, const int32_t* dst_row, int64_t dst_rows, void* k_dst,
+                    void* v_dst, void* stream) {
+  Geo g;
+  int s;
+  if ((s = build_geo(tree, &g))) return s;
+  if (kv_heads < 1 || head_dim < 1 || (dtype != EAGLE_BF16 && dtype != EAGLE_F32)) return EAGLE_EINVAL;
+  if (!accept_len || !accept_path || !k_tree || !v_tree || !dst_row || !k_dst || !v_dst)
+    return EAGLE_EINVAL;
+  if (dst_rows < 1) return EAGLE_EINVAL;
+  const int64_t row_bytes = (int64_t)kv_heads * head_dim * (dtype == EAGLE_BF16 ? 2 : 4);
+  if (row_bytes % 16 || row_bytes > INT32_MAX) return EAGLE_EINVAL;
+  for (const void* p : {k_tree, v_tree, (const void*)k_dst, (const void*)v_dst})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return EAGLE_EINVAL;
+  ProfScope ps(EAGLE_PROF_OTHER, 0, 0, (hipStream_t)stream);
+  launch_kv_commit(g.B, g.gamma, (int)row_bytes, accept_len,
+                   accept_path, k_tree, v_tree, dst_row, dst_rows, k_dst, v_dst,
+                   (hipStream_t)stream);
   return finish(EAGLE_OK);
 }
 

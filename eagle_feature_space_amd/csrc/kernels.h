@@ -227,6 +227,10 @@ void launch_verify_sample(const TreeDev& t, int B, const void* logits, int posit
                           int dtype, float inv_temp, const float* draws, int gamma,
                           int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
                           hipStream_t st);
+void launch_kv_commit(int B, int gamma, int row_bytes, const int32_t* accept_len,
+                      const int32_t* accept_path, const void* k_tree, const void* v_tree,
+                      const int32_t* dst_row, int64_t dst_rows, void* k_dst, void* v_dst,
+                      hipStream_t st);
 void launch_tree_rows_final(const TreeDev& t, int B, int32_t* tok_idx,
                             int32_t* kv_idx, int32_t* pos, uint64_t* mask,
                             hipStream_t st);

@@ -631,6 +631,37 @@ void launch_verify_sample(const TreeDev& t, int B, const void* logits, int posit
                     accept_len, accept_path, out_tokens, st);
 }
 
+// Commit of the accepted path's keys and values: request b's path positions
+// accept_path[b][0 .. accept_len[b]] (root first) of the tree K/V
+// ([B][64][row_bytes]) are copied to rows dst_row[b] + i of the destination
+// cache; rows outside [0, dst_rows) and positions outside [0, 64) are
+// skipped.  One workgroup per (request, path index), 16-byte copies.
+__global__ void k_kv_commit(int gamma, int row_bytes, const int32_t* accept_len,
+                            const int32_t* accept_path, const char* k_tree, const char* v_tree,
+                            const int32_t* dst_row, int64_t dst_rows, char* k_dst, char* v_dst) {
+  const int b = blockIdx.y, i = blockIdx.x;
+  const int acc = accept_len[b];
+  if (i > acc || i > gamma) return;
+  const int u = accept_path[(int64_t)b * (gamma + 1) + i];
+  const int64_t r = (int64_t)dst_row[b] + i;
+  if (u < 0 || u >= kMaxPos || r < 0 || r >= dst_rows) return;
+  const int64_t src = ((int64_t)b * kSlots + u) * row_bytes;
+  const int64_t dst = r * row_bytes;
+  for (int o = threadIdx.x * 16; o < row_bytes; o += blockDim.x * 16) {
+    *reinterpret_cast<u32x4*>(k_dst + dst + o) = *reinterpret_cast<const u32x4*>(k_tree + src + o);
+    *reinterpret_cast<u32x4*>(v_dst + dst + o) = *reinterpret_cast<const u32x4*>(v_tree + src + o);
+  }
+}
+
+void launch_kv_commit(int B, int gamma, int row_bytes, const int32_t* accept_len,
+                      const int32_t* accept_path, const void* k_tree, const void* v_tree,
+                      const int32_t* dst_row, int64_t dst_rows, void* k_dst, void* v_dst,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(k_kv_commit, dim3(gamma + 1, B), dim3(128), 0, st, gamma, row_bytes,
+                     accept_len, accept_path, (const char*)k_tree, (const char*)v_tree, dst_row,
+                     dst_rows, (char*)k_dst, (char*)v_dst);
+}
+
 // dense rows of the verify tree (row m = b * positions + u)
 __global__ void k_tree_rows_final(TreeDev t, int B, int32_t* tok_idx, int32_t* kv_idx,
                                   int32_t* pos, uint64_t* mask) {

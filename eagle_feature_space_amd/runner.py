@@ -16,6 +16,7 @@ import numpy as np
 import torch
 
 from . import binding as E
+from . import synth
 from .configs import DTYPE_BF16, MODE_EAGLE3, TREE_STATIC, RoundCfg
 
 
@@ -44,7 +45,8 @@ class StepSnapshot:
 
 
 class GpuRound:
-    def __init__(self, cfg: RoundCfg, weights: Dict[str, np.ndarray], inputs, device="cuda:0"):
+    def __init__(self, cfg: RoundCfg, weights: Dict[str, np.ndarray], inputs, device="cuda:0",
+                 keep_tree_kv=False):
         self.cfg = cfg
         h = cfg.head
         self.dev = torch.device(device)
@@ -119,6 +121,56 @@ class GpuRound:
         self.accept_path = torch.zeros((B, cfg.gamma + 1), dtype=torch.int32, device=self.dev)
         self.out_tokens = torch.zeros((B, cfg.gamma + 1), dtype=torch.int32, device=self.dev)
         self.attn_out = None
+        self.target = None
+        if cfg.target_layers > 0:
+            self._build_target(keep_tree_kv)
+
+    def _build_target(self, keep_tree_kv):
+        """Random-init target layers (the head's layer shape, sharing its
+        embedding and LM head) and their context caches, one layer at a time."""
+        cfg, h = self.cfg, self.cfg.head
+        L = cfg.target_layers
+        self.t_w, self.t_ctx = [], []
+        layers = (E.eagle_layer * L)()
+        for l in range(L):
+            w = {k: to_dev(v, self.dev) for k, v in synth.target_layer_weights(h, cfg.seed_tm, l).items()}
+            kc, vc = (to_dev(a, self.dev) for a in synth.target_context(cfg, l))
+            self.t_w.append(w)
+            self.t_ctx.append((kc, vc))
+            for k, t in w.items():
+                setattr(layers[l], k, t.data_ptr())
+            layers[l].k_ctx, layers[l].v_ctx = kc.data_ptr(), vc.data_ptr()
+        self.t_final = to_dev(synth.target_final_gain(h, cfg.seed_tm), self.dev)
+        tg = E.eagle_target()
+        tg.n_layers, tg.layers, tg.final_norm_g = L, layers, self.t_final.data_ptr()
+        self._t_layers = layers
+        self.target = tg
+        P = self.layout.positions
+        self.t_logits = torch.empty((cfg.B, P, h.vocab), dtype=torch.float32, device=self.dev)
+        self.k_tree = self.v_tree = None
+        if keep_tree_kv:
+            self.k_tree = torch.zeros((L, cfg.B, E.MAX_SLOTS, h.n_kv, h.head_dim), dtype=self.dt,
+                                      device=self.dev)
+            self.v_tree = torch.zeros_like(self.k_tree)
+        wsb = E.eagle_target_workspace_bytes(self.head, tg, self.kv, self.tree)
+        if wsb == 0:
+            raise E.EagleError(E.EAGLE_EINVAL, "eagle_target_workspace_bytes")
+        if wsb > self.ws.numel():
+            self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
+
+    def target_logits(self, stream=None):
+        """The target's pass over the verify tree -> fp32 logits [B, positions, |V|]."""
+        E.eagle_target_verify_logits(self.head, self.target, self.kv, self.tree, self.t_logits,
+                                     self.k_tree, self.v_tree, self.ws, self.ws.numel(), stream)
+        return self.t_logits
+
+    def commit(self, layer, dst_row, k_dst, v_dst, stream=None):
+        """Append the accepted path's K/V of target layer `layer` to (k_dst, v_dst)."""
+        h = self.cfg.head
+        kt, vt = self.k_tree[layer], self.v_tree[layer]
+        E.eagle_kv_commit(self.tree, h.n_kv, h.head_dim, 0 if self.dt == torch.bfloat16 else 1,
+                          self.accept_len, self.accept_path, kt, vt, dst_row, k_dst.shape[0],
+                          k_dst, v_dst, stream)
 
     # ------------------------------------------------------------ state views
     def view(self, name, dtype, shape):
@@ -215,6 +267,8 @@ class GpuRound:
             self.expand(s)
         if attend:
             self.attend()
+        if self.target is not None:
+            target = self.target_logits()
         if target is not None:
             if sample is None:
                 self.verify(target)

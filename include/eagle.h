@@ -10,6 +10,9 @@
  *   eagle_tree_attend         (optional) tree-masked attention over the verify tree
  *   eagle_tree_verify         accept the longest root path matching the target
  *   (or eagle_tree_verify_sample: lossless multi-round speculative sampling)
+ *   eagle_target_verify_logits (optional) the target's own pass over the tree
+ *                             (its logits feed the verify calls)
+ *   eagle_kv_commit           (optional) append the accepted path's K/V to a cache
  *
  * The method is the one described on the pages
  *   "transformer_math / tm_eagle_deep" (aicassindra.com), sections "The
@@ -303,6 +306,75 @@ int eagle_tree_verify_sample(const eagle_tree *tree, const void *target_logits,
                              const float *draws, int32_t *accept_len,
                              int32_t *accept_path, int32_t *out_tokens,
                              void *stream);
+
+/*
+ * The target model for its verification pass: n_layers decoder layers of the
+ * draft head's layer shape (d, heads, head_dim, ffn, act, norm, eps,
+ * rope_theta and dtype are the head's), each with its own context cache, a
+ * final RMSNorm, and the embedding and LM head the draft head shares.
+ * Every pointer is a device pointer except `layers` (a HOST array).
+ */
+typedef struct eagle_layer {
+  const void *w_q, *w_k, *w_v, *w_o;          /* [out][in], as in eagle_head */
+  const void *w_gate, *w_up, *w_down;
+  const void *norm1_g, *norm1_b, *norm2_g, *norm2_b;  /* [d]; b: LayerNorm */
+  const void *k_ctx, *v_ctx;   /* [total_n][Hkv][hd] this layer's context cache
+                                  (rotated), packed like eagle_kv's */
+} eagle_layer;
+
+typedef struct eagle_target {
+  int32_t n_layers;
+  const eagle_layer *layers;   /* HOST array [n_layers] */
+  const void *final_norm_g;    /* [d] RMSNorm gain before the LM head */
+} eagle_target;
+
+/*
+ * The target's verification pass over the verify tree ("transformer_math /
+ * tm_eagle_deep", "Tree attention in one verification pass": the flattened
+ * tree goes through the target once; each position attends to the context
+ * and to its ancestors-or-self, at position id root position + depth).
+ * Row m = b * positions + u is verify position u of request b: x = emb(f_tok),
+ * then every layer (as eagle_draft_step's decoder layer, with the layer's
+ * context cache and the tree masks f_mask), then RMSNorm(final_norm_g) and the
+ * LM head.
+ * head:   dims, dtype, emb and lm_head (its draft weights are not read)
+ * kv:     B, n, cu_n, max_n, total_n of the target's context: request b's
+ *         cache holds positions [0, n[b]), which must end where the tree's
+ *         root position starts (EAGLE-1 roots sit at n[b]); k_ctx / v_ctx are
+ *         not read (each layer brings its own); slots as for eagle_draft_step
+ * logits_out: device fp32 [B * positions][vocab] (positions from
+ *         eagle_tree_layout_of), for eagle_tree_verify(_sample) with EAGLE_F32
+ * k_tree, v_tree: optional device [n_layers][B][64][Hkv][hd]: every layer's
+ *         keys / values of the verify positions (for eagle_kv_commit); both
+ *         NULL: kept in the workspace only
+ * ws:     device workspace of eagle_target_workspace_bytes
+ */
+int eagle_target_verify_logits(const eagle_head *head, const eagle_target *target,
+                               const eagle_kv *kv, const eagle_tree *tree,
+                               float *logits_out, void *k_tree, void *v_tree,
+                               void *ws, size_t ws_bytes, void *stream);
+/* Workspace bytes eagle_target_verify_logits needs (0 on invalid arguments). */
+size_t eagle_target_workspace_bytes(const eagle_head *head, const eagle_target *target,
+                                    const eagle_kv *kv, const eagle_tree *tree);
+
+/*
+ * Commit of the accepted path to a key/value cache ("EAGLE / DFlash / DSpark"
+ * explainer, "How speculative decoding works", step 4: the accepted prefix
+ * joins the sequence before the next round): for request b and
+ * i = 0 .. accept_len[b], row accept_path[b][i] of request b in k_tree /
+ * v_tree ([B][64][kv_heads][head_dim], one layer's tree keys and values, e.g.
+ * from eagle_target_verify_logits) is copied to row dst_row[b] + i of k_dst /
+ * v_dst ([dst_rows][kv_heads][head_dim]): the root first, then the accepted
+ * nodes in path order; the rest of the tree is dropped.  accept_len /
+ * accept_path as written by eagle_tree_verify(_sample).  The caller leaves
+ * room for accept_len[b] + 1 rows after dst_row[b]; rows outside
+ * [0, dst_rows) are skipped.  Rows must be whole 16-byte multiples and every
+ * buffer 16-byte aligned (EAGLE_EINVAL otherwise).
+ */
+int eagle_kv_commit(const eagle_tree *tree, int kv_heads, int head_dim, int dtype,
+                    const int32_t *accept_len, const int32_t *accept_path,
+                    const void *k_tree, const void *v_tree, const int32_t *dst_row,
+                    int64_t dst_rows, void *k_dst, void *v_dst, void *stream);
 
 /*
  * Kernel timing for benchmarks (off by default).  While enabled, every launch

@@ -35,14 +35,16 @@ def mask_bits(mask, T):
     return [j for j in range(T) if (m >> j) & 1]
 
 
-def tree_forward(layers, emb, final_g, eps, lm_head, tok, pos, masks, ctx):
+def tree_forward(layers, emb, final_g, eps, lm_head, tok, pos, masks, ctx, store=None):
     """Target logits at every verify-tree position of one request.
 
     layers: list of L DraftHead objects (only their decoder-layer weights are
     used) or a callable l -> DraftHead (so callers can materialise one layer
     at a time); emb [V, d]; final_g [d]; lm_head [V, d]; tok, pos [T];
     masks [T] ancestor-or-self bitmasks over positions; ctx: list of L pairs
-    (K [n, Hkv, hd], V [n, Hkv, hd]), the layer's context cache.
+    (K [n, Hkv, hd], V [n, Hkv, hd]), the layer's context cache; store:
+    optional map applied to every layer's output rows (e.g. rounding to the
+    storage type of a bf16 model).
     Returns (logits [T, V], per-layer tree keys and values [(k, v)] of shape
     [T, Hkv, hd]).
     """
@@ -60,6 +62,8 @@ def tree_forward(layers, emb, final_g, eps, lm_head, tok, pos, masks, ctx):
             att[u] = attend(q[u], np.concatenate([ck, k[sel]]), np.concatenate([cv, v[sel]]),
                             layer.group)
         x = layer.finish(x, att)
+        if store is not None:
+            x = store(x)
         kv_tree.append((k, v))
     return rms_norm(x, final_g, eps) @ lm_head.T, kv_tree
 

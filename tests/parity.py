@@ -21,6 +21,7 @@ import numpy as np
 
 from eagle_feature_space_amd import configs as C
 from eagle_feature_space_amd import synth
+from oracle import target as OTG
 from oracle import tree as OT
 from oracle import verify as OV
 from oracle.head import DraftHead
@@ -56,7 +57,7 @@ class Case:
 
     def gpu(self, device="cuda:0"):
         from eagle_feature_space_amd.runner import GpuRound
-        return GpuRound(self.cfg, self.w, self.inp, device)
+        return GpuRound(self.cfg, self.w, self.inp, device, keep_tree_kv=self.cfg.target_layers > 0)
 
     def target_dev(self, device="cuda:0", target=None):
         from eagle_feature_space_amd.runner import to_dev
@@ -376,6 +377,90 @@ def sampling_checks(case: Case, gr, device, seeds=(0, 1, 2), inv_temps=(1.0, 0.7
     return out
 
 
+# ------------------------------------------------------------------ P5: target pass
+def _target_layers(cfg):
+    """Oracle target layers; materialised one at a time at large widths."""
+    h = cfg.head
+    make = lambda l: DraftHead(h, {k: synth.f32(v) for k, v in
+                                   synth.target_layer_weights(h, cfg.seed_tm, l).items()})
+    if h.d > 1024:
+        return make
+    cache = [make(l) for l in range(cfg.target_layers)]
+    return lambda l: cache[l]
+
+
+def check_target_pass(case: Case, gr):
+    """The GPU target logits (and every layer's tree K/V) against the oracle's
+    tree pass, per request, on the GPU's verify tree (checked bit-exact in P2)."""
+    from eagle_feature_space_amd.runner import to_f32
+    cfg, h = case.cfg, case.cfg.head
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    logits = gr.t_logits.cpu().numpy()
+    kt = to_f32(gr.k_tree) if gr.k_tree is not None else None
+    vt = to_f32(gr.v_tree) if gr.v_tree is not None else None
+    layers = _target_layers(cfg)
+    emb, lm = case.head.w["emb"], case.head.w["lm_head"]
+    g = synth.f32(synth.target_final_gain(h, cfg.seed_tm))
+    cu = case.inp.cu_n
+    ctx_all = [tuple(synth.f32(a) for a in synth.target_context(cfg, l)) for l in range(cfg.target_layers)]
+    worst = dict(t_logit=0.0, t_kv=0.0, t_bound=0.0)
+    bf = h.dtype == C.DTYPE_BF16
+    rnd = (lambda x: synth.bf16_to_f32(synth.bf16_bits(x))) if bf else None
+    for b in range(cfg.B):
+        T = int(fv["count"][b])
+        ctx = [(K[cu[b]:cu[b + 1]], V[cu[b]:cu[b + 1]]) for K, V in ctx_all]
+        args = (layers, emb, g, h.eps, lm, fv["tok"][b, :T], fv["pos"][b, :T], fv["mask"][b, :T], ctx)
+        ref, kvt = OTG.tree_forward(*args)
+        # tolerance: the one-layer bar plus twice what storing each layer's
+        # output in the model dtype does to the oracle itself (independent
+        # bf16 roundings of the residual stream add up with depth)
+        sens = 0.0
+        if rnd is not None:
+            ref_b, _ = OTG.tree_forward(*args, store=rnd)
+            sens = max(rel_err(ref_b[u], ref[u]) for u in range(T))
+        tol = TOL + 2.0 * sens
+        worst["t_bound"] = max(worst["t_bound"], tol)
+        for u in range(T):
+            e = rel_err(logits[b, u], ref[u])
+            worst["t_logit"] = max(worst["t_logit"], e)
+            assert e <= tol, f"target logits request {b} position {u}: rel err {e:.3g} > {tol:.3g}"
+        if kt is not None:
+            for l, (k, v) in enumerate(kvt):
+                e = max(rel_err(kt[l, b, :T], k), rel_err(vt[l, b, :T], v))
+                worst["t_kv"] = max(worst["t_kv"], e)
+                assert e <= tol, f"target K/V layer {l} request {b}: rel err {e:.3g} > {tol:.3g}"
+    return worst
+
+
+def check_commit(case: Case, gr, device):
+    """eagle_kv_commit copies exactly the accepted path's rows (root first) of
+    the first and last layer, at an offset, and nothing else."""
+    import torch
+    cfg, h = case.cfg, case.cfg.head
+    G = cfg.gamma + 1
+    acc = gr.accept_len.cpu().numpy()
+    path = gr.accept_path.cpu().numpy()
+    dst_row = torch.tensor([b * G + 1 for b in range(cfg.B)], dtype=torch.int32, device=device)
+    rows = cfg.B * G + 2
+    for l in sorted({0, cfg.target_layers - 1}):
+        kd = torch.zeros((rows, h.n_kv, h.head_dim), dtype=gr.dt, device=device)
+        vd = torch.zeros_like(kd)
+        gr.commit(l, dst_row, kd, vd)
+        kd, vd = kd.cpu(), vd.cpu()
+        want_k = torch.zeros_like(kd)
+        want_v = torch.zeros_like(vd)
+        kt, vt = gr.k_tree[l].cpu(), gr.v_tree[l].cpu()
+        for b in range(cfg.B):
+            for i in range(int(acc[b]) + 1):
+                want_k[b * G + 1 + i] = kt[b, int(path[b, i])]
+                want_v[b * G + 1 + i] = vt[b, int(path[b, i])]
+        assert torch.equal(kd.view(torch.int16) if kd.dtype == torch.bfloat16 else kd,
+                           want_k.view(torch.int16) if kd.dtype == torch.bfloat16 else want_k), l
+        assert torch.equal(vd.view(torch.int16) if vd.dtype == torch.bfloat16 else vd,
+                           want_v.view(torch.int16) if vd.dtype == torch.bfloat16 else want_v), l
+    return [int(a) for a in acc]
+
+
 # ------------------------------------------------------------------ tree attention
 def check_tree_attend(case: Case, gr):
     cfg, hd = case.cfg, case.head
@@ -449,7 +534,12 @@ def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:
         check_step(case, gr, snaps, s, rows=rows, report=report)
         say(f"step {s} checked")
     check_tree_logic(case, gr, snaps)
-    check_verify(case, gr, case.target, cfg.gamma)
+    if cfg.target_layers > 0:
+        report.update(check_target_pass(case, gr))
+        say("target pass checked")
+        check_verify(case, gr, gr.t_logits.cpu().numpy(), cfg.gamma)
+    else:
+        check_verify(case, gr, case.target, cfg.gamma)
     if attend:
         report["attend"] = check_tree_attend(case, gr)
     if planted:
@@ -458,6 +548,8 @@ def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:
         acc = check_verify(case, gr, pt, cfg.gamma)
         assert list(acc) == want, (list(acc), want)
         report["planted_accept"] = list(map(int, acc))
+        if cfg.target_layers > 0:
+            report["committed"] = check_commit(case, gr, device)
     if sampling:
         st = sampling_checks(case, gr, device)
         say(f"stochastic verify checked: {st['tests']} tests, {st['draws']} draws, "

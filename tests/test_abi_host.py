@@ -187,3 +187,40 @@ def test_steady_state_kv_is_validated(lib):
     h1 = _head(replace(cfg.head, mode=C.MODE_EAGLE1))
     assert lib.eagle_draft_step(h1, kv, ts, 0, 1, None, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
     assert lib.eagle_tree_init(h1, kv, ts, 1, None) == E.EAGLE_EINVAL
+
+
+def test_target_pass_and_commit_are_validated(lib):
+    """The target pass needs every layer's weights and a final gain; its
+    workspace covers the B * positions verify rows; eagle_kv_commit refuses
+    misaligned buffers and bad shapes before any launch."""
+    cfg = C.CONFIGS["c1_8b_static"]
+    h, t = _head(cfg.head), _tree(cfg)
+    kv = _kv(cfg, list(cfg.n))
+    L = 3
+    layers = (E.eagle_layer * L)()
+    for l in range(L):
+        for f, _ in E.eagle_layer._fields_:
+            setattr(layers[l], f, 1 << 20)
+    tg = E.eagle_target()
+    tg.n_layers, tg.layers, tg.final_norm_g = L, layers, 1 << 20
+    ws = E.eagle_target_workspace_bytes(h, tg, kv, t)
+    assert ws >= cfg.B * cfg.positions * cfg.head.ffn * 2
+    for field, val in [("n_layers", 0), ("final_norm_g", None)]:
+        tb = E.eagle_target()
+        tb.n_layers, tb.layers, tb.final_norm_g = L, layers, 1 << 20
+        setattr(tb, field, val)
+        assert E.eagle_target_workspace_bytes(h, tb, kv, t) == 0, field
+    layers[1].w_down = None
+    assert E.eagle_target_workspace_bytes(h, tg, kv, t) == 0
+    layers[1].w_down = 1 << 20
+    ts = _tree(cfg, state=1 << 20, nbytes=1 << 30)
+    # null logits, k_tree without v_tree, workspace too small
+    assert lib.eagle_target_verify_logits(h, tg, kv, ts, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
+    assert lib.eagle_target_verify_logits(h, tg, kv, ts, 1 << 20, 1 << 20, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
+    assert lib.eagle_target_verify_logits(h, tg, kv, ts, 1 << 20, None, None, 1 << 20, 16, None) == E.EAGLE_ECAPACITY
+    # commit: misaligned destination, bad dtype, rows not a 16-byte multiple, no rows
+    a = 1 << 20
+    assert lib.eagle_kv_commit(ts, 8, 128, 0, a, a, a, a, a, 100, a + 2, a, None) == E.EAGLE_EINVAL
+    assert lib.eagle_kv_commit(ts, 8, 128, 9, a, a, a, a, a, 100, a, a, None) == E.EAGLE_EINVAL
+    assert lib.eagle_kv_commit(ts, 1, 4, 0, a, a, a, a, a, 100, a, a, None) == E.EAGLE_EINVAL
+    assert lib.eagle_kv_commit(ts, 8, 128, 0, a, a, a, a, a, 0, a, a, None) == E.EAGLE_EINVAL
