@@ -143,12 +143,158 @@ __global__ __launch_bounds__(256) void k_gemm_direct(GemmArgs a) {
   }
 }
 
+// 17..32 rows: the workgroup's 4 waves share one K range, so the activation
+// rows of each batch of U MFMA steps are staged once in LDS (double buffer)
+// and read by all four waves, while each wave streams its own 32 weight rows
+// through registers (double buffer); one barrier per batch.  Without the
+// sharing every wave re-reads all 32 activation rows from L2 (as many bytes
+// as its weights).  Rows past M re-read row M-1 (never stored).
+template <typename T, int MB, int NB, int U>
+__global__ __launch_bounds__(256) void k_gemm_shared(GemmArgs a) {
+  constexpr int VEC = DT<T>::VEC;
+  constexpr int KS = 4 * VEC;                  // K of one MFMA step
+  constexpr int STEP = U * KS;
+  constexpr int MT = 16 * MB;
+  constexpr int ROWB = STEP * (int)sizeof(T) + 16;
+  constexpr int PIECES = STEP / VEC;           // 16-byte pieces per row and batch
+  constexpr int PT = (MT * PIECES + 255) / 256;
+  __shared__ __attribute__((aligned(16))) char xl[2][MT * ROWB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int n_base = (blockIdx.x * 4 + wave) * (16 * NB);
+  const int k_begin = blockIdx.z * a.kps;
+  const int k_end = min(a.K, k_begin + a.kps);
+  const T* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = min(n_base + nb * 16 + c, a.N - 1);
+    const T* base;
+    int off;
+    if (n < a.nseg1) { base = (const T*)a.w[0]; off = 0; }
+    else if (n < a.nseg2) { base = (const T*)a.w[1]; off = a.nseg1; }
+    else { base = (const T*)a.w[2]; off = a.nseg2; }
+    wrow[nb] = base + (int64_t)(n - off) * a.K;
+  }
+  // this thread's staging pieces: row r, 16-byte piece j of the batch
+  const T* xrow0[PT];
+  const T* xrow1[PT];
+  int xj[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int p = min(tid + 256 * i, MT * PIECES - 1);
+    xj[i] = p % PIECES;
+    const int m = min(p / PIECES, a.M - 1);
+    xrow0[i] = row_ptr<T>(a.xs[0], m);
+    xrow1[i] = a.xs[1].base ? row_ptr<T>(a.xs[1], m) : xrow0[i];
+  }
+  auto stage = [&](int k, int len, int buf) {
+    u32x4 v[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int p = tid + 256 * i;
+      const int kk = k + xj[i] * VEC;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (p < MT * PIECES && xj[i] * VEC < len)
+        v[i] = ld16(kk < a.ksplit_x ? xrow0[i] + kk : xrow1[i] + (kk - a.ksplit_x));
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int p = tid + 256 * i;
+      if (p < MT * PIECES) st16(xl[buf] + (p / PIECES) * ROWB + xj[i] * 16, v[i]);
+    }
+  };
+  u32x4 wa[U][NB], wb[U][NB];
+  auto ldw = [&](int k, int len, u32x4(&w)[U][NB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u * KS < len)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) w[u][nb] = ld16(wrow[nb] + k + u * KS + g * VEC);
+  };
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const u32x4(&w)[U][NB], int len, int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u * KS < len) {
+        u32x4 xf[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xf[mb] = ld16(xl[buf] + (mb * 16 + c) * ROWB + (u * KS + g * VEC) * (int)sizeof(T));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = DT<T>::mma(w[u][nb], xf[mb], acc[nb][mb]);
+      }
+    }
+  };
+  // batches of STEP (the last one shorter: K spans are whole MFMA steps);
+  // the control flow is the same in every wave of the workgroup
+  int k = k_begin, buf = 0;
+  if (k < k_end) {
+    int len = min(STEP, k_end - k);
+    stage(k, len, 0);
+    ldw(k, len, wa);
+    __syncthreads();
+    while (true) {
+      const int k2 = k + len;
+      const int len2 = min(STEP, k_end - k2);
+      if (len2 > 0) { stage(k2, len2, buf ^ 1); ldw(k2, len2, wb); }
+      mma(wa, len, buf);
+      __syncthreads();
+      k = k2; len = len2; buf ^= 1;
+      if (len <= 0) break;
+      const int k3 = k + len;
+      const int len3 = min(STEP, k_end - k3);
+      if (len3 > 0) { stage(k3, len3, buf ^ 1); ldw(k3, len3, wa); }
+      mma(wb, len, buf);
+      __syncthreads();
+      k = k3; len = len3; buf ^= 1;
+      if (len <= 0) break;
+    }
+  }
+  if (n_base >= a.N) return;
+  float* P = a.P + (int64_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n_base + nb * 16 + 4 * g;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + c;
+      if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
+    }
+  }
+}
+
 // ----------------------------------------------------------------- planning
 static int kc_of(int dtype) { return dtype == EAGLE_BF16 ? 256 : 128; }
 
 GemmShape plan_gemm(int dtype, int M, int N, int K) {
   GemmShape s;
   if (big_gemm_ok(dtype, M, N, K)) return plan_gemm_big(M, N, K);
+  if (M > 16 && M <= 32) {
+    // activation-sharing kernel: waves of 2 n-blocks (32 columns), ~2048
+    // waves, K spans of whole MFMA steps
+    s.direct = 3;
+    s.MB = 2;
+    s.mtiles = 1;
+    s.NB = 2;
+    const int wcols = (N + 31) / 32;
+    s.ntiles = (wcols + 3) / 4;
+    const int ks = dtype == EAGLE_BF16 ? 32 : 16;
+    const int ksteps = (K + ks - 1) / ks;
+    int S = (2048 + wcols - 1) / wcols;
+    if (S > ksteps) S = ksteps;
+    if (S < 1) S = 1;
+    const int sps = (ksteps + S - 1) / S;
+    s.kps = sps * ks;
+    s.S = (K + s.kps - 1) / s.kps;
+    return s;
+  }
   if (M <= 32) {
     // direct kernel: waves of 2 n-blocks (32 columns); ~2048 waves, K spans
     // that are whole multiples of the 4-step unroll
@@ -208,15 +354,16 @@ void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st) {
     launch_gemm_big(a, s, st);
     return;
   }
+  if (s.direct == 3) {
+    dim3 grid(s.ntiles, 1, s.S), block(256);
+    if (dtype == EAGLE_BF16) hipLaunchKernelGGL((k_gemm_shared<bf16s, 2, 2, 4>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_gemm_shared<float, 2, 2, 4>), grid, block, 0, st, a);
+    return;
+  }
   if (s.direct) {
     dim3 grid(s.ntiles, 1, s.S), block(256);
-    if (dtype == EAGLE_BF16) {
-      if (s.MB == 1) hipLaunchKernelGGL((k_gemm_direct<bf16s, 1, 2>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((k_gemm_direct<bf16s, 2, 2>), grid, block, 0, st, a);
-    } else {
-      if (s.MB == 1) hipLaunchKernelGGL((k_gemm_direct<float, 1, 2>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((k_gemm_direct<float, 2, 2>), grid, block, 0, st, a);
-    }
+    if (dtype == EAGLE_BF16) hipLaunchKernelGGL((k_gemm_direct<bf16s, 1, 2>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_gemm_direct<float, 1, 2>), grid, block, 0, st, a);
     return;
   }
   if (dtype == EAGLE_BF16) {

@@ -19,9 +19,11 @@ struct GemmArgs {
 };
 struct GemmShape {
   int MB, NB, mtiles, ntiles, S, kps;
-  int direct;          // 1: barrier-free streaming (M <= 32), 2: MFMA-tiled big GEMM
+  int direct;          // 1: barrier-free streaming (M <= 16), 2: MFMA-tiled big GEMM,
+                       // 3: streaming with LDS-shared activation rows (17..32)
 };
-// plan_gemm picks the kernel: direct streaming (M <= 32), LDS-staged
+// plan_gemm picks the kernel: direct streaming (M <= 16), activation-sharing
+// streaming (17..32), LDS-staged
 // streaming (M < 64 or unsupported shape) or the MFMA-tiled big GEMM.
 // The A operand's split point (ksplit_x) must be a multiple of 64.
 GemmShape plan_gemm(int dtype, int M, int N, int K);
