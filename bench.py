@@ -4,10 +4,13 @@
 One "step" is one full round on resident inputs: tree init, gamma draft steps
 (fc, decoder layer with tree-masked attention, LM head + softmax/top-k), the
 tree expand/rerank after each, and greedy verification against synthetic
-target logits.  The metric is draft-tree nodes per second (nodes of the
-verify tree, root excluded, summed over the batch).
+target logits (workloads with a target model run the target's own pass over
+the tree instead; --verify sample verifies by speculative sampling).  The
+metric is draft-tree nodes per second (nodes of the verify tree, root
+excluded, summed over the batch).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--verify greedy|sample] [--no-cpu] [--no-breakdown]
 
 Prints one JSON line.  Besides the contract fields it carries
   roofline      the dominant kernel (the LM head with its fused top-k):
@@ -223,10 +226,11 @@ def main():
             if cfg.tree_attend:
                 gr.attend()
             ev[r][1].record()
+            vt = gr.target_logits() if gr.target is not None else tgt
             if sample is None:
-                gr.verify(tgt)
+                gr.verify(vt)
             else:
-                gr.verify_sample(tgt, *sample)
+                gr.verify_sample(vt, *sample)
             ev[r][2].record()
         torch.cuda.synchronize()
         tot = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in ev)
@@ -236,9 +240,13 @@ def main():
         round_stats = {"rounds": R, "round_us_p10": q(tot, 0.1), "round_us_p50": q(tot, 0.5),
                        "round_us_p90": q(tot, 0.9), "draft_us_p50": q(drf, 0.5),
                        "verify_us_p50": q(ver, 0.5)}
+        if gr.target is not None:
+            round_stats["verify_includes"] = "the target's pass over the tree"
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and cfg.target_layers > 0:
+        cpu = {"value": None, "skipped": "the oracle's target pass at this size is not a bounded sample"}
+    elif not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, weights, inp, target, args.cpu_seconds)
 
