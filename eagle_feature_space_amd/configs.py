@@ -144,6 +144,14 @@ CONFIGS = {
         gamma=4, top_k=4, template=STATIC_TREE_25, seed_w=1001, seed_in=2001,
         seed_t=3001, target_layers=32, seed_tm=4006,
         note="c1 with a 32-layer 8B-shaped target's tree-attention verification pass"),
+    # c2's round in the steady state: each request's cache holds 4096
+    # positions and 1..7 newly verified ones are ingested from the target's
+    # features before the round
+    "c7_8b_dynamic_steady": RoundCfg(
+        name="c7_8b_dynamic_steady", head=HEAD_8B, B=8, n=(4096,) * 8, new_range=(1, 7),
+        tree=TREE_DYNAMIC, gamma=6, top_k=10, top_m=60, inv_temp=C2_INV_TEMP, seed_w=1002,
+        seed_in=2007, seed_t=3007,
+        note="EAGLE-2 dynamic tree on the 8B head, B=8, cached n=4096 + 1..7 new positions"),
     "c5_8b_eagle3_steady": RoundCfg(
         name="c5_8b_eagle3_steady", head=HEAD_8B_E3, B=32, n_range=(256, 1024),
         new_range=(1, 8), tree=TREE_CHAIN, gamma=7, top_k=1, seed_w=1003,
@@ -226,6 +234,17 @@ SMALL_CONFIGS["s12_eagle3_steady_chain"] = RoundCfg(
     name="s12_eagle3_steady_chain", head=replace(_HEAD_SMALL, mode=MODE_EAGLE3), B=20,
     n_range=(0, 60), new_range=(1, 8), tree=TREE_CHAIN, gamma=3, top_k=1,
     seed_w=1112, seed_in=2112, seed_t=3112)
+
+# EAGLE-1 steady state: cached contexts plus 1..5 newly verified positions
+# ingested from the target's features (a dynamic tree, one empty cache; a
+# 20-request chain on the split-K kernels)
+SMALL_CONFIGS["s17_eagle1_steady_dynamic"] = RoundCfg(
+    name="s17_eagle1_steady_dynamic", head=_HEAD_SMALL, B=3, n=(0, 33, 90),
+    new_range=(1, 5), tree=TREE_DYNAMIC, gamma=3, top_k=4, top_m=12, inv_temp=4.0,
+    seed_w=1117, seed_in=2117, seed_t=3117)
+SMALL_CONFIGS["s18_eagle1_steady_chain"] = RoundCfg(
+    name="s18_eagle1_steady_chain", head=_HEAD_SMALL, B=20, n_range=(0, 50), new_range=(1, 5),
+    tree=TREE_CHAIN, gamma=3, top_k=1, seed_w=1118, seed_in=2118, seed_t=3118)
 
 # The target's verification pass: a static tree (52 rows, tiled kernels), a
 # dynamic tree with an empty context, an fp32 LayerNorm / GELU head, and a

@@ -391,7 +391,8 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g, bool target = 
     P = std::max(P, gemm_bytes(h->dtype, M, d, h->ffn));
   }
   w.P = bp.take(P);
-  const int Mrow = std::max(Mr, h->mode == EAGLE_MODE_3 ? (int)ingest_rows(kv) : 0);
+  const bool ingests = h->mode == EAGLE_MODE_3 || kv->n_new;
+  const int Mrow = std::max(Mr, ingests ? (int)ingest_rows(kv) : 0);
   w.y32 = bp.take((size_t)Mrow * d * 4);
   w.stats = bp.take((size_t)Mrow * ((d + 255) / 256) * 2 * 4);
   w.ap = plan_attn(h, kv);
@@ -418,11 +419,12 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g, bool target = 
   w.t_kv = bp.take((size_t)Mt * 4);
   w.t_pos = bp.take((size_t)Mt * 4);
   w.t_mask = bp.take((size_t)Mt * 8);
-  if (h->mode == EAGLE_MODE_3) {
+  if (ingests) {
     const int Tn = (int)ingest_rows(kv);
+    const int kin = h->mode == EAGLE_MODE_3 ? 3 * d : 2 * d;
     w.x_in = bp.take((size_t)Tn * d * e);
     w.xn_in = bp.take((size_t)Tn * d * e);
-    w.P_in = bp.take(std::max(gemm_bytes(h->dtype, Tn, d, 3 * d),
+    w.P_in = bp.take(std::max(gemm_bytes(h->dtype, Tn, d, kin),
                               gemm_bytes(h->dtype, Tn, 2 * kvd, d)));
   } else {
     w.x_in = w.xn_in = w.P_in = 0;
@@ -580,6 +582,50 @@ void run_rows(const eagle_head* h, int ep, const RowsArgs& r, hipStream_t st) {
   ProfScope ps(EAGLE_PROF_GEMM, (double)esz(h) * ((double)r.g.N * r.g.K + (double)r.g.M * r.g.K),
                2.0 * r.g.M * (double)r.g.N * r.g.K, st);
   launch_gemm_rows(h->dtype, ep, r, st);
+}
+
+// Ingest of verified context positions (all of them, or each request's newest
+// n_new[b] in the steady state): their layer inputs, then N1 and the key /
+// value projections with RoPE, written to k_ctx / v_ctx at each position's
+// own row.  EAGLE-3: x_j = [l;m;h]_j W_fuse^T + emb(t_{j+1}), kept in x_in (the
+// root row of each request is its last position).  EAGLE-1: x_j =
+// fc([f_{j-1} ; emb(t_j)]) from the target's features (only the K/V are kept).
+void ingest(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, const void* lmh,
+            const int32_t* ctx_tokens, hipStream_t st) {
+  const int d = h->d, kvd = h->n_kv_heads * h->head_dim;
+  const int Tn = (int)ingest_rows(kv);
+  float* Pin = (float*)(ws + w.P_in);
+  GemmShape sh;
+  if (h->mode == EAGLE_MODE_3) {
+    gemm(h, rs(lmh, nullptr, 3 * d), kNone, 3 * d, Tn, d, 3 * d, h->w_fuse, nullptr, nullptr, d,
+         d, Pin, &sh, st);
+    reduce(h, Pin, sh.S, Tn, d, kNone, rs(h->emb, ctx_tokens, d, h->vocab), ws + w.x_in, kNone,
+           ws + w.xn_in, 1, st);
+  } else {
+    gemm(h, rs(lmh, nullptr, d), rs(h->emb, ctx_tokens, d, h->vocab), d, Tn, d, 2 * d, h->w_fc,
+         nullptr, nullptr, d, d, Pin, &sh, st);
+    reduce(h, Pin, sh.S, Tn, d, kNone, kNone, nullptr, kNone, ws + w.xn_in, 1, st);
+  }
+  gemm(h, rs(ws + w.xn_in, nullptr, d), kNone, d, Tn, 2 * kvd, d, h->w_k, h->w_v, nullptr, kvd,
+       2 * kvd, Pin, &sh, st);
+  QkvArgs q;
+  q.P = Pin;
+  q.S = sh.S;
+  q.M = Tn;
+  q.Hq = 0;
+  q.Hkv = h->n_kv_heads;
+  q.hd = h->head_dim;
+  q.theta = h->rope_theta;
+  q.cu_row = kv->n_new ? kv->cu_new : kv->cu_n;
+  q.n = kv->n;
+  q.n_new = kv->n_new;
+  q.cu_n = kv->cu_n;
+  q.total_rows = kv->total_n;
+  q.B = kv->B;
+  q.k = kv->k_ctx;
+  q.v = kv->v_ctx;
+  ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
+  launch_epi_qkv(h->dtype, q, st);
 }
 
 // One pre-norm decoder layer over io.M rows (io.W per request), from the
@@ -782,7 +828,6 @@ int eagle_tree_init(const eagle_head* head, const eagle_kv* kv, const eagle_tree
   if ((s = check_tree_state(tree, g))) return s;
   if (!root_tokens) return EAGLE_EINVAL;
   if (head->mode == EAGLE_MODE_3 && ingest_rows(kv) < kv->B) return EAGLE_EINVAL;
-  if (head->mode != EAGLE_MODE_3 && kv->n_new) return EAGLE_EINVAL;
   // EAGLE-3 root rows: the last ingested row of each request
   launch_tree_init(tree_dev(tree, g), g.B, head->mode == EAGLE_MODE_3, head->vocab, root_tokens,
                    kv->n, kv->n_new ? kv->cu_new : kv->cu_n, (hipStream_t)stream);
@@ -805,7 +850,7 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   const bool e3 = h->mode == EAGLE_MODE_3;
   if (step == 0 && !e3 && !f_root) return EAGLE_EINVAL;
   if (step == 0 && e3 && (!lmh || !ctx_tokens || ingest_rows(kv) < kv->B)) return EAGLE_EINVAL;
-  if (!e3 && kv->n_new) return EAGLE_EINVAL;
+  if (step == 0 && !e3 && kv->n_new && (!lmh || !ctx_tokens)) return EAGLE_EINVAL;
   if (!ws_v) return EAGLE_EINVAL;
   const Ws w = plan_ws(h, kv, g);
   if (ws_bytes < w.total) return EAGLE_ECAPACITY;
@@ -827,10 +872,10 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   // one kernel with its epilogue fused; N1 / N2 are folded through the next
   // projection (operand h * g, result rows scaled by rstd from the statistics).
   const bool rows = rows_gemm_ok(M, d, 32) && h->norm == EAGLE_NORM_RMS;
-  const int kvd = h->n_kv_heads * h->head_dim;
   const float* nst = g_stats;          // row statistics of h (row path)
   int nblk = (d + 255) / 256;
   if (!e3) {
+    if (step == 0 && kv->n_new) ingest(h, kv, ws, w, lmh, ctx_tokens, st);
     const void* fsrc = step == 0 ? f_root : kv->feat_slot;
     const RowSrc xf = rs(fsrc, td.row_pidx, d, step == 0 ? (int64_t)B : (int64_t)B * kSlots);
     const RowSrc xe = rs(h->emb, td.row_tok, d, h->vocab);
@@ -854,37 +899,9 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
     reduce(h, nullptr, 0, M, d, rs(kv->feat_slot, td.row_pidx, d, (int64_t)B * kSlots), rs(h->emb, td.row_tok, d, h->vocab),
            hbuf, kNone, rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
   } else {
-    // ingest of the new verified positions: g = [l;m;h] W_fuse^T, x = g + emb(t_next)
-    const int Tn = (int)ingest_rows(kv);
-    float* Pin = (float*)(ws + w.P_in);
-    gemm(h, rs(lmh, nullptr, 3 * d), kNone, 3 * d, Tn, d, 3 * d, h->w_fuse, nullptr, nullptr, d,
-         d, Pin, &sh, st);
-    reduce(h, Pin, sh.S, Tn, d, kNone, rs(h->emb, ctx_tokens, d, h->vocab), ws + w.x_in, kNone,
-           ws + w.xn_in, 1, st);
-    gemm(h, rs(ws + w.xn_in, nullptr, d), kNone, d, Tn, 2 * kvd, d, h->w_k, h->w_v, nullptr, kvd,
-         2 * kvd, Pin, &sh, st);
-    QkvArgs q;
-    q.P = Pin;
-    q.S = sh.S;
-    q.M = Tn;
-    q.Hq = 0;
-    q.Hkv = h->n_kv_heads;
-    q.hd = h->head_dim;
-    q.theta = h->rope_theta;
-    q.cu_row = kv->n_new ? kv->cu_new : kv->cu_n;
-    q.n = kv->n;
-    q.n_new = kv->n_new;
-    q.cu_n = kv->cu_n;
-    q.total_rows = kv->total_n;
-    q.B = B;
-    q.k = kv->k_ctx;
-    q.v = kv->v_ctx;
-    {
-      ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
-      launch_epi_qkv(h->dtype, q, st);
-    }
+    ingest(h, kv, ws, w, lmh, ctx_tokens, st);
     // root rows = each request's last verified position
-    reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, Tn), kNone, hbuf, kNone,
+    reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, ingest_rows(kv)), kNone, hbuf, kNone,
            rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
   }
 

@@ -80,6 +80,9 @@ class GpuRound:
             self.v_ctx = to_dev(inputs.v_ctx, self.dev) if total else None
             self.f_root = to_dev(inputs.f_root, self.dev)
             self.lmh = self.ctx_tokens = None
+            if steady:   # the target's features and tokens of the new positions
+                self.lmh = to_dev(inputs.lmh, self.dev)
+                self.ctx_tokens = to_dev(inputs.ctx_tokens.astype(np.int32), self.dev)
         self.k_slot = torch.zeros((B * E.MAX_SLOTS, h.n_kv, h.head_dim), dtype=self.dt, device=self.dev)
         self.v_slot = torch.zeros_like(self.k_slot)
         self.feat_slot = torch.zeros((B * E.MAX_SLOTS, h.d), dtype=self.dt, device=self.dev)

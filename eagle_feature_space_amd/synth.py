@@ -159,7 +159,7 @@ def round_inputs(r: RoundCfg) -> RoundInputs:
     total = int(cu[-1])
     s = r.seed_in
     t_root = integers(s, _T["t_root"], (r.B,), 0, h.vocab - 1)
-    if h.mode == MODE_EAGLE1:
+    if h.mode == MODE_EAGLE1 and r.new_range is None:
         return RoundInputs(
             n=n, cu_n=cu, t_root=t_root,
             k_ctx=normal(s, _T["k_ctx"], (total, h.n_kv, h.head_dim), bf16=bf),
@@ -181,6 +181,13 @@ def round_inputs(r: RoundCfg) -> RoundInputs:
             k[cu[b] + n_old[b]:cu[b + 1]] = 0
             v[cu[b] + n_old[b]:cu[b + 1]] = 0
         ctx = integers(s, _T["ctx_tokens"], (int(cun[-1]),), 0, h.vocab - 1)
+        if h.mode == MODE_EAGLE1:
+            # the target's features of the positions before the new ones, the
+            # tokens at them; the root row keeps its own (f_root, t_root)
+            return RoundInputs(n=n, cu_n=cu, t_root=t_root, k_ctx=k, v_ctx=v,
+                               f_root=normal(s, _T["f_root"], (r.B, h.d), bf16=bf),
+                               lmh=normal(s, _T["lmh"], (int(cun[-1]), h.d), bf16=bf),
+                               ctx_tokens=ctx, n_new=tau.astype(np.int32), cu_new=cun)
         ctx[cun[1:] - 1] = t_root
         return RoundInputs(n=n, cu_n=cu, t_root=t_root, k_ctx=k, v_ctx=v,
                            lmh=normal(s, _T["lmh"], (int(cun[-1]), 3 * h.d), bf16=bf),

@@ -104,15 +104,20 @@ typedef struct eagle_head {
  * layer runs over a cache).  Requests are packed without padding (explainer,
  * "Serving batch": variable-length blocks may be packed).
  *   k_ctx, v_ctx  [total_n][Hkv][hd]  context K/V (rotated); read by the
- *                                     attention, written by the EAGLE-3 ingest
+ *                                     attention, written by the ingest
  *   k_slot,v_slot [B][64][Hkv][hd]    K/V of every expanded tree node (slot)
  *   feat_slot     [B][64][d]          layer output of every expanded node
- * EAGLE-3 steady state ("Speculative Decoding Deep Dive III", EAGLE-3
- * example: each round feeds the fused features of the tokens the target has
- * just verified; the draft cache of older positions is kept).  With n_new set, request b already holds the K/V of its first
- * n[b] - n_new[b] positions in k_ctx/v_ctx, and step 0 ingests only its last
- * n_new[b] >= 1 positions (the accepted path and the target's token).  With
- * n_new NULL every one of the n[b] positions is ingested (a first round).
+ * Steady state ("Speculative Decoding Deep Dive III", EAGLE-3 example: each
+ * round feeds the fused features of the tokens the target has just verified;
+ * EAGLE-1 "Inference": the drafter reads the target's features of the
+ * verified prefix; the draft cache of older positions is kept).  With n_new
+ * set, request b already holds the K/V of its first n[b] - n_new[b]
+ * positions in k_ctx/v_ctx, and step 0 ingests only its last n_new[b] >= 1
+ * positions (EAGLE-3: the accepted path and the target's token; EAGLE-1: the
+ * positions verified since the last round, whose rows are
+ * fc([f_{j-1} ; emb(t_j)]) from the target's features; the EAGLE-1 root row
+ * stays at position n[b]).  With n_new NULL an EAGLE-3 round ingests every
+ * one of the n[b] positions (a first round) and an EAGLE-1 round none.
  * The caller keeps 1 <= n_new[b] <= n[b] and cu_new the prefix sum of n_new;
  * rows that break this are skipped on the device, never written outside
  * k_ctx/v_ctx.
@@ -125,7 +130,7 @@ typedef struct eagle_kv {
   const int32_t *cu_n; /* device [B+1] */
   void *k_ctx, *v_ctx, *k_slot, *v_slot, *feat_slot; /* device */
   int64_t total_new;      /* host copy of sum_b n_new[b] (0 when n_new NULL) */
-  const int32_t *n_new;   /* device [B] or NULL (EAGLE-3 only)              */
+  const int32_t *n_new;   /* device [B] or NULL                             */
   const int32_t *cu_new;  /* device [B+1] or NULL; required with n_new      */
 } eagle_kv;
 
@@ -211,7 +216,10 @@ int eagle_tree_init(const eagle_head *head, const eagle_kv *kv,
  * One draft step ("The recurrence, written out"): for every row of the step
  * (node u of request b at depth `step`):
  *   EAGLE-1: x = [f ; emb(tok(u))] with f = f_root[b] for the root, else the
- *            layer output stored in the parent's slot; h = x W_fc^T
+ *            layer output stored in the parent's slot; h = x W_fc^T.  In the
+ *            steady state step 0 first ingests the new positions j:
+ *            h_j = [lmh_j ; emb(ctx_tokens[j])] W_fc^T, K/V of N1(h_j) to
+ *            their rows of k_ctx/v_ctx.
  *   EAGLE-3: step 0 ingests every new verified position j of every request
  *            (all n[b] of them, or the last n_new[b] in the steady state):
  *            g_j = lmh_j W_fuse^T, x_j = g_j + emb(ctx_tokens[j]); K/V of each
@@ -226,9 +234,11 @@ int eagle_tree_init(const eagle_head *head, const eagle_kv *kv,
  * f_root:     device [B][d]           (EAGLE-1, step 0; else unused)
  * lmh:        device [T][3d]          (EAGLE-3, step 0; l, m, h concatenated;
  *             T = total_new in the steady state, else total_n; packed by
- *             cu_new, else cu_n)
- * ctx_tokens: device [T] int32        (EAGLE-3, step 0; token after each
- *             ingested position, the anchor token last)
+ *             cu_new, else cu_n); EAGLE-1 steady state: [total_new][d], the
+ *             target's feature of the position before each new one
+ * ctx_tokens: device [T] int32        (step 0 of an ingest; EAGLE-3: token
+ *             after each ingested position, the anchor token last; EAGLE-1:
+ *             the token at each new position)
  * logits_out: optional device [M][V] fp32 (M = B * eagle_step_rows)
  * feat_out:   optional device [M][d] in the head dtype (layer outputs)
  * ws:         device workspace of at least eagle_workspace_bytes

@@ -27,6 +27,10 @@ Readings (listed in the design notes):
     Decoding Deep Dive III", EAGLE-3 example: each round feeds the fused
     features of the verified tokens): only the positions verified since the
     last round are ingested; their K/V join the cache after the old ones.
+  * EAGLE-1 steady state (the same page, EAGLE-1 "Inference": the drafter
+    reads the target's features of the verified prefix): the newest positions
+    are ingested from the target's features f_{j-1} and tokens t_j through fc
+    and the layer's key/value projections; the round's root row stays at n_b.
 """
 from __future__ import annotations
 
@@ -68,6 +72,17 @@ def ingest(head: DraftHead, lmh, ctx_tokens, pos0=0):
     return K, V, x[-1]
 
 
+def ingest_features(head: DraftHead, feats, tokens, pos0):
+    """EAGLE-1 verified positions pos0 .. pos0 + n - 1 of ONE request: the row
+    of position j is fc([f_{j-1} ; emb(t_j)]) (the target's feature of the
+    position before it, the token at it), as for every context position.
+    feats [n, d], tokens [n].  Returns (K [n, Hkv, hd], V [n, Hkv, hd])."""
+    n = feats.shape[0]
+    h = head.fc_input(feats, tokens)
+    _, K, V = head.qkv(h, np.arange(pos0, pos0 + n))
+    return K, V
+
+
 @dataclass
 class StepTrace:
     rows: list                      # per request: list of row tuples (RequestTree.rows)
@@ -99,7 +114,9 @@ def run_round(cfg, head: DraftHead, n, t_root, k_ctx=None, v_ctx=None,
     [sum n, 3d] and ctx_tokens [sum n] -- or, in the steady state (n_new
     given), the K/V of each request's first n - n_new positions in k_ctx /
     v_ctx (segments of n rows) and lmh / ctx_tokens for its newest n_new
-    positions only, packed.  target [B, T, |V|] are the verification logits
+    positions only, packed (EAGLE-1: lmh [sum n_new, d] holds the target
+    features of the positions before them, ctx_tokens the tokens at them;
+    f_root as always).  target [B, T, |V|] are the verification logits
     (verify is skipped when None).
     teacher(step) -> (ids, conf) makes the tree follow someone else's
     discrete choices (teacher forcing); the oracle's own logits are still
@@ -127,6 +144,13 @@ def run_round(cfg, head: DraftHead, n, t_root, k_ctx=None, v_ctx=None,
             ctxK.append(K)
             ctxV.append(V)
             root_h.append(hl)
+        elif cun is not None:
+            # EAGLE-1 steady state: lmh holds the target features f_{j-1} and
+            # ctx_tokens the tokens t_j of the newest n_new[b] positions
+            n_old = int(n[b]) - int(n_new[b])
+            K, V = ingest_features(head, lmh[cun[b]:cun[b + 1]], ctx_tokens[cun[b]:cun[b + 1]], n_old)
+            ctxK.append(np.concatenate([k_ctx[lo:lo + n_old], K]))
+            ctxV.append(np.concatenate([v_ctx[lo:lo + n_old], V]))
         else:
             ctxK.append(k_ctx[lo:hi])
             ctxV.append(v_ctx[lo:hi])

@@ -26,7 +26,7 @@ from oracle import tree as OT
 from oracle import verify as OV
 from oracle.head import DraftHead
 from oracle.head import attend as o_attend
-from oracle.round import ingest, row_forward
+from oracle.round import ingest, ingest_features, row_forward
 
 TOL = 2e-2          # logits: max relative error (bf16 inputs, fp32 accumulation)
 U64 = (1 << 64) - 1
@@ -66,7 +66,7 @@ class Case:
     def ctx(self, gr=None):
         """Per-request context K/V (fp32) the attention reads."""
         cu = self.inp.cu_n
-        if self.cfg.head.mode == C.MODE_EAGLE3:
+        if self.cfg.head.mode == C.MODE_EAGLE3 or self.inp.n_new is not None:
             from eagle_feature_space_amd.runner import to_f32
             K, V = to_f32(gr.k_ctx), to_f32(gr.v_ctx)
         else:
@@ -91,6 +91,18 @@ def check_step(case: Case, gr, snaps, s, rows=None, report=None):
     sel = range(M) if rows is None else rows
     worst = dict(logit=0.0, feat=0.0, kv=0.0, ctxkv=0.0, conf=0.0)
     ingested = {}
+    if not e3 and s == 0 and inp.n_new is not None:
+        # EAGLE-1 steady state: the newest positions' K/V from the target's
+        # features, the cached ones untouched
+        for b in range(B):
+            lo, hi = inp.cu_new[b], inp.cu_new[b + 1]
+            n_old = int(inp.n[b]) - int(inp.n_new[b])
+            ck, cv = ctx[b]
+            old = slice(cu[b], cu[b] + n_old)
+            assert np.array_equal(ck[:n_old], synth.f32(inp.k_ctx[old])), f"request {b}: old K changed"
+            assert np.array_equal(cv[:n_old], synth.f32(inp.v_ctx[old])), f"request {b}: old V changed"
+            K, V = ingest_features(hd, synth.f32(inp.lmh[lo:hi]), inp.ctx_tokens[lo:hi], n_old)
+            worst["ctxkv"] = max(worst["ctxkv"], rel_err(ck[n_old:], K), rel_err(cv[n_old:], V))
     for m in sel:
         b = m // W
         pidx = int(snap.rows["pidx"][m])

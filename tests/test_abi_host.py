@@ -165,8 +165,8 @@ def test_rejects_bad_arguments_before_launch(lib):
 
 
 def test_steady_state_kv_is_validated(lib):
-    """EAGLE-3 steady state: n_new needs cu_new and 1 <= total_new / B; an
-    EAGLE-1 head refuses it; its workspace is sized by the new rows only."""
+    """Steady state: n_new needs cu_new and 1 <= total_new / B; step 0 needs
+    the ingest inputs (EAGLE-1 too); the workspace is sized by the new rows."""
     cfg = C.CONFIGS["c5_8b_eagle3_steady"]
     n = [600] * cfg.B
     h, t = _head(cfg.head), _tree(cfg)
@@ -185,8 +185,9 @@ def test_steady_state_kv_is_validated(lib):
     assert E.eagle_workspace_bytes(h, kb, t) == 0
     ts = _tree(cfg, state=1 << 20, nbytes=1 << 30)
     h1 = _head(replace(cfg.head, mode=C.MODE_EAGLE1))
+    # EAGLE-1 steady state without its ingest inputs (target features, tokens)
     assert lib.eagle_draft_step(h1, kv, ts, 0, 1, None, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
-    assert lib.eagle_tree_init(h1, kv, ts, 1, None) == E.EAGLE_EINVAL
+    assert lib.eagle_draft_step(h1, kv, ts, 0, 1, 1 << 20, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
 
 
 def test_target_pass_and_commit_are_validated(lib):

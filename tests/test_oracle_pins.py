@@ -17,7 +17,7 @@ from oracle import head as H
 from oracle import tree as T
 from oracle import target as TG
 from oracle import verify as VF
-from oracle.round import run_round
+from oracle.round import ingest_features, run_round
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -693,6 +693,40 @@ def test_eagle3_steady_state_equals_full_causal_recompute():
             t = int(np.argmax(hd.lm_head(a[None])[0]))
             assert steady.final[b]["tok"][s + 1] == t
             xs.append(a + hd.w["emb"][t])
+
+
+def test_eagle1_steady_state_equals_full_ingest():
+    """EAGLE-1 steady state: with every context position's K/V produced by
+    ingesting (f_{j-1}, t_j), a round that takes the first n - tau positions'
+    K/V as given and ingests only the newest tau (at their own positions)
+    drafts exactly what the round over the fully ingested context drafts."""
+    cfg = _round_cfg(T.DYNAMIC, TINY, B=2, n=(8, 5), gamma=3, top_k=3, top_m=7)
+    hd = _head(TINY, np.float64)
+    inp = _inputs64(cfg)
+    rng = np.random.default_rng(5)
+    n = inp["n"]
+    cu = np.concatenate([[0], np.cumsum(n)])
+    feats = rng.standard_normal((cu[-1], TINY.d))
+    toks = rng.integers(0, TINY.vocab, cu[-1])
+    k_full = np.zeros((cu[-1], TINY.n_kv, TINY.head_dim))
+    v_full = np.zeros_like(k_full)
+    for b in range(cfg.B):
+        K, V = ingest_features(hd, feats[cu[b]:cu[b + 1]], toks[cu[b]:cu[b + 1]], 0)
+        k_full[cu[b]:cu[b + 1]], v_full[cu[b]:cu[b + 1]] = K, V
+    full = run_round(cfg, hd, n=n, t_root=inp["t_root"], k_ctx=k_full, v_ctx=v_full,
+                     f_root=inp["f_root"])
+    tau = np.array([3, 5], np.int32)          # request 1 ingests its whole context
+    k_old, v_old = k_full.copy(), v_full.copy()
+    sel = np.concatenate([np.arange(cu[b + 1] - tau[b], cu[b + 1]) for b in range(cfg.B)])
+    k_old[sel] = 0
+    v_old[sel] = 0
+    steady = run_round(cfg, hd, n=n, t_root=inp["t_root"], k_ctx=k_old, v_ctx=v_old,
+                       f_root=inp["f_root"], lmh=feats[sel], ctx_tokens=toks[sel], n_new=tau)
+    for s in range(cfg.gamma):
+        np.testing.assert_allclose(steady.steps[s].feat, full.steps[s].feat, rtol=1e-10, atol=1e-10)
+        np.testing.assert_array_equal(steady.steps[s].ids, full.steps[s].ids)
+    for b in range(cfg.B):
+        assert list(steady.final[b]["tok"]) == list(full.final[b]["tok"])
 
 
 def test_oracle_float32_tracks_float64():
