@@ -54,7 +54,8 @@ class eagle_tree(ctypes.Structure):
     _fields_ = [("kind", c_int32), ("B", c_int32), ("gamma", c_int32), ("top_k", c_int32),
                 ("top_m", c_int32), ("n_template", c_int32),
                 ("template_parent", ctypes.POINTER(c_int32)), ("inv_temp", c_float),
-                ("state", c_void_p), ("state_bytes", c_size_t)]
+                ("state", c_void_p), ("state_bytes", c_size_t),
+                ("sample_seed", ctypes.c_uint64), ("sample", c_int32)]
 
 
 _LAYOUT_FIELDS = ("pool_tok", "pool_parent", "pool_depth", "pool_slot", "pool_conf", "pool_value",

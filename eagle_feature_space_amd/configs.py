@@ -68,6 +68,9 @@ class RoundCfg:
     # its embedding and LM head) produce the target logits (0: synthetic logits)
     target_layers: int = 0
     seed_tm: int = 0
+    # sampled drafting: children drawn by Gumbel-top-k with this 64-bit round
+    # seed (None: the top_k by logit)
+    sample_seed: Optional[int] = None
     tree: int = TREE_CHAIN
     gamma: int = 4                    # draft depth = number of draft steps
     top_k: int = 1
@@ -152,6 +155,13 @@ CONFIGS = {
         tree=TREE_DYNAMIC, gamma=6, top_k=10, top_m=60, inv_temp=C2_INV_TEMP, seed_w=1002,
         seed_in=2007, seed_t=3007,
         note="EAGLE-2 dynamic tree on the 8B head, B=8, cached n=4096 + 1..7 new positions"),
+    # c2 with sampled drafting: each node's 10 children drawn without
+    # replacement (Gumbel-top-k) instead of its top 10
+    "c8_8b_dynamic_sampled": RoundCfg(
+        name="c8_8b_dynamic_sampled", head=HEAD_8B, B=8, n=(4096,) * 8, tree=TREE_DYNAMIC,
+        gamma=6, top_k=10, top_m=60, inv_temp=C2_INV_TEMP, seed_w=1002, seed_in=2002,
+        seed_t=3002, sample_seed=0x5EED0000C0FFEE,
+        note="c2 with sampled drafting (Gumbel-top-k children)"),
     "c5_8b_eagle3_steady": RoundCfg(
         name="c5_8b_eagle3_steady", head=HEAD_8B_E3, B=32, n_range=(256, 1024),
         new_range=(1, 8), tree=TREE_CHAIN, gamma=7, top_k=1, seed_w=1003,
@@ -245,6 +255,19 @@ SMALL_CONFIGS["s17_eagle1_steady_dynamic"] = RoundCfg(
 SMALL_CONFIGS["s18_eagle1_steady_chain"] = RoundCfg(
     name="s18_eagle1_steady_chain", head=_HEAD_SMALL, B=20, n_range=(0, 50), new_range=(1, 5),
     tree=TREE_CHAIN, gamma=3, top_k=1, seed_w=1118, seed_in=2118, seed_t=3118)
+
+# Sampled drafting (Gumbel-top-k over Philox noise) on every LM-head path:
+# fused epilogue at <= 32 rows, the 33..63-row kernel, and the tiled GEMM with
+# logits partials from 64 rows on
+SMALL_CONFIGS["s19_sampled_dynamic"] = RoundCfg(
+    name="s19_sampled_dynamic", head=_HEAD_SMALL, B=3, n=(60, 1, 130), tree=TREE_DYNAMIC,
+    gamma=4, top_k=4, top_m=12, inv_temp=4.0, seed_w=1119, seed_in=2119, seed_t=3119,
+    sample_seed=0x0123456789ABCDEF)
+for _i, _b in enumerate((40, 70)):
+    SMALL_CONFIGS[f"s20_sampled_chain_b{_b}"] = RoundCfg(
+        name=f"s20_sampled_chain_b{_b}", head=replace(_HEAD_SMALL, vocab=3008), B=_b,
+        n=tuple((5 * j + _b) % 37 for j in range(_b)), tree=TREE_CHAIN, gamma=2, top_k=1,
+        seed_w=1120 + _i, seed_in=2120 + _i, seed_t=3120 + _i, sample_seed=0xFEEDFACE + _i)
 
 # The target's verification pass: a static tree (52 rows, tiled kernels), a
 # dynamic tree with an empty context, an fp32 LayerNorm / GELU head, and a

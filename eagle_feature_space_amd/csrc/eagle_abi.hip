@@ -38,6 +38,7 @@ int build_geo(const eagle_tree* t, Geo* g) {
   if (t->B < 1 || t->gamma < 1 || t->top_k < 1) return EAGLE_EINVAL;
   if (t->top_k > EAGLE_MAX_TOPK) return EAGLE_EUNSUPPORTED;
   if (!(t->inv_temp > 0.f)) return EAGLE_EINVAL;
+  if (t->sample != 0 && t->sample != 1) return EAGLE_EINVAL;
   g->kind = t->kind;
   g->B = t->B;
   g->gamma = t->gamma;
@@ -339,7 +340,7 @@ AttnPlan plan_attn(const eagle_head* h, const eagle_kv* kv) {
 struct Ws {
   size_t h, hn, h1, h1n, f, q, o, act, P, y32, stats, logits;
   size_t rs0, rs1;   // row-complete path (M <= 16): per-block row statistics
-  size_t att_o, att_ml, lm_max, lm_sum, lm_id, lm_val;
+  size_t att_o, att_ml, lm_max, lm_sum, lm_id, lm_val, lm_lg;
   size_t tk, tv, t_tok, t_kv, t_pos, t_mask;
   size_t x_in, xn_in, P_in;
   size_t total;
@@ -408,6 +409,7 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g, bool target = 
   w.lm_sum = bp.take((size_t)ls.ntiles * Mmax * 4);
   w.lm_id = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
   w.lm_val = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
+  w.lm_lg = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
   w.tk = bp.take((size_t)g.B * kSlots * kvd * e);
   w.tv = bp.take((size_t)g.B * kSlots * kvd * e);
   {
@@ -940,6 +942,14 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   la.part_sum = (float*)(ws + w.lm_sum);
   la.part_id = (int*)(ws + w.lm_id);
   la.part_val = (float*)(ws + w.lm_val);
+  if (tree->sample) {
+    la.gumbel = 1;
+    la.seed_lo = (uint32_t)(tree->sample_seed & 0xFFFFFFFFu);
+    la.seed_hi = (uint32_t)(tree->sample_seed >> 32);
+    la.row_node = td.row_node;
+    la.rows_per_req = W;
+    la.part_logit = (float*)(ws + w.lm_lg);
+  }
   if (big_gemm_ok(h->dtype, M, h->vocab, d)) {
     // MFMA-bound: tiled GEMM into fp32 logits, then tile partials
     float* lg = logits_out ? logits_out : (float*)(ws + w.logits);
@@ -983,6 +993,7 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   ma.topk_conf = td.topk_conf;
   ma.lse = td.lse;
   ma.vocab = h->vocab;
+  ma.part_logit = la.part_logit;
   {
     ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
     launch_topk_merge(ma, st);

@@ -160,6 +160,15 @@ struct LmArgs {
   float* part_sum;        // [ntiles][M]
   int* part_id;           // [ntiles][M][top_k]
   float* part_val;        // [ntiles][M][top_k]
+  // sampled drafting (Gumbel-top-k): the top-k are taken by the key
+  // s * logit + G, G = -log(-log(u)), u from Philox4x32-10 (key = seed,
+  // counter = (id / 4, row key, 0, 0)); row key = (m / rows_per_req) * 1024 +
+  // row_node[m].  part_val then holds keys and part_logit the logits.
+  int gumbel = 0;
+  uint32_t seed_lo = 0, seed_hi = 0;
+  const int32_t* row_node = nullptr;
+  int rows_per_req = 1;
+  float* part_logit = nullptr;  // [ntiles][M][top_k]
 };
 struct LmShape {
   int MB, mtiles, ntiles, cols;
@@ -181,6 +190,7 @@ struct MergeArgs {
   float* topk_conf;       // [M][top_k]
   float* lse;             // [M]
   int vocab;              // ids are clamped to [0, vocab)
+  const float* part_logit = nullptr;  // Gumbel-top-k: candidates' logits (part_val = keys)
 };
 void launch_topk_merge(const MergeArgs& a, hipStream_t st);
 

@@ -89,8 +89,38 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   lm_epilogue<T, MB, NB>(a, acc, m0, lds);
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64-bit multiplies and a word permutation, the key bumped by the Weyl
+// constants after each round.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Standard Gumbel variable of vocabulary id `id` in the row with key `rk`:
+// u = ((bits >> 9) + 0.5) 2^-23 in (0, 1), G = -log(-log(u)), fp32.
+__device__ __forceinline__ float gumbel_of(const LmArgs& a, uint32_t rk, int id) {
+  const uint4 w = philox4x32_10(make_uint4((uint32_t)id >> 2, rk, 0u, 0u), a.seed_lo, a.seed_hi);
+  const uint32_t sel = id & 3;
+  const uint32_t bits = sel == 0 ? w.x : (sel == 1 ? w.y : (sel == 2 ? w.z : w.w));
+  const float u = ((float)(bits >> 9) + 0.5f) * 1.1920928955078125e-07f;   // 2^-23
+  return -logf(-logf(u));
+}
+
+__device__ __forceinline__ uint32_t row_key_of(const LmArgs& a, int m) {
+  return (uint32_t)((m / a.rows_per_req) * 1024 + a.row_node[m]);
+}
+
 // Epilogue shared by both LM-head kernels: optional raw logits, then per row
-// the tile max, tile sum of exp(s (l - max)) and the tile top-k.
+// the tile max, tile sum of exp(s (l - max)) and the tile top-k (by logit, or
+// by the Gumbel key when drafting samples).
 template <typename T, int MB, int NB, int WAVES>
 __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB], int m0, char* lds) {
   constexpr int TCOLS = 16 * NB * WAVES;  // tile columns (WAVES waves x 16*NB)
@@ -159,6 +189,13 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
         a.part_max[pi] = mx;
         a.part_sum[pi] = se;
       }
+      // sampled drafting: rank by the Gumbel key s * logit + G instead
+      if (a.gumbel) {
+        const uint32_t rk = row_key_of(a, m);
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+          v[j] = v[j] == -INFINITY ? -INFINITY : __fadd_rn(__fmul_rn(a.inv_temp, v[j]), gumbel_of(a, rk, id[j]));
+      }
       // top-k: round k takes the best entry strictly worse than round k-1's
       float pv = INFINITY;
       int pid = -1;
@@ -174,6 +211,10 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
         if (lane == 0) {
           a.part_val[pi * a.top_k + k] = bv;
           a.part_id[pi * a.top_k + k] = bi;
+          if (a.gumbel) {
+            const int col = bi - tile * TCOLS;
+            a.part_logit[pi * a.top_k + k] = col >= 0 && col < TCOLS ? tl[r * TROW + col] : -INFINITY;
+          }
         }
         pv = bv;
         pid = bi;
@@ -293,6 +334,16 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
     a.part_max[pi] = mx;
     a.part_sum[pi] = se;
   }
+  if (a.gumbel) {   // sampled drafting: rank by s * logit + G
+    const uint32_t rk = row_key_of(a, m);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = c0 + 256 * j + 4 * lane + e;
+        v[j][e] = v[j][e] == -INFINITY ? -INFINITY : __fadd_rn(__fmul_rn(a.inv_temp, v[j][e]), gumbel_of(a, rk, id));
+      }
+  }
   float pv = INFINITY;
   int pid = -1;
   for (int k = 0; k < a.top_k; ++k) {
@@ -309,6 +360,7 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
     if (lane == 0) {
       a.part_val[pi * a.top_k + k] = bv;
       a.part_id[pi * a.top_k + k] = bi;
+      if (a.gumbel) a.part_logit[pi * a.top_k + k] = bi >= c0 && bi < a.V ? row[bi - c0] : -INFINITY;
     }
     pv = bv;
     pid = bi;
@@ -412,7 +464,24 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
       if (better(pv, pid, v, id) && better(v, id, bv, bi)) { bv = v; bi = id; }
     }
     block_best(bv, bi, sv, si);
-    if (tid == 0) {
+    if (a.part_logit) {
+      // Gumbel keys ranked the candidates; the confidence is the winner's
+      // softmax probability, from its logit (the thread holding it writes)
+      for (int q = tid; q < ncand; q += 256) {
+        const int t = q / a.top_k, j = q - t * a.top_k;
+        const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
+        const float v = staged ? cval[q] : a.part_val[i];
+        const int id = staged ? cid[q] : a.part_id[i];
+        if (v == bv && id == bi) {
+          a.topk_id[(int64_t)m * a.top_k + k] = bi < 0 ? 0 : (bi >= a.vocab ? a.vocab - 1 : bi);
+          a.topk_conf[(int64_t)m * a.top_k + k] = expf(a.inv_temp * a.part_logit[i] - lse);
+        }
+      }
+      if (tid == 0 && bi == 0x7fffffff) {
+        a.topk_id[(int64_t)m * a.top_k + k] = 0;
+        a.topk_conf[(int64_t)m * a.top_k + k] = 0.f;
+      }
+    } else if (tid == 0) {
       // a NaN row leaves no candidate: keep ids inside the vocabulary
       a.topk_id[(int64_t)m * a.top_k + k] = bi < 0 ? 0 : (bi >= a.vocab ? a.vocab - 1 : bi);
       a.topk_conf[(int64_t)m * a.top_k + k] = expf(a.inv_temp * bv - lse);

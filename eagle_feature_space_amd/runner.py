@@ -106,6 +106,8 @@ class GpuRound:
         tr.n_template = len(cfg.template) if cfg.tree == TREE_STATIC else 0
         tr.template_parent = ctypes.cast(self._tmpl, ctypes.POINTER(ctypes.c_int32))
         tr.inv_temp = cfg.inv_temp
+        if cfg.sample_seed is not None:
+            tr.sample, tr.sample_seed = 1, cfg.sample_seed
         nbytes = E.eagle_tree_state_bytes(tr)
         if nbytes == 0:
             raise E.EagleError(E.EAGLE_EINVAL, "eagle_tree_state_bytes")

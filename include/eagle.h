@@ -162,6 +162,17 @@ typedef struct eagle_tree {
   float inv_temp;                /* s in conf = softmax(s * logits)       */
   void *state;                   /* device */
   size_t state_bytes;
+  /* Sampled drafting ("Speculative Decoding Deep Dive III", EAGLE-1
+   * "Inference": the drafter samples t ~ p-hat).  sample = 1: the top_k
+   * children of a row are drawn without replacement from
+   * softmax(inv_temp * logits) by Gumbel-top-k: the top_k of
+   * inv_temp * logit + G, G = -log(-log(u)) in fp32 with
+   * u = ((bits >> 9) + 0.5) 2^-23 and bits from Philox4x32-10 (Salmon et al.,
+   * SC'11) with key (low, high word of sample_seed) and counter
+   * (id / 4, b * 1024 + node, 0, 0), word id % 4; confidences stay the
+   * softmax probabilities.  sample = 0: top_k by logit. */
+  uint64_t sample_seed;
+  int32_t sample;
 } eagle_tree;
 
 /* Byte offsets of the arrays inside eagle_tree.state (all per request b).

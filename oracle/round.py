@@ -41,6 +41,7 @@ import numpy as np
 
 from .head import DraftHead, attend
 from .tree import CHAIN, DYNAMIC, STATIC, RequestTree
+from .sampling import gumbel_topk
 from .verify import verify
 
 MAX_SLOTS = 64
@@ -194,6 +195,17 @@ def run_round(cfg, head: DraftHead, n, t_root, k_ctx=None, v_ctx=None,
         F = np.stack(feats)
         logits = head.lm_head(F)
         ids, conf, lse = DraftHead.draft_choices(logits, top_k, cfg.inv_temp)
+        seed = getattr(cfg, "sample_seed", None)
+        if seed is not None:
+            # sampled drafting: top_k drawn without replacement (Gumbel-top-k),
+            # row key b * 1024 + node; confidences of the drawn ids
+            r = 0
+            for b in range(B):
+                for (u, *_rest) in rows[b]:
+                    ids[r] = gumbel_topk(logits[r], top_k, cfg.inv_temp, seed, b * 1024 + u)[0]
+                    z = logits[r] * logits.dtype.type(cfg.inv_temp)
+                    conf[r] = np.exp(z[ids[r]] - lse[r])
+                    r += 1
         res.steps.append(StepTrace(rows, H, F, logits, ids, conf, lse))
         use_ids, use_conf = (ids, conf) if teacher is None else teacher(s)
         r0 = 0

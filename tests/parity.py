@@ -21,6 +21,7 @@ import numpy as np
 
 from eagle_feature_space_amd import configs as C
 from eagle_feature_space_amd import synth
+from oracle import sampling as OS
 from oracle import target as OTG
 from oracle import tree as OT
 from oracle import verify as OV
@@ -144,7 +145,8 @@ def check_step(case: Case, gr, snaps, s, rows=None, report=None):
         e = rel_err(lg, lo)
         worst["logit"] = max(worst["logit"], e)
         assert e <= TOL, f"step {s} row {m}: logit rel err {e:.3g}"
-        _check_topk(cfg, lg, lo, snap.topk_id[m], snap.topk_conf[m], snap.lse[m], s, m, worst)
+        rk = b * 1024 + int(snap.rows["node"][m])
+        _check_topk(cfg, lg, lo, snap.topk_id[m], snap.topk_conf[m], snap.lse[m], s, m, worst, rk)
     assert worst["feat"] <= TOL, worst
     assert worst["kv"] <= TOL, worst
     assert worst["ctxkv"] <= TOL, worst
@@ -154,26 +156,30 @@ def check_step(case: Case, gr, snaps, s, rows=None, report=None):
     return worst
 
 
-def _check_topk(cfg, lg, lo, ids, conf, lse, s, m, worst):
+def _check_topk(cfg, lg, lo, ids, conf, lse, s, m, worst, rk=0):
     K = cfg.top_k
     st = cfg.inv_temp
-    # the fused kernel equals the top-k / softmax of the GPU's own logits
-    own = np.lexsort((np.arange(lg.size), -lg))[:K]
-    assert list(ids) == list(own), f"step {s} row {m}: fused top-k {ids} != top-k of GPU logits {own}"
+    if cfg.sample_seed is not None:
+        _check_sampled(cfg, lg, lo, ids, s, m, rk)
+    else:
+        # the fused kernel equals the top-k / softmax of the GPU's own logits
+        own = np.lexsort((np.arange(lg.size), -lg))[:K]
+        assert list(ids) == list(own), f"step {s} row {m}: fused top-k {ids} != top-k of GPU logits {own}"
     z = st * lg.astype(np.float64)
     zmax = z.max()
     ref_lse = zmax + np.log(np.exp(z - zmax).sum())
     assert abs(lse - ref_lse) <= 1e-5 * max(1.0, abs(ref_lse)) + 1e-5, (lse, ref_lse)
     np.testing.assert_allclose(conf, np.exp(z[ids] - ref_lse), rtol=1e-4, atol=1e-12)
     # against the oracle: ids fixed wherever every gap up to the rank is clear
-    tol = TOL * np.max(np.abs(lo))
-    order = np.lexsort((np.arange(lo.size), -lo))
-    srt = lo[order]
-    clear = True
-    for i in range(K):
-        clear = clear and (srt[i] - srt[i + 1] > tol)
-        if clear:
-            assert ids[i] == order[i], f"step {s} row {m} rank {i}: {ids[i]} != {order[i]}"
+    if cfg.sample_seed is None:
+        tol = TOL * np.max(np.abs(lo))
+        order = np.lexsort((np.arange(lo.size), -lo))
+        srt = lo[order]
+        clear = True
+        for i in range(K):
+            clear = clear and (srt[i] - srt[i + 1] > tol)
+            if clear:
+                assert ids[i] == order[i], f"step {s} row {m} rank {i}: {ids[i]} != {order[i]}"
     err = np.max(np.abs(lg.astype(np.float64) - lo))
     zo = st * lo.astype(np.float64)
     lse_o = zo.max() + np.log(np.exp(zo - zo.max()).sum())
@@ -185,6 +191,29 @@ def _check_topk(cfg, lg, lo, ids, conf, lse, s, m, worst):
         d = abs(np.log(max(float(conf[i]), floor)) - np.log(max(c_o, floor)))
         worst["conf"] = max(worst["conf"], d)
         assert d <= 2 * st * err + 1e-5, f"step {s} row {m}: log-conf diff {d:.3g} > {2 * st * err:.3g}"
+
+
+def _clear_prefix(keys, ids, tol, what, s, m):
+    """ids must follow the key order at every rank up to which each gap
+    between consecutive keys exceeds tol (ties by lowest id)."""
+    order = np.lexsort((np.arange(keys.size), -keys.astype(np.float64)))
+    srt = keys[order].astype(np.float64)
+    for i in range(len(ids)):
+        if not srt[i] - srt[i + 1] > tol:
+            break
+        assert ids[i] == order[i], f"step {s} row {m} rank {i} ({what}): {ids[i]} != {order[i]}"
+
+
+def _check_sampled(cfg, lg, lo, ids, s, m, rk):
+    """Gumbel-top-k: the fused ids are the k largest s * logit + G with the
+    oracle's Philox noise, on the GPU's own logits (exact but for keys within
+    a few fp32 ulps: the two sides' log differ in the last bit) and on the
+    oracle's logits wherever the key gaps exceed the logits tolerance."""
+    st = cfg.inv_temp
+    key_g = OS.gumbel_keys(lg, st, cfg.sample_seed, rk)
+    _clear_prefix(key_g, ids, 1e-5 * max(1.0, float(np.max(np.abs(key_g)))), "own logits", s, m)
+    key_o = OS.gumbel_keys(lo, st, cfg.sample_seed, rk)
+    _clear_prefix(key_o, ids, st * TOL * float(np.max(np.abs(lo))) + 1e-5, "oracle logits", s, m)
 
 
 # ------------------------------------------------------------------ P2

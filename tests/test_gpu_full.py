@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 # (workload, rows checked per draft step; None = all)
 FULL = [("c1_8b_static", None), ("c2_8b_dynamic", 6), ("c3_8b_eagle3", 4),
         ("c4_70b_dynamic", 3), ("c5_8b_eagle3_steady", 4), ("c6_8b_target", None),
-        ("c7_8b_dynamic_steady", 6)]
+        ("c7_8b_dynamic_steady", 6), ("c8_8b_dynamic_sampled", 6)]
 
 
 @pytest.mark.parametrize("name,rows", FULL, ids=[f[0] for f in FULL])

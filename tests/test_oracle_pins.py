@@ -15,6 +15,7 @@ from eagle_feature_space_amd import configs as C
 from eagle_feature_space_amd import synth
 from oracle import head as H
 from oracle import tree as T
+from oracle import sampling as SM
 from oracle import target as TG
 from oracle import verify as VF
 from oracle.round import ingest_features, run_round
@@ -590,6 +591,57 @@ def test_verify_sample_residual_is_inverse_cdf():
     for u in np.linspace(0, 1, 101)[:-1]:
         x = VF.residual_draw(p, excl, u)
         assert x not in excl and edges[x] <= u < edges[x + 1] + 1e-12
+
+
+# ------------------------------------------------- sampled drafting (Gumbel-top-k)
+def test_philox_known_answers():
+    """Philox4x32-10 against the known-answer vectors published with its
+    definition (Salmon et al., SC'11; the Random123 test vectors)."""
+    kat = [((0, 0, 0, 0), (0, 0), (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+           ((0xffffffff,) * 4, (0xffffffff,) * 2, (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+           ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+            (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1))]
+    for ctr, key, want in kat:
+        got = SM.philox4x32_10([np.array([x], np.uint64) for x in ctr], key)
+        assert [int(w[0]) for w in got] == list(want)
+
+
+def test_uniforms_are_open_interval_and_gumbel_finite():
+    u = SM.uniforms(12345, 7, 4096)
+    assert u.dtype == np.float32 and u.min() > 0 and u.max() < 1
+    # the extreme bit patterns still give finite Gumbel values
+    for bits in (0, 0xFFFFFFFF):
+        ue = ((np.uint32(bits) >> np.uint32(9)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -23)
+        assert np.isfinite(-np.log(-np.log(ue)))
+    # uniform: 16 equal bins within 5 sigma
+    h = np.bincount((SM.uniforms(99, 3, 1 << 16) * 16).astype(int), minlength=16) / (1 << 16)
+    assert np.all(np.abs(h - 1 / 16) <= 5 * np.sqrt((1 / 16) * (15 / 16) / (1 << 16)))
+
+
+def test_gumbel_topk_samples_without_replacement():
+    """Gumbel-max draws follow softmax(s * logits); the first two of
+    Gumbel-top-2 follow sequential sampling without replacement
+    (Monte Carlo over row keys, 5-sigma bounds)."""
+    l = np.array([1.0, -0.5, 2.0, 0.3, 0.0, -1.2], np.float32)
+    s = 1.3
+    p = np.exp(s * l.astype(np.float64))
+    p /= p.sum()
+    n = 40000
+    first = np.zeros(6)
+    pair = np.zeros((6, 6))
+    for r in range(n):
+        ids, _ = SM.gumbel_topk(l, 2, s, 2024, r)
+        first[ids[0]] += 1
+        pair[ids[0], ids[1]] += 1
+    f = first / n
+    assert np.all(np.abs(f - p) <= 5 * np.sqrt(p * (1 - p) / n) + 1e-4)
+    for i in range(6):
+        for j in range(6):
+            if i == j:
+                assert pair[i, j] == 0
+                continue
+            q = p[i] * p[j] / (1 - p[i])
+            assert abs(pair[i, j] / n - q) <= 5 * np.sqrt(q * (1 - q) / n) + 1e-4
 
 
 # ------------------------------------------------- target verification pass
