@@ -1044,7 +1044,7 @@ int eagle_tree_attend(const eagle_head* h, const eagle_kv* kv, const eagle_tree*
   return finish(EAGLE_OK);
 }
 
-int check_target(const eagle_head* h, const eagle_target* t) {
+int check_target(const eagle_head* h, const eagle_target* t, const eagle_kv* kv) {
   if (!t || t->n_layers < 1 || !t->layers || !t->final_norm_g) return EAGLE_EINVAL;
   for (int l = 0; l < t->n_layers; ++l) {
     const eagle_layer& L = t->layers[l];
@@ -1052,6 +1052,7 @@ int check_target(const eagle_head* h, const eagle_target* t) {
     if (h->act == EAGLE_ACT_SWIGLU && !L.w_gate) return EAGLE_EINVAL;
     if (!L.norm1_g || !L.norm2_g) return EAGLE_EINVAL;
     if (h->norm == EAGLE_NORM_LAYER && (!L.norm1_b || !L.norm2_b)) return EAGLE_EINVAL;
+    if (kv && kv->total_n > 0 && (!L.k_ctx || !L.v_ctx)) return EAGLE_EINVAL;
   }
   return EAGLE_OK;
 }
@@ -1059,7 +1060,7 @@ int check_target(const eagle_head* h, const eagle_target* t) {
 size_t eagle_target_workspace_bytes(const eagle_head* head, const eagle_target* target,
                                     const eagle_kv* kv, const eagle_tree* tree) {
   Geo g;
-  if (check_head(head) || check_target(head, target) || build_geo(tree, &g) || check_kv(kv, g.B))
+  if (check_head(head) || check_target(head, target, kv) || build_geo(tree, &g) || check_kv(kv, g.B))
     return 0;
   return plan_ws(head, kv, g, true).total;
 }
@@ -1071,7 +1072,7 @@ int eagle_target_verify_logits(const eagle_head* head, const eagle_target* targe
   Geo g;
   int s;
   if ((s = check_head(head))) return s;
-  if ((s = check_target(head, target))) return s;
+  if ((s = check_target(head, target, kv))) return s;
   if ((s = build_geo(tree, &g))) return s;
   if ((s = check_kv(kv, g.B))) return s;
   if ((s = check_attn_plan(head, kv))) return s;
@@ -1113,7 +1114,6 @@ int eagle_target_verify_logits(const eagle_head* head, const eagle_target* targe
     eagle_kv kl = *kv;
     kl.k_ctx = const_cast<void*>(L.k_ctx);
     kl.v_ctx = const_cast<void*>(L.v_ctx);
-    if (kl.total_n > 0 && (!kl.k_ctx || !kl.v_ctx)) return EAGLE_EINVAL;
     void* x = xb[l & 1];
     // N1 of the layer input (plain normalised rows; the row path takes them
     // without a folded scale)

@@ -214,6 +214,9 @@ def test_target_pass_and_commit_are_validated(lib):
     layers[1].w_down = None
     assert E.eagle_target_workspace_bytes(h, tg, kv, t) == 0
     layers[1].w_down = 1 << 20
+    layers[2].v_ctx = None           # a layer without its context cache
+    assert E.eagle_target_workspace_bytes(h, tg, kv, t) == 0
+    layers[2].v_ctx = 1 << 20
     ts = _tree(cfg, state=1 << 20, nbytes=1 << 30)
     # null logits, k_tree without v_tree, workspace too small
     assert lib.eagle_target_verify_logits(h, tg, kv, ts, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
