@@ -17,10 +17,10 @@ namespace eagle {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int MB, int NB, int WAVES = 4>
+template <typename T, int MB, int NB, int WAVES = 4, bool GUMBEL = false>
 __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB], int m0, char* lds);
 
-template <typename T, int MB>
+template <typename T, int MB, bool GUMBEL = false>
 __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
   constexpr int NB = 4;
   constexpr int VEC = DT<T>::VEC;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
     }
   }
 
-  lm_epilogue<T, MB, NB>(a, acc, m0, lds);
+  lm_epilogue<T, MB, NB, 4, GUMBEL>(a, acc, m0, lds);
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
@@ -121,7 +121,7 @@ __device__ __forceinline__ uint32_t row_key_of(const LmArgs& a, int m) {
 // Epilogue shared by both LM-head kernels: optional raw logits, then per row
 // the tile max, tile sum of exp(s (l - max)) and the tile top-k (by logit, or
 // by the Gumbel key when drafting samples).
-template <typename T, int MB, int NB, int WAVES>
+template <typename T, int MB, int NB, int WAVES, bool GUMBEL>
 __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB], int m0, char* lds) {
   constexpr int TCOLS = 16 * NB * WAVES;  // tile columns (WAVES waves x 16*NB)
   constexpr int TROW = TCOLS + 4;
@@ -190,7 +190,7 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
         a.part_sum[pi] = se;
       }
       // sampled drafting: rank by the Gumbel key s * logit + G instead
-      if (a.gumbel) {
+      if constexpr (GUMBEL) {
         const uint32_t rk = row_key_of(a, m);
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -211,7 +211,7 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
         if (lane == 0) {
           a.part_val[pi * a.top_k + k] = bv;
           a.part_id[pi * a.top_k + k] = bi;
-          if (a.gumbel) {
+          if constexpr (GUMBEL) {
             const int col = bi - tile * TCOLS;
             a.part_logit[pi * a.top_k + k] = col >= 0 && col < TCOLS ? tl[r * TROW + col] : -INFINITY;
           }
@@ -226,7 +226,7 @@ __device__ __forceinline__ void lm_epilogue(const LmArgs& a, f32x4 (&acc)[NB][MB
 // M <= 32: barrier-free streaming main loop (see k_gemm_direct), full K per
 // wave, 128 vocabulary rows per wave (eight 16-row MFMA blocks share each X
 // fragment and keep 32 KB of W loads in flight per wave), 512 per workgroup.
-template <typename T, int MB, int NB = 8, int U = 2, int WAVES = 4>
+template <typename T, int MB, bool GUMBEL = false, int NB = 8, int U = 2, int WAVES = 4>
 __global__ __launch_bounds__(64 * WAVES) void k_lmhead_direct(LmArgs a) {
   constexpr int TCOLS = 16 * NB * WAVES;
   constexpr int TBYTES = 16 * (TCOLS + 4) * 4;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead_direct(LmArgs a) {
   ga.N = a.V;
   ga.K = a.K;
   direct_mainloop<T, MB, NB, U>(ga, wrow, 0, a.K, g, c, acc);
-  lm_epilogue<T, MB, NB, WAVES>(a, acc, 0, lds);
+  lm_epilogue<T, MB, NB, WAVES, GUMBEL>(a, acc, 0, lds);
 }
 
 LmShape plan_lmhead(int dtype, int M, int V) {
@@ -267,32 +267,36 @@ LmShape plan_lmhead(int dtype, int M, int V) {
   return s;
 }
 
-template <typename T>
+template <typename T, bool G>
 static void launch_lm_t(const LmArgs& a, const LmShape& s, hipStream_t st) {
   dim3 grid(s.ntiles, s.mtiles), block(256);
   switch (s.MB) {
-    case 1: hipLaunchKernelGGL((k_lmhead<T, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_lmhead<T, 2>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_lmhead<T, 3>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_lmhead<T, 4>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_lmhead<T, 5>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_lmhead<T, 1, G>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_lmhead<T, 2, G>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_lmhead<T, 3, G>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_lmhead<T, 4, G>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_lmhead<T, 5, G>), grid, block, 0, st, a); break;
   }
 }
 
+template <typename T, bool G>
+static void launch_direct_t(const LmArgs& a, const LmShape& s, hipStream_t st) {
+  dim3 grid(s.ntiles, 1), block(256);
+  if (a.M <= 16) hipLaunchKernelGGL((k_lmhead_direct<T, 1, G>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_lmhead_direct<T, 2, G>), grid, block, 0, st, a);
+}
+
+// the Gumbel-top-k epilogue is a separate instantiation, so the default one
+// carries none of its code or registers
 void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st) {
+  const bool bf = dtype == EAGLE_BF16;
   if (a.M <= 32) {
-    dim3 grid(s.ntiles, 1), block(256);
-    if (dtype == EAGLE_BF16) {
-      if (a.M <= 16) hipLaunchKernelGGL((k_lmhead_direct<bf16s, 1>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((k_lmhead_direct<bf16s, 2>), grid, block, 0, st, a);
-    } else {
-      if (a.M <= 16) hipLaunchKernelGGL((k_lmhead_direct<float, 1>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((k_lmhead_direct<float, 2>), grid, block, 0, st, a);
-    }
+    if (a.gumbel) bf ? launch_direct_t<bf16s, true>(a, s, st) : launch_direct_t<float, true>(a, s, st);
+    else bf ? launch_direct_t<bf16s, false>(a, s, st) : launch_direct_t<float, false>(a, s, st);
     return;
   }
-  if (dtype == EAGLE_BF16) launch_lm_t<bf16s>(a, s, st);
-  else launch_lm_t<float>(a, s, st);
+  if (a.gumbel) bf ? launch_lm_t<bf16s, true>(a, s, st) : launch_lm_t<float, true>(a, s, st);
+  else bf ? launch_lm_t<bf16s, false>(a, s, st) : launch_lm_t<float, false>(a, s, st);
 }
 
 // Tile partials from materialised logits (large M, after the MFMA-tiled GEMM):
