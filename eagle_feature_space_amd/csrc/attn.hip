@@ -38,6 +38,28 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// P^T operand: VEC probabilities -> one 16-byte fragment (bf16: hardware
+// round-to-nearest-even pair conversions)
+template <typename T>
+__device__ __forceinline__ u32x4 pack_p(const float* f) {
+  if constexpr (sizeof(T) == 2) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{f[2 * i], f[2 * i + 1]}), bf16x2_t));
+    return r;
+  } else {
+    return DT<T>::pack(f);
+  }
+}
+
+// two keys' bf16 values of one d (element e of each 16-byte vector) as one word
+__device__ __forceinline__ uint32_t pair16(uint32_t lo_word, uint32_t hi_word, int e) {
+  return __builtin_amdgcn_perm(hi_word, lo_word, (e & 1) ? 0x07060302u : 0x05040100u);
+}
+
 // One key split of (request b, kv head): the context split `split` or, for
 // split == nsplit, the request's tree-node slots gated by the rows' masks.
 // Folds its tiles into the running (max, sum, O^T) state of the wave's rows.
@@ -73,6 +95,15 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
   }
 
   for (int t0 = kbeg; t0 < kend; t0 += 64) {
+    // ---- K fragments of the tile: issued first, they land while V is staged
+    u32x4 kf[4][DSTEPS];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = min(t0 + (c >> 2) * 16 + j * 4 + (c & 3), kend - 1);
+      const T* kp = kb + (int64_t)key * kstride;
+#pragma unroll
+      for (int u = 0; u < DSTEPS; ++u) kf[j][u] = ld16(kp + u * 4 * VEC + g * VEC);
+    }
     // ---- V tile -> LDS, transposed: vt[d][key]
     wave_lds_sync();
     {
@@ -91,9 +122,8 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
         for (int e = 0; e < VEC; ++e) {
           char* dst = vt + vt_off<T>(dg * VEC + e, 4 * kq, ROWB);
           if constexpr (sizeof(T) == 2) {
-            const int sh = (e & 1) * 16;
-            uint32_t w0 = ((v4[0][e >> 1] >> sh) & 0xffffu) | (((v4[1][e >> 1] >> sh) & 0xffffu) << 16);
-            uint32_t w1 = ((v4[2][e >> 1] >> sh) & 0xffffu) | (((v4[3][e >> 1] >> sh) & 0xffffu) << 16);
+            const uint32_t w0 = pair16(v4[0][e >> 1], v4[1][e >> 1], e);
+            const uint32_t w1 = pair16(v4[2][e >> 1], v4[3][e >> 1], e);
             *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
           } else {
             st16(dst, u32x4{v4[0][e], v4[1][e], v4[2][e], v4[3][e]});
@@ -105,21 +135,17 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
     f32x4 s[4][RB];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = min(t0 + (c >> 2) * 16 + j * 4 + (c & 3), kend - 1);
-      const T* kp = kb + (int64_t)key * kstride;
-      u32x4 kf[DSTEPS];
-#pragma unroll
-      for (int u = 0; u < DSTEPS; ++u) kf[u] = ld16(kp + u * 4 * VEC + g * VEC);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < DSTEPS; ++u) acc = DT<T>::mma(kf[u], qf[rb][u], acc);
+        for (int u = 0; u < DSTEPS; ++u) acc = DT<T>::mma(kf[j][u], qf[rb][u], acc);
         s[j][rb] = acc;
       }
     }
     wave_lds_sync();
     // ---- online softmax and O^T += V^T P^T
+    const bool full = !extra && t0 + 64 <= kend;   // no key of the tile is masked
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float tmax = -INFINITY;
@@ -128,7 +154,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = t0 + g * 16 + j * 4 + i;
-          bool valid = key < kend;
+          bool valid = full || key < kend;
           if (extra) valid = valid && ((msk[rb] >> key) & 1ull);
           const float v = valid ? s[j][rb][i] * a.scale_log2 : -INFINITY;
           s[j][rb][i] = v;
@@ -153,11 +179,13 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
       psum += __shfl_xor(psum, 32, 64);
       lrun[rb] = lrun[rb] * alpha + psum;
       mrun[rb] = mnew;
+      // scaling by 1 is exact: skipped when no row's maximum moved
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
+        for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const u32x4 pf = DT<T>::pack(p + v * VEC);
+        const u32x4 pf = pack_p<T>(p + v * VEC);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x4 vf = ld16(vt + vt_off<T>(db * 16 + c, g * 16 + v * VEC, ROWB));
@@ -320,7 +348,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int q = tid + i * NT;
-      if (q < KCH) {
+      if (KCH % NT == 0 || q < KCH) {
         const int key = min(t0 + q / DG, kend - 1);
         r.kr[i] = ld16(kb + (int64_t)key * kstride + (q % DG) * VEC);
       }
@@ -328,7 +356,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int q = tid + i * NT;
-      if (q < VUN) {
+      if (VUN % NT == 0 || q < VUN) {
         const int kq = q / DG, dg = q % DG;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -358,9 +386,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
         for (int e = 0; e < VEC; ++e) {
           char* dst = vt + vt_off<T>(dg * VEC + e, 4 * kq, VROW);
           if constexpr (sizeof(T) == 2) {
-            const int sh = (e & 1) * 16;
-            const uint32_t w0 = ((r.vr[i][0][e >> 1] >> sh) & 0xffffu) | (((r.vr[i][1][e >> 1] >> sh) & 0xffffu) << 16);
-            const uint32_t w1 = ((r.vr[i][2][e >> 1] >> sh) & 0xffffu) | (((r.vr[i][3][e >> 1] >> sh) & 0xffffu) << 16);
+            const uint32_t w0 = pair16(r.vr[i][0][e >> 1], r.vr[i][1][e >> 1], e);
+            const uint32_t w1 = pair16(r.vr[i][2][e >> 1], r.vr[i][3][e >> 1], e);
             *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
           } else {
             st16(dst, u32x4{r.vr[i][0][e], r.vr[i][1][e], r.vr[i][2][e], r.vr[i][3][e]});
@@ -392,13 +419,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
         sc[j] = acc;
       }
       // ---- online softmax, O^T += V^T P^T
+      const bool full = !extra && t0 + 64 <= kend;   // no key of the tile is masked
       float tmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = t0 + g * 16 + j * 4 + i;
-          bool valid = key < kend;
+          bool valid = full || key < kend;
           if (extra) valid = valid && ((msk >> key) & 1ull);
           const float v = valid ? sc[j][i] * a.scale_log2 : -INFINITY;
           sc[j][i] = v;
@@ -423,12 +451,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
       psum += __shfl_xor(psum, 32, 64);
       lrun = lrun * alpha + psum;
       mrun = mnew;
+      // scaling by 1 is exact: skipped when no row's maximum moved
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
       const char* vt = cur + 64 * KROW;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const u32x4 pf = DT<T>::pack(p + v * VEC);
+        const u32x4 pf = pack_p<T>(p + v * VEC);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x4 vf = ld16(vt + vt_off<T>(db * 16 + c, g * 16 + v * VEC, VROW));
@@ -441,17 +471,22 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
   // two register stages in flight: while the waves compute tile i from one LDS
   // buffer, tile i+1 waits in registers for the other buffer and the loads of
   // tile i+2 are issued (unrolled by two so every stage index is static)
+  // The query fragments and the mask must have landed before the loop: the
+  // loads inside it are then the only ones outstanding, each stage issues
+  // the same count (tiles past the split re-read its last key), and a stage
+  // is awaited with the next stage's loads still in flight.
+  __builtin_amdgcn_s_waitcnt(0x0070);
   Stage ra, rb;
   if (ntiles > 0) {
     gload(ra, kbeg);
-    if (ntiles > 1) gload(rb, kbeg + 64);
+    gload(rb, kbeg + 64);
     lstore(ra, lds);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; it += 2) {
     {
       const int t0 = kbeg + it * 64;
-      if (it + 2 < ntiles) gload(ra, t0 + 128);
+      gload(ra, t0 + 128);
       compute(lds, t0);
       if (it + 1 < ntiles) lstore(rb, lds + BUF);
       __syncthreads();
@@ -459,7 +494,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
     if (it + 1 >= ntiles) break;
     {
       const int t0 = kbeg + (it + 1) * 64;
-      if (it + 3 < ntiles) gload(rb, t0 + 128);
+      gload(rb, t0 + 128);
       compute(lds + BUF, t0);
       if (it + 2 < ntiles) lstore(ra, lds);
       __syncthreads();

@@ -538,6 +538,13 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
   a.mask = mask;
   a.split_len = w.ap.split_len;
   a.nsplit = w.ap.nsplit;
+  if (W * (h->n_q_heads / h->n_kv_heads) > 16 && a.split_len < 256) {
+    // the workgroup kernel (more than 16 query rows per kv head) keeps two
+    // tiles in flight: splits of at least four tiles amortise its prologue.
+    // Fewer splits than the workspace was sized for.
+    a.split_len = 256;
+    a.nsplit = (std::max(kv->max_n, 1) + a.split_len - 1) / a.split_len;
+  }
   a.rowgroups = 1;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)h->head_dim);
   a.part_o = (float*)(ws + w.att_o);
