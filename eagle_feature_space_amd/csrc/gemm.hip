@@ -107,7 +107,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 template <typename T, int MB, int NB>
 __global__ __launch_bounds__(256) void k_gemm_direct(GemmArgs a) {
   constexpr int U = 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave: in a scalar register, loops
+  // bounded by it stay scalar loops
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int n_base = (blockIdx.x * 4 + wave) * (16 * NB);
   if (n_base >= a.N) return;

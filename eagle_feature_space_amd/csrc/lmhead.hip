@@ -231,7 +231,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead_direct(LmArgs a) {
   constexpr int TCOLS = 16 * NB * WAVES;
   constexpr int TBYTES = 16 * (TCOLS + 4) * 4;
   __shared__ __attribute__((aligned(16))) char lds[TBYTES];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave: in a scalar register, loops
+  // bounded by it stay scalar loops
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int n_base = blockIdx.x * TCOLS + wave * 16 * NB;
   const T* wrow[NB];

@@ -55,14 +55,22 @@ __device__ __forceinline__ void direct_mainloop(const GemmArgs& a, const T* cons
   const int kfull = k_begin + (k_end - k_begin) / STEP * STEP;
   int k = k_begin;
   if (k < kfull) {
+    // The prefetch is issued on every step (the last one re-reads the final
+    // batch, an L2 hit) so that each step has the same loads outstanding and a
+    // batch is awaited with the next one still in flight (a conditional
+    // prefetch makes the compiler wait for both); the scheduling barrier keeps
+    // the prefetch ahead of the MFMAs instead of letting it sink into them.
+    const int klast = kfull - STEP;
     u32x4 wa[U][NB], xa[U][MB], wb[U][NB], xb[U][MB];
     direct_load<T, MB, NB, U>(a, wrow, x0, x1, k, g, wa, xa);
     while (true) {
-      if (k + STEP < kfull) direct_load<T, MB, NB, U>(a, wrow, x0, x1, k + STEP, g, wb, xb);
+      direct_load<T, MB, NB, U>(a, wrow, x0, x1, min(k + STEP, klast), g, wb, xb);
+      __builtin_amdgcn_sched_barrier(0);
       direct_mma<T, MB, NB, U>(acc, wa, xa);
       k += STEP;
       if (k >= kfull) break;
-      if (k + STEP < kfull) direct_load<T, MB, NB, U>(a, wrow, x0, x1, k + STEP, g, wa, xa);
+      direct_load<T, MB, NB, U>(a, wrow, x0, x1, min(k + STEP, klast), g, wa, xa);
+      __builtin_amdgcn_sched_barrier(0);
       direct_mma<T, MB, NB, U>(acc, wb, xb);
       k += STEP;
       if (k >= kfull) break;
