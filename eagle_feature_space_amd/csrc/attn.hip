@@ -295,10 +295,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int kvh = blockIdx.y % a.Hkv;
-  const int rg = blockIdx.y / a.Hkv;
+  // kv heads vary fastest in dispatch order: the workgroups that read the
+  // same key positions (one 2 KB row of every kv head) run side by side
+  const int kvh = blockIdx.x % a.Hkv;
+  const int rg = blockIdx.x / a.Hkv;
+  const int split = blockIdx.y;
   const int b = blockIdx.z;
-  const int split = blockIdx.x;
   const int G = a.Hq / a.Hkv;
   const int R = a.W * G;
   const int M = a.B * a.W;
@@ -526,7 +528,7 @@ static void launch_wg(const AttnArgs& a, hipStream_t st) {
   }
   const int R = a.W * (a.Hq / a.Hkv);
   const int rowgroups = (R + 16 * NW - 1) / (16 * NW);
-  dim3 grid(a.nsplit + 1, a.Hkv * rowgroups, a.B);
+  dim3 grid(a.Hkv * rowgroups, a.nsplit + 1, a.B);
   hipLaunchKernelGGL((k_attn_wg<T, HD, NW>), grid, dim3(64 * NW), LDS, st, a);
 }
 

@@ -538,12 +538,31 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
   a.mask = mask;
   a.split_len = w.ap.split_len;
   a.nsplit = w.ap.nsplit;
-  if (W * (h->n_q_heads / h->n_kv_heads) > 16 && a.split_len < 256) {
+  if (W * (h->n_q_heads / h->n_kv_heads) > 16) {
     // the workgroup kernel (more than 16 query rows per kv head) keeps two
-    // tiles in flight: splits of at least four tiles amortise its prologue.
-    // Fewer splits than the workspace was sized for.
-    a.split_len = 256;
-    a.nsplit = (std::max(kv->max_n, 1) + a.split_len - 1) / a.split_len;
+    // tiles in flight: splits of an eighth of the context, between two and
+    // eight tiles, amortise its prologue (fewer splits than the workspace
+    // was sized for)
+    const int max_n = std::max(kv->max_n, 1);
+    const int min_len = std::min(512, std::max(128, (max_n / 8 + 63) / 64 * 64));
+    if (a.split_len < min_len) {
+      a.split_len = min_len;
+      a.nsplit = (max_n + a.split_len - 1) / a.split_len;
+    }
+  } else if (W * (h->n_q_heads / h->n_kv_heads) <= 16) {
+    // the per-wave kernel (two waves of LDS-staged V per workgroup): when the
+    // grid would need more than one pass of resident workgroups over the 256
+    // CUs, the splits are lengthened until it fits in one (a short last pass
+    // leaves most CUs idle while it runs)
+    const int64_t lds = 2LL * h->head_dim * (64 * (int64_t)esz(h) + 16);
+    const int64_t resident = (160 * 1024 / lds) * 256;
+    const int64_t per_split = (int64_t)((h->n_kv_heads + 1) / 2) * kv->B;
+    const int64_t fit = resident / per_split - 1;    // context splits beside the tree split
+    if ((int64_t)(a.nsplit + 1) * per_split > resident && fit >= 1) {
+      const int max_n = std::max(kv->max_n, 1);
+      a.split_len = (int)(((max_n + fit - 1) / fit + 63) / 64 * 64);
+      a.nsplit = (max_n + a.split_len - 1) / a.split_len;
+    }
   }
   a.rowgroups = 1;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)h->head_dim);
