@@ -350,19 +350,50 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
         v[j][e] = v[j][e] == -INFINITY ? -INFINITY : __fadd_rn(__fmul_rn(a.inv_temp, v[j][e]), gumbel_of(a, rk, id));
       }
   }
+  // Tile top-k in (value desc, id asc) order.  Every lane first keeps its
+  // own best two entries (one pass over its values); a round then takes the
+  // best of the lanes' next unused entries, which is the tile's next entry as
+  // long as no lane has used both of its own.  A tile where one lane holds
+  // three or more of the top-k (rare) finishes with full passes that take the
+  // best entry strictly below the previous winner.
+  float b1 = -INFINITY, b2 = -INFINITY;
+  int i1 = 0x7fffffff, i2 = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = v[j][e];
+      const int id = c0 + 256 * j + 4 * lane + e;
+      if (better(x, id, b1, i1)) {
+        b2 = b1; i2 = i1; b1 = x; i1 = id;
+      } else if (better(x, id, b2, i2)) {
+        b2 = x; i2 = id;
+      }
+    }
+  int used = 0;
   float pv = INFINITY;
   int pid = -1;
   for (int k = 0; k < a.top_k; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    float bv;
+    int bi;
+    if (!__builtin_amdgcn_ballot_w64(used >= 2)) {
+      bv = used == 0 ? b1 : b2;
+      bi = used == 0 ? i1 : i2;
+      wave_best(bv, bi);
+      const int mine = used == 0 ? i1 : i2;
+      if (mine == bi) ++used;
+    } else {
+      bv = -INFINITY;
+      bi = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
+      for (int j = 0; j < PER; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int id = c0 + 256 * j + 4 * lane + e;
-        if (better(pv, pid, v[j][e], id) && better(v[j][e], id, bv, bi)) { bv = v[j][e]; bi = id; }
-      }
-    wave_best(bv, bi);
+        for (int e = 0; e < 4; ++e) {
+          const int id = c0 + 256 * j + 4 * lane + e;
+          if (better(pv, pid, v[j][e], id) && better(v[j][e], id, bv, bi)) { bv = v[j][e]; bi = id; }
+        }
+      wave_best(bv, bi);
+    }
     if (lane == 0) {
       a.part_val[pi * a.top_k + k] = bv;
       a.part_id[pi * a.top_k + k] = bi;
