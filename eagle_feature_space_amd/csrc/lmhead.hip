@@ -483,6 +483,72 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
   __syncthreads();
   z = red[0] + red[1] + red[2] + red[3];
   const float lse = a.inv_temp * mx + logf(z);
+  if (staged) {
+    // One wave takes the top-k from the staged candidates with no barrier per
+    // round: each lane keeps its best two, a round takes the best of the
+    // lanes' next unused entries (exact while no lane has used both; after
+    // that a lane rescans its candidates below the previous winner).
+    if (tid >= 64) return;
+    float b1 = -INFINITY, b2 = -INFINITY;
+    int i1 = 0x7fffffff, i2 = 0x7fffffff, q1 = -1, q2 = -1;
+    for (int q = tid; q < ncand; q += 64) {
+      const float v = cval[q];
+      const int id = cid[q];
+      if (better(v, id, b1, i1)) {
+        b2 = b1; i2 = i1; q2 = q1; b1 = v; i1 = id; q1 = q;
+      } else if (better(v, id, b2, i2)) {
+        b2 = v; i2 = id; q2 = q;
+      }
+    }
+    int used = 0;
+    float pv = INFINITY;
+    int pid = -1;
+    for (int k = 0; k < a.top_k; ++k) {
+      float bv, lv;
+      int bi, li, lq;
+      if (!__builtin_amdgcn_ballot_w64(used >= 2)) {
+        lv = used == 0 ? b1 : b2;
+        li = used == 0 ? i1 : i2;
+        lq = used == 0 ? q1 : q2;
+      } else {
+        lv = -INFINITY;
+        li = 0x7fffffff;
+        lq = -1;
+        for (int q = tid; q < ncand; q += 64) {
+          const float v = cval[q];
+          const int id = cid[q];
+          if (better(pv, pid, v, id) && better(v, id, lv, li)) { lv = v; li = id; lq = q; }
+        }
+      }
+      bv = lv;
+      bi = li;
+      wave_best(bv, bi);
+      const bool mine = lq >= 0 && li == bi && lv == bv;
+      if (mine && used < 2 && li == (used == 0 ? i1 : i2)) ++used;
+      if (a.part_logit) {
+        // Gumbel keys ranked the candidates; the confidence is the winner's
+        // softmax probability, from its logit (the lane holding it writes)
+        if (mine) {
+          const int t = lq / a.top_k, j = lq - t * a.top_k;
+          const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
+          a.topk_id[(int64_t)m * a.top_k + k] = bi < 0 ? 0 : (bi >= a.vocab ? a.vocab - 1 : bi);
+          a.topk_conf[(int64_t)m * a.top_k + k] = expf(a.inv_temp * a.part_logit[i] - lse);
+        }
+        if (tid == 0 && bi == 0x7fffffff) {
+          a.topk_id[(int64_t)m * a.top_k + k] = 0;
+          a.topk_conf[(int64_t)m * a.top_k + k] = 0.f;
+        }
+      } else if (tid == 0) {
+        // a NaN row leaves no candidate: keep ids inside the vocabulary
+        a.topk_id[(int64_t)m * a.top_k + k] = bi < 0 ? 0 : (bi >= a.vocab ? a.vocab - 1 : bi);
+        a.topk_conf[(int64_t)m * a.top_k + k] = expf(a.inv_temp * bv - lse);
+      }
+      pv = bv;
+      pid = bi;
+    }
+    if (tid == 0) a.lse[m] = lse;
+    return;
+  }
   float pv = INFINITY;
   int pid = -1;
   for (int k = 0; k < a.top_k; ++k) {

@@ -66,15 +66,18 @@ __device__ __forceinline__ bool before(float va, int da, int ia, float vb, int d
 // arrays of the next step (the other half of the double buffer): the two
 // steps have different row counts per request, so writing in place would
 // overwrite rows other workgroups have not read yet.
-__global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, RowsDev nx, int kind, int step,
-                                                     int gamma, int W, int top_k, int top_m,
-                                                     int final_step, StaticPlan plan) {
+constexpr int kExpandThreads = 1024;   // one node of a full pool per thread
+
+__global__ __launch_bounds__(kExpandThreads) void k_tree_expand(TreeDev t, RowsDev nx, int kind, int step,
+                                                                int gamma, int W, int top_k, int top_m,
+                                                                int final_step, StaticPlan plan) {
+  constexpr int NT = kExpandThreads;
   __shared__ float sval[kPoolMax];
   __shared__ int sdep[kPoolMax];
   __shared__ int spar[kPoolMax];
   __shared__ int spos[kPoolMax];
-  __shared__ int skeep[kPoolMax];
   __shared__ int snext[256];
+  __shared__ int swave[NT / 64];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int P = t.pool_cap;
@@ -87,8 +90,8 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, RowsDev nx, int 
   if (!final_step && t.slot_count[b] + (kind == EAGLE_TREE_DYNAMIC ? min(top_k, nchild) : plan.nnext) > kSlots)
     return;
 
-  // 1. append the children of this step's rows
-  for (int cidx = tid; cidx < nchild; cidx += 256) {
+  // 1. append the children of this step's rows (their values also go to LDS)
+  for (int cidx = tid; cidx < nchild; cidx += NT) {
     int row, rank;
     if (kind == EAGLE_TREE_DYNAMIC) { row = cidx / top_k; rank = cidx % top_k; }
     else { row = plan.row[cidx]; rank = plan.rank[cidx]; }
@@ -97,12 +100,14 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, RowsDev nx, int 
     if (parent < 0 || parent >= p0) parent = 0;   // never reached with a consistent state
     const float conf = t.topk_conf[(int64_t)r * top_k + rank];
     const int node = p0 + cidx;
+    const float val = __fmul_rn(t.pool_value[pb + parent], conf);
     t.pool_tok[pb + node] = t.topk_id[(int64_t)r * top_k + rank];
     t.pool_parent[pb + node] = parent;
     t.pool_depth[pb + node] = t.pool_depth[pb + parent] + 1;
     t.pool_slot[pb + node] = -1;
     t.pool_conf[pb + node] = conf;
-    t.pool_value[pb + node] = __fmul_rn(t.pool_value[pb + parent], conf);
+    t.pool_value[pb + node] = val;
+    if (node < kPoolMax) sval[node] = val;
   }
   __syncthreads();
   __threadfence_block();
@@ -113,13 +118,13 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, RowsDev nx, int 
     int nnext;
     if (kind == EAGLE_TREE_DYNAMIC) {
       nnext = min(top_k, nchild);
-      for (int cidx = tid; cidx < nchild; cidx += 256) {
+      for (int cidx = tid; cidx < nchild; cidx += NT) {
         const int u = p0 + cidx;
-        const float vu = t.pool_value[pb + u];
+        const float vu = sval[u];
         int rank = 0;
         for (int j = 0; j < nchild; ++j) {
           const int v = p0 + j;
-          const float vv = t.pool_value[pb + v];
+          const float vv = sval[v];
           if (vv > vu || (vv == vu && v < u)) ++rank;
         }
         if (rank < nnext) snext[rank] = u;
@@ -158,36 +163,44 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, RowsDev nx, int 
     return;
   }
 
-  // 3. rerank and verify tree
-  for (int u = tid; u < pn; u += 256) {
+  // 3. rerank and verify tree (pool sizes are at most kPoolMax = one node per thread)
+  const int u = tid;
+  if (u < pn) {
     sval[u] = t.pool_value[pb + u];
     sdep[u] = t.pool_depth[pb + u];
     spar[u] = t.pool_parent[pb + u];
   }
   __syncthreads();
-  for (int u = tid; u < pn; u += 256) {
-    int keep;
-    if (u == 0) keep = 1;
-    else if (kind != EAGLE_TREE_DYNAMIC) keep = 1;
+  int keep = 0;
+  if (u < pn) {
+    if (u == 0 || kind != EAGLE_TREE_DYNAMIC) keep = 1;
     else {
       int rank = 0;
       for (int v = 1; v < pn; ++v)
         if (before(sval[v], sdep[v], v, sval[u], sdep[u], u)) ++rank;
       keep = rank < top_m;
     }
-    skeep[u] = keep;
   }
+  // positions in creation order: exclusive prefix count of the kept nodes
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(keep != 0);
+  const int lane = tid & 63, wv = tid >> 6;
+  if (lane == 0) swave[wv] = __builtin_popcountll(bal);
   __syncthreads();
-  if (tid == 0) {   // positions in creation order
-    int k = 0;
-    for (int u = 0; u < pn; ++u) spos[u] = skeep[u] ? k++ : -1;
-    t.f_count[b] = k;
+  int before_waves = 0, total = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    const int c = swave[w];
+    before_waves += w < wv ? c : 0;
+    total += c;
+  }
+  const int pos = before_waves + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+  if (u < pn) spos[u] = keep ? pos : -1;
+  if (tid == 0) {
+    t.f_count[b] = total;
     t.pool_count[b] = pn;
   }
   __syncthreads();
-  for (int u = tid; u < pn; u += 256) {
+  if (u < pn && spos[u] >= 0) {
     const int p = spos[u];
-    if (p < 0) continue;
     const int fb = b * kMaxPos;
     uint64_t msk = 0;
     // kept sets are ancestor-closed (confidences are <= 1, so values never
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(256) void k_tree_expand(TreeDev t, RowsDev nx, int 
 void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, int step,
                         int gamma, int rows, int top_k, int top_m, int final_step,
                         const StaticPlan& plan, hipStream_t st) {
-  hipLaunchKernelGGL(k_tree_expand, dim3(B), dim3(256), 0, st, t, next, kind, step, gamma, rows,
+  hipLaunchKernelGGL(k_tree_expand, dim3(B), dim3(kExpandThreads), 0, st, t, next, kind, step, gamma, rows,
                      top_k, top_m, final_step, plan);
 }
 
