@@ -476,7 +476,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
   // The query fragments and the mask must have landed before the loop: the
   // loads inside it are then the only ones outstanding, each stage issues
   // the same count (tiles past the split re-read its last key), and a stage
-  // is awaited with the next stage's loads still in flight.
+  // is awaited with the next stage's loads still in flight.  Immediate 0x0070
+  // = vmcnt(0) lgkmcnt(0) (expcnt 7: not waited on) in the gfx9 encoding.
   __builtin_amdgcn_s_waitcnt(0x0070);
   Stage ra, rb;
   if (ntiles > 0) {
