@@ -428,6 +428,11 @@ __device__ __forceinline__ void block_best(float& v, int& i, float* sv, int* si)
 constexpr int kMergeLds = 6144;   // candidates staged in LDS (48 KB)
 
 __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
+  // no fused multiply-adds here: with s * l and s * mx each rounded on its own
+  // and log(z) >= 0, fl(s l) <= fl(s mx) <= lse for every logit l <= mx, so
+  // each confidence exp(fl(s l) - lse) is at most 1 and path values never grow
+  // (a contracted fma(s, l, -lse) returned 1.0000013 for near-certain rows)
+#pragma clang fp contract(off)
   __shared__ float cval[kMergeLds];
   __shared__ int cid[kMergeLds];
   __shared__ float sv[4];
