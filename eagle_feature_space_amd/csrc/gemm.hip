@@ -477,10 +477,139 @@ __global__ __launch_bounds__(256) void k_rows_norm(ReduceArgs a) {
   DT<T>::st((T*)a.out_norm + (int64_t)m * a.N + n, v);
 }
 
+// Four columns per lane (16-byte fp32 / 8-byte bf16 accesses), one wave per
+// (row, 256-column block), four rows per workgroup; same partial-sum order per
+// element as k_rows_sum and the same per-block statistics layout.  Used for
+// 64 rows and more when N and every row stride are multiples of 4 and the
+// buffers 16-byte aligned.
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 ld4<bf16s>(const bf16s* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4{bf2f(v.x & 0xffffu), bf2f(v.x >> 16), bf2f(v.y & 0xffffu), bf2f(v.y >> 16)};
+}
+template <>
+__device__ __forceinline__ f32x4 ld4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void st4(T* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void st4<bf16s>(bf16s* p, const f32x4& v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f2bf(v[0]) | (f2bf(v[1]) << 16), f2bf(v[2]) | (f2bf(v[3]) << 16));
+}
+template <>
+__device__ __forceinline__ void st4<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rows_sum4(ReduceArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (m >= a.M) return;
+  const int n = blockIdx.x * 256 + 4 * lane;
+  const bool live = n < a.N;           // N % 4 == 0: all four columns or none
+  f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    if (a.P && a.S > 0) {
+      const float* p = a.P + (int64_t)m * a.N + n;
+      const int64_t stride = (int64_t)a.M * a.N;
+      constexpr int NB = 4;
+      for (int s0 = 0; s0 < a.S; s0 += NB) {
+        f32x4 v[NB];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) v[q] = *reinterpret_cast<const f32x4*>(p + (int64_t)min(s0 + q, a.S - 1) * stride);
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] += s0 + q < a.S ? v[q][e] : 0.f;
+      }
+    }
+    if (a.src1.base) y += ld4<T>(row_ptr<T>(a.src1, m) + n);
+    if (a.src2.base) y += ld4<T>(row_ptr<T>(a.src2, m) + n);
+    if (a.out) st4<T>((T*)a.out + (int64_t)m * a.N + n, y);
+    if (a.out_scatter.base)
+      st4<T>((T*)a.out_scatter.base + (int64_t)a.out_scatter.idx[m] * a.out_scatter.stride + n, y);
+    if (a.y32) *reinterpret_cast<f32x4*>(a.y32 + (int64_t)m * a.N + n) = y;
+    if (a.out_g) st4<T>((T*)a.out_g + (int64_t)m * a.N + n, y * ld4<T>((const T*)a.gain + n));
+  }
+  if (!a.stats) return;
+  float s1 = live ? (y[0] + y[1]) + (y[2] + y[3]) : 0.f;
+  float s2 = live ? (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]) : 0.f;
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (lane == 0) {
+    float* st = a.stats + ((int64_t)m * gridDim.x + blockIdx.x) * 2;
+    st[0] = s1;
+    st[1] = s2;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rows_norm4(ReduceArgs a, int nblk) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (m >= a.M) return;
+  const int n = blockIdx.x * 256 + 4 * lane;
+  const bool live = n < a.N;
+  f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f}, gn = y, bs = y;
+  if (live) {
+    y = *reinterpret_cast<const f32x4*>(a.y32 + (int64_t)m * a.N + n);
+    gn = ld4<T>((const T*)a.gain + n);
+    if (a.bias) bs = ld4<T>((const T*)a.bias + n);
+  }
+  // the row's block statistics, summed in block order (every lane alike)
+  const float* st = a.stats + (int64_t)m * nblk * 2;
+  float s1 = 0.f, s2 = 0.f;
+  for (int b = 0; b < nblk; ++b) {
+    const float2 v = *reinterpret_cast<const float2*>(st + 2 * b);
+    s1 += v.x;
+    s2 += v.y;
+  }
+  if (!live) return;
+  const float mean = a.layer_norm ? s1 / a.N : 0.f;
+  const float var = s2 / a.N - mean * mean;
+  const float rs = 1.0f / sqrtf(fmaxf(var, 0.f) + a.eps);
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = (y[e] - mean) * rs * gn[e];
+    if (a.bias) v[e] += bs[e];
+  }
+  st4<T>((T*)a.out_norm + (int64_t)m * a.N + n, v);
+}
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+static bool rows4_ok(const ReduceArgs& a) {
+  if (a.N % 4 != 0) return false;
+  const RowSrc* rs[3] = {&a.src1, &a.src2, &a.out_scatter};
+  for (const RowSrc* r : rs)
+    if (r->base && (!al16(r->base) || r->stride % 4 != 0)) return false;
+  const void* ps[7] = {a.P, a.out, a.y32, a.out_g, a.gain, a.bias, a.out_norm};
+  for (const void* q : ps)
+    if (q && !al16(q)) return false;
+  return true;
+}
+
 void launch_reduce_rows(int dtype, const ReduceArgs& a0, hipStream_t st) {
   ReduceArgs a = a0;
   if (!a.out_norm && !a.keep_stats) { a.y32 = nullptr; a.stats = nullptr; }
   dim3 grid((a.N + 255) / 256, a.M);
+  // few rows: one thread per column keeps more workgroups in flight
+  if (a.M >= 64 && rows4_ok(a)) {
+    const dim3 g4((a.N + 255) / 256, (a.M + 3) / 4);
+    const int nblk = (a.N + 255) / 256;
+    if (dtype == EAGLE_BF16) {
+      hipLaunchKernelGGL(k_rows_sum4<bf16s>, g4, dim3(256), 0, st, a);
+      if (a.out_norm) hipLaunchKernelGGL(k_rows_norm4<bf16s>, g4, dim3(256), 0, st, a, nblk);
+    } else {
+      hipLaunchKernelGGL(k_rows_sum4<float>, g4, dim3(256), 0, st, a);
+      if (a.out_norm) hipLaunchKernelGGL(k_rows_norm4<float>, g4, dim3(256), 0, st, a, nblk);
+    }
+    return;
+  }
   if (dtype == EAGLE_BF16) {
     hipLaunchKernelGGL(k_rows_sum<bf16s>, grid, dim3(256), 0, st, a);
     if (a.out_norm) hipLaunchKernelGGL(k_rows_norm<bf16s>, grid, dim3(256), 0, st, a);
