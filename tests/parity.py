@@ -566,6 +566,11 @@ def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:
     snaps = gr.run(target=tgt, snapshots=True, attend=attend)
     torch.cuda.synchronize()
     say("GPU round done")
+    # every row, every step: confidences are probabilities, so path values
+    # never grow and the kept set stays ancestor-closed
+    for s, sn in enumerate(snaps):
+        over = np.argwhere(sn.topk_conf > 1.0)
+        assert over.size == 0, f"step {s}: confidence above 1 at (row, rank) {over[:4].tolist()}"
     report = {}
     for s in range(cfg.gamma):
         rows = None
