@@ -699,7 +699,38 @@ __global__ __launch_bounds__(256) void k_epi_act(ActArgs a) {
   DT<T>::st((T*)a.out + t, y);
 }
 
+// The same activation, four columns per thread (16-byte partial loads, one
+// 8- or 16-byte store), grid (column blocks, rows): no 64-bit index division.
+// Used from 64 rows when F is a multiple of 4 and the buffers 16-byte aligned.
+template <typename T>
+__global__ __launch_bounds__(256) void k_epi_act4(ActArgs a) {
+  const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int m = blockIdx.y;
+  if (j >= a.F) return;
+  const int N = a.swiglu ? 2 * a.F : a.F;
+  const int64_t pst = (int64_t)a.M * N;
+  const float* row = a.P + (int64_t)m * N;
+  f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f}, gs = u;
+  for (int s = 0; s < a.S; ++s) {
+    u += *reinterpret_cast<const f32x4*>(row + s * pst + (a.swiglu ? a.F : 0) + j);
+    if (a.swiglu) gs += *reinterpret_cast<const f32x4*>(row + s * pst + j);
+  }
+  f32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (a.swiglu) y[e] = gs[e] / (1.0f + expf(-gs[e])) * u[e];
+    else y[e] = 0.5f * u[e] * (1.0f + erff(u[e] * 0.70710678118654752f));
+  }
+  st4<T>((T*)a.out + (int64_t)m * a.F + j, y);
+}
+
 void launch_epi_act(int dtype, const ActArgs& a, hipStream_t st) {
+  if (a.M >= 64 && a.F % 4 == 0 && al16(a.P) && al16(a.out)) {
+    const dim3 g4((a.F / 4 + 255) / 256, a.M);
+    if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_act4<bf16s>, g4, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_epi_act4<float>, g4, dim3(256), 0, st, a);
+    return;
+  }
   dim3 grid((unsigned)(((int64_t)a.M * a.F + 255) / 256));
   if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_act<bf16s>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_epi_act<float>, grid, dim3(256), 0, st, a);
