@@ -624,60 +624,67 @@ void launch_reduce_rows(int dtype, const ReduceArgs& a0, hipStream_t st) {
 // is formed and reduced in double precision.
 template <typename T>
 __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
+  // grid (pair blocks of a row, rows): the row and its position are uniform
+  // across the workgroup, the (head, pair) index needs only 32-bit arithmetic
   const int half = a.hd / 2;
   const int heads = a.Hq + 2 * a.Hkv;
-  const int64_t total = (int64_t)a.M * heads * half;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  const int i = (int)(t % half);
-  const int h = (int)((t / half) % heads);
-  const int m = (int)(t / ((int64_t)half * heads));
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= heads * half) return;
+  const int i = t % half;
+  const int h = t / half;
   const int N = heads * a.hd;
   const int c1 = h * a.hd + i, c2 = c1 + half;
   const int64_t pst = (int64_t)a.M * N;
-  float x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S);
-  float x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S);
-  int pos;
-  int64_t row = m;
-  if (a.pos) pos = a.pos[m];
-  else {  // packed context rows: position inside the request
-    int b = 0;
-    while (b + 1 < a.B && a.cu_row[b + 1] <= m) ++b;
-    pos = m - a.cu_row[b];
-    if (a.n_new) {
-      const int nb = a.n[b];
-      pos += nb - a.n_new[b];
-      row = (int64_t)a.cu_n[b] + pos;
-      if (pos < 0 || pos >= nb || row >= a.total_rows) return;
-    }
-  }
   const bool is_v = h >= a.Hq + a.Hkv;
-  if (!is_v && a.theta > 0.f) {
-    double inv = exp2(-(2.0 * i / a.hd) * log2((double)a.theta));
-    double ang = (double)pos * inv;
-    ang -= 6.283185307179586 * rint(ang / 6.283185307179586);
-    float cs, sn;
-    sincosf((float)ang, &sn, &cs);
-    float y1 = x1 * cs - x2 * sn;
-    float y2 = x2 * cs + x1 * sn;
-    x1 = y1;
-    x2 = y2;
+  // the rotation's frequency depends on the pair only
+  double inv = 0.0;
+  if (!is_v && a.theta > 0.f) inv = exp2(-(2.0 * i / a.hd) * log2((double)a.theta));
+  for (int m = blockIdx.y; m < a.M; m += gridDim.y) {
+    float x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S);
+    float x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S);
+    int pos;
+    int64_t row = m;
+    bool skip = false;
+    if (a.pos) pos = a.pos[m];
+    else {  // packed context rows: position inside the request
+      int b = 0;
+      while (b + 1 < a.B && a.cu_row[b + 1] <= m) ++b;
+      pos = m - a.cu_row[b];
+      if (a.n_new) {
+        const int nb = a.n[b];
+        pos += nb - a.n_new[b];
+        row = (int64_t)a.cu_n[b] + pos;
+        skip = pos < 0 || pos >= nb || row >= a.total_rows;
+      }
+    }
+    if (skip) continue;
+    if (!is_v && a.theta > 0.f) {
+      double ang = (double)pos * inv;
+      ang -= 6.283185307179586 * rint(ang / 6.283185307179586);
+      float cs, sn;
+      sincosf((float)ang, &sn, &cs);
+      float y1 = x1 * cs - x2 * sn;
+      float y2 = x2 * cs + x1 * sn;
+      x1 = y1;
+      x2 = y2;
+    }
+    T* dst;
+    if (h < a.Hq) {
+      dst = (T*)a.q + ((int64_t)m * a.Hq + h) * a.hd;
+    } else {
+      const int kh = is_v ? h - a.Hq - a.Hkv : h - a.Hq;
+      const int64_t r = a.kv_idx ? (int64_t)a.kv_idx[m] : row;
+      dst = (T*)(is_v ? a.v : a.k) + (r * a.Hkv + kh) * a.hd;
+    }
+    DT<T>::st(dst + i, x1);
+    DT<T>::st(dst + i + half, x2);
   }
-  T* dst;
-  if (h < a.Hq) {
-    dst = (T*)a.q + ((int64_t)m * a.Hq + h) * a.hd;
-  } else {
-    const int kh = is_v ? h - a.Hq - a.Hkv : h - a.Hq;
-    const int64_t r = a.kv_idx ? (int64_t)a.kv_idx[m] : row;
-    dst = (T*)(is_v ? a.v : a.k) + (r * a.Hkv + kh) * a.hd;
-  }
-  DT<T>::st(dst + i, x1);
-  DT<T>::st(dst + i + half, x2);
 }
 
 void launch_epi_qkv(int dtype, const QkvArgs& a, hipStream_t st) {
-  const int64_t total = (int64_t)a.M * (a.Hq + 2 * a.Hkv) * (a.hd / 2);
-  dim3 grid((unsigned)((total + 255) / 256));
+  const int pairs = (a.Hq + 2 * a.Hkv) * (a.hd / 2);
+  dim3 grid((unsigned)((pairs + 255) / 256), (unsigned)std::min(a.M, 65535));
+  if (a.M <= 0) return;
   if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_qkv<bf16s>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_epi_qkv<float>, grid, dim3(256), 0, st, a);
 }
