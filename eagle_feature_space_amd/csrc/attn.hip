@@ -570,6 +570,20 @@ void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
 // One workgroup per (head, row); split weights are formed once in LDS, then
 // every thread folds its d over the splits in split order.
 constexpr int kMaxParts = 1024;
+template <int NB>
+__device__ __forceinline__ float fold_parts(const float* po, int64_t stride, int np, const float* wts) {
+  float O = 0.f;
+  for (int s0 = 0; s0 < np; s0 += NB) {
+    float v[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) v[q] = po[(int64_t)min(s0 + q, np - 1) * stride];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+      if (s0 + q < np) O += wts[s0 + q] * v[q];
+  }
+  return O;
+}
+
 template <typename T>
 __global__ __launch_bounds__(128) void k_attn_combine(CombineArgs a) {
   __shared__ float wts[kMaxParts];
@@ -613,18 +627,14 @@ __global__ __launch_bounds__(128) void k_attn_combine(CombineArgs a) {
   __syncthreads();
   L = red[1][0] + red[1][1];
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  // O = sum_s weight_s O_s in split order; up to 16 partial loads in flight
+  // O = sum_s weight_s O_s in split order; batches of loads in flight sized to
+  // the split count (a short list is not padded to 16 repeated loads)
   for (int d = tid; d < a.hd; d += 128) {
     const float* po = a.part_o + base * a.hd + d;
-    float O = 0.f;
-    for (int s0 = 0; s0 < np; s0 += 16) {
-      float v[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) v[q] = po[(int64_t)min(s0 + q, np - 1) * stride * a.hd];
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (s0 + q < np) O += wts[s0 + q] * v[q];
-    }
+    float O;
+    if (np <= 4) O = fold_parts<4>(po, stride * a.hd, np, wts);
+    else if (np <= 8) O = fold_parts<8>(po, stride * a.hd, np, wts);
+    else O = fold_parts<16>(po, stride * a.hd, np, wts);
     DT<T>::st((T*)a.out + base * a.hd + d, O * inv);
   }
 }
