@@ -560,14 +560,18 @@ __global__ __launch_bounds__(256) void k_rows_norm4(ReduceArgs a, int nblk) {
     gn = ld4<T>((const T*)a.gain + n);
     if (a.bias) bs = ld4<T>((const T*)a.bias + n);
   }
-  // the row's block statistics, summed in block order (every lane alike)
+  // the row's block statistics: lane l sums blocks l, l + 64, ... and the
+  // wave reduces in a fixed butterfly order (all loads in flight at once;
+  // every wave of the row forms the same sums)
   const float* st = a.stats + (int64_t)m * nblk * 2;
   float s1 = 0.f, s2 = 0.f;
-  for (int b = 0; b < nblk; ++b) {
+  for (int b = lane; b < nblk; b += 64) {
     const float2 v = *reinterpret_cast<const float2*>(st + 2 * b);
     s1 += v.x;
     s2 += v.y;
   }
+  s1 = __shfl(wave_sum(s1), 0, 64);   // lane 0's association for the whole row
+  s2 = __shfl(wave_sum(s2), 0, 64);
   if (!live) return;
   const float mean = a.layer_norm ? s1 / a.N : 0.f;
   const float var = s2 / a.N - mean * mean;
