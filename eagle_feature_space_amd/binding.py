@@ -63,7 +63,7 @@ _LAYOUT_FIELDS = ("pool_tok", "pool_parent", "pool_depth", "pool_slot", "pool_co
                   "row_node", "row_tok", "row_pos", "row_slot", "row_pidx", "row_mask",
                   "topk_id", "topk_conf", "lse",
                   "f_node", "f_tok", "f_parent", "f_depth", "f_pos", "f_mask", "f_count",
-                  "choice", "choice_part", "total")
+                  "choice", "choice_part", "status", "total")
 
 
 class eagle_tree_layout(ctypes.Structure):

@@ -37,7 +37,9 @@ int build_geo(const eagle_tree* t, Geo* g) {
   if (!t) return EAGLE_EINVAL;
   if (t->B < 1 || t->gamma < 1 || t->top_k < 1) return EAGLE_EINVAL;
   if (t->top_k > EAGLE_MAX_TOPK) return EAGLE_EUNSUPPORTED;
-  if (!(t->inv_temp > 0.f)) return EAGLE_EINVAL;
+  // finite and bounded, so s * logit stays finite for any finite logit of
+  // the model (a NaN confidence would still be ordered last by the expansion)
+  if (!(t->inv_temp > 0.f) || !(t->inv_temp <= EAGLE_MAX_INV_TEMP)) return EAGLE_EINVAL;
   if (t->sample != 0 && t->sample != 1) return EAGLE_EINVAL;
   g->kind = t->kind;
   g->B = t->B;
@@ -154,6 +156,7 @@ void layout_of(const Geo& g, eagle_tree_layout* L) {
   L->f_count = bp.take(B * 4);
   L->choice = bp.take(B * kMaxPos * 4);
   L->choice_part = bp.take(B * kMaxPos * kVerifySplits * 8);
+  L->status = bp.take(B * 4);
   L->total = bp.off;
 }
 
@@ -206,6 +209,7 @@ TreeDev tree_dev(const eagle_tree* t, const Geo& g, int step = 0) {
   d.f_count = (int32_t*)(s + L.f_count);
   d.choice = (int32_t*)(s + L.choice);
   d.choice_part = (float2*)(s + L.choice_part);
+  d.status = (int32_t*)(s + L.status);
   d.pool_cap = g.pool_cap;
   d.max_rows = g.max_rows;
   d.positions = g.positions;

@@ -212,6 +212,7 @@ struct TreeDev {          // device pointers into eagle_tree.state
   int32_t* f_count;
   int32_t* choice;
   float2* choice_part;    // [B][64][kVerifySplits] (max value, index as float bits)
+  int32_t* status;        // [B] 0 = consistent, else EAGLE_TREE_STATE_BAD
   int pool_cap, max_rows, positions;
 };
 

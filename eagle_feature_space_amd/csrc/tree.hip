@@ -47,6 +47,7 @@ __global__ void k_tree_init(TreeDev t, int B, int eagle3, int vocab, const int32
   t.row_pidx[b] = eagle3 ? max(cu_n[b + 1] - 1, 0) : b;
   t.row_mask[b] = m0;
   t.f_count[b] = 0;
+  t.status[b] = 0;
 }
 
 void launch_tree_init(const TreeDev& t, int B, int eagle3, int vocab, const int32_t* root_tok,
@@ -55,8 +56,15 @@ void launch_tree_init(const TreeDev& t, int B, int eagle3, int vocab, const int3
                      root_tok, n, cu_n);
 }
 
-// key order: value desc, depth asc, index asc
+// Path values lie in [0, 1]; a NaN one (from a NaN logit row) ranks below
+// every other value, so the orders below stay total and every rank is a
+// permutation of the nodes compared.
+__device__ __forceinline__ float vkey(float v) { return v == v ? v : -1.0f; }
+
+// key order: value desc, depth asc, index asc (values through vkey)
 __device__ __forceinline__ bool before(float va, int da, int ia, float vb, int db, int ib) {
+  va = vkey(va);
+  vb = vkey(vb);
   if (va != vb) return va > vb;
   if (da != db) return da < db;
   return ia < ib;
@@ -85,10 +93,14 @@ __global__ __launch_bounds__(kExpandThreads) void k_tree_expand(TreeDev t, RowsD
   const int nchild = kind == EAGLE_TREE_DYNAMIC ? W * top_k : plan.nchild;
   const int rp = t.root_pos[b];
   const int64_t pb = (int64_t)b * P;
-  // a call out of order (pool or slots already full) must not write past them
-  if (p0 < 1 || p0 + nchild > P) return;
-  if (!final_step && t.slot_count[b] + (kind == EAGLE_TREE_DYNAMIC ? min(top_k, nchild) : plan.nnext) > kSlots)
+  // a call out of order (pool or slots already full) must not write past
+  // them: flag the request (its verify then reports accept_len -1)
+  if (p0 < 1 || p0 + nchild > P ||
+      (!final_step &&
+       t.slot_count[b] + (kind == EAGLE_TREE_DYNAMIC ? min(top_k, nchild) : plan.nnext) > kSlots)) {
+    if (tid == 0) t.status[b] = EAGLE_TREE_STATE_BAD;
     return;
+  }
 
   // 1. append the children of this step's rows (their values also go to LDS)
   for (int cidx = tid; cidx < nchild; cidx += NT) {
@@ -120,11 +132,11 @@ __global__ __launch_bounds__(kExpandThreads) void k_tree_expand(TreeDev t, RowsD
       nnext = min(top_k, nchild);
       for (int cidx = tid; cidx < nchild; cidx += NT) {
         const int u = p0 + cidx;
-        const float vu = sval[u];
+        const float vu = vkey(sval[u]);
         int rank = 0;
         for (int j = 0; j < nchild; ++j) {
           const int v = p0 + j;
-          const float vv = sval[v];
+          const float vv = vkey(sval[v]);
           if (vv > vu || (vv == vu && v < u)) ++rank;
         }
         if (rank < nnext) snext[rank] = u;
@@ -193,10 +205,14 @@ __global__ __launch_bounds__(kExpandThreads) void k_tree_expand(TreeDev t, RowsD
     total += c;
   }
   const int pos = before_waves + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-  if (u < pn) spos[u] = keep ? pos : -1;
+  // the ranks form a total order, so at most top_m + 1 (dynamic) or the whole
+  // template (<= 64 positions, checked on the host) are kept; positions past
+  // the verify tree's 64 are never written
+  if (u < pn) spos[u] = keep && pos < kMaxPos ? pos : -1;
   if (tid == 0) {
-    t.f_count[b] = total;
+    t.f_count[b] = min(total, kMaxPos);
     t.pool_count[b] = pn;
+    if (total > kMaxPos) t.status[b] = EAGLE_TREE_STATE_BAD;
   }
   __syncthreads();
   if (u < pn && spos[u] >= 0) {
@@ -225,6 +241,10 @@ void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, 
 }
 
 // ---------------------------------------------------------------- verify
+// A NaN logit counts as -inf, so every slice with at least one id has an
+// argmax inside the vocabulary.
+__device__ __forceinline__ float nan_low(float v) { return v == v ? v : -INFINITY; }
+
 // Argmax of one vocabulary slice of one verify position (value desc, lowest
 // index on ties); grid = (position, request, slice).
 template <typename T>
@@ -248,20 +268,20 @@ __global__ __launch_bounds__(256) void k_verify_argmax(TreeDev t, const T* logit
       const u32x4 x = ld16(row + q * VEC);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float v = DT<T>::elem(x, e);
+        const float v = nan_low(DT<T>::elem(x, e));
         const int j = q * VEC + e;
         if (better(v, j, bv, bi)) { bv = v; bi = j; }
       }
     }
   } else {
     for (int j = q0 * VEC + threadIdx.x; j < q1 * VEC; j += 256) {
-      const float v = DT<T>::ld(row + j);
+      const float v = nan_low(DT<T>::ld(row + j));
       if (better(v, j, bv, bi)) { bv = v; bi = j; }
     }
   }
   if (sp == kVerifySplits - 1)   // ragged tail past the last whole granule
     for (int j = nvec * VEC + threadIdx.x; j < V; j += 256) {
-      const float v = DT<T>::ld(row + j);
+      const float v = nan_low(DT<T>::ld(row + j));
       if (better(v, j, bv, bi)) { bv = v; bi = j; }
     }
   wave_best(bv, bi);
@@ -277,7 +297,7 @@ __global__ __launch_bounds__(256) void k_verify_argmax(TreeDev t, const T* logit
 }
 
 // target choice at a verify position: best of its slices, in slice order
-__device__ __forceinline__ int verify_choice(const TreeDev& t, int b, int u) {
+__device__ __forceinline__ int verify_choice(const TreeDev& t, int b, int u, int vocab) {
   const float2* p = t.choice_part + ((int64_t)b * kMaxPos + u) * kVerifySplits;
   float bv = p[0].x;
   int bi = __float_as_int(p[0].y);
@@ -285,23 +305,28 @@ __device__ __forceinline__ int verify_choice(const TreeDev& t, int b, int u) {
     const int i = __float_as_int(p[s].y);
     if (better(p[s].x, i, bv, bi)) { bv = p[s].x; bi = i; }
   }
+  if (bi < 0 || bi >= vocab) bi = 0;   // not reached: slice 0 always holds an id
   t.choice[b * kMaxPos + u] = bi;
   return bi;
 }
 
-__global__ void k_verify_walk(TreeDev t, int B, int gamma, int32_t* accept_len,
+__global__ void k_verify_walk(TreeDev t, int B, int gamma, int vocab, int32_t* accept_len,
                               int32_t* accept_path, int32_t* out_tokens) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
-  const int T = t.f_count[b];
+  const int T = min(t.f_count[b], kMaxPos);
   const int fb = b * kMaxPos;
   int32_t* path = accept_path + (int64_t)b * (gamma + 1);
   int32_t* out = out_tokens + (int64_t)b * (gamma + 1);
   for (int i = 0; i <= gamma; ++i) { path[i] = -1; out[i] = -1; }
+  if (t.status[b] != 0 || T < 1) {   // inconsistent tree state: nothing to verify
+    accept_len[b] = -1;
+    return;
+  }
   int u = 0, acc = 0;
   path[0] = 0;
   for (int it = 0; it <= gamma; ++it) {
-    const int choice = verify_choice(t, b, u);
+    const int choice = verify_choice(t, b, u, vocab);
     int nxt = -1;
     for (int v = u + 1; v < T; ++v)
       if (t.f_parent[fb + v] == u && t.f_tok[fb + v] == choice) { nxt = v; break; }
@@ -327,8 +352,8 @@ void launch_verify(const TreeDev& t, int B, const void* logits, int positions, i
   else
     hipLaunchKernelGGL(k_verify_argmax<float>, grid, dim3(256), 0, st, t, (const float*)logits,
                        positions, vocab);
-  hipLaunchKernelGGL(k_verify_walk, dim3((B + 63) / 64), dim3(64), 0, st, t, B, gamma, accept_len,
-                     accept_path, out_tokens);
+  hipLaunchKernelGGL(k_verify_walk, dim3((B + 63) / 64), dim3(64), 0, st, t, B, gamma, vocab,
+                     accept_len, accept_path, out_tokens);
 }
 
 // ------------------------------------------------- stochastic verification
@@ -417,7 +442,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(
   __shared__ double s_tgt, s_pre[NW];
   __shared__ int s_last[NW];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T_ = t.f_count[b];
+  const int T_ = min(t.f_count[b], kMaxPos);
   const int fb = b * kMaxPos;
   const int nvec = V / VEC;
   const int NQ = (V + VEC - 1) / VEC;             // granules, the last one maybe partial
@@ -429,6 +454,13 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(
     s_par[tid] = tid < T_ ? t.f_parent[fb + tid] : -2;
   }
   if (tid <= gamma) { path[tid] = tid == 0 ? 0 : -1; out[tid] = -1; }
+  if (t.status[b] != 0 || T_ < 1) {   // inconsistent tree state: nothing to verify
+    if (tid == 0) {
+      path[0] = -1;
+      accept_len[b] = -1;
+    }
+    return;
+  }
   __syncthreads();
 
   u32x4 raw[H];
@@ -611,6 +643,11 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(
       __syncthreads();
       pick = s_pick >= 0 ? s_pick : lastb;   // target at or past the round total (rounding)
     }
+    // No residual mass left in fp32 (the rejected children held all of it,
+    // e.g. a near-one-hot row): the last child tried is the token; a row with
+    // no finite probability at all emits token 0.
+    if (pick < 0) pick = s_nex > 0 ? s_excl[s_nex - 1] : 0;
+    if (pick >= V) pick = V - 1;
     if (tid == 0) {
       out[acc] = pick;
       accept_len[b] = acc;

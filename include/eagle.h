@@ -66,6 +66,7 @@ enum { EAGLE_TREE_CHAIN = 0, EAGLE_TREE_STATIC = 1, EAGLE_TREE_DYNAMIC = 2 };
 #define EAGLE_MAX_SLOTS 64      /* expanded nodes per request (64-bit masks)   */
 #define EAGLE_MAX_POSITIONS 64  /* verify-tree positions per request (root+m)  */
 #define EAGLE_MAX_TOPK 16
+#define EAGLE_MAX_INV_TEMP 65536.0f  /* largest inverse temperature s of the draft */
 #define EAGLE_VERIFY_DRAWS 17   /* uniforms per verify position: 16 child tests + 1 residual draw */
 
 /*
@@ -159,7 +160,8 @@ typedef struct eagle_tree {
   int32_t B, gamma, top_k, top_m;
   int32_t n_template;            /* STATIC: number of non-root nodes      */
   const int32_t *template_parent;/* STATIC: HOST array [n_template]       */
-  float inv_temp;                /* s in conf = softmax(s * logits)       */
+  float inv_temp;                /* s in conf = softmax(s * logits):
+                                    0 < s <= EAGLE_MAX_INV_TEMP           */
   void *state;                   /* device */
   size_t state_bytes;
   /* Sampled drafting ("Speculative Decoding Deep Dive III", EAGLE-1
@@ -193,7 +195,12 @@ typedef struct eagle_tree {
  *   choice [B][64] int32: target's greedy token per verify position
  *   choice_part [B][64][16] (float max, int32 index): argmax of each of the
  *     16 vocabulary slices of a verify position's target logits
+ *   status [B] int32: 0 while request b's tree state is consistent; set to
+ *     EAGLE_TREE_STATE_BAD by an expansion that finds its pool or slots
+ *     already full (calls out of order); eagle_tree_init clears it, and a
+ *     verify of a flagged request reports accept_len[b] = -1
  */
+#define EAGLE_TREE_STATE_BAD 1
 typedef struct eagle_tree_layout {
   int32_t pool_cap, max_rows, positions;
   size_t pool_tok, pool_parent, pool_depth, pool_slot, pool_conf, pool_value;
@@ -202,6 +209,7 @@ typedef struct eagle_tree_layout {
   size_t topk_id, topk_conf, lse;
   size_t f_node, f_tok, f_parent, f_depth, f_pos, f_mask, f_count;
   size_t choice, choice_part;
+  size_t status;
   size_t total;
 } eagle_tree_layout;
 

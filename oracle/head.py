@@ -178,11 +178,15 @@ class DraftHead:
             z = gelu(b @ self.w["w_up"].T)
         return z @ self.w["w_down"].T
 
-    def finish(self, h, attn):
+    def finish(self, h, attn, store=None):
         """Given the layer input h [R, d] and attention output [R, Hq, hd]:
-        h1 = h + o W_o^T; out = h1 + MLP(N2(h1))."""
+        h1 = h + o W_o^T; out = h1 + MLP(N2(h1)).  store: optional map applied
+        to the residual stream h1 (e.g. rounding to the storage type of a bf16
+        model); the caller applies it to the output."""
         R = h.shape[0]
         h1 = h + attn.reshape(R, -1) @ self.w["w_o"].T
+        if store is not None:
+            h1 = store(h1)
         return h1 + self.mlp(h1)
 
     def layer(self, h, pos, keys):

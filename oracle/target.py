@@ -43,8 +43,8 @@ def tree_forward(layers, emb, final_g, eps, lm_head, tok, pos, masks, ctx, store
     at a time); emb [V, d]; final_g [d]; lm_head [V, d]; tok, pos [T];
     masks [T] ancestor-or-self bitmasks over positions; ctx: list of L pairs
     (K [n, Hkv, hd], V [n, Hkv, hd]), the layer's context cache; store:
-    optional map applied to every layer's output rows (e.g. rounding to the
-    storage type of a bf16 model).
+    optional map applied to the residual stream, after attention and after
+    every layer (e.g. rounding to the storage type of a bf16 model).
     Returns (logits [T, V], per-layer tree keys and values [(k, v)] of shape
     [T, Hkv, hd]).
     """
@@ -61,7 +61,7 @@ def tree_forward(layers, emb, final_g, eps, lm_head, tok, pos, masks, ctx, store
             sel = mask_bits(masks[u], T)
             att[u] = attend(q[u], np.concatenate([ck, k[sel]]), np.concatenate([cv, v[sel]]),
                             layer.group)
-        x = layer.finish(x, att)
+        x = layer.finish(x, att, store)
         if store is not None:
             x = store(x)
         kv_tree.append((k, v))

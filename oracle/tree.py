@@ -19,7 +19,7 @@ Readings where the pages are silent (listed in the design notes):
   * the dynamic frontier at step s >= 1 is the top_k nodes of the newest depth
     by value (beam width top_k); unexpanded nodes stay in the pool;
   * ordering keys: top-k by (logit desc, id asc); frontier and rerank by
-    (value desc, depth asc, creation index asc);
+    (value desc, depth asc, creation index asc), a NaN value below all others;
   * value(root) = 1 and value(child) = float32(value(parent) * conf(child));
   * creation order = (step, frontier rank of the parent, child rank); the
     verify tree lists the kept nodes in creation order, root first;
@@ -128,8 +128,11 @@ class RequestTree:
             self.slot_mask.append(pm | (1 << s))
 
     def key(self, u):
-        """Frontier / rerank order: value desc, depth asc, creation index asc."""
-        return (-float(self.value[u]), self.depth[u], u)
+        """Frontier / rerank order: value desc, depth asc, creation index asc.
+        A NaN value (from a NaN logit row; values otherwise lie in [0, 1])
+        ranks below every other value, so the order stays total."""
+        v = float(self.value[u])
+        return (-(v if v == v else -1.0), self.depth[u], u)
 
     def expand(self, step, ids, conf):
         """Append the children produced by draft step `step`.

@@ -89,10 +89,14 @@ def target_probs(row, inv_temp):
 
 def residual_draw(p, excluded, u):
     """Inverse CDF over token ids of p with `excluded` tokens zeroed and the
-    rest renormalised: the smallest x whose cumulative mass exceeds u."""
+    rest renormalised: the smallest x whose cumulative mass exceeds u.  With
+    no mass left outside `excluded` (the rejected tokens held all of it) the
+    token is the last one excluded."""
     r = np.array(p, np.float64)
     r[list(excluded)] = 0.0
     c = np.cumsum(r)
+    if not c[-1] > 0.0:
+        return int(list(excluded)[-1]) if len(excluded) else 0
     target = u * c[-1]
     x = int(np.searchsorted(c, target, side="right"))
     x = min(x, len(r) - 1)

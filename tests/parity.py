@@ -170,16 +170,23 @@ def _check_topk(cfg, lg, lo, ids, conf, lse, s, m, worst, rk=0):
     ref_lse = zmax + np.log(np.exp(z - zmax).sum())
     assert abs(lse - ref_lse) <= 1e-5 * max(1.0, abs(ref_lse)) + 1e-5, (lse, ref_lse)
     np.testing.assert_allclose(conf, np.exp(z[ids] - ref_lse), rtol=1e-4, atol=1e-12)
-    # against the oracle: ids fixed wherever every gap up to the rank is clear
+    # against the oracle: wherever the gap between the oracle's i-th and
+    # (i+1)-th logits exceeds the tolerance, the top-(i+1) id sets are equal
+    # (also after a near-tie further up); ids are equal rank by rank up to the
+    # first gap that is not clear
     if cfg.sample_seed is None:
         tol = TOL * np.max(np.abs(lo))
         order = np.lexsort((np.arange(lo.size), -lo))
         srt = lo[order]
         clear = True
         for i in range(K):
-            clear = clear and (srt[i] - srt[i + 1] > tol)
+            gap_clear = bool(srt[i] - srt[i + 1] > tol)
+            clear = clear and gap_clear
             if clear:
                 assert ids[i] == order[i], f"step {s} row {m} rank {i}: {ids[i]} != {order[i]}"
+            if gap_clear:
+                assert set(int(x) for x in ids[:i + 1]) == set(int(x) for x in order[:i + 1]), \
+                    f"step {s} row {m}: top-{i + 1} id set {sorted(ids[:i + 1])} != {sorted(order[:i + 1])}"
     err = np.max(np.abs(lg.astype(np.float64) - lo))
     zo = st * lo.astype(np.float64)
     lse_o = zo.max() + np.log(np.exp(zo - zo.max()).sum())
@@ -465,6 +472,13 @@ def check_target_pass(case: Case, gr):
             e = rel_err(logits[b, u], ref[u])
             worst["t_logit"] = max(worst["t_logit"], e)
             assert e <= tol, f"target logits request {b} position {u}: rel err {e:.3g} > {tol:.3g}"
+            if rnd is not None:
+                # against the oracle that stores the residual stream in the
+                # model's dtype as the kernels do: the plain bar
+                eb = rel_err(logits[b, u], ref_b[u])
+                worst["t_logit_bf16store"] = max(worst.get("t_logit_bf16store", 0.0), eb)
+                assert eb <= TOL, f"target logits request {b} position {u}: rel err {eb:.3g} " \
+                                  f"against the bf16-storage oracle > {TOL}"
         if kt is not None:
             for l, (k, v) in enumerate(kvt):
                 e = max(rel_err(kt[l, b, :T], k), rel_err(vt[l, b, :T], v))
@@ -525,7 +539,7 @@ def check_tree_attend(case: Case, gr):
             ref = o_attend(q[u], K, V, hd.group).reshape(-1)
             got = out[b * T + u]
             err = float(np.max(np.abs(got.astype(np.float64) - ref)))
-            allowed = TOL * float(np.max(np.abs(ref))) + 1.5 * attn_bf16_bound(q[u], K, V, hd.group)
+            allowed = TOL * float(np.max(np.abs(ref))) + attn_bf16_bound(q[u], K, V, hd.group)
             assert err <= allowed, (b, u, err, allowed)
             worst = max(worst, err / allowed)
     return worst

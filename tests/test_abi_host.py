@@ -149,6 +149,15 @@ def test_rejects_bad_arguments_before_launch(lib):
     deep = C.RoundCfg(name="x", head=cfg.head, B=1, n=(4,), tree=C.TREE_DYNAMIC, gamma=9,
                       top_k=8, top_m=20)          # 1 + 8*8 expanded rows > 64 slots
     assert lib.eagle_tree_expand_rerank(_tree(deep, 1 << 20, 1 << 30), 0, None) == E.EAGLE_ECAPACITY
+    # the draft's inverse temperature: positive, finite, at most EAGLE_MAX_INV_TEMP
+    for temp in (0.0, -2.0, float("nan"), float("inf"), 1e30, 65536.5):
+        tb = _tree(cfg, state=1 << 20, nbytes=1 << 30)
+        tb.inv_temp = temp
+        assert lib.eagle_tree_expand_rerank(tb, 0, None) == E.EAGLE_EINVAL, temp
+        assert E.eagle_tree_state_bytes(tb) == 0, temp
+    tb = _tree(cfg)
+    tb.inv_temp = 65536.0
+    assert E.eagle_tree_state_bytes(tb) > 0
     # static template deeper than gamma
     st = C.SMALL_CONFIGS["s1_static"]
     bad = C.RoundCfg(name="x", head=st.head, B=1, n=(4,), tree=C.TREE_STATIC, gamma=3, top_k=4,

@@ -9,10 +9,12 @@ from eagle_feature_space_amd import configs as C
 
 pytestmark = pytest.mark.gpu
 
-# (workload, rows checked per draft step; None = all)
-FULL = [("c1_8b_static", None), ("c2_8b_dynamic", 6), ("c3_8b_eagle3", 4),
-        ("c4_70b_dynamic", 3), ("c5_8b_eagle3_steady", 4), ("c6_8b_target", None),
-        ("c7_8b_dynamic_steady", 6), ("c8_8b_dynamic_sampled", 6)]
+# (workload, rows checked per draft step; None = all).  Sampled rows are
+# spread evenly over the step, so at 512 rows the 16 rows fall in every
+# 64-row band of both 256-row tiles of the tiled kernels.
+FULL = [("c1_8b_static", None), ("c2_8b_dynamic", 12), ("c3_8b_eagle3", 8),
+        ("c4_70b_dynamic", 16), ("c5_8b_eagle3_steady", 8), ("c6_8b_target", None),
+        ("c7_8b_dynamic_steady", 8), ("c8_8b_dynamic_sampled", 8)]
 
 
 @pytest.mark.parametrize("name,rows", FULL, ids=[f[0] for f in FULL])

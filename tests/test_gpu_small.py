@@ -13,7 +13,7 @@ SMALL = ["c0_tiny_chain", "c0r_tiny_chain_rope", "s1_static", "s2_dynamic", "s3_
          "s10_chain_63", "s11_eagle3_steady_dynamic", "s12_eagle3_steady_chain", "s13_target_static",
          "s14_target_dynamic", "s15_target_f32", "s16_target_chain_rows",
          "s17_eagle1_steady_dynamic", "s18_eagle1_steady_chain", "s19_sampled_dynamic",
-         "s20_sampled_chain_b40", "s20_sampled_chain_b70"] + sorted(
+         "s20_sampled_chain_b40", "s20_sampled_chain_b70", "s21_dynamic_264"] + sorted(
              k for k in C.SMALL_CONFIGS if k.startswith("s7_chain_b"))
 
 
@@ -67,3 +67,37 @@ def test_profiling_every_family_eagle3():
         p = E.eagle_profile_read(fam)
         assert p["launches"] > 0 and p["timed"] == p["launches"] and p["ms"] > 0, (fam, p)
     E.eagle_profile_reset()
+
+
+def test_nan_feature_row_keeps_the_tree_in_bounds():
+    """A request whose root feature is NaN gets NaN logits, confidences and
+    path values.  Those values rank last, so the frontier and the kept set keep
+    their sizes: the verify tree stays within top_m + 1 positions with parents
+    in range, matches the oracle's tree logic on the GPU's (ids, conf), and
+    every emitted token is inside the vocabulary.  The other requests are
+    unaffected."""
+    import torch
+    from tests.parity import Case, check_tree_logic
+    cfg = C.SMALL_CONFIGS["s2_dynamic"]
+    case = Case(cfg)
+    f = case.inp.f_root.copy()
+    f[1] = 0x7FC0                                  # bf16 quiet NaN in every element
+    case.inp.f_root = f
+    print(f"\n[nan] {cfg.name} request 1 root feature NaN", flush=True)
+    gr = case.gpu()
+    snaps = gr.run(target=case.target_dev(), snapshots=True, attend=False)
+    torch.cuda.synchronize()
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    for b in range(cfg.B):
+        T = int(fv["count"][b])
+        assert 1 <= T <= cfg.top_m + 1, (b, T)
+        par = fv["parent"][b, :T]
+        assert par[0] == -1 and all(0 <= par[i] < i for i in range(1, T)), (b, par)
+    check_tree_logic(case, gr, snaps)
+    acc = gr.accept_len.cpu().numpy()
+    out = gr.out_tokens.cpu().numpy()
+    V = cfg.head.vocab
+    for b in range(cfg.B):
+        assert 0 <= int(acc[b]) <= cfg.gamma, (b, acc[b])
+        assert all(0 <= int(x) < V for x in out[b, :int(acc[b]) + 1]), (b, out[b])
+    assert np.isnan(snaps[1].topk_conf[cfg.top_k:2 * cfg.top_k]).all()

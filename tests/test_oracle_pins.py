@@ -143,6 +143,44 @@ def test_rope_closed_forms():
     np.testing.assert_array_equal(H.rope(q, np.array([7]), 0.0), q)   # theta 0: off
 
 
+def test_rope_frequency_schedule():
+    """Pair i of a head turns by pos * theta^(-2i/hd): with theta = 10^4 and
+    hd = 8 the four pairs turn by pos, pos/10, pos/100 and pos/1000 radians
+    (a schedule of theta^(-i/hd) or over hd/2 would move pairs 1-3)."""
+    hd, half, pos = 8, 4, 5
+    for i in range(half):
+        x = np.zeros((1, 1, hd))
+        x[0, 0, i] = 1.0                      # unit vector on pair i's first axis
+        y = H.rope(x, np.array([pos]), 10000.0)[0, 0]
+        ang = pos * 10.0 ** (-i)
+        want = np.zeros(hd)
+        want[i], want[i + half] = math.cos(ang), math.sin(ang)
+        np.testing.assert_allclose(y, want, atol=1e-15)
+        # the second axis of the pair turns the same way: (0, 1) -> (-sin, cos)
+        x2 = np.zeros((1, 1, hd))
+        x2[0, 0, i + half] = 1.0
+        y2 = H.rope(x2, np.array([pos]), 10000.0)[0, 0]
+        want2 = np.zeros(hd)
+        want2[i], want2[i + half] = -math.sin(ang), math.cos(ang)
+        np.testing.assert_allclose(y2, want2, atol=1e-15)
+
+
+def test_swiglu_roles():
+    """SwiGLU = W_down(silu(W_gate a) * W_up a): with d = ffn, W_gate = c I,
+    W_up = W_down = I and c != 1 the MLP branch is silu(c N2(x)) * N2(x),
+    which silu(W_up a) * W_gate a = silu(N2(x)) * c N2(x) does not equal."""
+    cfg = replace(TINY, ffn=TINY.d)
+    eye = np.eye(cfg.d)
+    c = 2.5
+    hd = _head(cfg, np.float64, w_gate=c * eye, w_up=eye, w_down=eye)
+    x = np.random.default_rng(11).standard_normal((3, cfg.d))
+    n2 = hd.norm(x, 2)
+    want = (c * n2) / (1.0 + np.exp(-c * n2)) * n2
+    np.testing.assert_allclose(hd.mlp(x), want, rtol=1e-13, atol=1e-14)
+    swapped = n2 / (1.0 + np.exp(-n2)) * (c * n2)
+    assert np.max(np.abs(hd.mlp(x) - swapped)) > 1e-2
+
+
 def test_attention_closed_forms():
     hd = 16
     rng = np.random.default_rng(6)
@@ -197,6 +235,32 @@ def test_static_template_shape():
     assert rows == [1, 4, 4, 4]
 
 
+def test_static_expansion_follows_template_ranks():
+    """Static tree ("Drafting a Tree, Not a Chain"): a node's template children
+    take its top-k ids in rank order; the frontier of the next step is the new
+    nodes with template children, in creation order.  Hand-built template
+    root -> {1, 2}, 1 -> {3, 4}, 2 -> {5} with known ids per row."""
+    tmpl = (0, 0, 1, 1, 2)
+    t = T.RequestTree.start(T.STATIC, root_tok=7, root_pos=10, gamma=2, top_k=3,
+                            template=tmpl)
+    # step 0: one row (the root); ranks 0, 1 become nodes 1, 2
+    t.expand(0, np.array([[100, 200, 300]]), np.array([[0.5, 0.25, 0.125]], np.float32))
+    assert t.tok == [7, 100, 200] and t.parent == [-1, 0, 0]
+    assert t.frontier == [1, 2]                      # both have template children
+    rows = t.rows()
+    assert [(r[0], r[2], r[3]) for r in rows] == [(1, 100, 11), (2, 200, 11)]
+    # step 1: row 0 is node 1 (two children), row 1 is node 2 (one child)
+    t.expand(1, np.array([[11, 12, 13], [21, 22, 23]]),
+             np.array([[0.5, 0.25, 0.125], [0.75, 0.125, 0.0625]], np.float32))
+    assert t.tok == [7, 100, 200, 11, 12, 21]
+    assert t.parent == [-1, 0, 0, 1, 1, 2]
+    assert t.depth == [0, 1, 1, 2, 2, 2]
+    assert [float(v) for v in t.value] == [1.0, 0.5, 0.25, 0.25, 0.125, 0.1875]
+    f = t.final_tree()
+    assert list(f["tok"]) == [7, 100, 200, 11, 12, 21]
+    assert list(f["pos"]) == [10, 11, 11, 12, 12, 12]
+
+
 def _closure(parent):
     """Ancestor-or-self relation by repeated composition (brute force)."""
     n = len(parent)
@@ -248,6 +312,37 @@ def test_values_masks_and_rerank(seed):
         for v in range(Tn):
             if bits[u, v]:
                 assert f["pos"][v] <= f["pos"][u] and v <= u
+
+
+def test_nan_values_rank_last_and_keep_the_tree_whole():
+    """A NaN confidence (a NaN logit row) gives NaN path values below it; they
+    rank after every finite value, so the frontier and the kept set keep
+    their sizes, the kept set stays ancestor-closed and fits the verify tree."""
+    t = T.RequestTree.start(T.DYNAMIC, root_tok=1, root_pos=0, gamma=3, top_k=3, top_m=7)
+    nan = np.float32("nan")
+    t.expand(0, np.array([[10, 11, 12]]), np.array([[nan, 0.5, 0.25]], np.float32))
+    assert t.frontier == [2, 3, 1]                  # the NaN child last
+    t.expand(1, np.array([[20, 21, 22], [30, 31, 32], [40, 41, 42]]),
+             np.array([[0.5, 0.25, 0.125], [nan, 0.5, 0.5], [0.5, 0.5, 0.5]], np.float32))
+    assert len(t.frontier) == 3 and all(not np.isnan(t.value[u]) for u in t.frontier)
+    t.expand(2, np.zeros((3, 3), np.int64), np.full((3, 3), 0.5, np.float32))
+    kept = t.rerank()
+    assert len(kept) == 7
+    assert all(not np.isnan(t.value[u]) for u in kept)
+    f = t.final_tree()
+    assert len(f["tok"]) == 8 and f["parent"][0] == -1
+    assert all(0 <= p < i for i, p in enumerate(f["parent"]) if i > 0)
+
+
+def test_residual_draw_with_no_mass_left_takes_the_last_rejected():
+    """A near-one-hot target whose only mass sat on rejected children leaves
+    no residual: the token is the last child rejected."""
+    p = np.zeros(8)
+    p[3] = 1.0
+    assert VF.residual_draw(p, [3], 0.7) == 3
+    p2 = np.zeros(8)
+    p2[[2, 5]] = 0.5
+    assert VF.residual_draw(p2, [5, 2], 0.1) == 2
 
 
 def test_frontier_is_top_k_of_newest_depth():
