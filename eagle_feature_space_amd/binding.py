@@ -105,8 +105,8 @@ def lib():
                                       ctypes.c_int, ctypes.c_float, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p], ctypes.c_int),
         "eagle_target_verify_logits": ([P(eagle_head), P(eagle_target), P(eagle_kv), P(eagle_tree),
-                                        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
-                                       ctypes.c_int),
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                        c_void_p], ctypes.c_int),
         "eagle_target_workspace_bytes": ([P(eagle_head), P(eagle_target), P(eagle_kv),
                                           P(eagle_tree)], c_size_t),
         "eagle_kv_commit": ([P(eagle_tree), ctypes.c_int, ctypes.c_int, ctypes.c_int, c_void_p,
@@ -230,10 +230,11 @@ def eagle_target_workspace_bytes(head, target, kv, tree):
 
 
 def eagle_target_verify_logits(head, target, kv, tree, logits_out, k_tree, v_tree, ws, ws_bytes,
-                               stream=None):
+                               stream=None, hidden_out=None):
     return _check(lib().eagle_target_verify_logits(
         ctypes.byref(head), ctypes.byref(target), ctypes.byref(kv), ctypes.byref(tree),
-        _ptr(logits_out), _ptr(k_tree), _ptr(v_tree), _ptr(ws), ws_bytes, _stream(stream)),
+        _ptr(logits_out), _ptr(k_tree), _ptr(v_tree), _ptr(hidden_out), _ptr(ws), ws_bytes,
+        _stream(stream)),
         "eagle_target_verify_logits")
 
 

@@ -1097,8 +1097,8 @@ size_t eagle_target_workspace_bytes(const eagle_head* head, const eagle_target* 
 
 int eagle_target_verify_logits(const eagle_head* head, const eagle_target* target,
                                const eagle_kv* kv, const eagle_tree* tree, float* logits_out,
-                               void* k_tree, void* v_tree, void* ws_v, size_t ws_bytes,
-                               void* stream) {
+                               void* k_tree, void* v_tree, void* hidden_out, void* ws_v,
+                               size_t ws_bytes, void* stream) {
   Geo g;
   int s;
   if ((s = check_head(head))) return s;
@@ -1123,9 +1123,12 @@ int eagle_target_verify_logits(const eagle_head* head, const eagle_target* targe
   uint64_t* t_mask = (uint64_t*)(ws + w.t_mask);
   launch_tree_rows_final(td, g.B, t_tok, t_kv, t_pos, t_mask, st);
   const bool rows = rows_gemm_ok(M, d, 32) && head->norm == EAGLE_NORM_RMS;
-  // layer inputs alternate between two row buffers; layer 0 reads the
+  // layer inputs alternate between two row buffers (or go to the caller's
+  // hidden_out, one [M][d] block per layer boundary); layer 0 reads the
   // embeddings of the verify-tree tokens
   void* xb[2] = {ws + w.h, ws + w.f};
+  const size_t hid = (size_t)M * d * esz(head);
+  auto xin = [&](int l) -> void* { return hidden_out ? (char*)hidden_out + l * hid : xb[l & 1]; };
   const size_t tree_kv = (size_t)g.B * kSlots * kvd * esz(head);
   for (int l = 0; l < target->n_layers; ++l) {
     const eagle_layer& L = target->layers[l];
@@ -1144,7 +1147,7 @@ int eagle_target_verify_logits(const eagle_head* head, const eagle_target* targe
     eagle_kv kl = *kv;
     kl.k_ctx = const_cast<void*>(L.k_ctx);
     kl.v_ctx = const_cast<void*>(L.v_ctx);
-    void* x = xb[l & 1];
+    void* x = xin(l);
     // N1 of the layer input (plain normalised rows; the row path takes them
     // without a folded scale)
     if (l == 0)
@@ -1162,7 +1165,7 @@ int eagle_target_verify_logits(const eagle_head* head, const eagle_target* targe
     io.vdst = v_tree ? (char*)v_tree + l * tree_kv : (void*)(ws + w.tv);
     io.kv_idx = t_kv;
     io.mask = t_mask;
-    io.out = xb[(l + 1) & 1];
+    io.out = xin(l + 1);
     layer_body(&hl, &kl, ws, w, rows, io, st);
   }
   // final RMSNorm, then the shared LM head into fp32 logits
@@ -1170,7 +1173,7 @@ int eagle_target_verify_logits(const eagle_head* head, const eagle_target* targe
   hf.norm = EAGLE_NORM_RMS;
   hf.norm1_g = target->final_norm_g;
   hf.norm1_b = nullptr;
-  reduce(&hf, nullptr, 0, M, d, rs(xb[target->n_layers & 1], nullptr, d), kNone, nullptr, kNone,
+  reduce(&hf, nullptr, 0, M, d, rs(xin(target->n_layers), nullptr, d), kNone, nullptr, kNone,
          ws + w.hn, 1, st);
   const double lm_bytes = (double)esz(head) * ((double)head->vocab * d + (double)M * d);
   const double lm_flops = 2.0 * M * (double)head->vocab * d;

@@ -153,7 +153,9 @@ class GpuRound:
         P = self.layout.positions
         self.t_logits = torch.empty((cfg.B, P, h.vocab), dtype=torch.float32, device=self.dev)
         self.k_tree = self.v_tree = None
+        self.t_hidden = None
         if keep_tree_kv:
+            self.t_hidden = torch.zeros((L + 1, cfg.B * P, h.d), dtype=self.dt, device=self.dev)
             self.k_tree = torch.zeros((L, cfg.B, E.MAX_SLOTS, h.n_kv, h.head_dim), dtype=self.dt,
                                       device=self.dev)
             self.v_tree = torch.zeros_like(self.k_tree)
@@ -164,9 +166,11 @@ class GpuRound:
             self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
 
     def target_logits(self, stream=None):
-        """The target's pass over the verify tree -> fp32 logits [B, positions, |V|]."""
+        """The target's pass over the verify tree -> fp32 logits [B, positions, |V|]
+        (with keep_hidden, every layer boundary's rows go to self.t_hidden)."""
         E.eagle_target_verify_logits(self.head, self.target, self.kv, self.tree, self.t_logits,
-                                     self.k_tree, self.v_tree, self.ws, self.ws.numel(), stream)
+                                     self.k_tree, self.v_tree, self.ws, self.ws.numel(), stream,
+                                     hidden_out=self.t_hidden)
         return self.t_logits
 
     def commit(self, layer, dst_row, k_dst, v_dst, stream=None):

@@ -268,6 +268,7 @@ int eagle_draft_step(const eagle_head *head, const eagle_kv *kv,
                      float *logits_out, void *feat_out, void *ws,
                      size_t ws_bytes, void *stream);
 
+
 /*
  * Grow the tree from draft step `step`'s top-k ("EAGLE-2: expand and
  * rerank"; chain and static trees follow their shape).  Writes the rows of
@@ -376,12 +377,16 @@ typedef struct eagle_target {
  * k_tree, v_tree: optional device [n_layers][B][64][Hkv][hd]: every layer's
  *         keys / values of the verify positions (for eagle_kv_commit); both
  *         NULL: kept in the workspace only
+ * hidden_out: optional device [n_layers + 1][B * positions][d] in the head
+ *         dtype: the residual stream entering every layer (entry 0 =
+ *         emb(f_tok)) and leaving the last one, as stored between kernels;
+ *         NULL: kept in the workspace only
  * ws:     device workspace of eagle_target_workspace_bytes
  */
 int eagle_target_verify_logits(const eagle_head *head, const eagle_target *target,
                                const eagle_kv *kv, const eagle_tree *tree,
                                float *logits_out, void *k_tree, void *v_tree,
-                               void *ws, size_t ws_bytes, void *stream);
+                               void *hidden_out, void *ws, size_t ws_bytes, void *stream);
 /* Workspace bytes eagle_target_verify_logits needs (0 on invalid arguments). */
 size_t eagle_target_workspace_bytes(const eagle_head *head, const eagle_target *target,
                                     const eagle_kv *kv, const eagle_tree *tree);

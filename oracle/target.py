@@ -35,6 +35,27 @@ def mask_bits(mask, T):
     return [j for j in range(T) if (m >> j) & 1]
 
 
+def tree_layer(layer, x, pos, masks, ctx, store=None):
+    """One decoder layer over the T tree positions of one request: rows x
+    [T, d] at position ids pos, row u attending to the layer's context cache
+    ctx = (K, V) and to the tree positions in its ancestor-or-self mask.
+    Returns (out [T, d], k, v [T, Hkv, hd])."""
+    T = len(x)
+    q, k, v = layer.qkv(x, np.asarray(pos))
+    att = np.empty_like(q)
+    ck, cv = ctx
+    for u in range(T):
+        sel = mask_bits(masks[u], T)
+        att[u] = attend(q[u], np.concatenate([ck, k[sel]]), np.concatenate([cv, v[sel]]),
+                        layer.group)
+    return layer.finish(x, att, store), k, v
+
+
+def final_logits(x, final_g, eps, lm_head):
+    """Final RMSNorm, then the shared LM head: logits [T, V]."""
+    return rms_norm(x, final_g, eps) @ lm_head.T
+
+
 def tree_forward(layers, emb, final_g, eps, lm_head, tok, pos, masks, ctx, store=None):
     """Target logits at every verify-tree position of one request.
 
@@ -48,24 +69,15 @@ def tree_forward(layers, emb, final_g, eps, lm_head, tok, pos, masks, ctx, store
     Returns (logits [T, V], per-layer tree keys and values [(k, v)] of shape
     [T, Hkv, hd]).
     """
-    T = len(tok)
     get = layers if callable(layers) else (lambda l: layers[l])
     x = emb[np.asarray(tok)]
     kv_tree = []
     for l in range(len(ctx)):
-        layer = get(l)
-        q, k, v = layer.qkv(x, np.asarray(pos))
-        att = np.empty_like(q)
-        ck, cv = ctx[l]
-        for u in range(T):
-            sel = mask_bits(masks[u], T)
-            att[u] = attend(q[u], np.concatenate([ck, k[sel]]), np.concatenate([cv, v[sel]]),
-                            layer.group)
-        x = layer.finish(x, att, store)
+        x, k, v = tree_layer(get(l), x, pos, masks, ctx[l], store)
         if store is not None:
             x = store(x)
         kv_tree.append((k, v))
-    return rms_norm(x, final_g, eps) @ lm_head.T, kv_tree
+    return final_logits(x, final_g, eps, lm_head), kv_tree
 
 
 def causal_forward(layers, emb, final_g, eps, lm_head, tokens, pos0, ctx):

@@ -228,9 +228,9 @@ def test_target_pass_and_commit_are_validated(lib):
     layers[2].v_ctx = 1 << 20
     ts = _tree(cfg, state=1 << 20, nbytes=1 << 30)
     # null logits, k_tree without v_tree, workspace too small
-    assert lib.eagle_target_verify_logits(h, tg, kv, ts, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
-    assert lib.eagle_target_verify_logits(h, tg, kv, ts, 1 << 20, 1 << 20, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
-    assert lib.eagle_target_verify_logits(h, tg, kv, ts, 1 << 20, None, None, 1 << 20, 16, None) == E.EAGLE_ECAPACITY
+    assert lib.eagle_target_verify_logits(h, tg, kv, ts, None, None, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
+    assert lib.eagle_target_verify_logits(h, tg, kv, ts, 1 << 20, 1 << 20, None, None, 1 << 20, 1 << 40, None) == E.EAGLE_EINVAL
+    assert lib.eagle_target_verify_logits(h, tg, kv, ts, 1 << 20, None, None, None, 1 << 20, 16, None) == E.EAGLE_ECAPACITY
     # commit: misaligned destination, bad dtype, rows not a 16-byte multiple, no rows
     a = 1 << 20
     assert lib.eagle_kv_commit(ts, 8, 128, 0, a, a, a, a, a, 100, a + 2, a, None) == E.EAGLE_EINVAL
