@@ -21,6 +21,7 @@ EAGLE_OK, EAGLE_EINVAL, EAGLE_EUNSUPPORTED, EAGLE_ECAPACITY, EAGLE_EHIP = 0, -1,
 MAX_SLOTS = 64
 MAX_POSITIONS = 64
 VERIFY_DRAWS = 17
+NOALLOC_SCRATCH_BYTES = 32 << 20   # EAGLE_NOALLOC_SCRATCH_BYTES
 
 
 class eagle_head(ctypes.Structure):
@@ -96,6 +97,9 @@ def lib():
         "eagle_draft_step": ([P(eagle_head), P(eagle_kv), P(eagle_tree), ctypes.c_int, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p], ctypes.c_int),
+        "eagle_draft_step_noalloc": ([P(eagle_head), P(eagle_kv), P(eagle_tree), ctypes.c_int,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+                                     ctypes.c_int),
         "eagle_tree_expand_rerank": ([P(eagle_tree), ctypes.c_int, c_void_p], ctypes.c_int),
         "eagle_tree_attend": ([P(eagle_head), P(eagle_kv), P(eagle_tree), c_void_p, c_void_p,
                                c_size_t, c_void_p], ctypes.c_int),
@@ -127,6 +131,7 @@ def lib():
 
 EXPORTED = ("eagle_version", "eagle_strerror", "eagle_tree_layout_of", "eagle_tree_state_bytes",
             "eagle_step_rows", "eagle_workspace_bytes", "eagle_tree_init", "eagle_draft_step",
+            "eagle_draft_step_noalloc",
             "eagle_tree_expand_rerank", "eagle_tree_attend", "eagle_tree_verify",
             "eagle_tree_verify_sample", "eagle_target_verify_logits",
             "eagle_target_workspace_bytes", "eagle_kv_commit",
@@ -194,6 +199,14 @@ def eagle_draft_step(head, kv, tree, step, f_root=None, lmh=None, ctx_tokens=Non
         ctypes.byref(head), ctypes.byref(kv), ctypes.byref(tree), step, _ptr(f_root), _ptr(lmh),
         _ptr(ctx_tokens), _ptr(logits_out), _ptr(feat_out), _ptr(ws), ws_bytes,
         _stream(stream)), f"eagle_draft_step({step})")
+
+
+def eagle_draft_step_noalloc(head, kv, tree, step, f_root=None, lmh=None, ctx_tokens=None,
+                             logits_out=None, feat_out=None, stream=None):
+    return _check(lib().eagle_draft_step_noalloc(
+        ctypes.byref(head), ctypes.byref(kv), ctypes.byref(tree), step, _ptr(f_root), _ptr(lmh),
+        _ptr(ctx_tokens), _ptr(logits_out), _ptr(feat_out), _stream(stream)),
+        f"eagle_draft_step_noalloc({step})")
 
 
 def eagle_tree_expand_rerank(tree, step, stream=None):

@@ -127,6 +127,7 @@ class GpuRound:
         self.out_tokens = torch.zeros((B, cfg.gamma + 1), dtype=torch.int32, device=self.dev)
         self.attn_out = None
         self.target = None
+        self.noalloc = False      # draft steps through eagle_draft_step_noalloc
         if cfg.target_layers > 0:
             self._build_target(keep_tree_kv)
 
@@ -220,6 +221,11 @@ class GpuRound:
         E.eagle_tree_init(self.head, self.kv, self.tree, self.root_tok, stream)
 
     def step(self, s, logits_out=None, feat_out=None, stream=None):
+        if self.noalloc:
+            E.eagle_draft_step_noalloc(self.head, self.kv, self.tree, s, f_root=self.f_root,
+                                       lmh=self.lmh, ctx_tokens=self.ctx_tokens,
+                                       logits_out=logits_out, feat_out=feat_out, stream=stream)
+            return
         E.eagle_draft_step(self.head, self.kv, self.tree, s, f_root=self.f_root, lmh=self.lmh,
                            ctx_tokens=self.ctx_tokens, logits_out=logits_out, feat_out=feat_out,
                            ws=self.ws, stream=stream)

@@ -268,6 +268,24 @@ int eagle_draft_step(const eagle_head *head, const eagle_kv *kv,
                      float *logits_out, void *feat_out, void *ws,
                      size_t ws_bytes, void *stream);
 
+/*
+ * eagle_draft_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step and arguments, with the workspace taken from a device array
+ * the library holds, EAGLE_NOALLOC_SCRATCH_BYTES on every GPU it runs on,
+ * until the process ends, instead of a caller buffer.  Nothing in the call
+ * allocates.  Returns EAGLE_ECAPACITY when eagle_workspace_bytes(head, kv,
+ * tree) exceeds the array (it covers the 8B-shaped static tree and the small
+ * shapes, not the large-batch trees), EAGLE_EHIP if the array's address
+ * cannot be obtained.  Every call on one GPU shares that GPU's array and
+ * leaves its contents behind: calls that overlap on one GPU race, whatever
+ * their streams, so order them on one stream.
+ */
+#define EAGLE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int eagle_draft_step_noalloc(const eagle_head *head, const eagle_kv *kv,
+                             const eagle_tree *tree, int step, const void *f_root,
+                             const void *lmh, const int32_t *ctx_tokens,
+                             float *logits_out, void *feat_out, void *stream);
 
 /*
  * Grow the tree from draft step `step`'s top-k ("EAGLE-2: expand and

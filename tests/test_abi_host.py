@@ -173,6 +173,25 @@ def test_rejects_bad_arguments_before_launch(lib):
     assert lib.eagle_strerror(E.EAGLE_ECAPACITY).startswith(b"capacity")
 
 
+def test_noalloc_step_is_validated(lib):
+    """eagle_draft_step_noalloc refuses a workspace larger than its array
+    (the 8B EAGLE-2 tree at B 8 needs ~400 MB) and bad arguments, before any
+    HIP call; the header's array size matches the binding's."""
+    txt = open(os.path.join(ROOT, "include", "eagle.h")).read()
+    m = re.search(r"#define EAGLE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == E.NOALLOC_SCRATCH_BYTES
+    cfg = C.CONFIGS["c2_8b_dynamic"]
+    h, kv = _head(cfg.head), _kv(cfg, list(cfg.n))
+    t = _tree(cfg, state=1 << 20, nbytes=1 << 30)
+    assert E.eagle_workspace_bytes(h, kv, t) > E.NOALLOC_SCRATCH_BYTES
+    assert lib.eagle_draft_step_noalloc(h, kv, t, 0, 1 << 20, None, None, None, None, None) == E.EAGLE_ECAPACITY
+    small = C.SMALL_CONFIGS["s2_dynamic"]
+    hs, kvs = _head(small.head), _kv(small, list(small.n))
+    ts = _tree(small, state=1 << 20, nbytes=1 << 30)
+    ts.inv_temp = float("nan")
+    assert lib.eagle_draft_step_noalloc(hs, kvs, ts, 0, 1 << 20, None, None, None, None, None) == E.EAGLE_EINVAL
+
+
 def test_steady_state_kv_is_validated(lib):
     """Steady state: n_new needs cu_new and 1 <= total_new / B; step 0 needs
     the ingest inputs (EAGLE-1 too); the workspace is sized by the new rows."""
