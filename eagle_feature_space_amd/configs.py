@@ -270,9 +270,12 @@ for _i, _b in enumerate((40, 70)):
         seed_w=1120 + _i, seed_in=2120 + _i, seed_t=3120 + _i, sample_seed=0xFEEDFACE + _i)
 
 # 264 rows per step after the root: the tiled kernels at their 256-row tile
-# height with a ragged second tile of 8 rows (every row checked)
+# height with a ragged second tile of 8 rows (every row checked); |V| = 16400
+# and ffn = 8320 give the LM head and gate|up at least 128 tiles, so they run
+# on the direct-to-LDS kernel (ragged last vocabulary tile of 16 rows; gate|up
+# with the fused SwiGLU epilogue)
 SMALL_CONFIGS["s21_dynamic_264"] = RoundCfg(
-    name="s21_dynamic_264", head=replace(_HEAD_SMALL, vocab=3008), B=33,
+    name="s21_dynamic_264", head=replace(_HEAD_SMALL, vocab=16400, ffn=8320), B=33,
     n=tuple((13 * j + 5) % 97 + (200 if j % 5 == 0 else 0) for j in range(33)),
     tree=TREE_DYNAMIC, gamma=4, top_k=8, top_m=24, inv_temp=5.0,
     seed_w=1122, seed_in=2122, seed_t=3122)

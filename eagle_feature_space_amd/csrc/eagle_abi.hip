@@ -742,20 +742,40 @@ void layer_body(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, 
     r2.scatter = io.scatter;
     run_rows(h, EP_STORE, r2, st);
   } else {
-    if (swiglu)
-      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, io.M, 2 * ffn, d, h->w_gate, h->w_up, nullptr,
-           ffn, 2 * ffn, P, &sh, st);
-    else
-      gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, io.M, ffn, d, h->w_up, nullptr, nullptr, ffn, ffn,
-           P, &sh, st);
-    ActArgs aa;
-    aa.P = P;
-    aa.S = sh.S;
-    aa.M = io.M;
-    aa.F = ffn;
-    aa.swiglu = swiglu;
-    aa.out = ws + w.act;
-    {
+    if (swiglu && big_swiglu_ok(h->dtype, io.M, ffn, d)) {
+      // one split: the tiled GEMM writes silu(gate) * up itself
+      GemmArgs ga;
+      ga.xs[0] = rs(ws + w.h1n, nullptr, d);
+      ga.xs[1] = kNone;
+      ga.ksplit_x = d;
+      ga.M = io.M;
+      ga.N = 2 * ffn;
+      ga.K = d;
+      ga.w[0] = h->w_gate;
+      ga.w[1] = ga.w[2] = h->w_up;
+      ga.nseg1 = ffn;
+      ga.nseg2 = 2 * ffn;
+      ga.P = nullptr;
+      ga.pair_F = ffn;
+      ga.act = ws + w.act;
+      const GemmShape gs = plan_gemm_big(io.M, 2 * ffn, d);
+      ProfScope ps(EAGLE_PROF_GEMM, (double)esz(h) * (2.0 * ffn * d + (double)io.M * d),
+                   2.0 * io.M * 2.0 * ffn * d, st);
+      launch_gemm_big(ga, gs, st);
+    } else {
+      if (swiglu)
+        gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, io.M, 2 * ffn, d, h->w_gate, h->w_up, nullptr,
+             ffn, 2 * ffn, P, &sh, st);
+      else
+        gemm(h, rs(ws + w.h1n, nullptr, d), kNone, d, io.M, ffn, d, h->w_up, nullptr, nullptr, ffn,
+             ffn, P, &sh, st);
+      ActArgs aa;
+      aa.P = P;
+      aa.S = sh.S;
+      aa.M = io.M;
+      aa.F = ffn;
+      aa.swiglu = swiglu;
+      aa.out = ws + w.act;
       ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
       launch_epi_act(h->dtype, aa, st);
     }

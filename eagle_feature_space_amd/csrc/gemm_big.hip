@@ -21,6 +21,31 @@
 //   that XCD's L2.
 // The result goes to fp32 split-K partials P[z][m][n], consumed by the same
 // epilogue kernels as the weight-streaming GEMM.
+//
+// From 256 rows, when the tiles alone give at least 128 workgroups (the
+// 512-row LM head and gate|up, the ~20k-row EAGLE-3 ingest), k_gemm_dma
+// replaces it:
+//   tile 256 (n) x 256 (m), eight waves in 2 (n) x 4 (m), wave tile 128 x 64
+//   (32 accumulators of 16 x 16: 1.5x the MFMAs per LDS fragment of a 64 x 64
+//   wave tile);
+//   BK = 32 per stage and a four-stage LDS ring filled by direct-to-LDS loads
+//   (global_load_lds_dwordx4: no staging registers), issued three stages
+//   ahead; one barrier per stage, preceded by a partial vmcnt wait that lets
+//   the two younger stages stay in flight (a __syncthreads would wait for all
+//   of them);
+//   every fragment is read from LDS half a stage before its MFMAs (the
+//   barrier sits between the two halves of a stage's MFMAs), so no MFMA waits
+//   on an LDS read;
+//   LDS rows of 64 bytes: 16-byte chunk j of row r sits at j ^ ((r >> 1) & 2)
+//   (chosen by measuring the bank-conflict counter over every linear
+//   row-bit swizzle; the 128-byte-row swizzle of k_gemm_big does not carry
+//   over).  A direct-to-LDS load writes 64 lanes x 16 B contiguously, so the
+//   swizzle is applied by choosing each lane's global chunk.
+// With one split and pair_F set it writes the SwiGLU activations itself: the
+// W tile takes gate and up rows in alternating 16-row blocks, so a lane holds
+// gate and up of the same (row, column) in two accumulators.
+// Same MFMA order over K as k_gemm_big (ascending 32-wide steps), so the two
+// kernels give bit-identical sums.
 #include "kernels.h"
 
 namespace eagle {
@@ -156,12 +181,217 @@ __global__ __launch_bounds__(64 * WN * WM) void k_gemm_big(GemmArgs a, int nt, i
   }
 }
 
+// ------------------------------------------------------------ direct-to-LDS
+constexpr int kDN = 256, kDM = 256, kDK = 32, kDStages = 4;
+constexpr int kDRow = kDK * 2;                              // 64 B per row per stage
+constexpr int kDStage = (kDN + kDM) * kDRow;                // 32 KB
+constexpr int kDLds = kDStages * kDStage;                   // 128 KB
+
+__device__ __forceinline__ int dma_off(int r, int j) { return r * kDRow + 16 * (j ^ ((r >> 1) & 2)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int EPI>   // 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
+__global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, int S) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int wn = wave >> 2, wm = wave & 3;
+  const int total = nt * mt * S;
+  const int per = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int mtile = lin % mt;
+  const int ntile = (lin / mt) % nt;
+  const int z = lin / (mt * nt);
+  const int n0 = ntile * kDN, m0 = mtile * kDM;
+  const int k_begin = z * a.kps, k_end = min(a.K, k_begin + a.kps);
+  const int nst = (k_end - k_begin) / kDK;
+
+  // waves 0-3 load W rows 64 w .. 64 w + 63, waves 4-7 X rows: four 1 KB
+  // blocks of 16 rows each; lane l writes chunk slot l & 3 of block row l >> 2
+  const bool is_w = wave < 4;
+  const char* src[4];
+  const char* src1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave & 3) * 64 + i * 16 + (lane >> 2);     // row of the W or X tile
+    const int j = (lane & 3) ^ ((r >> 1) & 2);
+    if (is_w) {
+      int n;
+      if (EPI == 1) {   // 16-row blocks alternate gate (even) and up (odd)
+        const int b = r >> 4;
+        const int q = ntile * (kDN / 2) + (b >> 1) * 16 + (r & 15);
+        n = (b & 1) ? a.pair_F + min(q, a.pair_F - 1) : min(q, a.pair_F - 1);
+      } else {
+        n = min(n0 + r, a.N - 1);
+      }
+      const bf16s* base;
+      int off;
+      if (n < a.nseg1) { base = (const bf16s*)a.w[0]; off = 0; }
+      else if (n < a.nseg2) { base = (const bf16s*)a.w[1]; off = a.nseg1; }
+      else { base = (const bf16s*)a.w[2]; off = a.nseg2; }
+      src[i] = (const char*)(base + (int64_t)(n - off) * a.K + j * 8);
+      src1[i] = src[i];
+    } else {
+      const int m = min(m0 + r, a.M - 1);
+      src[i] = (const char*)(row_ptr<bf16s>(a.xs[0], m) + j * 8);
+      src1[i] = a.xs[1].base ? (const char*)(row_ptr<bf16s>(a.xs[1], m) + j * 8) : src[i];
+    }
+  }
+  const int ldsrow0 = (is_w ? 0 : kDN) + (wave & 3) * 64;
+  // stage s (clamped to the last one, so every stage issues the same number
+  // of loads and the vmcnt waits stay exact) into ring slot s % 4
+  auto issue = [&](int s) {
+    const int sc = min(s, nst - 1);
+    const int k0 = k_begin + sc * kDK;
+    const bool hi = !is_w && k0 >= a.ksplit_x;    // a stage never straddles the split
+    char* dst = lds + (s & (kDStages - 1)) * kDStage + ldsrow0 * kDRow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* p = hi ? src1[i] + (int64_t)(k0 - a.ksplit_x) * 2 : src[i] + (int64_t)k0 * 2;
+      __builtin_amdgcn_global_load_lds((const void*)p, (lds_void*)(dst + i * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nst > 0) {
+    // Fragments are read half a stage ahead of their MFMAs, the barrier sits
+    // in the middle of a stage:
+    //   MFMAs n-blocks 0-3 of stage s | wait for stage s+1, barrier, loads of
+    //   stage s+3, reads of stage s+1 (W blocks 0-3 and X) | MFMAs n-blocks
+    //   4-7 of stage s | reads of stage s+1 W blocks 4-7.
+    // The X fragments alternate between two register sets, so the loop body
+    // covers two stages (nst is even: K per split is a multiple of 64).
+    // After a barrier every wave has issued all its reads of stage s (they
+    // completed before the MFMAs that used them, in front of the barrier), so
+    // the slot stage s+3 overwrites (stage s-1's) is free.
+    const int wr0 = wn * 128, xr0 = kDN + wm * 64;
+    issue(0);
+    issue(1);
+    issue(2);
+    __builtin_amdgcn_s_waitcnt(0x0F78);          // vmcnt(8): stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 wf[8], xa[4], xb[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) xa[mb] = ld16(lds + dma_off(xr0 + mb * 16 + c, g));
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) wf[nb] = ld16(lds + dma_off(wr0 + nb * 16 + c, g));
+#define DMA_STAGE(S_, XC, XN)                                                                 \
+    {                                                                                       \
+      _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
+      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                      \
+        acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+      __builtin_amdgcn_s_waitcnt(0x0F74);    /* vmcnt(4): stage S_+1 landed */              \
+      __builtin_amdgcn_s_barrier();                                                         \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+      issue((S_) + 3);                                                                      \
+      const char* st_ = lds + (((S_) + 1) & (kDStages - 1)) * kDStage;                      \
+      _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
+        wf[nb] = ld16(st_ + dma_off(wr0 + nb * 16 + c, g));                                 \
+      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                      \
+        XN[mb] = ld16(st_ + dma_off(xr0 + mb * 16 + c, g));                                 \
+      _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
+      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                      \
+        acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
+      _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
+        wf[nb] = ld16(st_ + dma_off(wr0 + nb * 16 + c, g));                                 \
+      __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   /* loads */                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   /* reads W 0-3, X */            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  /* MFMAs n-blocks 4-7 */        \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   /* reads W 4-7 */               \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+    }
+    for (int s = 0; s < nst; s += 2) {
+      DMA_STAGE(s, xa, xb)
+      DMA_STAGE(s + 1, xb, xa)
+    }
+#undef DMA_STAGE
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load in flight when the wave ends
+
+  // acc[nb][mb]: lane holds out[m = m0 + 64 wm + 16 mb + c][n = n0 + 128 wn + 16 nb + 4 g + 0..3]
+  if (EPI == 1) {
+    // gate block nb (even) pairs with up block nb + 1: columns
+    // j = 128 ntile + 16 ((16 wn + nb) / 2) + 4 g + 0..3 of act (F columns)
+#pragma unroll
+    for (int nb = 0; nb < 8; nb += 2) {
+      const int j = ntile * (kDN / 2) + ((wn * 8 + nb) >> 1) * 16 + 4 * g;
+      if (j >= a.pair_F) continue;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int m = m0 + wm * 64 + mb * 16 + c;
+        if (m >= a.M) continue;
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gs = acc[nb][mb][e], u = acc[nb + 1][mb][e];
+          y[e] = gs / (1.0f + expf(-gs)) * u;
+        }
+        uint2 v;
+        v.x = f2bf(y[0]) | (f2bf(y[1]) << 16);
+        v.y = f2bf(y[2]) | (f2bf(y[3]) << 16);
+        *reinterpret_cast<uint2*>((bf16s*)a.act + (int64_t)m * a.pair_F + j) = v;
+      }
+    }
+    return;
+  }
+  float* P = a.P + (int64_t)z * a.M * a.N;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const int n = n0 + wn * 128 + nb * 16 + 4 * g;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 64 + mb * 16 + c;
+      if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
+    }
+  }
+}
+
+// the direct-to-LDS kernel's plan: one or two splits, or none (fall back)
+static bool plan_dma(int M, int N, int K, GemmShape* s) {
+  if (M < 256 || K % (2 * kDK) != 0) return false;
+  const int nt = (N + kDN - 1) / kDN, mt = (M + kDM - 1) / kDM;
+  const int tiles = nt * mt;
+  if (tiles < 128) return false;
+  const int kst = K / kDK;                  // even: K is a multiple of 64
+  int S = (256 + tiles - 1) / tiles;
+  if (S > kst / 8) S = kst / 8 > 0 ? kst / 8 : 1;
+  if (S < 1) S = 1;
+  int sps = (kst + S - 1) / S;
+  sps += sps & 1;                           // an even number of stages per split
+  s->direct = 2;
+  s->NB = 2;                // the direct-to-LDS kernel
+  s->MB = 16;
+  s->ntiles = nt;
+  s->mtiles = mt;
+  s->kps = sps * kDK;
+  s->S = (K + s->kps - 1) / s->kps;
+  return true;
+}
+
 bool big_gemm_ok(int dtype, int M, int N, int K) {
   return dtype == EAGLE_BF16 && M >= 64 && K % kBK == 0 && N % 16 == 0;
 }
 
+bool big_swiglu_ok(int dtype, int M, int F, int K) {
+  if (!big_gemm_ok(dtype, M, 2 * F, K) || F % (kDN / 2) != 0) return false;
+  GemmShape s;
+  return plan_dma(M, 2 * F, K, &s) && s.S == 1;
+}
+
 GemmShape plan_gemm_big(int M, int N, int K) {
   GemmShape s;
+  if (plan_dma(M, N, K, &s)) return s;
   s.direct = 2;
   s.MB = M >= 256 ? 16 : 8;                // tile height / 16
   s.NB = 0;
@@ -194,8 +424,26 @@ static void launch_big_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) 
                      s.ntiles, s.mtiles, s.S);
 }
 
+template <int EPI>
+static void launch_dma_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_dma<EPI>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kDLds);
+    attr = true;
+  }
+  const int total = s.ntiles * s.mtiles * s.S;
+  hipLaunchKernelGGL(k_gemm_dma<EPI>, dim3(((total + 7) / 8) * 8), dim3(512), kDLds, st, a,
+                     s.ntiles, s.mtiles, s.S);
+}
+
 void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
   a.kps = s.kps;
+  if (s.NB == 2) {
+    if (a.pair_F > 0) launch_dma_t<1>(a, s, st);
+    else launch_dma_t<0>(a, s, st);
+    return;
+  }
   if (s.MB == 16) launch_big_t<4, 4, 4>(a, s, st);
   else launch_big_t<4, 4, 2>(a, s, st);
 }

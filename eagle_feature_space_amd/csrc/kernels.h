@@ -16,6 +16,11 @@ struct GemmArgs {
   int nseg1, nseg2;
   float* P;
   int kps;
+  // SwiGLU epilogue of the tiled big GEMM (one split): W = [gate; up] with
+  // pair_F rows each; the tile pairs gate and up rows and writes
+  // act[m][j] = silu(gate_j) * up_j in bf16 instead of P (rows of pair_F)
+  int pair_F = 0;
+  void* act = nullptr;
 };
 struct GemmShape {
   int MB, NB, mtiles, ntiles, S, kps;
@@ -31,6 +36,9 @@ void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st);
 bool big_gemm_ok(int dtype, int M, int N, int K);
 GemmShape plan_gemm_big(int M, int N, int K);
 void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st);
+// the big-GEMM plan uses the direct-to-LDS kernel with one split, so the
+// SwiGLU epilogue can be fused (gate|up of F rows each, F % 128 == 0)
+bool big_swiglu_ok(int dtype, int M, int F, int K);
 
 // y = sum_s P + src1 + src2 ; out / out_scatter = y ; out_norm = Norm(y)
 struct ReduceArgs {
