@@ -19,7 +19,12 @@ Prints one JSON line.  Besides the contract fields it carries
   cpu_baseline  the CPU oracle timed on this host on whole rounds of the same
                 workload (a bounded sample of ~15 s)
   breakdown     per kernel family: launches per round, mean us, GB/s, TFLOP/s
-                (a separate profiled pass, outside the timed region)
+                and the per-launch roofline (max of bytes / 8 TB/s and flops /
+                MFMA peak) summed over the round (a separate profiled pass,
+                outside the timed region)
+  extra_workloads  (default workload only) the 8B EAGLE-2 tree (B 8) and the
+                EAGLE-3 chain (B 32): nodes/s, ms per round and the fraction of
+                their per-launch roofline the round reaches
 """
 from __future__ import annotations
 
@@ -97,6 +102,77 @@ def cpu_baseline(cfg, weights, inp, target, seconds):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def family_breakdown(E, R):
+    """Per kernel family over the last R profiled rounds: launches, time,
+    algorithmic bytes and flops, and the per-launch roofline time
+    max(bytes / 8 TB/s, flops / MFMA peak) summed over the family's launches."""
+    out = {}
+    tot_ms = tot_bytes = tot_roof = 0.0
+    for fam in E.PROF_FAMILIES:
+        p = E.eagle_profile_read(fam)
+        if p["launches"] == 0:
+            continue
+        ms = p["ms"] * p["launches"] / max(1, p["timed"])
+        tot_ms += ms
+        tot_bytes += p["bytes"]
+        tot_roof += p["roof_ms"]
+        out[fam] = {"launches_per_round": p["launches"] / R,
+                    "us_per_round": round(ms * 1e3 / R, 2),
+                    "GB_per_round": round(p["bytes"] / R / 1e9, 4),
+                    "GBps": round(p["bytes"] / (ms * 1e-3) / 1e9, 1) if ms > 0 and p["bytes"] else None,
+                    "TFLOPps": round(p["flops"] / (ms * 1e-3) / 1e12, 2) if ms > 0 and p["flops"] else None,
+                    "roofline_us_per_round": round(p["roof_ms"] * 1e3 / R, 2),
+                    "roofline_frac": round(p["roof_ms"] / ms, 4) if ms > 0 and p["roof_ms"] else None}
+    out["kernels_us_per_round"] = round(tot_ms * 1e3 / R, 2)
+    out["round_bytes_GB"] = round(tot_bytes / R / 1e9, 4)
+    out["round_hbm_roofline_us"] = round(tot_bytes / R / (HBM_PEAK_GBS * 1e9) * 1e6, 2)
+    # each launch bound by HBM or by the MFMA peak, whichever takes longer
+    out["round_roofline_us"] = round(tot_roof * 1e3 / R, 2)
+    return out
+
+
+def extra_workload(name, steps, warmup):
+    """Throughput of another workload (no CPU baseline): nodes/s, ms per round
+    and the fraction of its per-launch roofline the round reaches."""
+    import torch
+
+    from eagle_feature_space_amd import binding as E
+    from eagle_feature_space_amd import configs as C
+    from eagle_feature_space_amd import synth
+    from eagle_feature_space_amd.runner import GpuRound, to_dev
+
+    cfg = C.ALL_CONFIGS[name]
+    print(f"[bench] extra {name}: generating inputs", file=sys.stderr, flush=True)
+    gr = GpuRound(cfg, synth.head_weights(cfg.head, cfg.seed_w), synth.round_inputs(cfg))
+    tgt = to_dev(synth.target_logits(cfg), gr.dev)
+    for _ in range(warmup):
+        gr.run(target=tgt, attend=cfg.tree_attend)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        gr.run(target=tgt, attend=cfg.tree_attend)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    R = 5
+    E.eagle_profile_reset()
+    E.eagle_profile_enable(True)
+    for _ in range(R):
+        gr.run(target=tgt, attend=cfg.tree_attend)
+    torch.cuda.synchronize()
+    E.eagle_profile_enable(False)
+    fb = family_breakdown(E, R)
+    ms = el * 1e3 / steps
+    nodes = cfg.B * cfg.n_final
+    res = {"value": round(nodes * steps / el, 2), "unit": "nodes/s", "ms_per_step": round(ms, 4),
+           "steps": steps, "warmup": warmup, "nodes_per_round": nodes,
+           "round_roofline_us": fb["round_roofline_us"],
+           "round_roofline_frac": round(fb["round_roofline_us"] / (ms * 1e3), 4),
+           "families_us_per_round": {k: v["us_per_round"] for k, v in fb.items() if isinstance(v, dict)}}
+    del gr, tgt
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +185,9 @@ def main():
                     help="greedy verification (default) or lossless speculative sampling "
                          "(inverse temperature 1, seeded uniforms)")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the extra workloads (8B EAGLE-2 tree, EAGLE-3 chain) the default "
+                         "run reports beside the headline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="one 1 GiB device-to-device copy before warm-up (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -175,12 +254,22 @@ def main():
     value = nodes * args.steps / elapsed
     avg_ms = lm["ms"] / max(1, lm["timed"])
     bytes_per_launch = lm["bytes"] / max(1, lm["launches"])
-    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    flops_per_launch = lm["flops"] / max(1, lm["launches"])
     traffic = measured_traffic("lmhead", cfg.name)
-    roofline = {"kernel": "k_lmhead (LM head + fused softmax/top-k partials)",
-                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+    peak_tf = BF16_PEAK_TFLOPS if cfg.head.dtype == C.DTYPE_BF16 else FP32_PEAK_TFLOPS
+    # the binding resource of the launch: HBM bytes or MFMA flops, whichever
+    # takes longer at the datasheet peak
+    if flops_per_launch / (peak_tf * 1e12) > bytes_per_launch / (HBM_PEAK_GBS * 1e9):
+        achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4)}
+    else:
+        achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roofline = {"kernel": "LM head + fused softmax/top-k partials", **roofline,
                 "traffic": traffic, "bytes_per_launch": bytes_per_launch,
+                "flops_per_launch": flops_per_launch,
                 "mean_launch_us": round(avg_ms * 1e3, 2), "launches_timed": lm["timed"]}
 
     # ---- per-family breakdown (separate profiled pass)
@@ -193,23 +282,9 @@ def main():
             gr.run(target=tgt, attend=cfg.tree_attend, sample=sample)
         torch.cuda.synchronize()
         E.eagle_profile_enable(False)
-        breakdown = {}
-        tot_ms = tot_bytes = 0.0
-        for fam in E.PROF_FAMILIES:
-            p = E.eagle_profile_read(fam)
-            if p["launches"] == 0:
-                continue
-            ms = p["ms"] * p["launches"] / max(1, p["timed"])
-            tot_ms += ms
-            tot_bytes += p["bytes"]
-            breakdown[fam] = {"launches_per_round": p["launches"] / R,
-                              "us_per_round": round(ms * 1e3 / R, 2),
-                              "GB_per_round": round(p["bytes"] / R / 1e9, 4),
-                              "GBps": round(p["bytes"] / (ms * 1e-3) / 1e9, 1) if ms > 0 and p["bytes"] else None,
-                              "TFLOPps": round(p["flops"] / (ms * 1e-3) / 1e12, 2) if ms > 0 and p["flops"] else None}
-        breakdown["kernels_us_per_round"] = round(tot_ms * 1e3 / R, 2)
-        breakdown["round_bytes_GB"] = round(tot_bytes / R / 1e9, 4)
-        breakdown["round_hbm_roofline_us"] = round(tot_bytes / R / (HBM_PEAK_GBS * 1e9) * 1e6, 2)
+        breakdown = family_breakdown(E, R)
+        breakdown["round_roofline_frac_of_timed_round"] = round(
+            breakdown["round_roofline_us"] / (ms_per_step * 1e3), 4)
 
     # ---- per-round distribution (separate pass, events at round start, end of
     # drafting and end of verify; the events add a few µs to each round)
@@ -243,6 +318,12 @@ def main():
         if gr.target is not None:
             round_stats["verify_includes"] = "the target's pass over the tree"
 
+    extras = None
+    if args.workload == "c1_8b_static" and not args.no_extras:
+        del gr, tgt
+        torch.cuda.empty_cache()
+        extras = {w: extra_workload(w, 10, 3) for w in ("c2_8b_dynamic", "c3_8b_eagle3")}
+
     cpu = None
     if not args.no_cpu and cfg.target_layers > 0:
         cpu = {"value": None, "skipped": "the oracle's target pass at this size is not a bounded sample"}
@@ -267,6 +348,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": breakdown,
         "round_stats": round_stats,
+        "extra_workloads": extras,
     }
     print(json.dumps(out))
 

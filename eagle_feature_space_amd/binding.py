@@ -119,7 +119,8 @@ def lib():
         "eagle_profile_enable": ([ctypes.c_int], ctypes.c_int),
         "eagle_profile_reset": ([], ctypes.c_int),
         "eagle_profile_read": ([ctypes.c_int, P(c_int64), P(c_int64), P(ctypes.c_double),
-                                P(ctypes.c_double), P(ctypes.c_double)], ctypes.c_int),
+                                P(ctypes.c_double), P(ctypes.c_double), P(ctypes.c_double)],
+                               ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -270,10 +271,12 @@ def eagle_profile_reset():
 
 
 def eagle_profile_read(family):
-    """-> dict(launches, timed, ms, bytes, flops) for a kernel family."""
+    """-> dict(launches, timed, ms, bytes, flops, roof_ms) for a kernel family."""
     fam = PROF_FAMILIES[family] if isinstance(family, str) else family
     n, t = c_int64(), c_int64()
-    ms, by, fl = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    ms, by, fl, rf = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     _check(lib().eagle_profile_read(fam, ctypes.byref(n), ctypes.byref(t), ctypes.byref(ms),
-                                    ctypes.byref(by), ctypes.byref(fl)), "eagle_profile_read")
-    return dict(launches=n.value, timed=t.value, ms=ms.value, bytes=by.value, flops=fl.value)
+                                    ctypes.byref(by), ctypes.byref(fl), ctypes.byref(rf)),
+           "eagle_profile_read")
+    return dict(launches=n.value, timed=t.value, ms=ms.value, bytes=by.value, flops=fl.value,
+                roof_ms=rf.value)

@@ -234,8 +234,11 @@ int check_tree_state(const eagle_tree* t, const Geo& g) {
 // ---------------------------------------------------------------- head / kv
 int esz(const eagle_head* h) { return h->dtype == EAGLE_BF16 ? 2 : 4; }
 
+void prof_set_dtype(int dtype);   // roofline peak of the profiled launches
+
 int check_head(const eagle_head* h) {
   if (!h) return EAGLE_EINVAL;
+  prof_set_dtype(h->dtype);
   if (h->dtype != EAGLE_BF16 && h->dtype != EAGLE_F32) return EAGLE_EINVAL;
   if (h->act != EAGLE_ACT_SWIGLU && h->act != EAGLE_ACT_GELU) return EAGLE_EINVAL;
   if (h->norm != EAGLE_NORM_RMS && h->norm != EAGLE_NORM_LAYER) return EAGLE_EINVAL;
@@ -284,12 +287,19 @@ struct ProfFamily {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
   size_t used = 0;
   double bytes = 0, flops = 0;
+  double roof_s = 0;          // sum over launches of max(bytes / HBM peak, flops / MFMA peak)
 };
+// MI355X datasheet peaks the per-launch roofline is taken against
+constexpr double kPeakHbm = 8.0e12;             // B/s, HBM3E
+constexpr double kPeakBf16 = 2.5e15;            // flop/s, dense bf16 MFMA
+constexpr double kPeakF32 = 157.3e12;           // flop/s, fp32
 struct Prof {
   unsigned mask = 0;          // bit f set: family f is profiled
+  double peak_flops = kPeakBf16;   // of the head of the current call
   ProfFamily fam[EAGLE_PROF_FAMILIES];
 };
 Prof g_prof;
+void prof_set_dtype(int dtype) { g_prof.peak_flops = dtype == EAGLE_F32 ? kPeakF32 : kPeakBf16; }
 
 // Brackets one launch with events on its stream when profiling is enabled.
 // Each scope reserves its own event pair when it opens, so scopes may nest.
@@ -305,6 +315,7 @@ struct ProfScope {
     f->launches += 1;
     f->bytes += bytes;
     f->flops += flops;
+    f->roof_s += std::max(bytes / kPeakHbm, flops / g_prof.peak_flops);
     if (f->used >= kMaxTimed) return;
     if (f->used == f->ev.size()) {
       hipEvent_t a, b;
@@ -809,12 +820,13 @@ int eagle_profile_reset(void) {
     f.launches = 0;
     f.used = 0;
     f.bytes = f.flops = 0;
+    f.roof_s = 0;
   }
   return EAGLE_OK;
 }
 
 int eagle_profile_read(int family, int64_t* launches, int64_t* timed_launches, double* total_ms,
-                       double* bytes, double* flops) {
+                       double* bytes, double* flops, double* roofline_ms) {
   if (family < 0 || family >= EAGLE_PROF_FAMILIES) return EAGLE_EINVAL;
   ProfFamily& f = g_prof.fam[family];
   double ms = 0;
@@ -829,6 +841,7 @@ int eagle_profile_read(int family, int64_t* launches, int64_t* timed_launches, d
   if (total_ms) *total_ms = ms;
   if (bytes) *bytes = f.bytes;
   if (flops) *flops = f.flops;
+  if (roofline_ms) *roofline_ms = f.roof_s * 1e3;
   return EAGLE_OK;
 }
 

@@ -434,7 +434,9 @@ int eagle_kv_commit(const eagle_tree *tree, int kv_heads, int head_dim, int dtyp
  * and the algorithmic bytes and flops of that launch (each weight, cache and
  * logit byte counted once) are added up.  eagle_profile_read waits for the
  * recorded events and returns, since the last reset, the launch count, the
- * summed kernel time in milliseconds and the summed bytes / flops.  Up to
+ * summed kernel time in milliseconds, the summed bytes / flops and the summed
+ * per-launch roofline time max(bytes / 8 TB/s, flops / peak) in milliseconds
+ * (peak: 2.5 PFLOP/s dense bf16 MFMA, 157.3 TFLOP/s fp32; MI355X datasheet).  Up to
  * 16384 launches per family are timed; later ones are counted but not timed
  * (timed_launches tells how many were).  Not thread-safe across concurrent
  * callers.
@@ -451,7 +453,8 @@ enum {
 int eagle_profile_enable(int family_mask);
 int eagle_profile_reset(void);
 int eagle_profile_read(int family, int64_t *launches, int64_t *timed_launches,
-                       double *total_ms, double *bytes, double *flops);
+                       double *total_ms, double *bytes, double *flops,
+                       double *roofline_ms);
 
 /* Text for a status code. */
 const char *eagle_strerror(int status);
