@@ -145,3 +145,105 @@ def verify_sample(tok, parent, logits, inv_temp, draws, gamma):
     pth[:len(path)] = path
     o[:len(out)] = out
     return acc, pth, o
+
+
+# ----------------------------------------------- verification of sampled drafts
+# Follows "Speculative Decoding Deep Dive III", section "EAGLE-1", its
+# "Inference" list (the drafter samples its tokens and one target pass checks
+# the tree by multi-round speculative sampling, keeping the target's
+# distribution), and "transformer_math / tm_eagle_deep", section "Why draft
+# confidence is a usable acceptance proxy" (keep a drafted token with
+# probability min(1, p_target / p_draft)).
+#
+# Reading: when drafting samples, the children of a node are an ordered sample
+# without replacement from the draft distribution q = softmax(s_d * z_draft)
+# at that node (Gumbel-top-k gives them in draw order).  They are tested in
+# that order; the j-th test uses the residual target r_j and the draft's
+# proposal distribution q_j for the j-th draw: q restricted to the tokens not
+# drawn before it, renormalised.  x_j is kept with probability
+# min(1, r_j(x_j) / q_j(x_j)); after a rejection r_{j+1} = max(r_j - q_j, 0)
+# renormalised.  r_1 = p, the target distribution.  When all are rejected one
+# token is drawn from the last residual.  Every drawn child takes part, also
+# one the verify tree dropped: accepting such a child ends the walk with its
+# token (the target has no row below it).
+
+
+def draft_probs_remaining(row, inv_temp, drawn_before):
+    """q_j: softmax(s * z) over the tokens not in `drawn_before`; s * z is
+    formed in fp32 (as the drafter forms it), the rest in fp64.  All zero if
+    no token is left."""
+    v = (np.float32(inv_temp) * np.asarray(row, np.float32)).astype(np.float64)
+    keep = np.ones(v.size, bool)
+    keep[list(drawn_before)] = False
+    out = np.zeros(v.size)
+    if not keep.any():
+        return out
+    e = np.exp(v[keep] - v[keep].max())
+    out[keep] = e / e.sum()
+    return out
+
+
+def drafted_tests(p, draft_row, draft_inv_temp, drawn):
+    """The successive tests at one node whose children `drawn` (token ids, in
+    draw order) came from the draft row `draft_row`.
+
+    Returns (thr, resid): thr[j] = r_j(x_j) / q_j(x_j) (x_j is kept iff its
+    uniform is below thr[j]; +inf when q_j(x_j) = 0 < r_j(x_j)), and resid =
+    the residual after every child was rejected, normalised (all zero when no
+    mass is left).  r_j is the residual after rejecting x_1 .. x_{j-1}."""
+    r = np.array(p, np.float64)
+    thr = []
+    for j, x in enumerate(drawn):
+        qj = draft_probs_remaining(draft_row, draft_inv_temp, drawn[:j])
+        if qj[x] > 0.0:
+            thr.append(r[x] / qj[x])
+        else:
+            thr.append(np.inf if r[x] > 0.0 else 0.0)
+        r = np.maximum(r - qj, 0.0)
+        tot = r.sum()
+        r = r / tot if tot > 0.0 else np.zeros_like(r)
+    return np.array(thr, np.float64), r
+
+
+def verify_sample_drafted(tok, parent, drawn, logits, inv_temp, draft_rows, draft_inv_temp,
+                          draws, gamma):
+    """Multi-round speculative sampling over one request's verify tree when
+    the children were drawn from the draft.
+
+    tok, parent, logits, draws as for `verify_sample` (draws[u][j] tests the
+    j-th drawn child of position u, draws[u][16] is the residual draw);
+    drawn[u]: list of (token, verify position or -1) of the children drafting
+    drew at position u, in draw order (empty for a node never expanded);
+    draft_rows[u]: the draft's logits at u (used when drawn[u] is not empty);
+    draft_inv_temp: the drafter's s.  Returns (accept_len, path, out_tokens)
+    as `verify_sample`.
+    """
+    path = [0]
+    out = []
+    u = 0
+    while True:
+        p = target_probs(logits[u], inv_temp)
+        kids = list(drawn[u]) if len(path) - 1 < gamma else []
+        if kids:
+            thr, resid = drafted_tests(p, draft_rows[u], draft_inv_temp, [x for x, _ in kids])
+        else:
+            thr, resid = np.zeros(0), p
+        take = None
+        for j, (x, v) in enumerate(kids):
+            if draws[u][j] < thr[j]:
+                take = (int(x), int(v))
+                break
+        if take is None:
+            out.append(residual_draw(resid, [int(x) for x, _ in kids], draws[u][N_DRAWS - 1]))
+            break
+        out.append(take[0])
+        if take[1] < 0:          # a child the verify tree dropped: its token ends the walk
+            break
+        u = take[1]
+        path.append(u)
+    acc = len(path) - 1
+    pth = np.full(gamma + 1, -1, np.int32)
+    o = np.full(gamma + 1, -1, np.int32)
+    pth[:len(path)] = path
+    o[:len(out)] = out
+    return acc, pth, o

@@ -688,6 +688,143 @@ def test_verify_sample_residual_is_inverse_cdf():
         assert x not in excl and edges[x] <= u < edges[x + 1] + 1e-12
 
 
+# ------------------------------------------------- verification of sampled drafts
+def _draft_logp(z, s):
+    """log q for q = softmax(s * z), s * z in fp32 (the drafter's arithmetic)."""
+    l = (np.float32(s) * np.asarray(z, np.float32)).astype(np.float64)
+    return l - logsumexp(l)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+@pytest.mark.parametrize("case", ["random", "draft_is_target", "draft_peaked", "target_peaked",
+                                  "target_one_hot"])
+def test_drafted_verify_law_is_the_target(k, case):
+    """Exact law, brute force over every ordered draw: with children drawn one
+    after another without replacement from q (the probability of a sequence is
+    the product of q(x_j) / (mass of q not yet drawn)), each tested with
+    probability min(1, thr_j) and the residual drawn when all fail, the token
+    emitted at a node has the target distribution p exactly ("Speculative
+    Decoding Deep Dive III", EAGLE-1 "Inference": multi-round speculative
+    sampling keeps the target's distribution)."""
+    V = 5
+    rng = np.random.default_rng(hash(case) % 1000 + 10 * k)
+    zt = rng.standard_normal(V).astype(np.float32)
+    zd = rng.standard_normal(V).astype(np.float32)
+    st, sd = 1.3, 0.9
+    if case == "draft_is_target":
+        zd, sd = zt.copy(), st
+    elif case == "draft_peaked":
+        sd = 40.0
+    elif case == "target_peaked":
+        zt = (3 * rng.standard_normal(V)).astype(np.float32)
+    elif case == "target_one_hot":
+        st = 1e4
+    p = VF.target_probs(zt, st)
+    lq = _draft_logp(zd, sd)
+    law = np.zeros(V)
+    total = 0.0
+    for seq in itertools.permutations(range(V), k):
+        rem = list(range(V))
+        lp = 0.0
+        for x in seq:
+            lp += lq[x] - logsumexp(lq[rem])
+            rem.remove(x)
+        pr = math.exp(lp)
+        total += pr
+        thr, resid = VF.drafted_tests(p, zd, sd, list(seq))
+        stay = 1.0
+        for j, x in enumerate(seq):
+            a = min(1.0, thr[j])
+            law[x] += pr * stay * a
+            stay *= 1.0 - a
+        law += pr * stay * resid
+    assert abs(total - 1.0) < 1e-12
+    np.testing.assert_allclose(law, p, rtol=0, atol=1e-13)
+
+
+def test_drafted_verify_with_a_certain_draft_is_the_point_mass_rule():
+    """A draft with all its mass on one token (s_d -> infinity) that proposes
+    that token as the only child reduces the test to the one for top-k
+    drafting: keep x iff u < p(x), else draw from p with x removed.  Both
+    verifications give the same walk on random chains."""
+    rng = np.random.default_rng(55)
+    V, gamma = 9, 4
+    for _ in range(40):
+        tok = rng.integers(0, V, gamma + 1)
+        parent = np.arange(-1, gamma)
+        logits = rng.standard_normal((gamma + 1, V)).astype(np.float32)
+        for u in range(gamma):
+            if rng.random() < 0.6:
+                logits[u, tok[u + 1]] += 2.5
+        drafts = rng.standard_normal((gamma + 1, V)).astype(np.float32)
+        for u in range(gamma):
+            drafts[u, tok[u + 1]] = drafts[u].max() + 1.0
+        drawn = [[(int(tok[u + 1]), u + 1)] if u < gamma else [] for u in range(gamma + 1)]
+        draws = rng.random((gamma + 1, VF.N_DRAWS))
+        a = VF.verify_sample(tok, parent, logits, 1.1, draws, gamma)
+        b = VF.verify_sample_drafted(tok, parent, drawn, logits, 1.1, drafts, 1e5, draws, gamma)
+        assert a[0] == b[0] and list(a[1]) == list(b[1]) and list(a[2]) == list(b[2])
+
+
+def test_drafted_verify_keeps_the_first_child_when_draft_is_the_target():
+    """q = p makes the first test's ratio exactly 1: the first drawn child is
+    always kept, down to the leaf; a first child the tree dropped ends the walk
+    with its token."""
+    rng = np.random.default_rng(56)
+    V = 7
+    logits = rng.standard_normal((4, V)).astype(np.float32)
+    tok = np.array([0, 3, 5, 2])
+    parent = np.array([-1, 0, 0, 1])
+    drawn = [[(3, 1), (5, 2)], [(2, 3)], [], []]
+    for _ in range(50):
+        draws = rng.random((4, VF.N_DRAWS))
+        acc, path, out = VF.verify_sample_drafted(tok, parent, drawn, logits, 0.8, logits, 0.8,
+                                                  draws, 2)
+        assert acc == 2 and list(path) == [0, 1, 3] and out[:2].tolist() == [3, 2]
+        dropped = [[(6, -1), (3, 1)], [(2, 3)], [], []]
+        acc, path, out = VF.verify_sample_drafted(tok, parent, dropped, logits, 0.8, logits, 0.8,
+                                                  draws, 2)
+        assert acc == 0 and list(path) == [0, -1, -1] and list(out) == [6, -1, -1]
+
+
+def test_drafted_verify_walk_is_lossless():
+    """Monte Carlo through the whole walk: a bigram target and a different
+    bigram draft; the root's 3 children drawn by Gumbel-top-k, the verify tree
+    keeping draw ranks 0 and 2 (rank 1 dropped) and the rank-0 child's 2 drawn
+    children.  The first two emitted tokens (the second completed from the
+    target when the round stops after one) follow p(x0) p(x1 | x0) within 5
+    sigma per cell.  Leaving the dropped child out of the root's tests moves a
+    cell by ~20 sigma here."""
+    V, st, sd = 5, 1.0, 3.0      # a peaked draft: the dropped child carries real mass
+    rng = np.random.default_rng(57)
+    Pz = rng.standard_normal((V, V)).astype(np.float32)       # target logits after token a
+    Qz = rng.standard_normal((V, V)).astype(np.float32)       # draft logits after token a
+    root = 0
+    p0 = VF.target_probs(Pz[root], st)
+    pn = np.array([VF.target_probs(Pz[a], st) for a in range(V)])
+    n = 20000
+    joint = np.zeros((V, V))
+    gum = lambda z, k: np.argsort(-(np.float32(sd) * z + -np.log(-np.log(rng.random(V)))),
+                                  kind="stable")[:k]
+    for _ in range(n):
+        r = gum(Qz[root], 3)
+        c = gum(Qz[r[0]], 2)
+        tok = np.array([root, r[0], r[2], c[0], c[1]])
+        parent = np.array([-1, 0, 0, 1, 1])
+        drawn = [[(int(r[0]), 1), (int(r[1]), -1), (int(r[2]), 2)],
+                 [(int(c[0]), 3), (int(c[1]), 4)], [], [], []]
+        logits = Pz[tok]
+        drafts = Qz[tok]
+        acc, path, out = VF.verify_sample_drafted(tok, parent, drawn, logits, st, drafts, sd,
+                                                  rng.random((5, VF.N_DRAWS)), 2)
+        x0 = int(out[0])
+        x1 = int(out[1]) if acc >= 1 else int(rng.choice(V, p=pn[x0]))
+        joint[x0, x1] += 1
+    want = p0[:, None] * pn
+    f = joint / n
+    assert np.all(np.abs(f - want) <= 5 * np.sqrt(want * (1 - want) / n) + 1.0 / n)
+
+
 # ------------------------------------------------- sampled drafting (Gumbel-top-k)
 def test_philox_known_answers():
     """Philox4x32-10 against the known-answer vectors published with its
