@@ -108,6 +108,9 @@ def lib():
         "eagle_tree_verify_sample": ([P(eagle_tree), c_void_p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_float, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p], ctypes.c_int),
+        "eagle_tree_verify_sample_drafted": ([P(eagle_tree), c_void_p, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_float, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p, c_void_p], ctypes.c_int),
         "eagle_target_verify_logits": ([P(eagle_head), P(eagle_target), P(eagle_kv), P(eagle_tree),
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p], ctypes.c_int),
@@ -134,7 +137,8 @@ EXPORTED = ("eagle_version", "eagle_strerror", "eagle_tree_layout_of", "eagle_tr
             "eagle_step_rows", "eagle_workspace_bytes", "eagle_tree_init", "eagle_draft_step",
             "eagle_draft_step_noalloc",
             "eagle_tree_expand_rerank", "eagle_tree_attend", "eagle_tree_verify",
-            "eagle_tree_verify_sample", "eagle_target_verify_logits",
+            "eagle_tree_verify_sample", "eagle_tree_verify_sample_drafted",
+            "eagle_target_verify_logits",
             "eagle_target_workspace_bytes", "eagle_kv_commit",
             "eagle_profile_enable", "eagle_profile_reset", "eagle_profile_read")
 
@@ -236,6 +240,16 @@ def eagle_tree_verify_sample(tree, target_logits, positions, vocab, dtype, inv_t
                                                  vocab, dtype, inv_temp, _ptr(draws), _ptr(accept_len),
                                                  _ptr(accept_path), _ptr(out_tokens), _stream(stream)),
                   "eagle_tree_verify_sample")
+
+
+def eagle_tree_verify_sample_drafted(tree, target_logits, positions, vocab, dtype, inv_temp,
+                                     draft_logits, draws, accept_len, accept_path, out_tokens,
+                                     stream=None):
+    return _check(lib().eagle_tree_verify_sample_drafted(
+        ctypes.byref(tree), _ptr(target_logits), positions, vocab, dtype, inv_temp,
+        _ptr(draft_logits), _ptr(draws), _ptr(accept_len), _ptr(accept_path), _ptr(out_tokens),
+        _stream(stream)),
+        "eagle_tree_verify_sample_drafted")
 
 
 def eagle_target_workspace_bytes(head, target, kv, tree):

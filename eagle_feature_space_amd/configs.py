@@ -269,6 +269,13 @@ for _i, _b in enumerate((40, 70)):
         n=tuple((5 * j + _b) % 37 for j in range(_b)), tree=TREE_CHAIN, gamma=2, top_k=1,
         seed_w=1120 + _i, seed_in=2120 + _i, seed_t=3120 + _i, sample_seed=0xFEEDFACE + _i)
 
+# the static template with sampled drafting: every node's children are the
+# first draw ranks of its Gumbel-top-k sample (a prefix of the draws)
+SMALL_CONFIGS["s22_sampled_static"] = RoundCfg(
+    name="s22_sampled_static", head=_HEAD_SMALL, B=4, n=(90, 0, 17, 200), tree=TREE_STATIC,
+    gamma=4, top_k=4, template=STATIC_TREE_25, inv_temp=2.0, seed_w=1122, seed_in=2122,
+    seed_t=3122, sample_seed=0x5A5A5A5A12345678)
+
 # 264 rows per step after the root: the tiled kernels at their 256-row tile
 # height with a ragged second tile of 8 rows (every row checked); |V| = 16400
 # and ffn = 8320 give the LM head and gate|up at least 128 tiles, so they run

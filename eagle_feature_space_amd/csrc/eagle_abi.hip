@@ -1288,6 +1288,34 @@ int eagle_tree_verify(const eagle_tree* tree, const void* target_logits, int pos
   return finish(EAGLE_OK);
 }
 
+int eagle_tree_verify_sample_drafted(const eagle_tree* tree, const void* target_logits,
+                                     int positions, int vocab, int dtype, float inv_temp,
+                                     const float* draft_logits, const float* draws,
+                                     int32_t* accept_len, int32_t* accept_path,
+                                     int32_t* out_tokens, void* stream) {
+  Geo g;
+  int s;
+  if ((s = build_geo(tree, &g))) return s;
+  if ((s = check_tree_state(tree, g))) return s;
+  if (tree->sample != 1) return EAGLE_EINVAL;     // top-k drafts: eagle_tree_verify_sample
+  if (!target_logits || !draft_logits || !draws || !accept_len || !accept_path || !out_tokens)
+    return EAGLE_EINVAL;
+  if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_EINVAL;
+  if (vocab < 1 || positions < g.positions) return EAGLE_EINVAL;
+  if (!(inv_temp > 0.f) || !std::isfinite(inv_temp)) return EAGLE_EINVAL;
+  if (!verify_drafted_ok(vocab)) return EAGLE_EUNSUPPORTED;
+  DraftRows dr{};
+  dr.n = g.gamma;
+  for (int i = 0; i < g.gamma; ++i) dr.rows[i] = g.rows[i];
+  {
+    ProfScope ps(EAGLE_PROF_VERIFY, 0, 0, (hipStream_t)stream);
+    launch_verify_drafted(tree_dev(tree, g), g.B, target_logits, draft_logits, positions, vocab,
+                          dtype, inv_temp, tree->inv_temp, draws, g.gamma, dr, accept_len,
+                          accept_path, out_tokens, (hipStream_t)stream);
+  }
+  return finish(EAGLE_OK);
+}
+
 int eagle_tree_verify_sample(const eagle_tree* tree, const void* target_logits, int positions,
                              int vocab, int dtype, float inv_temp, const float* draws,
                              int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,

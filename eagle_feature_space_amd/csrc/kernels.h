@@ -243,6 +243,15 @@ void launch_tree_expand(const TreeDev& t, const RowsDev& next, int B, int kind, 
 void launch_verify(const TreeDev& t, int B, const void* logits, int positions,
                    int vocab, int dtype, int gamma, int32_t* accept_len,
                    int32_t* accept_path, int32_t* out_tokens, hipStream_t st);
+struct DraftRows {         // rows per request of each draft step (the draft logits' blocks)
+  int n;
+  int rows[kSlots];
+};
+bool verify_drafted_ok(int vocab);
+void launch_verify_drafted(const TreeDev& t, int B, const void* logits, const float* draft_logits,
+                           int positions, int vocab, int dtype, float inv_temp, float draft_inv_temp,
+                           const float* draws, int gamma, const DraftRows& dr, int32_t* accept_len,
+                           int32_t* accept_path, int32_t* out_tokens, hipStream_t st);
 bool verify_sample_ok(int vocab, int dtype);
 void launch_verify_sample(const TreeDev& t, int B, const void* logits, int positions, int vocab,
                           int dtype, float inv_temp, const float* draws, int gamma,

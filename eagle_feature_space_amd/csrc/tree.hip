@@ -681,6 +681,479 @@ void launch_verify_sample(const TreeDev& t, int B, const void* logits, int posit
                     accept_len, accept_path, out_tokens, st);
 }
 
+// ---------------------------------- stochastic verification of sampled drafts
+// Multi-round speculative sampling when drafting drew each node's children
+// without replacement from the draft q = softmax(s_d * z_draft): at a visited
+// node u the drawn children x_1 .. x_k (pool order = draw order, including
+// children the verify tree dropped) are tested one after another.  With
+// p = softmax(s_t * z_target), the j-th test uses the draft's proposal
+// distribution for the j-th draw, q_j = q over the tokens not drawn before x_j,
+// renormalised, and the residual r_j (r_1 = p; after a rejection
+// r_{j+1} = max(r_j - q_j, 0) renormalised); x_j is kept iff
+// u_j < r_j(x_j) / q_j(x_j).
+//
+// Closed form used here (exact in real arithmetic): a rejected token has
+// r_j(x_j) < q_j(x_j), so it keeps no residual mass, and for every other token
+//   C_{j+1} r_{j+1}(y) = max(p(y) - K_j exp(l_y - m_j), 0),
+// with l_y = fp32(s_d * z_y), m_j the largest l over the tokens not drawn
+// before x_j, E_j = sum of exp(l - m_j) over those tokens,
+// K_j = K_{j-1} exp(m_j - m_{j-1}) + C_j / E_j (K_0 = 0), C_1 = 1 and C_{j+1} the
+// residual mass.  So one pass over the vocabulary per rejection gives C_{j+1};
+// the test of x_{j+1} needs only scalars.  m_j <= m_{j-1} and E_j >= 1 keep
+// every factor within [0, 16].
+//
+// Granule = 4 ids; round k = granules [k * NT, (k + 1) * NT), granule
+// k * NT + t read by thread t.  Per element: fp32 scaled logits and expf;
+// granule sums in fp32; above that fp64 in a fixed order (bit-reproducible).
+// A bitmap over granules in LDS marks those holding a drawn token, so only
+// their elements are compared against the drawn ids.
+constexpr int kDrThreads = 1024;
+constexpr int kDrWaves = kDrThreads / 64;
+constexpr int kDrMaxRounds = 128;                            // vocabularies up to 2^19 ids
+constexpr int kDrBitmapWords = kDrMaxRounds * kDrThreads / 32;
+
+template <typename T>
+__device__ __forceinline__ void ld4(const T* row, int q, int V, bool aligned, float (&f)[4]);
+
+template <>
+__device__ __forceinline__ void ld4<float>(const float* row, int q, int V, bool aligned,
+                                           float (&f)[4]) {
+  if (aligned && 4 * q + 4 <= V) {
+    const u32x4 w = ld16(row + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = 4 * q + e < V ? row[4 * q + e] : -INFINITY;
+}
+
+template <>
+__device__ __forceinline__ void ld4<bf16s>(const bf16s* row, int q, int V, bool aligned,
+                                           float (&f)[4]) {
+  if (aligned && 4 * q + 4 <= V) {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + 4 * q);
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xffff0000u);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = 4 * q + e < V ? bf2f(row[4 * q + e]) : -INFINITY;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDrThreads) void k_verify_drafted(
+    TreeDev t, const T* logits, const float* dlog, int positions, int V, float s_t, float s_d,
+    const float* draws, int gamma, DraftRows dr, int32_t* accept_len, int32_t* accept_path,
+    int32_t* out_tokens) {
+  constexpr int NT = kDrThreads, NW = kDrWaves;
+  __shared__ uint32_t s_bm[kDrBitmapWords];
+  __shared__ double s_wr[NW][kDrMaxRounds];
+  __shared__ double s_rt[kDrMaxRounds];
+  __shared__ double s_acc[NW][2];
+  __shared__ float s_mx[NW][2];
+  __shared__ int s_fnode[kMaxPos];
+  __shared__ float s_dr[kDraws];
+  __shared__ int s_x[kMaxTopK], s_v[kMaxTopK], s_j[kMaxTopK];
+  __shared__ float s_lx[kMaxTopK], s_ex[kMaxTopK];
+  __shared__ int s_nk, s_bad, s_row, s_pick;
+  __shared__ double s_pre[NW];
+  __shared__ int s_last[NW];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = gridDim.x;
+  const int T_ = min(t.f_count[b], kMaxPos);
+  const int fb = b * kMaxPos;
+  const int cap = t.pool_cap;
+  const int cnt = min(t.pool_count[b], cap);
+  const int NQ = (V + 3) / 4;
+  const int G = (NQ + NT - 1) / NT;
+  int32_t* path = accept_path + (int64_t)b * (gamma + 1);
+  int32_t* out = out_tokens + (int64_t)b * (gamma + 1);
+  if (tid <= gamma) { path[tid] = tid == 0 ? 0 : -1; out[tid] = -1; }
+  if (t.status[b] != 0 || T_ < 1) {
+    if (tid == 0) {
+      path[0] = -1;
+      accept_len[b] = -1;
+    }
+    return;
+  }
+  if (tid < kMaxPos) s_fnode[tid] = tid < T_ ? t.f_node[fb + tid] : -1;
+  for (int i = tid; i < kDrBitmapWords; i += NT) s_bm[i] = 0u;
+  __syncthreads();
+
+  int u = 0, acc = 0;
+  while (true) {
+    // (a) the drawn children of u in pool order, and u's uniforms (wave 0)
+    if (wave == 0) {
+      const int node = s_fnode[u];
+      const bool bad = node < 0 || node >= cnt;
+      int nk = 0;
+      if (!bad && acc < gamma) {
+        for (int base = 0; base < cnt; base += 64) {
+          const int j = base + lane;
+          const bool kid = j < cnt && t.pool_parent[b * cap + j] == node;
+          const uint64_t km = __ballot(kid);
+          const int rank = nk + __popcll(km & ((1ull << lane) - 1ull));
+          if (kid && rank < kMaxTopK) {
+            s_j[rank] = j;
+            s_x[rank] = t.pool_tok[b * cap + j];
+          }
+          nk += __popcll(km);
+        }
+        nk = min(nk, kMaxTopK);
+      }
+      if (lane == 0) {
+        s_nk = nk;
+        s_bad = bad;
+      }
+      if (lane < kDraws) s_dr[lane] = draws[((int64_t)b * positions + u) * kDraws + lane];
+    }
+    __syncthreads();
+    const int nk = s_nk;
+    if (wave == 0 && nk > 0) {
+      // verify position of each drawn child (-1: dropped from the tree)
+      for (int i = 0; i < nk; ++i) {
+        const uint64_t m = __ballot(lane < T_ && s_fnode[lane] == s_j[i]);
+        if (lane == 0) s_v[i] = m ? (int)__ffsll((unsigned long long)m) - 1 : -1;
+      }
+      if (lane == 0) {
+        // the draft row of u: step depth(u), row b * rows + (slot - first slot of that step)
+        const int node = s_fnode[u];
+        const int slot = t.pool_slot[b * cap + node], d = t.pool_depth[b * cap + node];
+        int row = -1;
+        if (d >= 0 && d < dr.n) {
+          int first = 0;
+          for (int s = 0; s < d; ++s) first += dr.rows[s];
+          if (slot >= first && slot < first + dr.rows[d])
+            row = B * first + b * dr.rows[d] + (slot - first);
+        }
+        s_row = row;
+        if (row < 0) s_bad = 1;
+      }
+      if (lane < nk) {
+        const int x = s_x[lane];
+        if (x < 0 || x >= V) s_bad = 1;
+        else atomicOr(&s_bm[(x >> 2) >> 5], 1u << ((x >> 2) & 31));
+      }
+    }
+    __syncthreads();
+    if (s_bad) {       // inconsistent tree state: nothing to verify
+      if (tid <= gamma) { path[tid] = -1; out[tid] = -1; }
+      if (tid == 0) accept_len[b] = -1;
+      return;
+    }
+    const T* row = logits + ((int64_t)b * positions + u) * V;
+    const bool al = (reinterpret_cast<uintptr_t>(row) & (sizeof(T) * 4 - 1)) == 0;
+    const float* drow = nk > 0 ? dlog + (int64_t)s_row * V : dlog;
+    const bool dal = (reinterpret_cast<uintptr_t>(drow) & 15) == 0;
+
+    // (b) maxima: M_t over the target's scaled logits, M_r over the draft's
+    // for the tokens not drawn; the drawn tokens' draft logits to LDS
+    float mt = -INFINITY, mr = -INFINITY;
+    for (int r = 0; r < G; ++r) {
+      const int q = r * NT + tid;
+      if (q >= NQ) break;
+      float f[4];
+      ld4<T>(row, q, V, al, f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mt = fmaxf(mt, __fmul_rn(s_t, f[e]));
+      if (nk > 0) {
+        float g[4];
+        ld4<float>(drow, q, V, dal, g);
+        const bool fl = (s_bm[q >> 5] >> (q & 31)) & 1u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float l = __fmul_rn(s_d, g[e]);
+          bool ex = false;
+          if (fl)
+            for (int i = 0; i < nk; ++i)
+              if (s_x[i] == 4 * q + e) {
+                ex = true;
+                s_lx[i] = l;
+              }
+          if (!ex) mr = fmaxf(mr, l);
+        }
+      }
+    }
+    mt = wave_max(mt);
+    mr = wave_max(mr);
+    if (lane == 0) {
+      s_mx[wave][0] = mt;
+      s_mx[wave][1] = mr;
+    }
+    __syncthreads();
+    float Mt = s_mx[0][0], Mr = s_mx[0][1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      Mt = fmaxf(Mt, s_mx[w][0]);
+      Mr = fmaxf(Mr, s_mx[w][1]);
+    }
+
+    // (c) S = sum exp(s_t z - M_t) (per round when u has no drawn child: the
+    // residual is then p itself), R = sum over the undrawn tokens of
+    // exp(l - M_r); the drawn tokens' target terms to LDS
+    {
+      double sa = 0.0, ra = 0.0;
+      for (int r = 0; r < G; ++r) {
+        const int q = r * NT + tid;
+        float gs = 0.f, gr = 0.f;
+        if (q < NQ) {
+          float f[4];
+          ld4<T>(row, q, V, al, f);
+          const bool fl = (s_bm[q >> 5] >> (q & 31)) & 1u;
+          float g[4];
+          if (nk > 0) ld4<float>(drow, q, V, dal, g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float et = expf(__fsub_rn(__fmul_rn(s_t, f[e]), Mt));
+            gs += et;
+            if (nk > 0) {
+              bool ex = false;
+              if (fl)
+                for (int i = 0; i < nk; ++i)
+                  if (s_x[i] == 4 * q + e) {
+                    ex = true;
+                    s_ex[i] = et;
+                  }
+              if (!ex) gr += expf(__fsub_rn(__fmul_rn(s_d, g[e]), Mr));
+            }
+          }
+        }
+        if (nk == 0) {
+          if (r * NT < NQ) {     // wave-uniform: every lane takes part in the butterfly
+            const double w = wave_sum_d((double)gs);
+            if (lane == 0) s_wr[wave][r] = w;
+          }
+        } else {
+          sa += (double)gs;
+          ra += (double)gr;
+        }
+      }
+      if (nk > 0) {
+        sa = wave_sum_d(sa);
+        ra = wave_sum_d(ra);
+        if (lane == 0) {
+          s_acc[wave][0] = sa;
+          s_acc[wave][1] = ra;
+        }
+      }
+    }
+    __syncthreads();
+    if (nk == 0 && tid < G) {
+      double r = 0.0;
+      for (int w = 0; w < NW; ++w) r += s_wr[w][tid];
+      s_rt[tid] = r;
+    }
+    double S = 0.0, R = 0.0;
+    if (nk > 0)
+      for (int w = 0; w < NW; ++w) {
+        S += s_acc[w][0];
+        R += s_acc[w][1];
+      }
+    __syncthreads();
+
+    // (d) the tests, every thread computing the same scalars
+    int take = -1, nex = 0;
+    double C = 1.0, K = 0.0, mprev = 0.0;
+    float Kf = 0.f, mf = 0.f;
+    const float invS = (float)(1.0 / S);
+    for (int j = 0; j < nk; ++j) {
+      double m = (double)Mr;                    // -inf when every token was drawn
+      for (int i = j; i < nk; ++i) m = fmax(m, (double)s_lx[i]);
+      double E = R > 0.0 ? R * exp((double)Mr - m) : 0.0;
+      for (int i = j; i < nk; ++i) E += exp((double)s_lx[i] - m);
+      const double Kj = j == 0 ? 0.0 : K * exp(m - mprev);
+      const double ex = exp((double)s_lx[j] - m);
+      const double A = fmax((double)s_ex[j] / S - Kj * ex, 0.0);
+      if ((double)s_dr[j] * C * (ex / E) < A) {
+        take = j;
+        break;
+      }
+      K = Kj + C / E;
+      mprev = m;
+      nex = j + 1;
+      Kf = (float)K;
+      mf = (float)m;
+      // C_{j+2}: the residual mass after rejecting x_1 .. x_{j+1}; per round for
+      // the last child (its totals serve the residual draw)
+      const bool fin = j == nk - 1;
+      double ca = 0.0;
+      for (int r = 0; r < G; ++r) {
+        const int q = r * NT + tid;
+        float gs = 0.f;
+        if (q < NQ) {
+          float f[4], g[4];
+          ld4<T>(row, q, V, al, f);
+          ld4<float>(drow, q, V, dal, g);
+          const bool fl = (s_bm[q >> 5] >> (q & 31)) & 1u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float et = expf(__fsub_rn(__fmul_rn(s_t, f[e]), Mt));
+            const float ed = expf(__fsub_rn(__fmul_rn(s_d, g[e]), mf));
+            float tm = fmaxf(__fsub_rn(__fmul_rn(et, invS), __fmul_rn(Kf, ed)), 0.f);
+            if (fl)
+              for (int i = 0; i < nex; ++i)
+                if (s_x[i] == 4 * q + e) tm = 0.f;
+            gs += tm;
+          }
+        }
+        if (fin) {
+          if (r * NT < NQ) {
+            const double w = wave_sum_d((double)gs);
+            if (lane == 0) s_wr[wave][r] = w;
+          }
+        } else {
+          ca += (double)gs;
+        }
+      }
+      if (!fin) {
+        ca = wave_sum_d(ca);
+        if (lane == 0) s_acc[wave][0] = ca;
+      }
+      __syncthreads();
+      if (fin) {
+        if (tid < G) {
+          double r = 0.0;
+          for (int w = 0; w < NW; ++w) r += s_wr[w][tid];
+          s_rt[tid] = r;
+        }
+      } else {
+        C = 0.0;
+        for (int w = 0; w < NW; ++w) C += s_acc[w][0];
+      }
+      __syncthreads();
+    }
+
+    if (take >= 0) {
+      const int x = s_x[take], v = s_v[take];
+      if (tid == 0) {
+        out[acc] = x;
+        if (v >= 0) path[acc + 1] = v;
+        else accept_len[b] = acc;
+      }
+      if (tid < nk) atomicAnd(&s_bm[(s_x[tid] >> 2) >> 5], ~(1u << ((s_x[tid] >> 2) & 31)));
+      __syncthreads();
+      if (v < 0) return;          // a dropped child: its token ends the walk
+      ++acc;
+      u = v;
+      continue;
+    }
+
+    // (e) residual draw by inverse CDF over token ids, from the round totals
+    double tot = 0.0;
+    for (int k = 0; k < G; ++k) tot += s_rt[k];
+    const double target = (double)s_dr[kDraws - 1] * tot;
+    int kk = -1;
+    double pre = 0.0, pre_k = 0.0;
+    for (int k = 0; k < G; ++k) {
+      if (s_rt[k] > 0.0) {
+        kk = k;
+        pre_k = pre;
+        if (target < pre + s_rt[k]) break;        // else: rounding past the end
+      }
+      pre += s_rt[k];
+    }
+    int pick = -1;
+    if (kk >= 0) {
+      if (tid == 0) s_pick = -1;
+      const int q = kk * NT + tid;
+      double e[4];
+      double part = 0.0;
+      int last = -1;
+      {
+        float f[4], g[4];
+        if (q < NQ) {
+          ld4<T>(row, q, V, al, f);
+          if (nk > 0) ld4<float>(drow, q, V, dal, g);
+        }
+        const bool fl = q < NQ && ((s_bm[q >> 5] >> (q & 31)) & 1u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float tm = 0.f;
+          if (q < NQ) {
+            const float et = expf(__fsub_rn(__fmul_rn(s_t, f[j]), Mt));
+            if (nk == 0) {
+              tm = et;
+            } else {
+              const float ed = expf(__fsub_rn(__fmul_rn(s_d, g[j]), mf));
+              tm = fmaxf(__fsub_rn(__fmul_rn(et, invS), __fmul_rn(Kf, ed)), 0.f);
+              if (fl)
+                for (int i = 0; i < nex; ++i)
+                  if (s_x[i] == 4 * q + j) tm = 0.f;
+            }
+          }
+          e[j] = (double)tm;
+          part += e[j];
+          if (tm > 0.f) last = 4 * q + j;
+        }
+      }
+      double inc = part;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double xo = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += xo;
+      }
+      int lastw = last;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) lastw = max(lastw, __shfl_xor(lastw, o, 64));
+      if (lane == 63) s_pre[wave] = inc;
+      if (lane == 0) s_last[wave] = lastw;
+      __syncthreads();
+      double before = 0.0, total = 0.0;
+      int lastb = -1;
+      for (int w = 0; w < NW; ++w) {
+        if (w == wave) before = total;
+        total += s_pre[w];
+        lastb = max(lastb, s_last[w]);
+      }
+      const double end = before + inc;
+      double start = __shfl_up(end, 1, 64);
+      if (lane == 0) start = before;
+      const double tg = target - pre_k;
+      if (part > 0.0 && start <= tg && tg < end) {
+        double c = start;
+        int pk = -1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c += e[j];
+          if (pk < 0 && e[j] > 0.0 && c > tg) pk = 4 * q + j;
+        }
+        s_pick = pk >= 0 ? pk : last;
+      }
+      __syncthreads();
+      pick = s_pick >= 0 ? s_pick : lastb;
+    }
+    // no residual mass left (or no finite term): the last child tried, else token 0
+    if (pick < 0) pick = nk > 0 ? s_x[nk - 1] : 0;
+    if (pick >= V) pick = V - 1;
+    if (tid == 0) {
+      out[acc] = pick;
+      accept_len[b] = acc;
+    }
+    return;
+  }
+}
+
+bool verify_drafted_ok(int vocab) {
+  return vocab >= 1 && (int64_t)vocab <= (int64_t)kDrMaxRounds * kDrThreads * 4;
+}
+
+void launch_verify_drafted(const TreeDev& t, int B, const void* logits, const float* draft_logits,
+                           int positions, int vocab, int dtype, float inv_temp, float draft_inv_temp,
+                           const float* draws, int gamma, const DraftRows& dr, int32_t* accept_len,
+                           int32_t* accept_path, int32_t* out_tokens, hipStream_t st) {
+  if (dtype == EAGLE_BF16)
+    hipLaunchKernelGGL(k_verify_drafted<bf16s>, dim3(B), dim3(kDrThreads), 0, st, t,
+                       (const bf16s*)logits, draft_logits, positions, vocab, inv_temp,
+                       draft_inv_temp, draws, gamma, dr, accept_len, accept_path, out_tokens);
+  else
+    hipLaunchKernelGGL(k_verify_drafted<float>, dim3(B), dim3(kDrThreads), 0, st, t,
+                       (const float*)logits, draft_logits, positions, vocab, inv_temp,
+                       draft_inv_temp, draws, gamma, dr, accept_len, accept_path, out_tokens);
+}
+
 // Commit of the accepted path's keys and values: request b's path positions
 // accept_path[b][0 .. accept_len[b]] (root first) of the tree K/V
 // ([B][64][row_bytes]) are copied to rows dst_row[b] + i of the destination

@@ -128,6 +128,7 @@ class GpuRound:
         self.attn_out = None
         self.target = None
         self.noalloc = False      # draft steps through eagle_draft_step_noalloc
+        self.draft_logits = None  # sampled drafting: every step's logits, for verification
         if cfg.target_layers > 0:
             self._build_target(keep_tree_kv)
 
@@ -254,19 +255,50 @@ class GpuRound:
                                    inv_temp, draws, self.accept_len, self.accept_path,
                                    self.out_tokens, stream)
 
+    def step_logits(self, s):
+        """Step s's block of the draft-logits buffer: fp32 [B * rows_s, V], the
+        blocks of steps 0 .. gamma-1 one after another (allocated on first use)."""
+        B, V = self.cfg.B, self.cfg.head.vocab
+        if self.draft_logits is None:
+            self.draft_logits = torch.empty((B * sum(self.rows), V), dtype=torch.float32,
+                                            device=self.dev)
+        off = B * sum(self.rows[:s])
+        return self.draft_logits[off:off + B * self.rows[s]]
+
+    def verify_sample_drafted(self, target: torch.Tensor, inv_temp: float, draws: torch.Tensor,
+                              stream=None, draft_logits=None):
+        """Lossless verification of a sampled draft, with the draft's
+        probabilities from the logits every step kept (run() keeps them), or
+        from `draft_logits` of the same layout."""
+        dtype = 0 if target.dtype == torch.bfloat16 else 1
+        dl = self.draft_logits if draft_logits is None else draft_logits
+        assert dl is not None, "no draft logits kept"
+        assert dl.dtype == torch.float32 and dl.is_contiguous()
+        assert tuple(dl.shape) == (self.cfg.B * sum(self.rows), self.cfg.head.vocab)
+        assert draws.dtype == torch.float32 and draws.is_contiguous()
+        assert tuple(draws.shape) == (self.cfg.B, target.shape[1], E.VERIFY_DRAWS)
+        E.eagle_tree_verify_sample_drafted(self.tree, target, target.shape[1], target.shape[2],
+                                           dtype, inv_temp, dl, draws,
+                                           self.accept_len, self.accept_path, self.out_tokens,
+                                           stream)
+
     def run(self, target=None, snapshots=False, attend=False, sample=None) -> List[StepSnapshot]:
         """One round; with snapshots=True the state after every draft step is
         copied to the host (for parity checks; synchronises).  sample =
-        (inv_temp, draws) verifies by speculative sampling instead of greedily."""
+        (inv_temp, draws) verifies by speculative sampling instead of greedily
+        (with the draft's probabilities when drafting samples)."""
         cfg = self.cfg
         snaps = []
+        keep = self.tree.sample == 1
         self.init()
         for s in range(cfg.gamma):
             M = cfg.B * self.rows[s]
-            logits = feat = None
+            logits = self.step_logits(s) if keep else None
+            feat = None
             if snapshots:
                 rows = {k: v.cpu().numpy() for k, v in self.rows_view(s).items()}
-                logits = torch.empty((M, cfg.head.vocab), dtype=torch.float32, device=self.dev)
+                if logits is None:
+                    logits = torch.empty((M, cfg.head.vocab), dtype=torch.float32, device=self.dev)
                 feat = torch.empty((M, cfg.head.d), dtype=self.dt, device=self.dev)
             self.step(s, logits_out=logits, feat_out=feat)
             if snapshots:
@@ -287,6 +319,8 @@ class GpuRound:
         if target is not None:
             if sample is None:
                 self.verify(target)
+            elif keep:
+                self.verify_sample_drafted(target, *sample)
             else:
                 self.verify_sample(target, *sample)
         return snaps

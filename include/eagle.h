@@ -356,6 +356,44 @@ int eagle_tree_verify_sample(const eagle_tree *tree, const void *target_logits,
                              void *stream);
 
 /*
+ * Lossless verification of a sampled draft (tree->sample = 1): multi-round
+ * speculative sampling with the draft's proposal probabilities
+ * ("Speculative Decoding Deep Dive III", EAGLE-1 "Inference": the drafter
+ * samples its tokens and one target pass checks the tree, keeping the
+ * target's distribution; "transformer_math / tm_eagle_deep", "Why draft
+ * confidence is a usable acceptance proxy": keep a drafted token with
+ * probability min(1, p_target / p_draft)).
+ * At verify position u, with p = softmax(inv_temp * target_logits[b][u]) and
+ * the draft q = softmax(tree->inv_temp * z), z = u's row of draft_logits, the
+ * children drafting drew at u (every one of them, in draw order, also those
+ * the verify tree dropped) are tested in turn: the j-th, token x, is kept iff
+ *   draws[b][u][j] < r_j(x) / q_j(x),
+ * q_j = q over the tokens not drawn before x, renormalised; r_1 = p and, after
+ * a rejection, r_{j+1} = max(r_j - q_j, 0) renormalised.  A kept child in the
+ * verify tree continues the walk; a kept child the tree dropped ends it with
+ * its token.  With none kept (or no drawn child) one token is drawn from the
+ * last residual: the smallest id whose cumulative mass exceeds
+ * draws[b][u][16] times the residual mass.
+ * draft_logits: device fp32, the logits_out of draft steps 0 .. gamma-1 one
+ *   after another: step s's block holds B * eagle_step_rows(tree, s) rows of
+ *   vocab entries in that step's row order (rows b * W_s + i).
+ * Arithmetic: fp32 scaled logits and expf per id; sums of 4 consecutive ids in
+ * fp32, every sum above that and every test in fp64, in a fixed order
+ * (bit-reproducible).  One workgroup per request; each rejection costs one
+ * pass over the two rows of the visited position.
+ * Returns EAGLE_EINVAL when tree->sample != 1 (top-k drafts propose each child
+ * with certainty: eagle_tree_verify_sample), EAGLE_EUNSUPPORTED for
+ * vocab > 524288.  Other arguments and outputs as eagle_tree_verify_sample;
+ * accept_len[b] = -1 (path[b][0] = -1) when request b's tree state is
+ * inconsistent (flagged, or a drawn node without its draft row).
+ */
+int eagle_tree_verify_sample_drafted(const eagle_tree *tree, const void *target_logits,
+                                     int positions, int vocab, int dtype, float inv_temp,
+                                     const float *draft_logits, const float *draws,
+                                     int32_t *accept_len, int32_t *accept_path,
+                                     int32_t *out_tokens, void *stream);
+
+/*
  * The target model for its verification pass: n_layers decoder layers of the
  * draft head's layer shape (d, heads, head_dim, ffn, act, norm, eps,
  * rope_theta and dtype are the head's), each with its own context cache, a

@@ -187,12 +187,15 @@ def drafted_tests(p, draft_row, draft_inv_temp, drawn):
     """The successive tests at one node whose children `drawn` (token ids, in
     draw order) came from the draft row `draft_row`.
 
-    Returns (thr, resid): thr[j] = r_j(x_j) / q_j(x_j) (x_j is kept iff its
-    uniform is below thr[j]; +inf when q_j(x_j) = 0 < r_j(x_j)), and resid =
+    Returns (thr, resid, mass): thr[j] = r_j(x_j) / q_j(x_j) (x_j is kept iff
+    its uniform is below thr[j]; +inf when q_j(x_j) = 0 < r_j(x_j)); resid =
     the residual after every child was rejected, normalised (all zero when no
-    mass is left).  r_j is the residual after rejecting x_1 .. x_{j-1}."""
+    mass is left); mass[j] = the unnormalised residual mass before test j
+    relative to p (mass[0] = 1, mass[k] = that of resid).  r_j is the residual
+    after rejecting x_1 .. x_{j-1}."""
     r = np.array(p, np.float64)
     thr = []
+    mass = [1.0]
     for j, x in enumerate(drawn):
         qj = draft_probs_remaining(draft_row, draft_inv_temp, drawn[:j])
         if qj[x] > 0.0:
@@ -201,8 +204,9 @@ def drafted_tests(p, draft_row, draft_inv_temp, drawn):
             thr.append(np.inf if r[x] > 0.0 else 0.0)
         r = np.maximum(r - qj, 0.0)
         tot = r.sum()
+        mass.append(mass[-1] * tot)
         r = r / tot if tot > 0.0 else np.zeros_like(r)
-    return np.array(thr, np.float64), r
+    return np.array(thr, np.float64), r, np.array(mass, np.float64)
 
 
 def verify_sample_drafted(tok, parent, drawn, logits, inv_temp, draft_rows, draft_inv_temp,
@@ -225,7 +229,7 @@ def verify_sample_drafted(tok, parent, drawn, logits, inv_temp, draft_rows, draf
         p = target_probs(logits[u], inv_temp)
         kids = list(drawn[u]) if len(path) - 1 < gamma else []
         if kids:
-            thr, resid = drafted_tests(p, draft_rows[u], draft_inv_temp, [x for x, _ in kids])
+            thr, resid, _ = drafted_tests(p, draft_rows[u], draft_inv_temp, [x for x, _ in kids])
         else:
             thr, resid = np.zeros(0), p
         take = None

@@ -425,6 +425,147 @@ def sampling_checks(case: Case, gr, device, seeds=(0, 1, 2), inv_temps=(1.0, 0.7
     return out
 
 
+# ------------------------------------------------- P3d: verification of sampled drafts
+# The kernel's test of the j-th drawn child compares u_j with r_j(x) / q_j(x),
+# formed from fp32 exponentials (relative error ~1e-6 for terms far below the
+# row maximum) and residual masses C_j summed from fp32 terms: its absolute
+# error is within ~4e-6 (p(x) / q_j(x) + thr) (1 + j) / C_j, with C_j the
+# residual mass before the test.  The residual draw's cumulative sums carry an
+# absolute error of ~2e-6 (1 + k) / C_final in normalised units.  Inside those
+# margins either outcome is valid and the walk follows the GPU.
+def _draft_rows_of(snaps, B):
+    """(request, pool node) -> row of the stacked draft logits, from the row
+    descriptors each step recorded before it ran."""
+    where = {}
+    off = 0
+    for sn in snaps:
+        nodes = sn.rows["node"]
+        W = len(nodes) // B
+        for i, nd in enumerate(nodes):
+            where[(i // W, int(nd))] = off + i
+        off += len(nodes)
+    return where
+
+
+def check_verify_drafted(case: Case, gr, snaps, target_np, draft_np, draws, inv_temp):
+    cfg = case.cfg
+    gamma, B, s_d = cfg.gamma, cfg.B, cfg.inv_temp
+    fv = {k: v.cpu().numpy() for k, v in gr.final_view().items()}
+    pv = {k: v.cpu().numpy() for k, v in gr.pool_view().items()}
+    where = _draft_rows_of(snaps, B)
+    acc_g = gr.accept_len.cpu().numpy()
+    path_g = gr.accept_path.cpu().numpy()
+    out_g = gr.out_tokens.cpu().numpy()
+    V = target_np.shape[-1]
+    stats = dict(tests=0, draws=0, ambiguous=0, dropped=0, accepted=[])
+    for b in range(B):
+        T = int(fv["count"][b])
+        fnode = fv["node"][b, :T]
+        cnt = int(pv["count"][b])
+        ppar, ptok = pv["parent"][b, :cnt], pv["tok"][b, :cnt]
+        pos_of = {int(fnode[v]): v for v in range(T)}
+        a = int(acc_g[b])
+        assert 0 <= a <= gamma and path_g[b, 0] == 0, (b, a, path_g[b])
+        u = 0
+        for depth in range(a + 1):
+            p = OV.target_probs(synth.f32(target_np[b, u]), inv_temp)
+            nd = int(fnode[u])
+            kids = [(int(ptok[j]), pos_of.get(j, -1)) for j in range(cnt) if ppar[j] == nd] \
+                if depth < gamma else []
+            if kids:
+                row = draft_np[where[(b, nd)]]
+                thr, resid, mass = OV.drafted_tests(p, row, s_d, [x for x, _ in kids])
+            else:
+                row, thr, resid, mass = None, [], p, np.ones(1)
+            if depth < a:
+                took = [i for i, (_, v) in enumerate(kids) if v == int(path_g[b, depth + 1])]
+                assert len(took) == 1, (b, depth, kids, path_g[b])
+                i_take = took[0]
+            else:
+                x_out = int(out_g[b, a])
+                took = [i for i, (x, v) in enumerate(kids) if x == x_out and v < 0]
+                i_take = took[0] if took else None
+            n_test = len(kids) if i_take is None else i_take + 1
+            for j in range(n_test):
+                x = kids[j][0]
+                qj = OV.draft_probs_remaining(row, s_d, [k[0] for k in kids[:j]])[x]
+                th = float(thr[j])
+                d = float(draws[b, u, j])
+                stats["tests"] += 1
+                tol = ACC_MARGIN * th + 4e-6 * (p[x] / max(qj, 1e-300) + th) * (1 + j) / max(mass[j], 1e-300)
+                if abs(d - th) > tol:
+                    assert (d < th) == (j == i_take), (b, u, j, d, th, i_take)
+                else:
+                    stats["ambiguous"] += 1
+            if i_take is not None:
+                x, v = kids[i_take]
+                assert out_g[b, depth] == x, (b, depth, out_g[b], x)
+                if v < 0:
+                    assert depth == a, (b, depth, a)
+                    stats["dropped"] += 1
+                    break
+                u = v
+                continue
+            # the walk stopped at u: residual draw by inverse CDF
+            x = int(out_g[b, a])
+            tried = [k[0] for k in kids]
+            assert 0 <= x < V and x not in tried, (b, x, tried)
+            c = np.cumsum(resid)
+            total = c[-1]
+            stats["draws"] += 1
+            if not total > 0:
+                assert x == (tried[-1] if tried else 0), (b, x, tried)
+                continue
+            target = float(draws[b, u, OV.N_DRAWS - 1]) * total
+            lo_e = c[x - 1] if x > 0 else 0.0
+            tol = CDF_MARGIN * total + 2e-6 * (1 + len(kids)) / max(mass[-1], 1e-300)
+            assert lo_e - tol <= target < c[x] + tol, (b, x, lo_e, target, c[x], tol)
+            if not (target - lo_e > tol and c[x] - target > tol):
+                stats["ambiguous"] += 1
+        assert all(o == -1 for o in out_g[b, a + 1:]) and all(pp == -1 for pp in path_g[b, a + 1:])
+        stats["accepted"].append(a)
+    return stats
+
+
+def planted_draft(case: Case, gr, snaps, draft_np, seed=0):
+    """Draft logits that make the drawn children likely under the draft: at
+    each expanded node every drawn child's logit becomes (log |V| + U(0, 2)) / s,
+    so each holds a sizeable share of q."""
+    rng = np.random.default_rng(2000 + seed)
+    out = draft_np.copy()
+    pv = {k: v.cpu().numpy() for k, v in gr.pool_view().items()}
+    V = out.shape[-1]
+    s = case.cfg.inv_temp
+    for (b, nd), r in _draft_rows_of(snaps, case.cfg.B).items():
+        cnt = int(pv["count"][b])
+        for j in range(cnt):
+            if pv["parent"][b, j] == nd:
+                out[r, pv["tok"][b, j]] = np.float32((np.log(V) + rng.uniform(0.0, 2.0)) / s)
+    return out
+
+
+def drafted_checks(case: Case, gr, snaps, device, inv_temps=(1.0, 0.7, 1.3)):
+    """P3d: the drafted verification on the synthetic target with the draft's
+    own logits, on a planted target, and on a planted target and draft."""
+    import torch
+    out = dict(tests=0, draws=0, ambiguous=0, dropped=0, accepted=[])
+    T = case.target.shape[1]
+    own = gr.draft_logits.cpu().numpy()
+    for k in range(3):
+        draws = synth.verify_draws(case.cfg, T, 10 + k)
+        dd = torch.from_numpy(draws).to(device)
+        tnp = case.target if k == 0 else planted_sampling_target(case, gr, k)
+        dnp = own if k < 2 else planted_draft(case, gr, snaps, own, k)
+        s_ = inv_temps[k]
+        gr.verify_sample_drafted(case.target_dev(device, tnp), s_, dd,
+                                 draft_logits=None if k < 2 else torch.from_numpy(dnp).to(device))
+        st = check_verify_drafted(case, gr, snaps, tnp, dnp, draws, s_)
+        for key in ("tests", "draws", "ambiguous", "dropped"):
+            out[key] += st[key]
+        out["accepted"] += st["accepted"]
+    return out
+
+
 # ------------------------------------------------------------------ P5: target pass
 def _target_layers(cfg):
     """Oracle target layers; materialised one at a time at large widths."""
@@ -648,6 +789,14 @@ def full_check(cfg, attend=None, planted=True, rows_per_step=None, device="cuda:
             f"{st['ambiguous']} inside a margin")
         report["sample_accept_hist"] = np.bincount(st["accepted"], minlength=cfg.gamma + 1).tolist()
         report["sample_ambiguous"] = st["ambiguous"]
+        if cfg.sample_seed is not None:
+            st = drafted_checks(case, gr, snaps, device)
+            say(f"drafted verify checked: {st['tests']} tests, {st['draws']} draws, "
+                f"{st['dropped']} dropped children kept, {st['ambiguous']} inside a margin")
+            report["drafted_accept_hist"] = np.bincount(st["accepted"],
+                                                        minlength=cfg.gamma + 1).tolist()
+            report["drafted_ambiguous"] = st["ambiguous"]
+            report["drafted_dropped_kept"] = st["dropped"]
     torch.cuda.synchronize()
     return report
 

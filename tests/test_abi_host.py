@@ -170,6 +170,17 @@ def test_rejects_bad_arguments_before_launch(lib):
     for pos, temp, draws in [(64, 1.0, None), (64, 0.0, 1), (64, -1.0, 1), (64, float("nan"), 1),
                              (64, float("inf"), 1), (2, 1.0, 1)]:
         assert lib.eagle_tree_verify_sample(t, 1, pos, 100, 0, temp, draws, 1, 1, 1, None) == E.EAGLE_EINVAL
+    # verification of sampled drafts: only for sampled drafting, draft logits
+    # required, vocabularies up to 2^19
+    sd = _tree(C.CONFIGS["c8_8b_dynamic_sampled"], state=1 << 20, nbytes=1 << 30)
+    sd.sample = 1
+    f = lib.eagle_tree_verify_sample_drafted
+    assert f(t, 1, 64, 100, 0, 1.0, 1, 1, 1, 1, 1, None) == E.EAGLE_EINVAL       # sample = 0
+    for pos, temp, dl, draws, voc in [(64, 1.0, None, 1, 100), (64, 1.0, 1, None, 100),
+                                      (64, 0.0, 1, 1, 100), (64, float("nan"), 1, 1, 100),
+                                      (2, 1.0, 1, 1, 100), (64, 1.0, 1, 1, 0)]:
+        assert f(sd, 1, pos, voc, 0, temp, dl, draws, 1, 1, 1, None) == E.EAGLE_EINVAL
+    assert f(sd, 1, 64, (1 << 19) + 1, 0, 1.0, 1, 1, 1, 1, 1, None) == E.EAGLE_EUNSUPPORTED
     assert lib.eagle_strerror(E.EAGLE_ECAPACITY).startswith(b"capacity")
 
 

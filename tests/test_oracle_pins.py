@@ -731,7 +731,9 @@ def test_drafted_verify_law_is_the_target(k, case):
             rem.remove(x)
         pr = math.exp(lp)
         total += pr
-        thr, resid = VF.drafted_tests(p, zd, sd, list(seq))
+        thr, resid, mass = VF.drafted_tests(p, zd, sd, list(seq))
+        # the first rejection leaves the total variation distance sum max(p - q, 0)
+        assert abs(mass[1] - np.maximum(p - np.exp(lq), 0).sum()) < 1e-12
         stay = 1.0
         for j, x in enumerate(seq):
             a = min(1.0, thr[j])
