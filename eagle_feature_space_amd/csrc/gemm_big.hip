@@ -182,22 +182,40 @@ __global__ __launch_bounds__(64 * WN * WM) void k_gemm_big(GemmArgs a, int nt, i
 }
 
 // ------------------------------------------------------------ direct-to-LDS
-constexpr int kDN = 256, kDM = 256, kDK = 32, kDStages = 4;
+constexpr int kDN = 256, kDK = 32;
 constexpr int kDRow = kDK * 2;                              // 64 B per row per stage
-constexpr int kDStage = (kDN + kDM) * kDRow;                // 32 KB
-constexpr int kDLds = kDStages * kDStage;                   // 128 KB
+
+// Tiles BN x BM: 256 x 256 (from 256 rows) and 256 x 128 (64..255 rows).
+// Eight waves in 2 (n) x 4 (m), wave tile 128 x BM/4; each wave issues L 1 KB
+// direct-to-LDS loads per stage (16 rows of 64 B each), PF stages ahead.
+template <int BN, int BM>
+struct Dma {
+  static constexpr int WN = BN / 128, WM = 8 / WN;          // wave grid
+  static constexpr int WMB = BM / WM / 16;                  // 16-row m-blocks per wave
+  static constexpr int ROWS = BN + BM;                      // W rows, then X rows
+  static constexpr int STAGE = ROWS * kDRow;                // 32 / 24 KB
+  static constexpr int STAGES = BM == 256 ? 4 : 6;          // ring: 128 / 144 KB
+  static constexpr int PF = STAGES - 1;
+  static constexpr int L = ROWS / 16 / 8;                   // 4 / 3
+  static constexpr int LDS = STAGES * STAGE;
+};
+
+// s_waitcnt immediate for vmcnt(n) alone (vmcnt bits [3:0] and [15:14])
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ int dma_off(int r, int j) { return r * kDRow + 16 * (j ^ ((r >> 1) & 2)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int EPI>   // 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
+template <int EPI, int BN, int BM>   // EPI 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
 __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, int S) {
+  using D = Dma<BN, BM>;
+  constexpr int WMB = D::WMB, L = D::L, PF = D::PF, WM = D::WM;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int wn = wave >> 2, wm = wave & 3;
+  const int wn = wave / WM, wm = wave % WM;
   const int total = nt * mt * S;
   const int per = (total + 7) / 8;
   const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -205,24 +223,26 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, in
   const int mtile = lin % mt;
   const int ntile = (lin / mt) % nt;
   const int z = lin / (mt * nt);
-  const int n0 = ntile * kDN, m0 = mtile * kDM;
+  const int n0 = ntile * BN, m0 = mtile * BM;
   const int k_begin = z * a.kps, k_end = min(a.K, k_begin + a.kps);
   const int nst = (k_end - k_begin) / kDK;
 
-  // waves 0-3 load W rows 64 w .. 64 w + 63, waves 4-7 X rows: four 1 KB
-  // blocks of 16 rows each; lane l writes chunk slot l & 3 of block row l >> 2
-  const bool is_w = wave < 4;
-  const char* src[4];
-  const char* src1[4];
+  // wave w loads stage blocks L w .. L w + L - 1 (16 rows each; rows below BN
+  // are W rows, the rest X rows); lane l writes chunk slot l & 3 of block row
+  // l >> 2, i.e. global chunk (l & 3) ^ ((row >> 1) & 2) of that row
+  const char* src[L];
+  const char* src1[L];
+  bool isx[L];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave & 3) * 64 + i * 16 + (lane >> 2);     // row of the W or X tile
+  for (int i = 0; i < L; ++i) {
+    const int r = (wave * L + i) * 16 + (lane >> 2);        // stage row
     const int j = (lane & 3) ^ ((r >> 1) & 2);
-    if (is_w) {
+    isx[i] = r >= BN;
+    if (!isx[i]) {
       int n;
       if (EPI == 1) {   // 16-row blocks alternate gate (even) and up (odd)
         const int b = r >> 4;
-        const int q = ntile * (kDN / 2) + (b >> 1) * 16 + (r & 15);
+        const int q = ntile * (BN / 2) + (b >> 1) * 16 + (r & 15);
         n = (b & 1) ? a.pair_F + min(q, a.pair_F - 1) : min(q, a.pair_F - 1);
       } else {
         n = min(n0 + r, a.N - 1);
@@ -235,79 +255,77 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, in
       src[i] = (const char*)(base + (int64_t)(n - off) * a.K + j * 8);
       src1[i] = src[i];
     } else {
-      const int m = min(m0 + r, a.M - 1);
+      const int m = min(m0 + r - BN, a.M - 1);
       src[i] = (const char*)(row_ptr<bf16s>(a.xs[0], m) + j * 8);
       src1[i] = a.xs[1].base ? (const char*)(row_ptr<bf16s>(a.xs[1], m) + j * 8) : src[i];
     }
   }
-  const int ldsrow0 = (is_w ? 0 : kDN) + (wave & 3) * 64;
   // stage s (clamped to the last one, so every stage issues the same number
-  // of loads and the vmcnt waits stay exact) into ring slot s % 4
+  // of loads and the vmcnt waits stay exact) into ring slot s % STAGES
   auto issue = [&](int s) {
     const int sc = min(s, nst - 1);
     const int k0 = k_begin + sc * kDK;
-    const bool hi = !is_w && k0 >= a.ksplit_x;    // a stage never straddles the split
-    char* dst = lds + (s & (kDStages - 1)) * kDStage + ldsrow0 * kDRow;
+    char* dst = lds + (s % D::STAGES) * D::STAGE + wave * L * 1024;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < L; ++i) {
+      const bool hi = isx[i] && k0 >= a.ksplit_x;          // a stage never straddles the split
       const char* p = hi ? src1[i] + (int64_t)(k0 - a.ksplit_x) * 2 : src[i] + (int64_t)k0 * 2;
       __builtin_amdgcn_global_load_lds((const void*)p, (lds_void*)(dst + i * 1024), 16, 0, 0);
     }
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[8][WMB];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nst > 0) {
     // Fragments are read half a stage ahead of their MFMAs, the barrier sits
     // in the middle of a stage:
     //   MFMAs n-blocks 0-3 of stage s | wait for stage s+1, barrier, loads of
-    //   stage s+3, reads of stage s+1 (W blocks 0-3 and X) | MFMAs n-blocks
+    //   stage s+PF, reads of stage s+1 (W blocks 0-3 and X) | MFMAs n-blocks
     //   4-7 of stage s | reads of stage s+1 W blocks 4-7.
     // The X fragments alternate between two register sets, so the loop body
     // covers two stages (nst is even: K per split is a multiple of 64).
     // After a barrier every wave has issued all its reads of stage s (they
     // completed before the MFMAs that used them, in front of the barrier), so
-    // the slot stage s+3 overwrites (stage s-1's) is free.
-    const int wr0 = wn * 128, xr0 = kDN + wm * 64;
-    issue(0);
-    issue(1);
-    issue(2);
-    __builtin_amdgcn_s_waitcnt(0x0F78);          // vmcnt(8): stage 0 landed
+    // the slot stage s+PF overwrites (stage s-1's) is free.
+    const int wr0 = wn * 128, xr0 = BN + wm * 16 * WMB;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) issue(i);
+    __builtin_amdgcn_s_waitcnt(vm_wait((PF - 1) * L));     // stage 0 landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 wf[8], xa[4], xb[4];
+    u32x4 wf[8], xa[WMB], xb[WMB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) xa[mb] = ld16(lds + dma_off(xr0 + mb * 16 + c, g));
+    for (int mb = 0; mb < WMB; ++mb) xa[mb] = ld16(lds + dma_off(xr0 + mb * 16 + c, g));
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) wf[nb] = ld16(lds + dma_off(wr0 + nb * 16 + c, g));
 #define DMA_STAGE(S_, XC, XN)                                                                 \
     {                                                                                       \
       _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
-      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                      \
+      _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
         acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
       __builtin_amdgcn_sched_barrier(0);                                                    \
-      __builtin_amdgcn_s_waitcnt(0x0F74);    /* vmcnt(4): stage S_+1 landed */              \
+      __builtin_amdgcn_s_waitcnt(vm_wait((PF - 2) * L));    /* stage S_+1 landed */         \
       __builtin_amdgcn_s_barrier();                                                         \
       __builtin_amdgcn_sched_barrier(0);                                                    \
-      issue((S_) + 3);                                                                      \
-      const char* st_ = lds + (((S_) + 1) & (kDStages - 1)) * kDStage;                      \
+      issue((S_) + PF);                                                                     \
+      const char* st_ = lds + (((S_) + 1) % D::STAGES) * D::STAGE;                          \
       _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
         wf[nb] = ld16(st_ + dma_off(wr0 + nb * 16 + c, g));                                 \
-      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                      \
+      _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
         XN[mb] = ld16(st_ + dma_off(xr0 + mb * 16 + c, g));                                 \
       _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
-      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                      \
+      _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
         acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
       _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
         wf[nb] = ld16(st_ + dma_off(wr0 + nb * 16 + c, g));                                 \
-      __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   /* loads */                     \
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   /* reads W 0-3, X */            \
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  /* MFMAs n-blocks 4-7 */        \
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   /* reads W 4-7 */               \
+      __builtin_amdgcn_sched_group_barrier(0x020, L, 0);        /* loads */                 \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 + WMB, 0);  /* reads W 0-3, X */        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * WMB, 0);  /* MFMAs n-blocks 4-7 */    \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        /* reads W 4-7 */           \
       __builtin_amdgcn_sched_barrier(0);                                                    \
     }
     for (int s = 0; s < nst; s += 2) {
@@ -318,17 +336,17 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, in
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load in flight when the wave ends
 
-  // acc[nb][mb]: lane holds out[m = m0 + 64 wm + 16 mb + c][n = n0 + 128 wn + 16 nb + 4 g + 0..3]
+  // acc[nb][mb]: lane holds out[m = m0 + BM/WM wm + 16 mb + c][n = n0 + 128 wn + 16 nb + 4 g + 0..3]
   if (EPI == 1) {
     // gate block nb (even) pairs with up block nb + 1: columns
-    // j = 128 ntile + 16 ((16 wn + nb) / 2) + 4 g + 0..3 of act (F columns)
+    // j = BN/2 ntile + 16 ((8 wn + nb) / 2) + 4 g + 0..3 of act (F columns)
 #pragma unroll
     for (int nb = 0; nb < 8; nb += 2) {
-      const int j = ntile * (kDN / 2) + ((wn * 8 + nb) >> 1) * 16 + 4 * g;
+      const int j = ntile * (BN / 2) + ((wn * 8 + nb) >> 1) * 16 + 4 * g;
       if (j >= a.pair_F) continue;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int m = m0 + wm * 64 + mb * 16 + c;
+      for (int mb = 0; mb < WMB; ++mb) {
+        const int m = m0 + wm * 16 * WMB + mb * 16 + c;
         if (m >= a.M) continue;
         f32x4 y;
 #pragma unroll
@@ -350,28 +368,36 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, in
     const int n = n0 + wn * 128 + nb * 16 + 4 * g;
     if (n >= a.N) continue;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 64 + mb * 16 + c;
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int m = m0 + wm * 16 * WMB + mb * 16 + c;
       if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
     }
   }
 }
 
-// the direct-to-LDS kernel's plan: one or two splits, or none (fall back)
+// the direct-to-LDS kernel's plan (or none: fall back to k_gemm_big).
+// 128-row tiles for 64..255 rows, split along K until the grid is one wave
+// of at most 256 workgroups (one per CU); 256-row tiles from 256 rows where
+// the tiles alone give >= 128 workgroups.
 static bool plan_dma(int M, int N, int K, GemmShape* s) {
-  if (M < 256 || K % (2 * kDK) != 0) return false;
-  const int nt = (N + kDN - 1) / kDN, mt = (M + kDM - 1) / kDM;
+  if (M < 64 || K % (2 * kDK) != 0) return false;
+  const int BM = M >= 256 ? 256 : 128;
+  const int BN = kDN;
+  const int nt = (N + BN - 1) / BN, mt = (M + BM - 1) / BM;
   const int tiles = nt * mt;
-  if (tiles < 128) return false;
+  if (BM == 256 && tiles < 128) return false;
   const int kst = K / kDK;                  // even: K is a multiple of 64
-  int S = (256 + tiles - 1) / tiles;
+  // one workgroup per CU: 128-row tiles split until the grid is one wave of
+  // at most 256 workgroups (a partial second wave would double the time)
+  int S = BM == 128 ? 256 / tiles : (256 + tiles - 1) / tiles;
   if (S > kst / 8) S = kst / 8 > 0 ? kst / 8 : 1;
   if (S < 1) S = 1;
   int sps = (kst + S - 1) / S;
   sps += sps & 1;                           // an even number of stages per split
   s->direct = 2;
   s->NB = 2;                // the direct-to-LDS kernel
-  s->MB = 16;
+  s->MB = BM / 16;
+  s->BN = BN;
   s->ntiles = nt;
   s->mtiles = mt;
   s->kps = sps * kDK;
@@ -384,9 +410,9 @@ bool big_gemm_ok(int dtype, int M, int N, int K) {
 }
 
 bool big_swiglu_ok(int dtype, int M, int F, int K) {
-  if (!big_gemm_ok(dtype, M, 2 * F, K) || F % (kDN / 2) != 0) return false;
   GemmShape s;
-  return plan_dma(M, 2 * F, K, &s) && s.S == 1;
+  if (!big_gemm_ok(dtype, M, 2 * F, K) || !plan_dma(M, 2 * F, K, &s)) return false;
+  return s.S == 1 && F % (s.BN / 2) == 0;
 }
 
 GemmShape plan_gemm_big(int M, int N, int K) {
@@ -424,24 +450,26 @@ static void launch_big_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) 
                      s.ntiles, s.mtiles, s.S);
 }
 
-template <int EPI>
+template <int EPI, int BN, int BM>
 static void launch_dma_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+  constexpr int LDS = Dma<BN, BM>::LDS;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_dma<EPI>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kDLds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_dma<EPI, BN, BM>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     attr = true;
   }
   const int total = s.ntiles * s.mtiles * s.S;
-  hipLaunchKernelGGL(k_gemm_dma<EPI>, dim3(((total + 7) / 8) * 8), dim3(512), kDLds, st, a,
-                     s.ntiles, s.mtiles, s.S);
+  hipLaunchKernelGGL((k_gemm_dma<EPI, BN, BM>), dim3(((total + 7) / 8) * 8), dim3(512), LDS, st,
+                     a, s.ntiles, s.mtiles, s.S);
 }
 
 void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
   a.kps = s.kps;
   if (s.NB == 2) {
-    if (a.pair_F > 0) launch_dma_t<1>(a, s, st);
-    else launch_dma_t<0>(a, s, st);
+    const bool sw = a.pair_F > 0;
+    if (s.MB == 16) sw ? launch_dma_t<1, 256, 256>(a, s, st) : launch_dma_t<0, 256, 256>(a, s, st);
+    else sw ? launch_dma_t<1, 256, 128>(a, s, st) : launch_dma_t<0, 256, 128>(a, s, st);
     return;
   }
   if (s.MB == 16) launch_big_t<4, 4, 4>(a, s, st);

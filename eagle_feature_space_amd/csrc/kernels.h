@@ -24,6 +24,7 @@ struct GemmArgs {
 };
 struct GemmShape {
   int MB, NB, mtiles, ntiles, S, kps;
+  int BN = 256;        // direct-to-LDS kernel (NB == 2): tile width (columns of W)
   int direct;          // 1: barrier-free streaming (M <= 16), 2: MFMA-tiled big GEMM,
                        // 3: streaming with LDS-shared activation rows (17..32)
 };
