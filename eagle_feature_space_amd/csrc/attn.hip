@@ -421,31 +421,45 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
         sc[j] = acc;
       }
       // ---- online softmax, O^T += V^T P^T
-      const bool full = !extra && t0 + 64 <= kend;   // no key of the tile is masked
+      // A tile with every key inside the split and no tree-node mask (all but
+      // the last tile of a context split) takes the branch without masking.
+      const bool full = !extra && t0 + 64 <= kend;   // wave-uniform
       float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t0 + g * 16 + j * 4 + i;
-          bool valid = full || key < kend;
-          if (extra) valid = valid && ((msk >> key) & 1ull);
-          const float v = valid ? sc[j][i] * a.scale_log2 : -INFINITY;
-          sc[j][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+          for (int i = 0; i < 4; ++i) {
+            sc[j][i] *= a.scale_log2;
+            tmax = fmaxf(tmax, sc[j][i]);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = t0 + g * 16 + j * 4 + i;
+            bool valid = key < kend;
+            if (extra) valid = valid && ((msk >> key) & 1ull);
+            const float v = valid ? sc[j][i] * a.scale_log2 : -INFINITY;
+            sc[j][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mnew = fmaxf(mrun, tmax);
       const bool empty = mnew == -INFINITY;
-      const float alpha = empty ? 1.f : exp2f(mrun - mnew);
+      // v_exp_f32 directly: results below the normal range flush to 0, which
+      // for probabilities relative to the running maximum is exact enough
+      const float alpha = empty ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
       float p[16];
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = empty ? 0.f : exp2f(sc[j][i] - mnew);
+          const float e = empty ? 0.f : __builtin_amdgcn_exp2f(sc[j][i] - mnew);
           p[4 * j + i] = e;
           psum += e;
         }
