@@ -145,33 +145,46 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
     }
     wave_lds_sync();
     // ---- online softmax and O^T += V^T P^T
-    const bool full = !extra && t0 + 64 <= kend;   // no key of the tile is masked
+    // a tile with every key inside the split and no tree-node mask takes the
+    // branch without masking (wave-uniform)
+    const bool full = !extra && t0 + 64 <= kend;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t0 + g * 16 + j * 4 + i;
-          bool valid = full || key < kend;
-          if (extra) valid = valid && ((msk[rb] >> key) & 1ull);
-          const float v = valid ? s[j][rb][i] * a.scale_log2 : -INFINITY;
-          s[j][rb][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+          for (int i = 0; i < 4; ++i) {
+            s[j][rb][i] *= a.scale_log2;
+            tmax = fmaxf(tmax, s[j][rb][i]);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = t0 + g * 16 + j * 4 + i;
+            bool valid = key < kend;
+            if (extra) valid = valid && ((msk[rb] >> key) & 1ull);
+            const float v = valid ? s[j][rb][i] * a.scale_log2 : -INFINITY;
+            s[j][rb][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mnew = fmaxf(mrun[rb], tmax);
       const bool empty = mnew == -INFINITY;
-      const float alpha = empty ? 1.f : exp2f(mrun[rb] - mnew);
+      // v_exp_f32 directly (results below the normal range flush to 0)
+      const float alpha = empty ? 1.f : __builtin_amdgcn_exp2f(mrun[rb] - mnew);
       float p[16];
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = empty ? 0.f : exp2f(s[j][rb][i] - mnew);
+          const float e = empty ? 0.f : __builtin_amdgcn_exp2f(s[j][rb][i] - mnew);
           p[4 * j + i] = e;
           psum += e;
         }
