@@ -70,6 +70,17 @@ __device__ __forceinline__ bool before(float va, int da, int ia, float vb, int d
   return ia < ib;
 }
 
+// The same order as one unsigned 64-bit key (smaller = earlier): the value
+// through vkey mapped to an order-preserving unsigned word and inverted
+// (descending), then depth and index in 16 bits each.  +0 and -0 compare
+// equal as floats but not as words; values are products of confidences in
+// [0, 1] (or -1 for NaN), so -0 does not occur.
+__device__ __forceinline__ uint64_t order_key(float v, int depth, int index) {
+  const uint32_t u = __float_as_uint(vkey(v));
+  const uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)~mono << 32) | ((uint64_t)(depth & 0xFFFF) << 16) | (uint64_t)(index & 0xFFFF);
+}
+
 // `t` points its row_* arrays at the rows of this step; `nx` holds the row
 // arrays of the next step (the other half of the double buffer): the two
 // steps have different row counts per request, so writing in place would
@@ -84,6 +95,7 @@ __global__ __launch_bounds__(kExpandThreads) void k_tree_expand(TreeDev t, RowsD
   __shared__ int sdep[kPoolMax];
   __shared__ int spar[kPoolMax];
   __shared__ int spos[kPoolMax];
+  __shared__ uint64_t skey[kPoolMax];
   __shared__ int snext[256];
   __shared__ int swave[NT / 64];
   const int b = blockIdx.x;
@@ -130,16 +142,25 @@ __global__ __launch_bounds__(kExpandThreads) void k_tree_expand(TreeDev t, RowsD
     int nnext;
     if (kind == EAGLE_TREE_DYNAMIC) {
       nnext = min(top_k, nchild);
-      for (int cidx = tid; cidx < nchild; cidx += NT) {
-        const int u = p0 + cidx;
-        const float vu = vkey(sval[u]);
+      // rank of each new node among the new nodes (value desc, index asc:
+      // they share one depth) from packed keys; TPN consecutive lanes share a
+      // node, each counting a slice of the others
+      int tpn = 1;
+      while (tpn < 16 && nchild * tpn * 2 <= NT) tpn *= 2;
+      for (int cidx = tid; cidx < nchild; cidx += NT) skey[cidx] = order_key(sval[p0 + cidx], 0, p0 + cidx);
+      __syncthreads();
+      const int per = (nchild + tpn - 1) / tpn;
+      for (int base = 0; base < nchild * tpn; base += NT) {   // uniform trip count
+        const int slot = base + tid;
+        const int cidx = slot / tpn, part = slot % tpn;
         int rank = 0;
-        for (int j = 0; j < nchild; ++j) {
-          const int v = p0 + j;
-          const float vv = vkey(sval[v]);
-          if (vv > vu || (vv == vu && v < u)) ++rank;
+        if (cidx < nchild) {
+          const uint64_t ku = skey[cidx];
+          const int j1 = min(nchild, (part + 1) * per);
+          for (int j = part * per; j < j1; ++j) rank += skey[j] < ku;
         }
-        if (rank < nnext) snext[rank] = u;
+        for (int o = 1; o < tpn; o <<= 1) rank += __shfl_xor(rank, o, 64);
+        if (cidx < nchild && part == 0 && rank < nnext) snext[rank] = p0 + cidx;
       }
     } else {
       nnext = plan.nnext;
@@ -181,17 +202,30 @@ __global__ __launch_bounds__(kExpandThreads) void k_tree_expand(TreeDev t, RowsD
     sval[u] = t.pool_value[pb + u];
     sdep[u] = t.pool_depth[pb + u];
     spar[u] = t.pool_parent[pb + u];
+    skey[u] = order_key(sval[u], sdep[u], u);
   }
   __syncthreads();
   int keep = 0;
-  if (u < pn) {
-    if (u == 0 || kind != EAGLE_TREE_DYNAMIC) keep = 1;
-    else {
+  if (kind == EAGLE_TREE_DYNAMIC) {
+    // rank of node x among the non-root nodes: the count of smaller keys.
+    // With pn <= NT / 2 two threads share a node (lanes 2x and 2x+1, each
+    // counting half of the pool); the ranks land in spos.
+    const int half = pn <= NT / 2;
+    const int x = half ? tid >> 1 : tid;
+    if (x < pn && x > 0) {
+      const uint64_t kx = skey[x];
+      const int v0 = half ? 1 + (tid & 1) * ((pn - 1 + 1) / 2) : 1;
+      const int v1 = half ? min(pn, 1 + ((tid & 1) + 1) * ((pn - 1 + 1) / 2)) : pn;
       int rank = 0;
-      for (int v = 1; v < pn; ++v)
-        if (before(sval[v], sdep[v], v, sval[u], sdep[u], u)) ++rank;
-      keep = rank < top_m;
+      for (int v = v0; v < v1; ++v) rank += skey[v] < kx;
+      if (half) rank += __shfl_xor(rank, 1, 64);
+      if (!half || (tid & 1) == 0) spos[x] = rank;
     }
+    __syncthreads();
+    if (u < pn) keep = u == 0 || spos[u] < top_m;
+    __syncthreads();
+  } else if (u < pn) {
+    keep = 1;
   }
   // positions in creation order: exclusive prefix count of the kept nodes
   const uint64_t bal = __builtin_amdgcn_ballot_w64(keep != 0);
