@@ -427,6 +427,7 @@ __device__ __forceinline__ void block_best(float& v, int& i, float* sv, int* si)
 
 constexpr int kMergeLds = 6144;   // candidates staged in LDS (48 KB)
 
+template <int LD>   // sorted entries each lane keeps from the staged candidates
 __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
   // no fused multiply-adds here: with s * l and s * mx each rounded on its own
   // and log(z) >= 0, fl(s l) <= fl(s mx) <= lse for every logit l <= mx, so
@@ -490,19 +491,34 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
   const float lse = a.inv_temp * mx + logf(z);
   if (staged) {
     // One wave takes the top-k from the staged candidates with no barrier per
-    // round: each lane keeps its best two, a round takes the best of the
-    // lanes' next unused entries (exact while no lane has used both; after
-    // that a lane rescans its candidates below the previous winner).
+    // round: each lane keeps its best LD, sorted; a round takes the best of
+    // the lanes' next unused entries (exact while no lane has used all LD;
+    // after that a lane rescans its candidates below the previous winner).
+    // LD = 4 for top_k > 4: a lane holds ~ncand/64 candidates, and with two
+    // of them two of a row's top-10 often share a lane, which sends every
+    // later round to the rescans (one LDS latency per candidate).
     if (tid >= 64) return;
-    float b1 = -INFINITY, b2 = -INFINITY;
-    int i1 = 0x7fffffff, i2 = 0x7fffffff, q1 = -1, q2 = -1;
+    float b[LD];
+    int bi[LD], bq[LD];
+#pragma unroll
+    for (int r = 0; r < LD; ++r) {
+      b[r] = -INFINITY;
+      bi[r] = 0x7fffffff;
+      bq[r] = -1;
+    }
     for (int q = tid; q < ncand; q += 64) {
       const float v = cval[q];
       const int id = cid[q];
-      if (better(v, id, b1, i1)) {
-        b2 = b1; i2 = i1; q2 = q1; b1 = v; i1 = id; q1 = q;
-      } else if (better(v, id, b2, i2)) {
-        b2 = v; i2 = id; q2 = q;
+      if (better(v, id, b[LD - 1], bi[LD - 1])) {
+        // replace the last and let it bubble up (value desc, id asc)
+        b[LD - 1] = v; bi[LD - 1] = id; bq[LD - 1] = q;
+#pragma unroll
+        for (int r = LD - 1; r > 0; --r)
+          if (better(b[r], bi[r], b[r - 1], bi[r - 1])) {
+            const float tv = b[r]; b[r] = b[r - 1]; b[r - 1] = tv;
+            const int ti = bi[r]; bi[r] = bi[r - 1]; bi[r - 1] = ti;
+            const int tq = bq[r]; bq[r] = bq[r - 1]; bq[r - 1] = tq;
+          }
       }
     }
     int used = 0;
@@ -510,11 +526,14 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
     int pid = -1;
     for (int k = 0; k < a.top_k; ++k) {
       float bv, lv;
-      int bi, li, lq;
-      if (!__builtin_amdgcn_ballot_w64(used >= 2)) {
-        lv = used == 0 ? b1 : b2;
-        li = used == 0 ? i1 : i2;
-        lq = used == 0 ? q1 : q2;
+      int bidx, li, lq;
+      if (!__builtin_amdgcn_ballot_w64(used >= LD)) {
+        lv = b[0];
+        li = bi[0];
+        lq = bq[0];
+#pragma unroll
+        for (int r = 1; r < LD; ++r)
+          if (used == r) { lv = b[r]; li = bi[r]; lq = bq[r]; }
       } else {
         lv = -INFINITY;
         li = 0x7fffffff;
@@ -526,30 +545,30 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
         }
       }
       bv = lv;
-      bi = li;
-      wave_best(bv, bi);
-      const bool mine = lq >= 0 && li == bi && lv == bv;
-      if (mine && used < 2 && li == (used == 0 ? i1 : i2)) ++used;
+      bidx = li;
+      wave_best(bv, bidx);
+      const bool mine = lq >= 0 && li == bidx && lv == bv;
+      if (mine && used < LD) ++used;
       if (a.part_logit) {
         // Gumbel keys ranked the candidates; the confidence is the winner's
         // softmax probability, from its logit (the lane holding it writes)
         if (mine) {
           const int t = lq / a.top_k, j = lq - t * a.top_k;
           const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
-          a.topk_id[(int64_t)m * a.top_k + k] = bi < 0 ? 0 : (bi >= a.vocab ? a.vocab - 1 : bi);
+          a.topk_id[(int64_t)m * a.top_k + k] = bidx < 0 ? 0 : (bidx >= a.vocab ? a.vocab - 1 : bidx);
           a.topk_conf[(int64_t)m * a.top_k + k] = expf(a.inv_temp * a.part_logit[i] - lse);
         }
-        if (tid == 0 && bi == 0x7fffffff) {
+        if (tid == 0 && bidx == 0x7fffffff) {
           a.topk_id[(int64_t)m * a.top_k + k] = 0;
           a.topk_conf[(int64_t)m * a.top_k + k] = 0.f;
         }
       } else if (tid == 0) {
         // a NaN row leaves no candidate: keep ids inside the vocabulary
-        a.topk_id[(int64_t)m * a.top_k + k] = bi < 0 ? 0 : (bi >= a.vocab ? a.vocab - 1 : bi);
+        a.topk_id[(int64_t)m * a.top_k + k] = bidx < 0 ? 0 : (bidx >= a.vocab ? a.vocab - 1 : bidx);
         a.topk_conf[(int64_t)m * a.top_k + k] = expf(a.inv_temp * bv - lse);
       }
       pv = bv;
-      pid = bi;
+      pid = bidx;
     }
     if (tid == 0) a.lse[m] = lse;
     return;
@@ -601,7 +620,8 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
 }
 
 void launch_topk_merge(const MergeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk_merge, dim3(a.M), dim3(256), 0, st, a);
+  if (a.top_k > 4) hipLaunchKernelGGL(k_topk_merge<4>, dim3(a.M), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_topk_merge<2>, dim3(a.M), dim3(256), 0, st, a);
 }
 
 }  // namespace eagle
