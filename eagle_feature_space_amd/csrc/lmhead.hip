@@ -305,6 +305,7 @@ void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st)
 // one wave per (row, 2048-column tile), same partial format as the fused
 // epilogue: tile max, tile sum of exp(s (l - max)), tile top-k.
 constexpr int kLogitTile = 2048;
+template <int LD>   // sorted entries each lane keeps for the tile top-k
 __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* logits) {
   // lane owns columns 4 lane + 256 j + 0..3 (16-byte loads; V % 4 == 0 on this path)
   constexpr int PER = kLogitTile / 256;
@@ -351,23 +352,33 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
       }
   }
   // Tile top-k in (value desc, id asc) order.  Every lane first keeps its
-  // own best two entries (one pass over its values); a round then takes the
-  // best of the lanes' next unused entries, which is the tile's next entry as
-  // long as no lane has used both of its own.  A tile where one lane holds
-  // three or more of the top-k (rare) finishes with full passes that take the
-  // best entry strictly below the previous winner.
-  float b1 = -INFINITY, b2 = -INFINITY;
-  int i1 = 0x7fffffff, i2 = 0x7fffffff;
+  // own best LD entries, sorted (one pass over its values); a round then takes
+  // the best of the lanes' next unused entries, which is the tile's next entry
+  // as long as no lane has used all of its own.  A tile where one lane holds
+  // more than LD of the top-k finishes with full passes that take the best
+  // entry strictly below the previous winner.
+  float bb[LD];
+  int bid[LD];
+#pragma unroll
+  for (int r = 0; r < LD; ++r) {
+    bb[r] = -INFINITY;
+    bid[r] = 0x7fffffff;
+  }
 #pragma unroll
   for (int j = 0; j < PER; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float x = v[j][e];
       const int id = c0 + 256 * j + 4 * lane + e;
-      if (better(x, id, b1, i1)) {
-        b2 = b1; i2 = i1; b1 = x; i1 = id;
-      } else if (better(x, id, b2, i2)) {
-        b2 = x; i2 = id;
+      if (better(x, id, bb[LD - 1], bid[LD - 1])) {
+        bb[LD - 1] = x;
+        bid[LD - 1] = id;
+#pragma unroll
+        for (int r = LD - 1; r > 0; --r)
+          if (better(bb[r], bid[r], bb[r - 1], bid[r - 1])) {
+            const float tv = bb[r]; bb[r] = bb[r - 1]; bb[r - 1] = tv;
+            const int ti = bid[r]; bid[r] = bid[r - 1]; bid[r - 1] = ti;
+          }
       }
     }
   int used = 0;
@@ -376,11 +387,14 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
   for (int k = 0; k < a.top_k; ++k) {
     float bv;
     int bi;
-    if (!__builtin_amdgcn_ballot_w64(used >= 2)) {
-      bv = used == 0 ? b1 : b2;
-      bi = used == 0 ? i1 : i2;
+    if (!__builtin_amdgcn_ballot_w64(used >= LD)) {
+      bv = bb[0];
+      bi = bid[0];
+#pragma unroll
+      for (int r = 1; r < LD; ++r)
+        if (used == r) { bv = bb[r]; bi = bid[r]; }
+      const int mine = bi;
       wave_best(bv, bi);
-      const int mine = used == 0 ? i1 : i2;
       if (mine == bi) ++used;
     } else {
       bv = -INFINITY;
@@ -408,7 +422,8 @@ int logits_tiles(int V) { return (V + kLogitTile - 1) / kLogitTile; }
 
 void launch_logits_partials(const LmArgs& a, const float* logits, hipStream_t st) {
   dim3 grid(logits_tiles(a.V), (a.M + 3) / 4);
-  hipLaunchKernelGGL(k_logits_partials, grid, dim3(256), 0, st, a, logits);
+  if (a.top_k > 4) hipLaunchKernelGGL(k_logits_partials<4>, grid, dim3(256), 0, st, a, logits);
+  else hipLaunchKernelGGL(k_logits_partials<2>, grid, dim3(256), 0, st, a, logits);
 }
 
 // ---------------------------------------------------------------- merge
