@@ -510,9 +510,13 @@ void reduce(const eagle_head* h, const float* P, int S, int M, int N, RowSrc s1,
 
 const RowSrc kNone{nullptr, nullptr, 0, 0};
 
-// q|k|v projection of rows already normalised in `hn`, RoPE, scatter
+// q|k|v projection of rows already normalised in `hn`, RoPE, scatter.  With
+// xstats (RMSNorm folded through the projection) `hn` holds y * g and xstats
+// the per-256-column (sum, sum of squares) of y; the projected rows are
+// scaled by rstd before the rotation.
 void qkv_rope(const eagle_head* h, const char* ws, const Ws& w, const void* hn, int M,
-              const int32_t* pos, void* kdst, void* vdst, const int32_t* kv_idx, hipStream_t st) {
+              const int32_t* pos, void* kdst, void* vdst, const int32_t* kv_idx, hipStream_t st,
+              const float* xstats = nullptr) {
   const int d = h->d, qd = h->n_q_heads * h->head_dim, kvd = h->n_kv_heads * h->head_dim;
   GemmShape sh;
   float* P = (float*)(ws + w.P);
@@ -531,6 +535,10 @@ void qkv_rope(const eagle_head* h, const char* ws, const Ws& w, const void* hn, 
   q.k = kdst;
   q.v = vdst;
   q.kv_idx = kv_idx;
+  q.xstats = xstats;
+  q.xnblk = (d + 255) / 256;
+  q.xN = d;
+  q.eps = h->eps;
   ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
   launch_epi_qkv(h->dtype, q, st);
 }
@@ -637,17 +645,19 @@ void ingest(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, cons
             const int32_t* ctx_tokens, hipStream_t st) {
   const int d = h->d, kvd = h->n_kv_heads * h->head_dim;
   const int Tn = (int)ingest_rows(kv);
+  const bool fold = h->norm == EAGLE_NORM_RMS;   // N1 folded through the k|v projection
   float* Pin = (float*)(ws + w.P_in);
   GemmShape sh;
   if (h->mode == EAGLE_MODE_3) {
     gemm(h, rs(lmh, nullptr, 3 * d), kNone, 3 * d, Tn, d, 3 * d, h->w_fuse, nullptr, nullptr, d,
          d, Pin, &sh, st);
     reduce(h, Pin, sh.S, Tn, d, kNone, rs(h->emb, ctx_tokens, d, h->vocab), ws + w.x_in, kNone,
-           ws + w.xn_in, 1, st);
+           fold ? nullptr : ws + w.xn_in, 1, st, fold, fold ? ws + w.xn_in : nullptr);
   } else {
     gemm(h, rs(lmh, nullptr, d), rs(h->emb, ctx_tokens, d, h->vocab), d, Tn, d, 2 * d, h->w_fc,
          nullptr, nullptr, d, d, Pin, &sh, st);
-    reduce(h, Pin, sh.S, Tn, d, kNone, kNone, nullptr, kNone, ws + w.xn_in, 1, st);
+    reduce(h, Pin, sh.S, Tn, d, kNone, kNone, nullptr, kNone, fold ? nullptr : ws + w.xn_in, 1, st,
+           fold, fold ? ws + w.xn_in : nullptr);
   }
   gemm(h, rs(ws + w.xn_in, nullptr, d), kNone, d, Tn, 2 * kvd, d, h->w_k, h->w_v, nullptr, kvd,
        2 * kvd, Pin, &sh, st);
@@ -667,14 +677,20 @@ void ingest(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, cons
   q.B = kv->B;
   q.k = kv->k_ctx;
   q.v = kv->v_ctx;
+  if (fold) {
+    q.xstats = g_stats;
+    q.xnblk = (d + 255) / 256;
+    q.xN = d;
+    q.eps = h->eps;
+  }
   ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
   launch_epi_qkv(h->dtype, q, st);
 }
 
 // One pre-norm decoder layer over io.M rows (io.W per request), from the
-// attention sub-layer on.  Input rows io.x with N1(io.x) in io.xn (row path:
-// io.x * g1 with per-block statistics io.nst / io.nblk, or plain N1 rows when
-// io.nst is null); q|k|v with RoPE at io.pos, K/V rows written to io.kdst /
+// attention sub-layer on.  Input rows io.x with N1(io.x) in io.xn (RMSNorm
+// folded: io.x * g1 with per-block statistics io.nst / io.nblk, io.nblk =
+// ceil(d / 256) on the tiled path; plain N1 rows when io.nst is null); q|k|v with RoPE at io.pos, K/V rows written to io.kdst /
 // io.vdst rows io.kv_idx; attention over the request's context plus the rows
 // in io.mask; output rows to io.out (and to io.scatter rows when given).
 struct LayerIO {
@@ -699,6 +715,12 @@ void layer_body(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, 
   const bool swiglu = h->act == EAGLE_ACT_SWIGLU;
   float* P = (float*)(ws + w.P);
   GemmShape sh;
+  // tiled path: the fused-SwiGLU GEMM (one split, activation in its epilogue)
+  // takes normalised rows; otherwise, for RMSNorm, N2 is folded through the
+  // gate|up projection into the four-column activation epilogue
+  const bool big_act = swiglu && big_swiglu_ok(h->dtype, io.M, ffn, d);
+  const bool fold2 = !rows && !big_act && h->norm == EAGLE_NORM_RMS &&
+                     epi_act4_ok(io.M, ffn, P, ws + w.act);
   // ---- attention sub-layer
   if (rows) {
     RowsArgs r = rows_args(io.M, qd + 2 * kvd, d, h->w_q, h->w_k, h->w_v, qd, qd + kvd);
@@ -717,7 +739,7 @@ void layer_body(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, 
     r.kv_idx = io.kv_idx;
     run_rows(h, EP_ROPE, r, st);
   } else {
-    qkv_rope(h, ws, w, io.xn, io.M, io.pos, io.kdst, io.vdst, io.kv_idx, st);
+    qkv_rope(h, ws, w, io.xn, io.M, io.pos, io.kdst, io.vdst, io.kv_idx, st, io.nst);
   }
   attend(h, kv, ws, w, io.W, io.kdst, io.vdst, io.mask, ws + w.o, st);
   if (rows) {
@@ -732,7 +754,8 @@ void layer_body(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, 
   } else {
     gemm(h, rs(ws + w.o, nullptr, qd), kNone, qd, io.M, d, qd, h->w_o, nullptr, nullptr, d, d, P, &sh,
          st);
-    reduce(h, P, sh.S, io.M, d, rs(io.x, nullptr, d), kNone, ws + w.h1, kNone, ws + w.h1n, 2, st);
+    reduce(h, P, sh.S, io.M, d, rs(io.x, nullptr, d), kNone, ws + w.h1, kNone,
+           fold2 ? nullptr : ws + w.h1n, 2, st, fold2, fold2 ? ws + w.h1n : nullptr);
   }
 
   // ---- MLP sub-layer
@@ -753,7 +776,7 @@ void layer_body(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, 
     r2.scatter = io.scatter;
     run_rows(h, EP_STORE, r2, st);
   } else {
-    if (swiglu && big_swiglu_ok(h->dtype, io.M, ffn, d)) {
+    if (big_act) {
       // one split: the tiled GEMM writes silu(gate) * up itself
       GemmArgs ga;
       ga.xs[0] = rs(ws + w.h1n, nullptr, d);
@@ -787,6 +810,12 @@ void layer_body(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, 
       aa.F = ffn;
       aa.swiglu = swiglu;
       aa.out = ws + w.act;
+      if (fold2) {
+        aa.xstats = g_stats;
+        aa.xnblk = (d + 255) / 256;
+        aa.xN = d;
+        aa.eps = h->eps;
+      }
       ProfScope ps(EAGLE_PROF_OTHER, 0, 0, st);
       launch_epi_act(h->dtype, aa, st);
     }
@@ -937,7 +966,9 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
   // one kernel with its epilogue fused; N1 / N2 are folded through the next
   // projection (operand h * g, result rows scaled by rstd from the statistics).
   const bool rows = rows_gemm_ok(M, d, 32) && h->norm == EAGLE_NORM_RMS;
-  const float* nst = g_stats;          // row statistics of h (row path)
+  // RMSNorm: N1 is folded through the q|k|v projection on both paths
+  const bool fold = h->norm == EAGLE_NORM_RMS;
+  const float* nst = g_stats;          // row statistics of h
   int nblk = (d + 255) / 256;
   if (!e3) {
     if (step == 0 && kv->n_new) ingest(h, kv, ws, w, lmh, ctx_tokens, st);
@@ -958,16 +989,17 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
       nblk = d / 16;
     } else {
       gemm(h, xf, xe, d, M, d, 2 * d, h->w_fc, nullptr, nullptr, d, d, P, &sh, st);
-      reduce(h, P, sh.S, M, d, kNone, kNone, hbuf, kNone, hn, 1, st);
+      reduce(h, P, sh.S, M, d, kNone, kNone, hbuf, kNone, fold ? nullptr : hn, 1, st, fold,
+             fold ? hn : nullptr);
     }
   } else if (step > 0) {
     reduce(h, nullptr, 0, M, d, rs(kv->feat_slot, td.row_pidx, d, (int64_t)B * kSlots), rs(h->emb, td.row_tok, d, h->vocab),
-           hbuf, kNone, rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
+           hbuf, kNone, fold ? nullptr : hn, 1, st, fold, fold ? hn : nullptr);
   } else {
     ingest(h, kv, ws, w, lmh, ctx_tokens, st);
     // root rows = each request's last verified position
     reduce(h, nullptr, 0, M, d, rs(ws + w.x_in, td.row_pidx, d, ingest_rows(kv)), kNone, hbuf, kNone,
-           rows ? nullptr : hn, 1, st, rows, rows ? hn : nullptr);
+           fold ? nullptr : hn, 1, st, fold, fold ? hn : nullptr);
   }
 
   // ---- decoder layer from the attention sub-layer on
@@ -978,7 +1010,7 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
     io.W = W;
     io.x = hbuf;
     io.xn = hn;
-    io.nst = nst;
+    io.nst = fold ? nst : nullptr;
     io.nblk = nblk;
     io.pos = td.row_pos;
     io.kdst = kv->k_slot;
@@ -1101,8 +1133,10 @@ int eagle_tree_attend(const eagle_head* h, const eagle_kv* kv, const eagle_tree*
   int32_t* t_pos = (int32_t*)(ws + w.t_pos);
   uint64_t* t_mask = (uint64_t*)(ws + w.t_mask);
   launch_tree_rows_final(td, g.B, t_tok, t_kv, t_pos, t_mask, st);
-  reduce(h, nullptr, 0, M, d, rs(h->emb, t_tok, d, h->vocab), kNone, nullptr, kNone, ws + w.hn, 1, st);
-  qkv_rope(h, ws, w, ws + w.hn, M, t_pos, ws + w.tk, ws + w.tv, t_kv, st);
+  const bool fold = h->norm == EAGLE_NORM_RMS;   // N1 folded through the q|k|v projection
+  reduce(h, nullptr, 0, M, d, rs(h->emb, t_tok, d, h->vocab), kNone, nullptr, kNone,
+         fold ? nullptr : ws + w.hn, 1, st, fold, fold ? ws + w.hn : nullptr);
+  qkv_rope(h, ws, w, ws + w.hn, M, t_pos, ws + w.tk, ws + w.tv, t_kv, st, fold ? g_stats : nullptr);
   attend(h, kv, ws, w, Wt, ws + w.tk, ws + w.tv, t_mask, out, st);
   return finish(EAGLE_OK);
 }
@@ -1181,18 +1215,23 @@ int eagle_target_verify_logits(const eagle_head* head, const eagle_target* targe
     kl.k_ctx = const_cast<void*>(L.k_ctx);
     kl.v_ctx = const_cast<void*>(L.v_ctx);
     void* x = xin(l);
-    // N1 of the layer input (plain normalised rows; the row path takes them
-    // without a folded scale)
+    // N1 of the layer input (RMSNorm: x * g1 and its row statistics, the
+    // scale folded through the q|k|v projection)
+    const bool fold = head->norm == EAGLE_NORM_RMS;
+    void* n1 = fold ? nullptr : ws + w.hn;
+    void* n1g = fold ? ws + w.hn : nullptr;
     if (l == 0)
-      reduce(&hl, nullptr, 0, M, d, rs(head->emb, t_tok, d, head->vocab), kNone, x, kNone,
-             ws + w.hn, 1, st);
+      reduce(&hl, nullptr, 0, M, d, rs(head->emb, t_tok, d, head->vocab), kNone, x, kNone, n1, 1, st,
+             fold, n1g);
     else
-      reduce(&hl, nullptr, 0, M, d, rs(x, nullptr, d), kNone, nullptr, kNone, ws + w.hn, 1, st);
+      reduce(&hl, nullptr, 0, M, d, rs(x, nullptr, d), kNone, nullptr, kNone, n1, 1, st, fold, n1g);
     LayerIO io;
     io.M = M;
     io.W = Wt;
     io.x = x;
     io.xn = ws + w.hn;
+    io.nst = fold ? g_stats : nullptr;
+    io.nblk = (d + 255) / 256;
     io.pos = t_pos;
     io.kdst = k_tree ? (char*)k_tree + l * tree_kv : (void*)(ws + w.tk);
     io.vdst = v_tree ? (char*)v_tree + l * tree_kv : (void*)(ws + w.tv);

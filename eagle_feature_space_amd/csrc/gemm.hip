@@ -599,7 +599,8 @@ static bool rows4_ok(const ReduceArgs& a) {
 
 void launch_reduce_rows(int dtype, const ReduceArgs& a0, hipStream_t st) {
   ReduceArgs a = a0;
-  if (!a.out_norm && !a.keep_stats) { a.y32 = nullptr; a.stats = nullptr; }
+  if (!a.out_norm && !a.keep_stats) a.stats = nullptr;
+  if (!a.out_norm) a.y32 = nullptr;     // the fp32 rows only feed the norm kernels
   dim3 grid((a.N + 255) / 256, a.M);
   // few rows: one thread per column keeps more workgroups in flight
   if (a.M >= 64 && rows4_ok(a)) {
@@ -623,6 +624,18 @@ void launch_reduce_rows(int dtype, const ReduceArgs& a0, hipStream_t st) {
   }
 }
 
+// rstd of a row for a folded RMSNorm, from its per-block statistics [nblk][2]
+// (sum, sum of squares) in the association k_rows_norm4 uses: lane l sums
+// blocks l, l + 64, ..., the wave reduces by butterfly and lane 0's total is
+// taken.  Every lane of the wave must call it for the same row.
+__device__ __forceinline__ float row_rstd(const float* st, int nblk, int N, float eps) {
+  const int lane = threadIdx.x & 63;
+  float s2 = 0.f;
+  for (int b = lane; b < nblk; b += 64) s2 += st[2 * b + 1];
+  s2 = __shfl(wave_sum(s2), 0, 64);
+  return 1.0f / sqrtf(fmaxf(s2 / N, 0.f) + eps);
+}
+
 // RoPE + scatter of the fused q|k|v projection.  One thread per (row, head,
 // pair i) rotates elements (i, i + hd/2) by pos * theta^(-2i/hd); the angle
 // is formed and reduced in double precision.
@@ -632,8 +645,10 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
   // across the workgroup, the (head, pair) index needs only 32-bit arithmetic
   const int half = a.hd / 2;
   const int heads = a.Hq + 2 * a.Hkv;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= heads * half) return;
+  const int t0 = blockIdx.x * 256 + threadIdx.x;
+  const bool live = t0 < heads * half;   // lanes past the last pair only help form rstd
+  const int t = live ? t0 : 0;
+  if (!a.xstats && !live) return;
   const int i = t % half;
   const int h = t / half;
   const int N = heads * a.hd;
@@ -644,8 +659,10 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
   double inv = 0.0;
   if (!is_v && a.theta > 0.f) inv = exp2(-(2.0 * i / a.hd) * log2((double)a.theta));
   for (int m = blockIdx.y; m < a.M; m += gridDim.y) {
-    float x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S);
-    float x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S);
+    const float rs = a.xstats ? row_rstd(a.xstats + (int64_t)m * a.xnblk * 2, a.xnblk, a.xN, a.eps) : 1.f;
+    if (!live) continue;
+    float x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S) * rs;
+    float x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S) * rs;
     int pos;
     int64_t row = m;
     bool skip = false;
@@ -717,6 +734,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_epi_act4(ActArgs a) {
   const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int m = blockIdx.y;
+  const float rs = a.xstats ? row_rstd(a.xstats + (int64_t)m * a.xnblk * 2, a.xnblk, a.xN, a.eps) : 1.f;
   if (j >= a.F) return;
   const int N = a.swiglu ? 2 * a.F : a.F;
   const int64_t pst = (int64_t)a.M * N;
@@ -726,6 +744,8 @@ __global__ __launch_bounds__(256) void k_epi_act4(ActArgs a) {
     u += *reinterpret_cast<const f32x4*>(row + s * pst + (a.swiglu ? a.F : 0) + j);
     if (a.swiglu) gs += *reinterpret_cast<const f32x4*>(row + s * pst + j);
   }
+  u *= rs;
+  gs *= rs;
   f32x4 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -735,8 +755,12 @@ __global__ __launch_bounds__(256) void k_epi_act4(ActArgs a) {
   st4<T>((T*)a.out + (int64_t)m * a.F + j, y);
 }
 
+bool epi_act4_ok(int M, int F, const void* P, const void* out) {
+  return M >= 64 && F % 4 == 0 && al16(P) && al16(out);
+}
+
 void launch_epi_act(int dtype, const ActArgs& a, hipStream_t st) {
-  if (a.M >= 64 && a.F % 4 == 0 && al16(a.P) && al16(a.out)) {
+  if (epi_act4_ok(a.M, a.F, a.P, a.out)) {
     const dim3 g4((a.F / 4 + 255) / 256, a.M);
     if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_act4<bf16s>, g4, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(k_epi_act4<float>, g4, dim3(256), 0, st, a);

@@ -114,6 +114,12 @@ struct QkvArgs {
   void* k = nullptr;               // rows kv_idx[m] (or as above) of [..][Hkv][hd]
   void* v = nullptr;
   const int32_t* kv_idx = nullptr;
+  // RMSNorm folded through the projection: the A operand was y * g and xstats
+  // [M][xnblk] holds the (sum, sum of squares) of y per 256-column block
+  // (xN columns); the projected rows are scaled by rstd = 1 / sqrt(mean(y^2) + eps)
+  const float* xstats = nullptr;
+  int xnblk = 0, xN = 0;
+  float eps = 0.f;
 };
 void launch_epi_qkv(int dtype, const QkvArgs& a, hipStream_t st);
 
@@ -122,8 +128,15 @@ struct ActArgs {
   int S, M, F;
   int swiglu;
   void* out;            // [M][F]
+  // folded RMSNorm of the A operand, as in QkvArgs (four-column kernel only)
+  const float* xstats = nullptr;
+  int xnblk = 0, xN = 0;
+  float eps = 0.f;
 };
 void launch_epi_act(int dtype, const ActArgs& a, hipStream_t st);
+// whether launch_epi_act takes the four-column kernel, the one that applies a
+// folded RMSNorm's row scale
+bool epi_act4_ok(int M, int F, const void* P, const void* out);
 
 // ---------------------------------------------------------------- attention
 // Rows of request b are m = b*W .. b*W+W-1; query row (m, head h) reads kv
