@@ -304,38 +304,103 @@ void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st)
 // Tile partials from materialised logits (large M, after the MFMA-tiled GEMM):
 // one wave per (row, 2048-column tile), same partial format as the fused
 // epilogue: tile max, tile sum of exp(s (l - max)), tile top-k.
+//
+// The top-k works on 64-bit order keys: the float's bits mapped to an
+// unsigned order (negative values flipped, -0 taken as +0) above 11 bits of
+// 2047 - column within the tile, so one unsigned compare is the (value desc,
+// id asc) order and every key of a tile is distinct.  The wave reductions use
+// DPP row moves (butterfly within each 16-lane row) and four lane reads
+// instead of LDS permutes, which kept each wave waiting on LDS latency for
+// every step of its top-k rounds.
 constexpr int kLogitTile = 2048;
-template <int LD>   // sorted entries each lane keeps for the tile top-k
+
+__device__ __forceinline__ uint64_t tile_key(float x, int col) {
+  const uint32_t u = __float_as_uint(x + 0.0f);      // -0 -> +0
+  const uint32_t ord = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return ((uint64_t)ord << 11) | (uint32_t)(kLogitTile - 1 - col);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 11);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+__device__ __forceinline__ int key_col(uint64_t k) { return kLogitTile - 1 - (int)(k & (kLogitTile - 1)); }
+
+// DPP row butterfly (quad pairs, quad swap, half-row mirror, row mirror):
+// afterwards every lane of a 16-lane row holds the row's reduction
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float rows_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) +
+         (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ uint64_t rows_umax64(uint64_t v) {
+  v = umax64(v, dpp_u64<0xB1>(v));
+  v = umax64(v, dpp_u64<0x4E>(v));
+  v = umax64(v, dpp_u64<0x141>(v));
+  v = umax64(v, dpp_u64<0x140>(v));
+  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)), umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+template <int LD>   // sorted keys each lane keeps for the tile top-k
 __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* logits) {
   // lane owns columns 4 lane + 256 j + 0..3 (16-byte loads; V % 4 == 0 on this path)
   constexpr int PER = kLogitTile / 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int m = blockIdx.y * 4 + wave;
-  if (m >= a.M) return;
+  if (m >= a.M) return;                 // whole waves: every DPP source lane is active
   const int c0 = tile * kLogitTile;
   const float* row = logits + (int64_t)m * a.V + c0;
   float v[PER][4];
   float mx = -INFINITY;
+  const bool full = c0 + kLogitTile <= a.V;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int n = c0 + 256 * j + 4 * lane;
     f32x4 t = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (n < a.V) t = *reinterpret_cast<const f32x4*>(row + 256 * j + 4 * lane);
+    if (full || c0 + 256 * j + 4 * lane < a.V) t = *reinterpret_cast<const f32x4*>(row + 256 * j + 4 * lane);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[j][e] = t[e];
       mx = fmaxf(mx, t[e]);
     }
   }
-  mx = wave_max(mx);
+  mx = rows_max(mx);
   const float sl = a.inv_temp * kLog2e;
   float se = 0.f;
 #pragma unroll
   for (int j = 0; j < PER; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) se += exp2f((v[j][e] - mx) * sl);
-  se = wave_sum(se);
+    for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f((v[j][e] - mx) * sl);
+  se = rows_sum(se);
   const int64_t pi = (int64_t)tile * a.M + m;
   if (lane == 0) {
     a.part_max[pi] = mx;
@@ -351,70 +416,74 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
         v[j][e] = v[j][e] == -INFINITY ? -INFINITY : __fadd_rn(__fmul_rn(a.inv_temp, v[j][e]), gumbel_of(a, rk, id));
       }
   }
-  // Tile top-k in (value desc, id asc) order.  Every lane first keeps its
-  // own best LD entries, sorted (one pass over its values); a round then takes
-  // the best of the lanes' next unused entries, which is the tile's next entry
-  // as long as no lane has used all of its own.  A tile where one lane holds
-  // more than LD of the top-k finishes with full passes that take the best
-  // entry strictly below the previous winner.
-  float bb[LD];
-  int bid[LD];
+  // Tile top-k in key order.  Every lane first keeps its own best LD keys,
+  // sorted (an insertion network over its values); a round takes the wave's
+  // largest head key and the owning lane drops it, which is the tile's next
+  // entry as long as no lane has used all of its own.  Once one has, each
+  // remaining round takes the largest key strictly below the previous winner
+  // over all of the lanes' values.
+  uint64_t kb[LD];
 #pragma unroll
-  for (int r = 0; r < LD; ++r) {
-    bb[r] = -INFINITY;
-    bid[r] = 0x7fffffff;
-  }
+  for (int r = 0; r < LD; ++r) kb[r] = 0;    // below every real key
 #pragma unroll
   for (int j = 0; j < PER; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float x = v[j][e];
-      const int id = c0 + 256 * j + 4 * lane + e;
-      if (better(x, id, bb[LD - 1], bid[LD - 1])) {
-        bb[LD - 1] = x;
-        bid[LD - 1] = id;
+      // one element at a time (empty asm statements pin the order): with
+      // every key formed ahead of the network, or the network run level by
+      // level, 32 keys (64 registers) would be live at once
+      float x = v[j][e];
+      asm volatile("" : "+v"(x));
+      uint64_t t = tile_key(x, 256 * j + 4 * lane + e);
 #pragma unroll
-        for (int r = LD - 1; r > 0; --r)
-          if (better(bb[r], bid[r], bb[r - 1], bid[r - 1])) {
-            const float tv = bb[r]; bb[r] = bb[r - 1]; bb[r - 1] = tv;
-            const int ti = bid[r]; bid[r] = bid[r - 1]; bid[r - 1] = ti;
-          }
+      for (int r = 0; r < LD; ++r) {
+        const bool c = t > kb[r];
+        const uint64_t hi = c ? t : kb[r];
+        t = c ? kb[r] : t;
+        kb[r] = hi;
       }
+#pragma unroll
+      for (int r = 0; r < LD; ++r) asm volatile("" : "+v"(kb[r]));
     }
   int used = 0;
-  float pv = INFINITY;
-  int pid = -1;
+  uint64_t prev = ~0ull;
   for (int k = 0; k < a.top_k; ++k) {
-    float bv;
-    int bi;
+    uint64_t w;
     if (!__builtin_amdgcn_ballot_w64(used >= LD)) {
-      bv = bb[0];
-      bi = bid[0];
+      w = rows_umax64(kb[0]);
+      if (kb[0] == w) {
 #pragma unroll
-      for (int r = 1; r < LD; ++r)
-        if (used == r) { bv = bb[r]; bi = bid[r]; }
-      const int mine = bi;
-      wave_best(bv, bi);
-      if (mine == bi) ++used;
+        for (int r = 0; r + 1 < LD; ++r) kb[r] = kb[r + 1];
+        kb[LD - 1] = 0;
+        ++used;
+      }
     } else {
-      bv = -INFINITY;
-      bi = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
+      // rare: the values are read again (and re-keyed) rather than kept in
+      // registers through the rounds
+      const uint32_t rk = a.gumbel ? row_key_of(a, m) : 0u;
+      uint64_t best = 0;
+#pragma unroll 1
+      for (int j = 0; j < PER; ++j) {
+        f32x4 t = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (c0 + 256 * j + 4 * lane < a.V) t = *reinterpret_cast<const f32x4*>(row + 256 * j + 4 * lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int id = c0 + 256 * j + 4 * lane + e;
-          if (better(pv, pid, v[j][e], id) && better(v[j][e], id, bv, bi)) { bv = v[j][e]; bi = id; }
+          float x = t[e];
+          if (a.gumbel && x != -INFINITY)
+            x = __fadd_rn(__fmul_rn(a.inv_temp, x), gumbel_of(a, rk, c0 + 256 * j + 4 * lane + e));
+          const uint64_t q = tile_key(x, 256 * j + 4 * lane + e);
+          if (q < prev) best = umax64(best, q);
         }
-      wave_best(bv, bi);
+      }
+      w = rows_umax64(best);
     }
     if (lane == 0) {
-      a.part_val[pi * a.top_k + k] = bv;
+      const int bi = c0 + key_col(w);
+      a.part_val[pi * a.top_k + k] = key_value(w);
       a.part_id[pi * a.top_k + k] = bi;
-      if (a.gumbel) a.part_logit[pi * a.top_k + k] = bi >= c0 && bi < a.V ? row[bi - c0] : -INFINITY;
+      if (a.gumbel) a.part_logit[pi * a.top_k + k] = bi < a.V ? row[bi - c0] : -INFINITY;
     }
-    pv = bv;
-    pid = bi;
+    prev = w;
   }
 }
 
