@@ -172,8 +172,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
             tmax = fmaxf(tmax, v);
           }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_x32(max_x16(tmax));
       const float mnew = fmaxf(mrun[rb], tmax);
       const bool empty = mnew == -INFINITY;
       // v_exp_f32 directly (results below the normal range flush to 0)
@@ -188,8 +187,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, int b, int kvh, in
           p[4 * j + i] = e;
           psum += e;
         }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      psum = sum_x32(sum_x16(psum));
       lrun[rb] = lrun[rb] * alpha + psum;
       mrun[rb] = mnew;
       // scaling by 1 is exact: skipped when no row's maximum moved
@@ -459,8 +457,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
             tmax = fmaxf(tmax, v);
           }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_x32(max_x16(tmax));
       const float mnew = fmaxf(mrun, tmax);
       const bool empty = mnew == -INFINITY;
       // v_exp_f32 directly: results below the normal range flush to 0, which
@@ -476,8 +473,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
           p[4 * j + i] = e;
           psum += e;
         }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      psum = sum_x32(sum_x16(psum));
       lrun = lrun * alpha + psum;
       mrun = mnew;
       // scaling by 1 is exact: skipped when no row's maximum moved

@@ -625,14 +625,14 @@ void launch_reduce_rows(int dtype, const ReduceArgs& a0, hipStream_t st) {
 }
 
 // rstd of a row for a folded RMSNorm, from its per-block statistics [nblk][2]
-// (sum, sum of squares) in the association k_rows_norm4 uses: lane l sums
-// blocks l, l + 64, ..., the wave reduces by butterfly and lane 0's total is
-// taken.  Every lane of the wave must call it for the same row.
+// (sum, sum of squares): lane l sums blocks l, l + 64, ..., then a DPP wave
+// reduction (wave-uniform result).  Every lane of the wave must call it for
+// the same row.
 __device__ __forceinline__ float row_rstd(const float* st, int nblk, int N, float eps) {
   const int lane = threadIdx.x & 63;
   float s2 = 0.f;
   for (int b = lane; b < nblk; b += 64) s2 += st[2 * b + 1];
-  s2 = __shfl(wave_sum(s2), 0, 64);
+  s2 = rows_sum(s2);
   return 1.0f / sqrtf(fmaxf(s2 / N, 0.f) + eps);
 }
 
@@ -659,10 +659,17 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
   double inv = 0.0;
   if (!is_v && a.theta > 0.f) inv = exp2(-(2.0 * i / a.hd) * log2((double)a.theta));
   for (int m = blockIdx.y; m < a.M; m += gridDim.y) {
-    const float rs = a.xstats ? row_rstd(a.xstats + (int64_t)m * a.xnblk * 2, a.xnblk, a.xN, a.eps) : 1.f;
+    float x1 = 0.f, x2 = 0.f;
+    if (live) {      // partial loads first: the statistics load overlaps them
+      x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S);
+      x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S);
+    }
+    if (a.xstats) {
+      const float rs = row_rstd(a.xstats + (int64_t)m * a.xnblk * 2, a.xnblk, a.xN, a.eps);
+      x1 *= rs;
+      x2 *= rs;
+    }
     if (!live) continue;
-    float x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S) * rs;
-    float x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S) * rs;
     int pos;
     int64_t row = m;
     bool skip = false;
@@ -734,18 +741,23 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_epi_act4(ActArgs a) {
   const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int m = blockIdx.y;
-  const float rs = a.xstats ? row_rstd(a.xstats + (int64_t)m * a.xnblk * 2, a.xnblk, a.xN, a.eps) : 1.f;
-  if (j >= a.F) return;
+  const bool live = j < a.F;
   const int N = a.swiglu ? 2 * a.F : a.F;
   const int64_t pst = (int64_t)a.M * N;
   const float* row = a.P + (int64_t)m * N;
   f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f}, gs = u;
-  for (int s = 0; s < a.S; ++s) {
-    u += *reinterpret_cast<const f32x4*>(row + s * pst + (a.swiglu ? a.F : 0) + j);
-    if (a.swiglu) gs += *reinterpret_cast<const f32x4*>(row + s * pst + j);
+  if (live) {      // partial loads first: the statistics load overlaps them
+    for (int s = 0; s < a.S; ++s) {
+      u += *reinterpret_cast<const f32x4*>(row + s * pst + (a.swiglu ? a.F : 0) + j);
+      if (a.swiglu) gs += *reinterpret_cast<const f32x4*>(row + s * pst + j);
+    }
   }
-  u *= rs;
-  gs *= rs;
+  if (a.xstats) {  // every lane takes part in the row's reduction
+    const float rs = row_rstd(a.xstats + (int64_t)m * a.xnblk * 2, a.xnblk, a.xN, a.eps);
+    u *= rs;
+    gs *= rs;
+  }
+  if (!live) return;
   f32x4 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

@@ -219,10 +219,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_rows(RowsArgs a) {
     if (a.stats) {
       float s1 = live ? (y[0] + y[1]) + (y[2] + y[3]) : 0.f;
       float s2 = live ? (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]) : 0.f;
-      s1 += __shfl_xor(s1, 16, 64);
-      s2 += __shfl_xor(s2, 16, 64);
-      s1 += __shfl_xor(s1, 32, 64);
-      s2 += __shfl_xor(s2, 32, 64);
+      s1 = sum_x32(sum_x16(s1));
+      s2 = sum_x32(sum_x16(s2));
       if (g == 0 && live) {
         float* st = a.stats + ((int64_t)mrow * gridDim.x + blockIdx.x) * 2;
         st[0] = s1;

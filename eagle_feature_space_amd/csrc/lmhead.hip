@@ -306,7 +306,7 @@ void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st)
 // epilogue: tile max, tile sum of exp(s (l - max)), tile top-k.
 //
 // The top-k works on 64-bit order keys: the float's bits mapped to an
-// unsigned order (negative values flipped, -0 taken as +0) above 11 bits of
+// unsigned order (negative values flipped, -0 taken as +0, NaN lowest) above 11 bits of
 // 2047 - column within the tile, so one unsigned compare is the (value desc,
 // id asc) order and every key of a tile is distinct.  The wave reductions use
 // DPP row moves (butterfly within each 16-lane row) and four lane reads
@@ -314,61 +314,20 @@ void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st)
 // every step of its top-k rounds.
 constexpr int kLogitTile = 2048;
 
+// float -> unsigned with the same order (-0 taken as +0, NaN below everything)
+__device__ __forceinline__ uint32_t float_order(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  const uint32_t o = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return x != x ? 0u : o;
+}
+__device__ __forceinline__ float order_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
 __device__ __forceinline__ uint64_t tile_key(float x, int col) {
-  const uint32_t u = __float_as_uint(x + 0.0f);      // -0 -> +0
-  const uint32_t ord = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-  return ((uint64_t)ord << 11) | (uint32_t)(kLogitTile - 1 - col);
+  return ((uint64_t)float_order(x) << 11) | (uint32_t)(kLogitTile - 1 - col);
 }
-__device__ __forceinline__ float key_value(uint64_t k) {
-  const uint32_t ord = (uint32_t)(k >> 11);
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
-}
+__device__ __forceinline__ float key_value(uint64_t k) { return order_float((uint32_t)(k >> 11)); }
 __device__ __forceinline__ int key_col(uint64_t k) { return kLogitTile - 1 - (int)(k & (kLogitTile - 1)); }
-
-// DPP row butterfly (quad pairs, quad swap, half-row mirror, row mirror):
-// afterwards every lane of a 16-lane row holds the row's reduction
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ float rows_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
-               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
-}
-__device__ __forceinline__ float rows_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
-  return (readlane_f(v, 0) + readlane_f(v, 16)) +
-         (readlane_f(v, 32) + readlane_f(v, 48));
-}
-__device__ __forceinline__ uint64_t rows_umax64(uint64_t v) {
-  v = umax64(v, dpp_u64<0xB1>(v));
-  v = umax64(v, dpp_u64<0x4E>(v));
-  v = umax64(v, dpp_u64<0x141>(v));
-  v = umax64(v, dpp_u64<0x140>(v));
-  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)), umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
-}
 
 template <int LD>   // sorted keys each lane keeps for the tile top-k
 __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* logits) {
@@ -628,10 +587,12 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
           if (better(pv, pid, v, id) && better(v, id, lv, li)) { lv = v; li = id; lq = q; }
         }
       }
-      bv = lv;
-      bidx = li;
-      wave_best(bv, bidx);
-      const bool mine = lq >= 0 && li == bidx && lv == bv;
+      // (value desc, id asc) as one 64-bit key, reduced with DPP row moves
+      const uint64_t lk = ((uint64_t)float_order(lv) << 32) | (0xffffffffu - (uint32_t)li);
+      const uint64_t wk = rows_umax64(lk);
+      bv = order_float((uint32_t)(wk >> 32));
+      bidx = (int)(0xffffffffu - (uint32_t)wk);
+      const bool mine = lq >= 0 && lk == wk;
       if (mine && used < LD) ++used;
       if (a.part_logit) {
         // Gumbel keys ranked the candidates; the confidence is the winner's
