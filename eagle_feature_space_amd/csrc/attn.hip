@@ -20,6 +20,9 @@
 namespace eagle {
 
 constexpr int kAttnWaves = 2;   // kv heads per workgroup
+// tiles in flight ahead of the one computed by k_attn_dma: one (two 64 KB
+// workgroups per CU) measured faster than two (96 KB, one workgroup per CU)
+constexpr int kAttnPF = 1;
 
 // LDS byte offset of V^T[d][key] (64 keys per row of `rowb` bytes).  bf16 rows
 // hold 8 chunks of 8 keys and chunk j of row d sits at position
@@ -274,7 +277,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
 }
 
 // Many query rows per (request, kv head) -- the wide EAGLE-2 trees, the
-// verify-side tree attention: a workgroup of NW waves serves 16 * NW query
+// verify-side tree attention -- for fp32 and head dim 64 (bf16 at head dim
+// 128 takes k_attn_dma below): a workgroup of NW waves serves 16 * NW query
 // rows (16 per wave) of one (request, kv head, key split).  Its threads load
 // each 64-key K / V tile once, cooperatively, into LDS (K as [key][d], V
 // transposed as [d][key] by 4-key quads), double-buffered: the next tile's
@@ -539,6 +543,220 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wg(AttnArgs a) {
   for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * g) = o[db];
 }
 
+// bf16, head dim 128: k_attn_wg's arithmetic with the K and V tiles moved by
+// direct-to-LDS loads (global_load_lds_dwordx4, no staging registers and no
+// repacking VALU work) into a ring of PF + 1 tile slots, PF tiles ahead.
+// Both tiles keep the global [key][d] layout, 256-byte rows of 16 chunks,
+// chunk ch of tile key r at slot ch ^ (((r >> 4) & 3) | ((r & 3) << 2)) (the
+// K fragment swizzle of k_attn_wg; a direct-to-LDS load writes 64 lanes x
+// 16 B contiguously, so each lane picks the global chunk of its slot).  The
+// V^T operand comes from ds_read_b64_tr_b16: in each 16-lane group, lane j
+// receives element (j & 3) of the 8 bytes addressed by lane 4e + (j >> 2),
+// e = 0..3, so lane 4e + p addresses key 4e (+ 8v + 4h + 16g) at d = 4p and
+// lane (d = c, g) gets V[key][d] for four consecutive keys.
+constexpr int kDmaTile = 64 * 256;                    // K or V tile bytes (bf16, hd 128)
+
+__device__ __forceinline__ int kv_slot(int r) { return ((r >> 4) & 3) | ((r & 3) << 2); }
+
+__device__ __forceinline__ uint2 ld_tr16(const char* p) {
+  const short4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(__attribute__((address_space(3))) char*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+template <int NW, int PF>
+__global__ __launch_bounds__(64 * NW) void k_attn_dma(AttnArgs a) {
+  constexpr int HD = 128, DSTEPS = 4, DB = 8, NV = 2;
+  constexpr int S = PF + 1;                          // ring slots
+  constexpr int SLOT = 2 * kDmaTile;                 // K tile, then V tile
+  constexpr int L = 32 / NW;                         // 1 KB loads per wave per tile
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int kvh = blockIdx.x % a.Hkv;
+  const int rg = blockIdx.x / a.Hkv;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int R = a.W * G;
+  const int M = a.B * a.W;
+
+  const int qrow = rg * 16 * NW + w * 16 + c;
+  const bool qok = qrow < R;
+  const bool wave_live = rg * 16 * NW + w * 16 < R;
+  const int rl = qok ? qrow / G : 0, gi = qok ? qrow % G : 0;
+  const int qm = qok ? b * a.W + rl : -1;
+  const int qh = kvh * G + gi;
+  const uint64_t msk = qok ? a.mask[b * a.W + rl] : 0ull;
+  u32x4 qf[DSTEPS];
+  {
+    const bf16s* qp = (const bf16s*)a.q + ((int64_t)(b * a.W + rl) * a.Hq + qh) * HD;
+#pragma unroll
+    for (int u = 0; u < DSTEPS; ++u) qf[u] = qok ? ld16(qp + u * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const bool extra = split == a.nsplit;
+  int kbeg, kend;
+  const bf16s *kb, *vb;
+  const int64_t kstride = (int64_t)a.Hkv * HD;
+  if (!extra) {
+    const int nb = a.n[b];
+    kbeg = split * a.split_len;
+    kend = min(kbeg + a.split_len, nb);
+    kb = (const bf16s*)a.k_ctx + (int64_t)a.cu_n[b] * kstride + kvh * HD;
+    vb = (const bf16s*)a.v_ctx + (int64_t)a.cu_n[b] * kstride + kvh * HD;
+  } else {
+    uint64_t any = 0;
+    for (int r = 0; r < a.W; ++r) any |= a.mask[b * a.W + r];
+    kbeg = 0;
+    kend = any ? 64 - __builtin_clzll(any) : 0;
+    kb = (const bf16s*)a.k_ex + (int64_t)b * kSlots * kstride + kvh * HD;
+    vb = (const bf16s*)a.v_ex + (int64_t)b * kSlots * kstride + kvh * HD;
+  }
+  const int ntiles = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+
+  // tile t: wave w issues loads w L .. w L + L - 1 of the 32 (16 for K, 16
+  // for V, four keys each); keys past kend re-read key kend - 1 (masked)
+  auto issue = [&](int t) {
+    const int t0 = kbeg + t * 64;
+    char* dst = lds + (t % S) * SLOT;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int q = w * L + i;
+      const int kr = 4 * (q & 15) + (lane >> 4);        // key within the tile
+      const int key = min(t0 + kr, kend - 1);
+      const int ch = (lane & 15) ^ kv_slot(kr);
+      const bf16s* src = (q < 16 ? kb : vb) + (int64_t)key * kstride + ch * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (q >> 4) * kDmaTile + (q & 15) * 1024), 16, 0, 0);
+    }
+  };
+
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // lane-constant parts of the fragment addresses
+  const int kslot = (c >> 2) | ((c & 3) << 2);       // kv_slot of this lane's K rows
+  const int te = (lane >> 2) & 3, tp = lane & 3;     // transposing-read roles
+  const int vslot = g | (te << 2);                   // kv_slot of this lane's V rows
+
+  auto compute = [&](const char* cur, int t0) {
+    if (!wave_live) return;
+    f32x4 sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kl = (c >> 2) * 16 + j * 4 + (c & 3);
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < DSTEPS; ++u)
+        acc = DT<bf16s>::mma(ld16(cur + kl * 256 + ((4 * u + g) ^ kslot) * 16), qf[u], acc);
+      sc[j] = acc;
+    }
+    const bool full = !extra && t0 + 64 <= kend;     // wave-uniform
+    float tmax = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[j][i] *= a.scale_log2;
+          tmax = fmaxf(tmax, sc[j][i]);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = t0 + g * 16 + j * 4 + i;
+          bool valid = key < kend;
+          if (extra) valid = valid && ((msk >> key) & 1ull);
+          const float v = valid ? sc[j][i] * a.scale_log2 : -INFINITY;
+          sc[j][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
+    tmax = max_x32(max_x16(tmax));
+    const float mnew = fmaxf(mrun, tmax);
+    const bool empty = mnew == -INFINITY;
+    const float alpha = empty ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+    float p[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = empty ? 0.f : __builtin_amdgcn_exp2f(sc[j][i] - mnew);
+        p[4 * j + i] = e;
+        psum += e;
+      }
+    psum = sum_x32(sum_x16(psum));
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    const char* vt = cur + kDmaTile;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const u32x4 pf = pack_p<bf16s>(p + v * 8);
+      const char* vrow = vt + (16 * g + 8 * v + te) * 256 + 8 * (tp & 1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int off = 16 * ((2 * db + (tp >> 1)) ^ vslot);
+        const uint2 lo = ld_tr16(vrow + off);             // keys 16g + 8v + 0..3
+        const uint2 hi = ld_tr16(vrow + 4 * 256 + off);   // keys 16g + 8v + 4..7
+        o[db] = DT<bf16s>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, o[db]);
+      }
+    }
+  };
+
+  // the query fragments and the mask land before the loop, so the loads in
+  // it are the only ones outstanding and vmcnt counts tiles
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  const int pre = min(PF, ntiles);
+  for (int t = 0; t < pre; ++t) issue(t);
+  for (int it = 0; it < ntiles; ++it) {
+    // tile it landed (the younger tiles may stay in flight), then every wave
+    // is past its reads of tile it - 1, whose slot the next issue refills
+    if (it + PF - 1 < ntiles) __builtin_amdgcn_s_waitcnt(vm_wait((PF - 1) * L));
+    else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    // LDS-scoped fences around the barrier: a workgroup fence over all
+    // memory would wait for the tiles still in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (it + PF < ntiles) issue(it + PF);
+    compute(lds + (it % S) * SLOT, kbeg + it * 64);
+  }
+
+  if (qm < 0) return;
+  const int64_t idx = ((int64_t)split * M + qm) * a.Hq + qh;
+  if (g == 0) {
+    a.part_ml[2 * idx] = mrun;
+    a.part_ml[2 * idx + 1] = lrun;
+  }
+  float* po = a.part_o + idx * HD;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * g) = o[db];
+}
+
+template <int NW, int PF>
+static void launch_dma(const AttnArgs& a, hipStream_t st) {
+  constexpr int LDS = (PF + 1) * 2 * kDmaTile;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_dma<NW, PF>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    attr = true;
+  }
+  const int R = a.W * (a.Hq / a.Hkv);
+  const int rowgroups = (R + 16 * NW - 1) / (16 * NW);
+  dim3 grid(a.Hkv * rowgroups, a.nsplit + 1, a.B);
+  hipLaunchKernelGGL((k_attn_dma<NW, PF>), grid, dim3(64 * NW), LDS, st, a);
+}
+
 template <typename T, int HD, int NW>
 static void launch_wg(const AttnArgs& a, hipStream_t st) {
   constexpr bool KSW = sizeof(T) == 2 && HD == 128;
@@ -568,7 +786,10 @@ void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
   if (R > 16) {
     // more than one 16-row block per (request, kv head): workgroup kernel
     if (dtype == EAGLE_BF16) {
-      if (a.hd == 128) launch_wide<bf16s, 128>(a, R, st);
+      if (a.hd == 128) {   // direct-to-LDS tiles
+        if (R <= 32) launch_dma<2, kAttnPF>(a, st);
+        else launch_dma<4, kAttnPF>(a, st);
+      }
       else launch_wide<bf16s, 64>(a, R, st);
     } else {
       if (a.hd == 128) launch_wide<float, 128>(a, R, st);

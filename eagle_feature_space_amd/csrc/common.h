@@ -105,6 +105,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// s_waitcnt immediate for vmcnt(n) alone (vmcnt bits [3:0] and [15:14])
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// LDS pointers for the direct-to-LDS loads and the transposing LDS reads
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
 // Wave reductions without LDS permutes: a DPP butterfly inside each 16-lane
 // row (quad pairs, quad swap, half-row mirror, row mirror) leaves every lane
 // of a row with the row's result, then four lane reads combine the rows.  The

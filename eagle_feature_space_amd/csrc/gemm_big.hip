@@ -200,12 +200,9 @@ struct Dma {
   static constexpr int LDS = STAGES * STAGE;
 };
 
-// s_waitcnt immediate for vmcnt(n) alone (vmcnt bits [3:0] and [15:14])
-constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ int dma_off(int r, int j) { return r * kDRow + 16 * (j ^ ((r >> 1) & 2)); }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <int EPI, int BN, int BM>   // EPI 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
 __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, int S) {
