@@ -384,9 +384,9 @@ static bool plan_dma(int M, int N, int K, GemmShape* s) {
   const int tiles = nt * mt;
   if (BM == 256 && tiles < 128) return false;
   const int kst = K / kDK;                  // even: K is a multiple of 64
-  // one workgroup per CU: 128-row tiles split until the grid is one wave of
+  // one workgroup per CU: tiles split until the grid is one wave of
   // at most 256 workgroups (a partial second wave would double the time)
-  int S = BM == 128 ? 256 / tiles : (256 + tiles - 1) / tiles;
+  int S = 256 / tiles;
   if (S > kst / 8) S = kst / 8 > 0 ? kst / 8 : 1;
   if (S < 1) S = 1;
   int sps = (kst + S - 1) / S;
@@ -423,7 +423,9 @@ GemmShape plan_gemm_big(int M, int N, int K) {
   s.mtiles = (M + BM - 1) / BM;
   const int tiles = s.ntiles * s.mtiles;
   const int kst = K / kBK;
-  int S = (256 + tiles - 1) / tiles;      // one workgroup per CU (LDS-bound): fewer fp32 partials
+  // one workgroup per CU (LDS-bound): at most 256 workgroups, since a
+  // partial second pass costs a whole pass (80 tiles: 3 splits, not 4)
+  int S = 256 / tiles;
   if (S > kst / 4) S = kst / 4 > 0 ? kst / 4 : 1;   // keep >= 256 K per split
   if (S < 1) S = 1;
   const int sps = (kst + S - 1) / S;
