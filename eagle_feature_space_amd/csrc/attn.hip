@@ -883,7 +883,79 @@ __global__ __launch_bounds__(128) void k_attn_combine(CombineArgs a) {
   }
 }
 
+// One wave per (row, head) for up to 64 splits and head dims 64 / 128 (E =
+// hd / 64 elements per lane), four per workgroup: a quarter of the
+// workgroups of the kernel above and no barrier.  Lane s holds split s's
+// (max, sum); the first PB splits' outputs (PB = 8, 16 or 32, sized to the
+// split count) are loaded before the reductions so the row pays about one
+// memory latency; O is folded in split order with the weights read from
+// their lanes.
+template <typename T, int E, int PB>
+__global__ __launch_bounds__(256) void k_attn_combine_w(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.M * a.Hq) return;                    // whole waves
+  const int np = a.nparts;
+  const int64_t stride = (int64_t)a.M * a.Hq;
+  const int64_t base = pair;                         // m * Hq + h
+  const float* po = a.part_o + base * (int64_t)a.hd + lane * E;
+  const int64_t pstride = stride * a.hd;
+  float ov[PB][E];
+#pragma unroll
+  for (int q = 0; q < PB; ++q)
+#pragma unroll
+    for (int e = 0; e < E; ++e) ov[q][e] = po[(int64_t)min(q, np - 1) * pstride + e];
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < np) {
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * (lane * stride + base));
+    ms = ml.x;
+    ls = ml.y;
+  }
+  const float mx = rows_max(ms);
+  const float f = (mx == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+  const float L = rows_sum(f * ls);
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  float O[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) O[e] = 0.f;
+  for (int s0 = 0; s0 < np; s0 += PB) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e) ov[q][e] = po[(int64_t)min(s0 + q, np - 1) * pstride + e];
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      if (s0 + q >= np) break;
+      const float wq = readlane_f(f, s0 + q);
+#pragma unroll
+      for (int e = 0; e < E; ++e) O[e] += wq * ov[q][e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) DT<T>::st((T*)a.out + base * a.hd + lane * E + e, O[e] * inv);
+}
+
+template <typename T, int E>
+static void launch_combine_w(const CombineArgs& a, hipStream_t st) {
+  const dim3 g4((unsigned)(((int64_t)a.M * a.Hq + 3) / 4));
+  if (a.nparts <= 8) hipLaunchKernelGGL((k_attn_combine_w<T, E, 8>), g4, dim3(256), 0, st, a);
+  else if (a.nparts <= 16) hipLaunchKernelGGL((k_attn_combine_w<T, E, 16>), g4, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_combine_w<T, E, 32>), g4, dim3(256), 0, st, a);
+}
+
 void launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t st) {
+  if (a.nparts <= 64 && (a.hd == 64 || a.hd == 128)) {
+    if (dtype == EAGLE_BF16) {
+      if (a.hd == 128) launch_combine_w<bf16s, 2>(a, st);
+      else launch_combine_w<bf16s, 1>(a, st);
+    } else {
+      if (a.hd == 128) launch_combine_w<float, 2>(a, st);
+      else launch_combine_w<float, 1>(a, st);
+    }
+    return;
+  }
   dim3 grid(a.Hq, a.M);
   if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_attn_combine<bf16s>, grid, dim3(128), 0, st, a);
   else hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(128), 0, st, a);
