@@ -146,9 +146,14 @@ def extra_workload(name, steps, warmup):
     print(f"[bench] extra {name}: generating inputs", file=sys.stderr, flush=True)
     gr = GpuRound(cfg, synth.head_weights(cfg.head, cfg.seed_w), synth.round_inputs(cfg))
     tgt = to_dev(synth.target_logits(cfg), gr.dev)
-    for _ in range(warmup):
+    # warm-up of at least half a second: after the seconds of host-side input
+    # generation a few rounds leave the GPU below its working clocks
+    tw = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - tw < 0.5:
         gr.run(target=tgt, attend=cfg.tree_attend)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n_warm += 1
     t0 = time.perf_counter()
     for _ in range(steps):
         gr.run(target=tgt, attend=cfg.tree_attend)
@@ -165,13 +170,46 @@ def extra_workload(name, steps, warmup):
     ms = el * 1e3 / steps
     nodes = cfg.B * cfg.n_final
     res = {"value": round(nodes * steps / el, 2), "unit": "nodes/s", "ms_per_step": round(ms, 4),
-           "steps": steps, "warmup": warmup, "nodes_per_round": nodes,
+           "steps": steps, "warmup": n_warm, "nodes_per_round": nodes,
            "round_roofline_us": fb["round_roofline_us"],
            "round_roofline_frac": round(fb["round_roofline_us"] / (ms * 1e3), 4),
            "families_us_per_round": {k: v["us_per_round"] for k, v in fb.items() if isinstance(v, dict)}}
     del gr, tgt
     torch.cuda.empty_cache()
     return res
+
+
+LIB_GEMM_SHAPES = (("lm_head_512", 512, 128256, 8192), ("gate_up_512", 512, 57344, 8192),
+                   ("down_512", 512, 8192, 28672), ("qkv_512", 512, 10240, 8192),
+                   ("lm_head_80", 80, 128256, 4096), ("gate_up_80", 80, 28672, 4096))
+
+
+def lib_gemm():
+    """Reference only: the vendor GEMM (torch.nn.functional.linear, bf16 in and
+    out, hipBLASLt on ROCm) at the head's tiled-GEMM shapes, cold weights
+    (rotating copies beyond the 256 MB cache), median of 16 timed launches.
+    One JSON line per shape."""
+    import torch
+    for name, M, N, K in LIB_GEMM_SHAPES:
+        x = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        ws = [torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+              for _ in range(2 if N * K * 2 > (1 << 30) else 4)]
+        ts = []
+        for it in range(20):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.nn.functional.linear(x, ws[it % len(ws)])
+            e1.record()
+            e1.synchronize()
+            if it >= 4:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        us = sorted(ts)[len(ts) // 2]
+        print(json.dumps({"gemm": name, "M": M, "N": N, "K": K, "us": round(us, 1),
+                          "tflops": round(2 * M * N * K / us / 1e6, 1),
+                          "weight_tbps": round(N * K * 2 / us / 1e6, 3)}), flush=True)
+        del ws, x
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -189,6 +227,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra workloads (8B EAGLE-2 tree, EAGLE-3 chain) the default "
                          "run reports beside the headline")
+    ap.add_argument("--lib-gemm", action="store_true",
+                    help="instead of the benchmark: time the vendor GEMM (torch / hipBLASLt) at the "
+                         "tiled-GEMM shapes, for reference")
     ap.add_argument("--copy-probe", action="store_true",
                     help="one 1 GiB device-to-device copy before warm-up (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -202,6 +243,13 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.lib_gemm:
+        if not torch.cuda.is_available():
+            print("--lib-gemm needs a GPU", file=sys.stderr)
+            sys.exit(3)
+        lib_gemm()
+        return
 
     from eagle_feature_space_amd import binding as E
     from eagle_feature_space_amd import configs as C
@@ -330,7 +378,7 @@ def main():
     if args.workload == "c1_8b_static" and not args.no_extras:
         del gr, tgt
         torch.cuda.empty_cache()
-        extras = {w: extra_workload(w, 10, 3) for w in ("c2_8b_dynamic", "c3_8b_eagle3")}
+        extras = {w: extra_workload(w, 20, 3) for w in ("c2_8b_dynamic", "c3_8b_eagle3")}
 
     cpu = None
     if not args.no_cpu and cfg.target_layers > 0:
