@@ -372,6 +372,183 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, in
   }
 }
 
+// 256 x 128 tiles with 64 of K per stage: the tile, wave grid and MFMA order
+// of k_gemm_dma<*, 256, 128>, but each LDS row holds 128 bytes and one
+// direct-to-LDS load covers 8 rows x 128 B, half the memory requests per
+// weight byte of 16 rows x 64 B (a load-only probe of the two shapes: 3-10%
+// apart at 80 rows).  Three stages of 48 KB, two in flight.  Fragment reads
+// and MFMAs keep the 32-K sub-stage rhythm of k_gemm_dma (reads half a
+// sub-stage ahead, a barrier in the middle of each); DMA stage S holds
+// sub-stages 2S and 2S+1.  After the barrier of sub-stage 2S, stage S+2 is
+// issued into the slot of stage S-1, which every wave has finished (all are
+// past sub-stage 2S-1); before the barrier of sub-stage 2S+1 each wave waits
+// for its loads of stage S+1.  16-byte chunk j of a 128-byte row r sits at
+// j ^ ((r >> 1) & 7) (the swizzle k_gemm_big uses for its 128-byte rows).
+constexpr int kWRow = 128;
+__device__ __forceinline__ int dmaw_off(int r, int j) { return r * kWRow + 16 * (j ^ ((r >> 1) & 7)); }
+constexpr int kDmawStage = (256 + 128) * kWRow;             // 48 KB
+constexpr int kDmawLds = 3 * kDmawStage;                    // 144 KB
+
+template <int EPI>   // EPI 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
+__global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, int S) {
+  constexpr int BN = 256, BM = 128, WM = 4, WMB = 2;
+  constexpr int L = (BN + BM) / 8 / 8;                      // 6 loads of 8 rows per wave per stage
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int wn = wave / WM, wm = wave % WM;
+  const int total = nt * mt * S;
+  const int per = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int mtile = lin % mt;
+  const int ntile = (lin / mt) % nt;
+  const int z = lin / (mt * nt);
+  const int n0 = ntile * BN, m0 = mtile * BM;
+  const int k_begin = z * a.kps, k_end = min(a.K, k_begin + a.kps);
+  const int nsub = (k_end - k_begin) / 32;                  // even: K per split is a multiple of 64
+  const int nst = nsub / 2;
+
+  // load i of wave w: rows 8 (w L + i) .. +7; lane l takes row + (l >> 3),
+  // LDS slot l & 7, i.e. global chunk (l & 7) ^ ((row >> 1) & 7)
+  const char* src[L];
+  const char* src1[L];
+  bool isx[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int r = (wave * L + i) * 8 + (lane >> 3);
+    const int j = (lane & 7) ^ ((r >> 1) & 7);
+    isx[i] = r >= BN;
+    if (!isx[i]) {
+      int n;
+      if (EPI == 1) {   // 16-row blocks alternate gate (even) and up (odd)
+        const int b = r >> 4;
+        const int q = ntile * (BN / 2) + (b >> 1) * 16 + (r & 15);
+        n = (b & 1) ? a.pair_F + min(q, a.pair_F - 1) : min(q, a.pair_F - 1);
+      } else {
+        n = min(n0 + r, a.N - 1);
+      }
+      const bf16s* base;
+      int off;
+      if (n < a.nseg1) { base = (const bf16s*)a.w[0]; off = 0; }
+      else if (n < a.nseg2) { base = (const bf16s*)a.w[1]; off = a.nseg1; }
+      else { base = (const bf16s*)a.w[2]; off = a.nseg2; }
+      src[i] = (const char*)(base + (int64_t)(n - off) * a.K + j * 8);
+      src1[i] = src[i];
+    } else {
+      const int m = min(m0 + r - BN, a.M - 1);
+      src[i] = (const char*)(row_ptr<bf16s>(a.xs[0], m) + j * 8);
+      src1[i] = a.xs[1].base ? (const char*)(row_ptr<bf16s>(a.xs[1], m) + j * 8) : src[i];
+    }
+  }
+  // stage sd (clamped to the last one, so every stage issues L loads and the
+  // vmcnt waits stay exact) into ring slot sd % 3
+  auto issue = [&](int sd) {
+    const int sc = min(sd, nst - 1);
+    const int k0 = k_begin + sc * 64;
+    char* dst = lds + (sd % 3) * kDmawStage + wave * L * 1024;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool hi = isx[i] && k0 >= a.ksplit_x;          // a stage never straddles the split
+      const char* p = hi ? src1[i] + (int64_t)(k0 - a.ksplit_x) * 2 : src[i] + (int64_t)k0 * 2;
+      __builtin_amdgcn_global_load_lds((const void*)p, (lds_void*)(dst + i * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[8][WMB];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nst > 0) {
+    const int wr0 = wn * 128, xr0 = BN + wm * 16 * WMB;
+    issue(0);
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(vm_wait(L));                 // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 wf[8], xa[WMB], xb[WMB];
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) xa[mb] = ld16(lds + dmaw_off(xr0 + mb * 16 + c, g));
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) wf[nb] = ld16(lds + dmaw_off(wr0 + nb * 16 + c, g));
+    // sub-stage T_ (MFMAs on XC), reading sub-stage T_ + 1's fragments into
+    // XN / wf; EVEN_: T_ = 2S issues stage S + 2, else T_ = 2S + 1 waits for
+    // stage S + 1
+#define DMAW_SUB(T_, XC, XN, EVEN_)                                                           \
+    {                                                                                       \
+      _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
+      _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
+        acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+      if (!(EVEN_)) __builtin_amdgcn_s_waitcnt(vm_wait(L));   /* stage S + 1 landed */      \
+      __builtin_amdgcn_s_barrier();                                                         \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+      if (EVEN_) issue(((T_) >> 1) + 2);                                                    \
+      const int tn_ = (T_) + 1;                                                             \
+      const char* st_ = lds + ((tn_ >> 1) % 3) * kDmawStage;                                \
+      const int kc_ = (tn_ & 1) * 4 + g;                                                    \
+      _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
+        wf[nb] = ld16(st_ + dmaw_off(wr0 + nb * 16 + c, kc_));                              \
+      _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
+        XN[mb] = ld16(st_ + dmaw_off(xr0 + mb * 16 + c, kc_));                              \
+      _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
+      _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
+        acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
+      _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
+        wf[nb] = ld16(st_ + dmaw_off(wr0 + nb * 16 + c, kc_));                              \
+      if (EVEN_) __builtin_amdgcn_sched_group_barrier(0x020, L, 0);        /* loads */      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 + WMB, 0);  /* reads W 0-3, X */        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * WMB, 0);  /* MFMAs n-blocks 4-7 */    \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        /* reads W 4-7 */           \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+    }
+    for (int t = 0; t < nsub; t += 2) {
+      DMAW_SUB(t, xa, xb, true)
+      DMAW_SUB(t + 1, xb, xa, false)
+    }
+#undef DMAW_SUB
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load in flight when the wave ends
+
+  if (EPI == 1) {
+#pragma unroll
+    for (int nb = 0; nb < 8; nb += 2) {
+      const int j = ntile * (BN / 2) + ((wn * 8 + nb) >> 1) * 16 + 4 * g;
+      if (j >= a.pair_F) continue;
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb) {
+        const int m = m0 + wm * 16 * WMB + mb * 16 + c;
+        if (m >= a.M) continue;
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gs = acc[nb][mb][e], u = acc[nb + 1][mb][e];
+          y[e] = gs / (1.0f + expf(-gs)) * u;
+        }
+        uint2 v;
+        v.x = f2bf(y[0]) | (f2bf(y[1]) << 16);
+        v.y = f2bf(y[2]) | (f2bf(y[3]) << 16);
+        *reinterpret_cast<uint2*>((bf16s*)a.act + (int64_t)m * a.pair_F + j) = v;
+      }
+    }
+    return;
+  }
+  float* P = a.P + (int64_t)z * a.M * a.N;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const int n = n0 + wn * 128 + nb * 16 + 4 * g;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int m = m0 + wm * 16 * WMB + mb * 16 + c;
+      if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
+    }
+  }
+}
+
 // the direct-to-LDS kernel's plan (or none: fall back to k_gemm_big).
 // 128-row tiles for 64..255 rows, split along K until the grid is one wave
 // of at most 256 workgroups (one per CU); 256-row tiles from 256 rows where
@@ -463,12 +640,26 @@ static void launch_dma_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) 
                      a, s.ntiles, s.mtiles, s.S);
 }
 
+template <int EPI>
+static void launch_dmaw_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_dmaw<EPI>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kDmawLds);
+    attr = true;
+  }
+  const int total = s.ntiles * s.mtiles * s.S;
+  hipLaunchKernelGGL((k_gemm_dmaw<EPI>), dim3(((total + 7) / 8) * 8), dim3(512), kDmawLds, st,
+                     a, s.ntiles, s.mtiles, s.S);
+}
+
 void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
   a.kps = s.kps;
   if (s.NB == 2) {
     const bool sw = a.pair_F > 0;
     if (s.MB == 16) sw ? launch_dma_t<1, 256, 256>(a, s, st) : launch_dma_t<0, 256, 256>(a, s, st);
-    else sw ? launch_dma_t<1, 256, 128>(a, s, st) : launch_dma_t<0, 256, 128>(a, s, st);
+    else if (a.ksplit_x % 64 == 0) sw ? launch_dmaw_t<1>(a, s, st) : launch_dmaw_t<0>(a, s, st);
+    else sw ? launch_dma_t<1, 256, 128>(a, s, st) : launch_dma_t<0, 256, 128>(a, s, st);  // 64-K stages would straddle the A split
     return;
   }
   if (s.MB == 16) launch_big_t<4, 4, 4>(a, s, st);
