@@ -648,7 +648,30 @@ void ingest(const eagle_head* h, const eagle_kv* kv, char* ws, const Ws& w, cons
   const bool fold = h->norm == EAGLE_NORM_RMS;   // N1 folded through the k|v projection
   float* Pin = (float*)(ws + w.P_in);
   GemmShape sh;
-  if (h->mode == EAGLE_MODE_3) {
+  if (h->mode == EAGLE_MODE_3 && fold && big_rowepi_ok(h->dtype, Tn, d, 3 * d)) {
+    // one tiled GEMM: x = [l;m;h] W_fuse^T + emb(t) in bf16, x * g1 and the
+    // row statistics written by its epilogue (no fp32 partials, no row kernel)
+    GemmArgs ga;
+    ga.xs[0] = rs(lmh, nullptr, 3 * d);
+    ga.xs[1] = kNone;
+    ga.ksplit_x = 3 * d;
+    ga.M = Tn;
+    ga.N = d;
+    ga.K = 3 * d;
+    ga.w[0] = ga.w[1] = ga.w[2] = h->w_fuse;
+    ga.nseg1 = ga.nseg2 = d;
+    ga.P = nullptr;
+    ga.row_epi = 1;
+    ga.res = rs(h->emb, ctx_tokens, d, h->vocab);
+    ga.out = ws + w.x_in;
+    ga.out_g = ws + w.xn_in;
+    ga.gain = h->norm1_g;
+    ga.stats = g_stats;
+    const GemmShape gs = plan_gemm_big(Tn, d, 3 * d);
+    ProfScope ps(EAGLE_PROF_GEMM, (double)esz(h) * ((double)d * 3 * d + (double)Tn * 3 * d),
+                 2.0 * Tn * (double)d * 3 * d, st);
+    launch_gemm_big(ga, gs, st);
+  } else if (h->mode == EAGLE_MODE_3) {
     gemm(h, rs(lmh, nullptr, 3 * d), kNone, 3 * d, Tn, d, 3 * d, h->w_fuse, nullptr, nullptr, d,
          d, Pin, &sh, st);
     reduce(h, Pin, sh.S, Tn, d, kNone, rs(h->emb, ctx_tokens, d, h->vocab), ws + w.x_in, kNone,

@@ -334,6 +334,68 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, in
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load in flight when the wave ends
 
   // acc[nb][mb]: lane holds out[m = m0 + BM/WM wm + 16 mb + c][n = n0 + 128 wn + 16 nb + 4 g + 0..3]
+  if (EPI == 2) {
+    // row epilogue (one split, BN = 256): y = acc + res row, bf16 y and
+    // y * gain, and the row's (sum, sum of squares) over the tile's 256
+    // columns: each lane sums its 32 columns, the four lanes of a row (16 and
+    // 32 apart) by permlane swaps, the two n-waves through LDS
+    float* red = reinterpret_cast<float*>(lds);           // [WM][WMB][16][2] of the wn = 1 waves
+    __syncthreads();                                      // every wave is past its fragment reads
+    // the gains of the lane's 32 columns, then per m-block the 8 residual
+    // loads together (rows past M re-read row M - 1), so the epilogue pays a
+    // few memory latencies, not one per column block
+    uint2 gv[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      gv[nb] = *reinterpret_cast<const uint2*>((const bf16s*)a.gain + n0 + wn * 128 + nb * 16 + 4 * g);
+    float s1[WMB], s2[WMB];
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int m = m0 + wm * 16 * WMB + mb * 16 + c;
+      const bool live = m < a.M;
+      const bf16s* er = row_ptr<bf16s>(a.res, live ? m : a.M - 1);
+      uint2 ev[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) ev[nb] = *reinterpret_cast<const uint2*>(er + n0 + wn * 128 + nb * 16 + 4 * g);
+      float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int n = n0 + wn * 128 + nb * 16 + 4 * g;
+        const f32x4 y = acc[nb][mb] + f32x4{bf2f(ev[nb].x & 0xffffu), bf2f(ev[nb].x >> 16),
+                                            bf2f(ev[nb].y & 0xffffu), bf2f(ev[nb].y >> 16)};
+        const f32x4 gn = f32x4{bf2f(gv[nb].x & 0xffffu), bf2f(gv[nb].x >> 16),
+                               bf2f(gv[nb].y & 0xffffu), bf2f(gv[nb].y >> 16)};
+        const f32x4 yg = y * gn;
+        if (live) {
+          *reinterpret_cast<uint2*>((bf16s*)a.out + (int64_t)m * a.N + n) =
+              make_uint2(f2bf(y[0]) | (f2bf(y[1]) << 16), f2bf(y[2]) | (f2bf(y[3]) << 16));
+          *reinterpret_cast<uint2*>((bf16s*)a.out_g + (int64_t)m * a.N + n) =
+              make_uint2(f2bf(yg[0]) | (f2bf(yg[1]) << 16), f2bf(yg[2]) | (f2bf(yg[3]) << 16));
+          t1 += (y[0] + y[1]) + (y[2] + y[3]);
+          t2 += (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]);
+        }
+      }
+      s1[mb] = sum_x32(sum_x16(t1));
+      s2[mb] = sum_x32(sum_x16(t2));
+      if (wn == 1 && g == 0) {
+        red[((wm * WMB + mb) * 16 + c) * 2] = s1[mb];
+        red[((wm * WMB + mb) * 16 + c) * 2 + 1] = s2[mb];
+      }
+    }
+    __syncthreads();
+    if (wn == 0 && g == 0) {
+      const int nblk = a.N / 256;
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb) {
+        const int m = m0 + wm * 16 * WMB + mb * 16 + c;
+        if (m >= a.M) continue;
+        float* st = a.stats + ((int64_t)m * nblk + ntile) * 2;
+        st[0] = s1[mb] + red[((wm * WMB + mb) * 16 + c) * 2];
+        st[1] = s2[mb] + red[((wm * WMB + mb) * 16 + c) * 2 + 1];
+      }
+    }
+    return;
+  }
   if (EPI == 1) {
     // gate block nb (even) pairs with up block nb + 1: columns
     // j = BN/2 ntile + 16 ((8 wn + nb) / 2) + 4 g + 0..3 of act (F columns)
@@ -583,6 +645,12 @@ bool big_gemm_ok(int dtype, int M, int N, int K) {
   return dtype == EAGLE_BF16 && M >= 64 && K % kBK == 0 && N % 16 == 0;
 }
 
+bool big_rowepi_ok(int dtype, int M, int N, int K) {
+  GemmShape s;
+  if (!big_gemm_ok(dtype, M, N, K) || !plan_dma(M, N, K, &s)) return false;
+  return s.S == 1 && s.MB == 16 && N % 256 == 0;
+}
+
 bool big_swiglu_ok(int dtype, int M, int F, int K) {
   GemmShape s;
   if (!big_gemm_ok(dtype, M, 2 * F, K) || !plan_dma(M, 2 * F, K, &s)) return false;
@@ -657,6 +725,10 @@ void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
   a.kps = s.kps;
   if (s.NB == 2) {
     const bool sw = a.pair_F > 0;
+    if (a.row_epi) {   // big_rowepi_ok: 256-row tiles, one split
+      launch_dma_t<2, 256, 256>(a, s, st);
+      return;
+    }
     if (s.MB == 16) sw ? launch_dma_t<1, 256, 256>(a, s, st) : launch_dma_t<0, 256, 256>(a, s, st);
     else if (a.ksplit_x % 64 == 0) sw ? launch_dmaw_t<1>(a, s, st) : launch_dmaw_t<0>(a, s, st);
     else sw ? launch_dma_t<1, 256, 128>(a, s, st) : launch_dma_t<0, 256, 128>(a, s, st);  // 64-K stages would straddle the A split

@@ -21,6 +21,16 @@ struct GemmArgs {
   // act[m][j] = silu(gate_j) * up_j in bf16 instead of P (rows of pair_F)
   int pair_F = 0;
   void* act = nullptr;
+  // row epilogue of the tiled big GEMM (one split, 256-row and 256-column
+  // tiles, N % 256 == 0): y = acc + res row; out = bf16(y), out_g =
+  // bf16(y * gain), stats[m][n / 256] = (sum y, sum y^2) over the tile's 256
+  // columns, the layout the folded-RMSNorm consumers read
+  int row_epi = 0;
+  RowSrc res = RowSrc{nullptr, nullptr, 0, 0};
+  void* out = nullptr;
+  void* out_g = nullptr;
+  const void* gain = nullptr;
+  float* stats = nullptr;
 };
 struct GemmShape {
   int MB, NB, mtiles, ntiles, S, kps;
@@ -35,6 +45,8 @@ struct GemmShape {
 GemmShape plan_gemm(int dtype, int M, int N, int K);
 void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st);
 bool big_gemm_ok(int dtype, int M, int N, int K);
+// whether launch_gemm_big takes the row epilogue (row_epi) for this shape
+bool big_rowepi_ok(int dtype, int M, int N, int K);
 GemmShape plan_gemm_big(int M, int N, int K);
 void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st);
 // the big-GEMM plan uses the direct-to-LDS kernel with one split, so the
