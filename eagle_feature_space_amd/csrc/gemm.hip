@@ -675,8 +675,15 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
     bool skip = false;
     if (a.pos) pos = a.pos[m];
     else {  // packed context rows: position inside the request
-      int b = 0;
-      while (b + 1 < a.B && a.cu_row[b + 1] <= m) ++b;
+      // the last request b with cu_row[b] <= m, by bisection (the row is
+      // uniform across the workgroup: a few scalar loads instead of up to B
+      // dependent ones)
+      int b = 0, hi = a.B;
+      while (hi - b > 1) {
+        const int mid = (b + hi) >> 1;
+        if (a.cu_row[mid] <= m) b = mid;
+        else hi = mid;
+      }
       pos = m - a.cu_row[b];
       if (a.n_new) {
         const int nb = a.n[b];
