@@ -718,7 +718,10 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
 
 void launch_epi_qkv(int dtype, const QkvArgs& a, hipStream_t st) {
   const int pairs = (a.Hq + 2 * a.Hkv) * (a.hd / 2);
-  dim3 grid((unsigned)((pairs + 255) / 256), (unsigned)std::min(a.M, 65535));
+  // at most 2048 row slots: a workgroup takes every 2048th row, so the
+  // rotation frequencies (double-precision exp2 / log2 per pair) are formed
+  // once per ~M/2048 rows instead of once per row (the ~20k-row ingest)
+  dim3 grid((unsigned)((pairs + 255) / 256), (unsigned)std::min(a.M, 2048));
   if (a.M <= 0) return;
   if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_qkv<bf16s>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_epi_qkv<float>, grid, dim3(256), 0, st, a);
