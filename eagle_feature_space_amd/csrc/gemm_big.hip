@@ -451,9 +451,16 @@ __device__ __forceinline__ int dmaw_off(int r, int j) { return r * kWRow + 16 * 
 constexpr int kDmawStage = (256 + 128) * kWRow;             // 48 KB
 constexpr int kDmawLds = 3 * kDmawStage;                    // 144 KB
 
-template <int EPI>   // EPI 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
+// Wave grids: WN = 2 (2 x 4 waves, 128 x 32 wave tiles, all 128 rows) or, for
+// 65..80 rows, WN = 8 (8 x 1 waves, 32 x 80 wave tiles: only the five live
+// 16-row blocks are multiplied, 10 MFMAs per 32 of K per wave instead of 16,
+// and each wave reads 2 W + 5 X fragments instead of 8 + 2).
+template <int EPI, int WN = 2, int WMB = 2>   // EPI 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
 __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, int S) {
-  constexpr int BN = 256, BM = 128, WM = 4, WMB = 2;
+  constexpr int BN = 256, BM = 128, WM = 8 / WN;
+  constexpr int NBW = 16 / WN;                              // 16-row W blocks per wave
+  constexpr int MSPAN = BM / WM;                            // tile rows spanned by a wave
+  static_assert(WMB * 16 <= MSPAN, "m-blocks past the wave's rows");
   constexpr int L = (BN + BM) / 8 / 8;                      // 6 loads of 8 rows per wave per stage
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
@@ -518,30 +525,31 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
     }
   };
 
-  f32x4 acc[8][WMB];
+  f32x4 acc[NBW][WMB];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
+  for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nst > 0) {
-    const int wr0 = wn * 128, xr0 = BN + wm * 16 * WMB;
+    constexpr int H = NBW / 2;                              // n-blocks per half sub-stage
+    const int wr0 = wn * 16 * NBW, xr0 = BN + wm * MSPAN;
     issue(0);
     issue(1);
     __builtin_amdgcn_s_waitcnt(vm_wait(L));                 // stage 0 landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 wf[8], xa[WMB], xb[WMB];
+    u32x4 wf[NBW], xa[WMB], xb[WMB];
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb) xa[mb] = ld16(lds + dmaw_off(xr0 + mb * 16 + c, g));
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) wf[nb] = ld16(lds + dmaw_off(wr0 + nb * 16 + c, g));
+    for (int nb = 0; nb < NBW; ++nb) wf[nb] = ld16(lds + dmaw_off(wr0 + nb * 16 + c, g));
     // sub-stage T_ (MFMAs on XC), reading sub-stage T_ + 1's fragments into
     // XN / wf; EVEN_: T_ = 2S issues stage S + 2, else T_ = 2S + 1 waits for
     // stage S + 1
 #define DMAW_SUB(T_, XC, XN, EVEN_)                                                           \
     {                                                                                       \
-      _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
+      _Pragma("unroll") for (int nb = 0; nb < H; ++nb)                                      \
       _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
         acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
       __builtin_amdgcn_sched_barrier(0);                                                    \
@@ -552,19 +560,19 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
       const int tn_ = (T_) + 1;                                                             \
       const char* st_ = lds + ((tn_ >> 1) % 3) * kDmawStage;                                \
       const int kc_ = (tn_ & 1) * 4 + g;                                                    \
-      _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                      \
+      _Pragma("unroll") for (int nb = 0; nb < H; ++nb)                                      \
         wf[nb] = ld16(st_ + dmaw_off(wr0 + nb * 16 + c, kc_));                              \
       _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
         XN[mb] = ld16(st_ + dmaw_off(xr0 + mb * 16 + c, kc_));                              \
-      _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
+      _Pragma("unroll") for (int nb = H; nb < NBW; ++nb)                                    \
       _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
         acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
-      _Pragma("unroll") for (int nb = 4; nb < 8; ++nb)                                      \
+      _Pragma("unroll") for (int nb = H; nb < NBW; ++nb)                                    \
         wf[nb] = ld16(st_ + dmaw_off(wr0 + nb * 16 + c, kc_));                              \
       if (EVEN_) __builtin_amdgcn_sched_group_barrier(0x020, L, 0);        /* loads */      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 + WMB, 0);  /* reads W 0-3, X */        \
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * WMB, 0);  /* MFMAs n-blocks 4-7 */    \
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        /* reads W 4-7 */           \
+      __builtin_amdgcn_sched_group_barrier(0x100, H + WMB, 0);  /* reads W first half, X */ \
+      __builtin_amdgcn_sched_group_barrier(0x008, H * WMB, 0);  /* MFMAs second half */     \
+      __builtin_amdgcn_sched_group_barrier(0x100, H, 0);        /* reads W second half */   \
       __builtin_amdgcn_sched_barrier(0);                                                    \
     }
     for (int t = 0; t < nsub; t += 2) {
@@ -577,12 +585,12 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
 
   if (EPI == 1) {
 #pragma unroll
-    for (int nb = 0; nb < 8; nb += 2) {
-      const int j = ntile * (BN / 2) + ((wn * 8 + nb) >> 1) * 16 + 4 * g;
+    for (int nb = 0; nb < NBW; nb += 2) {
+      const int j = ntile * (BN / 2) + ((wn * NBW + nb) >> 1) * 16 + 4 * g;
       if (j >= a.pair_F) continue;
 #pragma unroll
       for (int mb = 0; mb < WMB; ++mb) {
-        const int m = m0 + wm * 16 * WMB + mb * 16 + c;
+        const int m = m0 + wm * MSPAN + mb * 16 + c;
         if (m >= a.M) continue;
         f32x4 y;
 #pragma unroll
@@ -600,12 +608,12 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
   }
   float* P = a.P + (int64_t)z * a.M * a.N;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const int n = n0 + wn * 128 + nb * 16 + 4 * g;
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int n = n0 + wn * 16 * NBW + nb * 16 + 4 * g;
     if (n >= a.N) continue;
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb) {
-      const int m = m0 + wm * 16 * WMB + mb * 16 + c;
+      const int m = m0 + wm * MSPAN + mb * 16 + c;
       if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
     }
   }
@@ -708,17 +716,22 @@ static void launch_dma_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) 
                      a, s.ntiles, s.mtiles, s.S);
 }
 
-template <int EPI>
-static void launch_dmaw_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+template <int EPI, int WN, int WMB>
+static void launch_dmaw_g(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_dmaw<EPI>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_dmaw<EPI, WN, WMB>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kDmawLds);
     attr = true;
   }
   const int total = s.ntiles * s.mtiles * s.S;
-  hipLaunchKernelGGL((k_gemm_dmaw<EPI>), dim3(((total + 7) / 8) * 8), dim3(512), kDmawLds, st,
+  hipLaunchKernelGGL((k_gemm_dmaw<EPI, WN, WMB>), dim3(((total + 7) / 8) * 8), dim3(512), kDmawLds, st,
                      a, s.ntiles, s.mtiles, s.S);
+}
+template <int EPI>
+static void launch_dmaw_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+  if (a.M > 64 && a.M <= 80) launch_dmaw_g<EPI, 8, 5>(a, s, st);   // one m-tile, five live blocks
+  else launch_dmaw_g<EPI, 2, 2>(a, s, st);
 }
 
 void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
