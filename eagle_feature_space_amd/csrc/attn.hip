@@ -787,8 +787,11 @@ void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
     // more than one 16-row block per (request, kv head): workgroup kernel
     if (dtype == EAGLE_BF16) {
       if (a.hd == 128) {   // direct-to-LDS tiles
+        // 16 rows per wave; past 64 rows one 8-wave workgroup per CU reads
+        // each K / V tile once for 128 rows instead of twice for 2 x 64
         if (R <= 32) launch_dma<2, kAttnPF>(a, st);
-        else launch_dma<4, kAttnPF>(a, st);
+        else if (R <= 64) launch_dma<4, kAttnPF>(a, st);
+        else launch_dma<8, kAttnPF>(a, st);
       }
       else launch_wide<bf16s, 64>(a, R, st);
     } else {
