@@ -287,6 +287,23 @@ SMALL_CONFIGS["s21_dynamic_264"] = RoundCfg(
     tree=TREE_DYNAMIC, gamma=4, top_k=8, top_m=24, inv_temp=5.0,
     seed_w=1122, seed_in=2122, seed_t=3122)
 
+# 80 rows per step after the root (8 requests x top-k 10) on the 64-K-stage
+# tiled GEMM: |V| = 69648 gives the LM head 273 tiles of 256 columns, more than
+# one per workgroup (ragged last tile of 16 columns), and d = 832 splits the
+# fc's K = 1664 into six 320-wide spans whose last is a single 64-K stage
+SMALL_CONFIGS["s24_dynamic_80_v69648"] = RoundCfg(
+    name="s24_dynamic_80_v69648", head=replace(_HEAD_SMALL, d=832, vocab=69648), B=8,
+    n=(40, 0, 77, 5, 130, 64, 1, 19), tree=TREE_DYNAMIC, gamma=3, top_k=10, top_m=20,
+    inv_temp=4.0, seed_w=1124, seed_in=2124, seed_t=3124)
+
+# 72 rows per step after the root (9 requests x top-k 8), the fused LM-head
+# epilogue with ragged rows: |V| = 16400 is 65 tiles over 72 workgroups, so
+# seven workgroups write empty parts
+SMALL_CONFIGS["s25_dynamic_72_v16400"] = RoundCfg(
+    name="s25_dynamic_72_v16400", head=replace(_HEAD_SMALL, vocab=16400), B=9,
+    n=(3, 90, 0, 41, 200, 17, 64, 8, 129), tree=TREE_DYNAMIC, gamma=3, top_k=8, top_m=16,
+    inv_temp=3.0, seed_w=1125, seed_in=2125, seed_t=3125)
+
 # The target's verification pass: a static tree (52 rows, tiled kernels), a
 # dynamic tree with an empty context, an fp32 LayerNorm / GELU head, and a
 # 12-row chain (row-complete kernels)

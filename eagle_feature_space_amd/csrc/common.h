@@ -151,6 +151,16 @@ __device__ __forceinline__ float rows_sum(float v) {
   return (readlane_f(v, 0) + readlane_f(v, 16)) +
          (readlane_f(v, 32) + readlane_f(v, 48));
 }
+// float -> unsigned with the same order (-0 taken as +0, NaN below everything)
+__device__ __forceinline__ uint32_t float_order(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  const uint32_t o = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return x != x ? 0u : o;
+}
+__device__ __forceinline__ float order_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 __device__ __forceinline__ uint64_t rows_umax64(uint64_t v) {
   v = umax64(v, dpp_u64<0xB1>(v));
   v = umax64(v, dpp_u64<0x4E>(v));

@@ -27,7 +27,7 @@ struct Bump {
 
 // ---------------------------------------------------------------- tree shape
 struct Geo {
-  int kind = 0, B = 0, gamma = 0, top_k = 0, top_m = 0;
+  int kind = 0, B = 0, gamma = 0, top_k = 0, top_m = 0, sample = 0;
   int pool_cap = 0, max_rows = 0, positions = 0, slots = 0;
   std::vector<int> rows;              // rows per request of each step
   std::vector<StaticPlan> plans;      // chain / static: children of each step
@@ -46,6 +46,7 @@ int build_geo(const eagle_tree* t, Geo* g) {
   g->gamma = t->gamma;
   g->top_k = t->top_k;
   g->top_m = t->top_m;
+  g->sample = t->sample;
   g->rows.assign(t->gamma, 0);
   g->plans.assign(t->gamma, StaticPlan{});
   if (t->kind == EAGLE_TREE_CHAIN) {
@@ -416,10 +417,22 @@ Ws plan_ws(const eagle_head* h, const eagle_kv* kv, const Geo& g, bool target = 
   w.att_o = bp.take(nparts * Mr * h->n_q_heads * h->head_dim * 4);
   w.att_ml = bp.take(nparts * Mr * h->n_q_heads * 2 * 4);
   LmShape ls = plan_lmhead(h->dtype, Mmax, h->vocab);
-  if (big_gemm_ok(h->dtype, Mmax, h->vocab, d)) ls.ntiles = std::max(ls.ntiles, logits_tiles(h->vocab));
+  // draft steps on the tiled GEMM: with the fused LM-head epilogue one part
+  // per workgroup and no logits buffer, else fp32 logits and tile partials
   // (the target pass writes its logits straight to the caller's buffer)
+  bool need_lg = false;
+  for (int s = 0; s < g.gamma; ++s) {
+    const int M = g.B * g.rows[s];
+    if (!big_gemm_ok(h->dtype, M, h->vocab, d)) continue;
+    if (!g.sample && lm_fused_ok(h->dtype, M, h->vocab, d, g.top_k)) {
+      ls.ntiles = std::max(ls.ntiles, lm_fused_parts(M, h->vocab, d));
+    } else {
+      need_lg = true;
+      ls.ntiles = std::max(ls.ntiles, logits_tiles(h->vocab));
+    }
+  }
   const int Mlg = g.B * g.max_rows;
-  w.logits = big_gemm_ok(h->dtype, Mlg, h->vocab, d) ? bp.take((size_t)Mlg * h->vocab * 4) : 0;
+  w.logits = need_lg ? bp.take((size_t)Mlg * h->vocab * 4) : 0;
   w.lm_max = bp.take((size_t)ls.ntiles * Mmax * 4);
   w.lm_sum = bp.take((size_t)ls.ntiles * Mmax * 4);
   w.lm_id = bp.take((size_t)ls.ntiles * Mmax * g.top_k * 4);
@@ -1068,7 +1081,33 @@ int eagle_draft_step(const eagle_head* h, const eagle_kv* kv, const eagle_tree* 
     la.rows_per_req = W;
     la.part_logit = (float*)(ws + w.lm_lg);
   }
-  if (big_gemm_ok(h->dtype, M, h->vocab, d)) {
+  if (!tree->sample && lm_fused_ok(h->dtype, M, h->vocab, d, g.top_k)) {
+    // the tiled GEMM folds softmax / top-k into its epilogue: one part per
+    // workgroup (the logits only when the caller asks for them)
+    GemmArgs ga;
+    ga.xs[0] = rs(fout, nullptr, d);
+    ga.xs[1] = kNone;
+    ga.ksplit_x = d;
+    ga.M = M;
+    ga.N = h->vocab;
+    ga.K = d;
+    ga.w[0] = ga.w[1] = ga.w[2] = h->lm_head;
+    ga.nseg1 = ga.nseg2 = h->vocab;
+    ga.P = logits_out;
+    ga.lm_top_k = g.top_k;
+    ga.lm_inv_temp = tree->inv_temp;
+    ga.lm_max = la.part_max;
+    ga.lm_sum = la.part_sum;
+    ga.lm_val = la.part_val;
+    ga.lm_id = la.part_id;
+    GemmShape gs = plan_gemm_big(M, h->vocab, d);
+    gs.S = 1;
+    gs.kps = d;
+    ls.ntiles = lm_fused_parts(M, h->vocab, d);
+    ProfScope ps(EAGLE_PROF_LMHEAD, (double)esz(h) * ((double)h->vocab * d + (double)M * d),
+                 2.0 * M * (double)h->vocab * d, st);
+    launch_gemm_big(ga, gs, st);
+  } else if (big_gemm_ok(h->dtype, M, h->vocab, d)) {
     // MFMA-bound: tiled GEMM into fp32 logits, then tile partials
     float* lg = logits_out ? logits_out : (float*)(ws + w.logits);
     GemmArgs ga;

@@ -446,22 +446,76 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int nt, int mt, in
 // past sub-stage 2S-1); before the barrier of sub-stage 2S+1 each wave waits
 // for its loads of stage S+1.  16-byte chunk j of a 128-byte row r sits at
 // j ^ ((r >> 1) & 7) (the swizzle k_gemm_big uses for its 128-byte rows).
+//
+// Persistent over tiles: at most 256 workgroups (one per CU), each walking
+// the tiles of its XCD's contiguous share.  The stages of its tiles form one
+// stream through the ring (a loader position: tile, stage, ring count), so
+// the last stage issues of a tile already fetch the next tile's first
+// stages and the last sub-stage reads the next tile's first fragments: the
+// epilogue's stores run while the next tile's weights are in flight and no
+// workgroup starts from an empty pipe.  Nothing is issued past the last
+// stage of a workgroup's last tile, and a split may be a single stage.
 constexpr int kWRow = 128;
 __device__ __forceinline__ int dmaw_off(int r, int j) { return r * kWRow + 16 * (j ^ ((r >> 1) & 7)); }
 constexpr int kDmawStage = (256 + 128) * kWRow;             // 48 KB
 constexpr int kDmawLds = 3 * kDmawStage;                    // 144 KB
 
+// LM-head epilogue (EPI 3): per-row running state after the ring, and the
+// rows of the finished tile staged (fp32, rows padded to 260 floats) in the
+// ring slot no stage occupies while the epilogue runs
+constexpr int kLmRows = 80;
+constexpr int kLmRunBytes = kLmRows * 8 + kLmRows * kLmFusedTopK * 8;
+constexpr int kLmStg = 260;
+constexpr int kLgkmWait0 = 0xC07F;                          // s_waitcnt lgkmcnt(0)
+constexpr int kLmLD = 4;                                    // keys each lane keeps sorted
+// reductions over each 16-lane row of the wave (every lane of the row gets
+// the result)
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return fmaxf(v, dpp_f<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+__device__ __forceinline__ uint64_t row16_umax64(uint64_t v) {
+  v = umax64(v, dpp_u64<0xB1>(v));
+  v = umax64(v, dpp_u64<0x4E>(v));
+  v = umax64(v, dpp_u64<0x141>(v));
+  return umax64(v, dpp_u64<0x140>(v));
+}
+// (logit desc, column asc) as one 64-bit key; 0 is below every real key
+__device__ __forceinline__ uint64_t lm_key(float v, int col) {
+  return ((uint64_t)float_order(v) << 32) | (0xffffffffu - (uint32_t)col);
+}
+// LDS writes of every wave done, then every wave here (no vmcnt wait: the
+// next tile's stages stay in flight)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wave grids: WN = 2 (2 x 4 waves, 128 x 32 wave tiles, all 128 rows) or, for
 // 65..80 rows, WN = 8 (8 x 1 waves, 32 x 80 wave tiles: only the five live
 // 16-row blocks are multiplied, 10 MFMAs per 32 of K per wave instead of 16,
 // and each wave reads 2 W + 5 X fragments instead of 8 + 2).
-template <int EPI, int WN = 2, int WMB = 2>   // EPI 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]
+// EPI 0: fp32 partials P[z][m][n]; 1: SwiGLU, bf16 act[m][j]; 3: LM-head
+// softmax / top-k parts (and the fp32 logits into P if set)
+template <int EPI, int WN = 2, int WMB = 2>
 __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, int S) {
+  static_assert(EPI != 3 || (WN == 8 && WMB * 16 == kLmRows), "the LM-head epilogue takes the 8 x 1 grid");
   constexpr int BN = 256, BM = 128, WM = 8 / WN;
   constexpr int NBW = 16 / WN;                              // 16-row W blocks per wave
   constexpr int MSPAN = BM / WM;                            // tile rows spanned by a wave
   static_assert(WMB * 16 <= MSPAN, "m-blocks past the wave's rows");
   constexpr int L = (BN + BM) / 8 / 8;                      // 6 loads of 8 rows per wave per stage
+  constexpr int H = NBW / 2;                                // n-blocks per half sub-stage
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -469,54 +523,93 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
   const int wn = wave / WM, wm = wave % WM;
   const int total = nt * mt * S;
   const int per = (total + 7) / 8;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= total) return;
-  const int mtile = lin % mt;
-  const int ntile = (lin / mt) % nt;
-  const int z = lin / (mt * nt);
-  const int n0 = ntile * BN, m0 = mtile * BM;
-  const int k_begin = z * a.kps, k_end = min(a.K, k_begin + a.kps);
-  const int nsub = (k_end - k_begin) / 32;                  // even: K per split is a multiple of 64
-  const int nst = nsub / 2;
+  const int G8 = gridDim.x >> 3;                            // workgroups per XCD
+  const int lin_end = min(((int)blockIdx.x & 7) * per + per, total);
+  int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  // EPI 3: LDS running state of row m: max, sum, top-k keys
+  float* run_max = reinterpret_cast<float*>(lds + kDmawLds);
+  float* run_sum = run_max + kLmRows;
+  uint64_t* run_key = reinterpret_cast<uint64_t*>(lds + kDmawLds + kLmRows * 8);
+  const int K_ = a.lm_top_k;
+  // part blockIdx.x of every row from the running state (an empty part for
+  // a workgroup without tiles)
+  auto write_part = [&](bool empty) {
+    const int64_t p0 = (int64_t)blockIdx.x * a.M;
+    for (int m = tid; m < a.M; m += 512) {
+      a.lm_max[p0 + m] = empty ? -INFINITY : run_max[m];
+      a.lm_sum[p0 + m] = empty ? 0.f : run_sum[m];
+    }
+    for (int q = tid; q < a.M * K_; q += 512) {
+      const int m = q / K_, k = q - m * K_;
+      const uint64_t key = empty ? 0ull : run_key[m * kLmFusedTopK + k];
+      a.lm_val[(p0 + m) * K_ + k] = key ? order_float((uint32_t)(key >> 32)) : -INFINITY;
+      a.lm_id[(p0 + m) * K_ + k] = key ? min((int)(0xffffffffu - (uint32_t)key), a.N - 1) : 0;
+    }
+  };
+  if (lin >= lin_end) {
+    if constexpr (EPI == 3) write_part(true);
+    return;
+  }
+  if constexpr (EPI == 3) {
+    for (int m = tid; m < kLmRows; m += 512) {
+      run_max[m] = -INFINITY;
+      run_sum[m] = 0.f;
+    }
+    for (int q = tid; q < kLmRows * kLmFusedTopK; q += 512) run_key[q] = 0ull;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);   // before the prologue's barrier
+    asm volatile("" ::: "memory");
+  }
 
   // load i of wave w: rows 8 (w L + i) .. +7; lane l takes row + (l >> 3),
-  // LDS slot l & 7, i.e. global chunk (l & 7) ^ ((row >> 1) & 7)
+  // LDS slot l & 7, i.e. global chunk (l & 7) ^ ((row >> 1) & 7).  These
+  // describe the tile whose stages are being issued (set up by `setup`).
   const char* src[L];
   const char* src1[L];
   bool isx[L];
+  // stages of 64 K in tile l's split (at least one)
+  auto tile_nst = [&](int l) {
+    const int k0 = (l / (mt * nt)) * a.kps;
+    return (min(a.K, k0 + a.kps) - k0) / 64;
+  };
+  int ld_k0 = 0, ld_nst = 0;
+  auto setup = [&](int l) {
+    const int mtile = l % mt, ntile = (l / mt) % nt, z = l / (mt * nt);
+    const int n0 = ntile * BN, m0 = mtile * BM;
+    ld_k0 = z * a.kps;
+    ld_nst = tile_nst(l);
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int r = (wave * L + i) * 8 + (lane >> 3);
-    const int j = (lane & 7) ^ ((r >> 1) & 7);
-    isx[i] = r >= BN;
-    if (!isx[i]) {
-      int n;
-      if (EPI == 1) {   // 16-row blocks alternate gate (even) and up (odd)
-        const int b = r >> 4;
-        const int q = ntile * (BN / 2) + (b >> 1) * 16 + (r & 15);
-        n = (b & 1) ? a.pair_F + min(q, a.pair_F - 1) : min(q, a.pair_F - 1);
+    for (int i = 0; i < L; ++i) {
+      const int r = (wave * L + i) * 8 + (lane >> 3);
+      const int j = (lane & 7) ^ ((r >> 1) & 7);
+      isx[i] = r >= BN;
+      if (!isx[i]) {
+        int n;
+        if (EPI == 1) {   // 16-row blocks alternate gate (even) and up (odd)
+          const int b = r >> 4;
+          const int q = ntile * (BN / 2) + (b >> 1) * 16 + (r & 15);
+          n = (b & 1) ? a.pair_F + min(q, a.pair_F - 1) : min(q, a.pair_F - 1);
+        } else {
+          n = min(n0 + r, a.N - 1);
+        }
+        const bf16s* base;
+        int off;
+        if (n < a.nseg1) { base = (const bf16s*)a.w[0]; off = 0; }
+        else if (n < a.nseg2) { base = (const bf16s*)a.w[1]; off = a.nseg1; }
+        else { base = (const bf16s*)a.w[2]; off = a.nseg2; }
+        src[i] = (const char*)(base + (int64_t)(n - off) * a.K + j * 8);
+        src1[i] = src[i];
       } else {
-        n = min(n0 + r, a.N - 1);
+        const int m = min(m0 + r - BN, a.M - 1);
+        src[i] = (const char*)(row_ptr<bf16s>(a.xs[0], m) + j * 8);
+        src1[i] = a.xs[1].base ? (const char*)(row_ptr<bf16s>(a.xs[1], m) + j * 8) : src[i];
       }
-      const bf16s* base;
-      int off;
-      if (n < a.nseg1) { base = (const bf16s*)a.w[0]; off = 0; }
-      else if (n < a.nseg2) { base = (const bf16s*)a.w[1]; off = a.nseg1; }
-      else { base = (const bf16s*)a.w[2]; off = a.nseg2; }
-      src[i] = (const char*)(base + (int64_t)(n - off) * a.K + j * 8);
-      src1[i] = src[i];
-    } else {
-      const int m = min(m0 + r - BN, a.M - 1);
-      src[i] = (const char*)(row_ptr<bf16s>(a.xs[0], m) + j * 8);
-      src1[i] = a.xs[1].base ? (const char*)(row_ptr<bf16s>(a.xs[1], m) + j * 8) : src[i];
     }
-  }
-  // stage sd (clamped to the last one, so every stage issues L loads and the
-  // vmcnt waits stay exact) into ring slot sd % 3
-  auto issue = [&](int sd) {
-    const int sc = min(sd, nst - 1);
-    const int k0 = k_begin + sc * 64;
-    char* dst = lds + (sd % 3) * kDmawStage + wave * L * 1024;
+  };
+  // stage sd of the set-up tile into ring slot `slot`
+  auto issue = [&](int slot, int sd) {
+    const int k0 = ld_k0 + sd * 64;
+    char* dst = lds + slot * kDmawStage + wave * L * 1024;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const bool hi = isx[i] && k0 >= a.ksplit_x;          // a stage never straddles the split
@@ -525,40 +618,64 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
     }
   };
 
-  f32x4 acc[NBW][WMB];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // loader: the next stage to issue is stage ld_sd of tile ld_lin, into ring
+  // slot ring % 3 (ring counts the stages issued so far)
+  int ld_lin = lin, ld_sd = 0, ring = 0;
+  bool ld_done = false;
+  setup(lin);
+  auto issue_next = [&]() {
+    if (ld_done) return;
+    issue(ring % 3, ld_sd);
+    ++ring;
+    if (++ld_sd == ld_nst) {
+      ld_lin += G8;
+      ld_sd = 0;
+      if (ld_lin < lin_end) setup(ld_lin);
+      else ld_done = true;
+    }
+  };
 
-  if (nst > 0) {
-    constexpr int H = NBW / 2;                              // n-blocks per half sub-stage
-    const int wr0 = wn * 16 * NBW, xr0 = BN + wm * MSPAN;
-    issue(0);
-    issue(1);
-    __builtin_amdgcn_s_waitcnt(vm_wait(L));                 // stage 0 landed
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 wf[NBW], xa[WMB], xb[WMB];
+  const int wr0 = wn * 16 * NBW, xr0 = BN + wm * MSPAN;
+  int cbase = 0;               // ring count of the current tile's stage 0
+  issue_next();
+  issue_next();
+  if (ring > 1) __builtin_amdgcn_s_waitcnt(vm_wait(L));     // stage 0 landed
+  else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 wf[NBW], xa[WMB], xb[WMB];
 #pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) xa[mb] = ld16(lds + dmaw_off(xr0 + mb * 16 + c, g));
+  for (int mb = 0; mb < WMB; ++mb) xa[mb] = ld16(lds + dmaw_off(xr0 + mb * 16 + c, g));
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) wf[nb] = ld16(lds + dmaw_off(wr0 + nb * 16 + c, g));
+  for (int nb = 0; nb < NBW; ++nb) wf[nb] = ld16(lds + dmaw_off(wr0 + nb * 16 + c, g));
+
+  for (;;) {
+    const int nst = tile_nst(lin);   // stages of the current tile
+    f32x4 acc[NBW][WMB];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
     // sub-stage T_ (MFMAs on XC), reading sub-stage T_ + 1's fragments into
-    // XN / wf; EVEN_: T_ = 2S issues stage S + 2, else T_ = 2S + 1 waits for
-    // stage S + 1
+    // XN / wf; EVEN_: T_ = 2S issues the stream's next stage (stage S + 2, or
+    // the next tile's first ones past the end), else T_ = 2S + 1 waits for
+    // stage S + 1 (with a younger stage still in flight if one was issued)
 #define DMAW_SUB(T_, XC, XN, EVEN_)                                                           \
     {                                                                                       \
       _Pragma("unroll") for (int nb = 0; nb < H; ++nb)                                      \
       _Pragma("unroll") for (int mb = 0; mb < WMB; ++mb)                                    \
         acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
       __builtin_amdgcn_sched_barrier(0);                                                    \
-      if (!(EVEN_)) __builtin_amdgcn_s_waitcnt(vm_wait(L));   /* stage S + 1 landed */      \
+      if (!(EVEN_)) {                                         /* stage S + 1 landed */      \
+        if (ring > cbase + ((T_) >> 1) + 2) __builtin_amdgcn_s_waitcnt(vm_wait(L));         \
+        else __builtin_amdgcn_s_waitcnt(vm_wait(0));                                        \
+      }                                                                                     \
       __builtin_amdgcn_s_barrier();                                                         \
       __builtin_amdgcn_sched_barrier(0);                                                    \
-      if (EVEN_) issue(((T_) >> 1) + 2);                                                    \
+      if (EVEN_) issue_next();                                                              \
       const int tn_ = (T_) + 1;                                                             \
-      const char* st_ = lds + ((tn_ >> 1) % 3) * kDmawStage;                                \
+      const char* st_ = lds + ((cbase + (tn_ >> 1)) % 3) * kDmawStage;                      \
       const int kc_ = (tn_ & 1) * 4 + g;                                                    \
       _Pragma("unroll") for (int nb = 0; nb < H; ++nb)                                      \
         wf[nb] = ld16(st_ + dmaw_off(wr0 + nb * 16 + c, kc_));                              \
@@ -569,54 +686,168 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
         acc[nb][mb] = DT<bf16s>::mma(wf[nb], XC[mb], acc[nb][mb]);                          \
       _Pragma("unroll") for (int nb = H; nb < NBW; ++nb)                                    \
         wf[nb] = ld16(st_ + dmaw_off(wr0 + nb * 16 + c, kc_));                              \
-      if (EVEN_) __builtin_amdgcn_sched_group_barrier(0x020, L, 0);        /* loads */      \
       __builtin_amdgcn_sched_group_barrier(0x100, H + WMB, 0);  /* reads W first half, X */ \
       __builtin_amdgcn_sched_group_barrier(0x008, H * WMB, 0);  /* MFMAs second half */     \
       __builtin_amdgcn_sched_group_barrier(0x100, H, 0);        /* reads W second half */   \
       __builtin_amdgcn_sched_barrier(0);                                                    \
     }
-    for (int t = 0; t < nsub; t += 2) {
+    for (int t = 0; t < 2 * nst; t += 2) {
       DMAW_SUB(t, xa, xb, true)
       DMAW_SUB(t + 1, xb, xa, false)
     }
 #undef DMAW_SUB
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load in flight when the wave ends
 
-  if (EPI == 1) {
+    // epilogue of tile `lin` (the next tile's first stages are in flight and
+    // its first fragments are in wf / xa)
+    {
+      const int mtile = lin % mt, ntile = (lin / mt) % nt, z = lin / (mt * nt);
+      const int n0 = ntile * BN, m0 = mtile * BM;
+      if (EPI == 1) {
 #pragma unroll
-    for (int nb = 0; nb < NBW; nb += 2) {
-      const int j = ntile * (BN / 2) + ((wn * NBW + nb) >> 1) * 16 + 4 * g;
-      if (j >= a.pair_F) continue;
+        for (int nb = 0; nb < NBW; nb += 2) {
+          const int j = ntile * (BN / 2) + ((wn * NBW + nb) >> 1) * 16 + 4 * g;
+          if (j >= a.pair_F) continue;
 #pragma unroll
-      for (int mb = 0; mb < WMB; ++mb) {
-        const int m = m0 + wm * MSPAN + mb * 16 + c;
-        if (m >= a.M) continue;
-        f32x4 y;
+          for (int mb = 0; mb < WMB; ++mb) {
+            const int m = m0 + wm * MSPAN + mb * 16 + c;
+            if (m >= a.M) continue;
+            f32x4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float gs = acc[nb][mb][e], u = acc[nb + 1][mb][e];
-          y[e] = gs / (1.0f + expf(-gs)) * u;
+            for (int e = 0; e < 4; ++e) {
+              const float gs_ = acc[nb][mb][e], u = acc[nb + 1][mb][e];
+              y[e] = gs_ / (1.0f + expf(-gs_)) * u;
+            }
+            uint2 v;
+            v.x = f2bf(y[0]) | (f2bf(y[1]) << 16);
+            v.y = f2bf(y[2]) | (f2bf(y[3]) << 16);
+            *reinterpret_cast<uint2*>((bf16s*)a.act + (int64_t)m * a.pair_F + j) = v;
+          }
         }
-        uint2 v;
-        v.x = f2bf(y[0]) | (f2bf(y[1]) << 16);
-        v.y = f2bf(y[2]) | (f2bf(y[3]) << 16);
-        *reinterpret_cast<uint2*>((bf16s*)a.act + (int64_t)m * a.pair_F + j) = v;
+      } else {
+        if (EPI == 0 || a.P) {
+          float* P = a.P + (int64_t)z * a.M * a.N;
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) {
+            const int n = n0 + wn * 16 * NBW + nb * 16 + 4 * g;
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int mb = 0; mb < WMB; ++mb) {
+              const int m = m0 + wm * MSPAN + mb * 16 + c;
+              if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
+            }
+          }
+        }
+        if constexpr (EPI == 3) {
+          // rows in groups of 32 (16 for the last) through the free ring
+          // slot: the waves store their 32-column slices, then each wave
+          // folds whole rows (4 logits a lane) into the running state
+          float* stg = reinterpret_cast<float*>(lds + ((cbase + nst + 2) % 3) * kDmawStage);
+          const float sl = a.lm_inv_temp * 1.4426950408889634f;
+          lds_barrier();   // every wave's reads of that slot (the tile's last stage) done
+#pragma unroll
+          for (int grp = 0; grp < 3; ++grp) {
+            const int mb0 = 2 * grp, nmb = grp < 2 ? 2 : 1;
+#pragma unroll
+            for (int mb = 0; mb < WMB; ++mb) {
+              if (mb < mb0 || mb >= mb0 + nmb) continue;
+#pragma unroll
+              for (int nb = 0; nb < NBW; ++nb)
+                *reinterpret_cast<f32x4*>(stg + ((mb - mb0) * 16 + c) * kLmStg + wn * 16 * NBW + nb * 16 + 4 * g) =
+                    acc[nb][mb];
+            }
+            lds_barrier();
+            // four rows a pass, 16 lanes a row (lane j: columns 64 i + 4 j + e)
+            for (int base = 4 * wave; base < 16 * nmb; base += 32) {
+              const int j = lane & 15;
+              const int rr = base + (lane >> 4);
+              const int m = mb0 * 16 + rr;
+              const bool live = m < a.M;
+              float v[16];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(stg + rr * kLmStg + 64 * i + 4 * j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * i + e] = t[e];
+              }
+              float mx = -INFINITY;
+#pragma unroll
+              for (int q = 0; q < 16; ++q)
+                if (n0 + 64 * (q >> 2) + 4 * j + (q & 3) < a.N) mx = fmaxf(mx, v[q]);
+              mx = row16_max(mx);
+              float se = 0.f;
+#pragma unroll
+              for (int q = 0; q < 16; ++q)
+                if (n0 + 64 * (q >> 2) + 4 * j + (q & 3) < a.N) se += __builtin_amdgcn_exp2f((v[q] - mx) * sl);
+              se = row16_sum(se);
+              // the lane's best kLmLD keys, sorted, over its 16 logits and (lanes
+              // j < k) running key j; then k rounds of the row's largest head
+              // key, which the owning lane drops.  Once some lane has used all
+              // of its kept keys, every lane offers its best key below the
+              // previous winner instead (from the logits it still holds).
+              const uint64_t rk = j < K_ ? run_key[m * kLmFusedTopK + j] : 0ull;
+              uint64_t kb[kLmLD];
+#pragma unroll
+              for (int r = 0; r < kLmLD; ++r) kb[r] = 0ull;
+#pragma unroll
+              for (int q = 0; q <= 16; ++q) {
+                const int col = n0 + 64 * (q >> 2) + 4 * j + (q & 3);
+                uint64_t t = q == 16 ? rk : (col < a.N ? lm_key(v[q], col) : 0ull);
+#pragma unroll
+                for (int r = 0; r < kLmLD; ++r) {
+                  const bool c = t > kb[r];
+                  const uint64_t hi = c ? t : kb[r];
+                  t = c ? kb[r] : t;
+                  kb[r] = hi;
+                }
+              }
+              int used = 0;
+              uint64_t prev = ~0ull, keep = 0ull;
+              for (int k = 0; k < K_; ++k) {
+                uint64_t cand;
+                const bool fast = !__builtin_amdgcn_ballot_w64(used >= kLmLD);
+                if (fast) {
+                  cand = kb[0];
+                } else {
+                  cand = rk < prev ? rk : 0ull;
+#pragma unroll
+                  for (int q = 0; q < 16; ++q) {
+                    const int col = n0 + 64 * (q >> 2) + 4 * j + (q & 3);
+                    const uint64_t t = col < a.N ? lm_key(v[q], col) : 0ull;
+                    if (t < prev && t > cand) cand = t;
+                  }
+                }
+                const uint64_t w = row16_umax64(cand);
+                if (fast && kb[0] == w && w != 0ull) {
+#pragma unroll
+                  for (int r = 0; r + 1 < kLmLD; ++r) kb[r] = kb[r + 1];
+                  kb[kLmLD - 1] = 0ull;
+                  ++used;
+                }
+                if (j == k) keep = w;
+                prev = w;
+              }
+              if (live && j < K_) run_key[m * kLmFusedTopK + j] = keep;
+              if (live && j == 0) {
+                const float m0_ = run_max[m], s0_ = run_sum[m];
+                const float mn = fmaxf(m0_, mx);
+                float sn = 0.f;
+                if (m0_ != -INFINITY) sn += s0_ * __builtin_amdgcn_exp2f((m0_ - mn) * sl);
+                if (mx != -INFINITY) sn += se * __builtin_amdgcn_exp2f((mx - mn) * sl);
+                run_max[m] = mn;
+                run_sum[m] = sn;
+              }
+            }
+            lds_barrier();
+          }
+        }
       }
     }
-    return;
+    lin += G8;
+    if (lin >= lin_end) break;
+    cbase += nst;
   }
-  float* P = a.P + (int64_t)z * a.M * a.N;
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int n = n0 + wn * 16 * NBW + nb * 16 + 4 * g;
-    if (n >= a.N) continue;
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) {
-      const int m = m0 + wm * MSPAN + mb * 16 + c;
-      if (m < a.M) *reinterpret_cast<f32x4*>(P + (int64_t)m * a.N + n) = acc[nb][mb];
-    }
-  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load in flight when the wave ends
+  if constexpr (EPI == 3) write_part(false);   // the last epilogue ended in a barrier
 }
 
 // the direct-to-LDS kernel's plan (or none: fall back to k_gemm_big).
@@ -663,6 +894,31 @@ bool big_swiglu_ok(int dtype, int M, int F, int K) {
   GemmShape s;
   if (!big_gemm_ok(dtype, M, 2 * F, K) || !plan_dma(M, 2 * F, K, &s)) return false;
   return s.S == 1 && F % (s.BN / 2) == 0;
+}
+
+// the stage stream needs whole 64-K stages and at least one in every split
+static bool dmaw_plan_ok(const GemmArgs& a, const GemmShape& s) {
+  return a.K % 64 == 0 && s.kps % 64 == 0 && s.kps > 0 && (int64_t)(s.S - 1) * s.kps < a.K &&
+         a.ksplit_x % 64 == 0;
+}
+
+bool lm_fused_ok(int dtype, int M, int V, int K, int top_k) {
+  GemmShape s;
+  if (!big_gemm_ok(dtype, M, V, K) || M <= 64 || M > kLmRows || top_k < 1 || top_k > kLmFusedTopK ||
+      V < top_k || !plan_dma(M, V, K, &s) || s.MB != 8)
+    return false;
+  GemmArgs a;
+  a.K = a.ksplit_x = K;
+  s.S = 1;
+  s.kps = K;
+  return dmaw_plan_ok(a, s);
+}
+
+int lm_fused_parts(int M, int V, int K) {
+  GemmShape s;
+  if (!plan_dma(M, V, K, &s)) return 0;
+  const int total = s.ntiles * s.mtiles;   // one split
+  return std::min(((total + 7) / 8) * 8, 256);
 }
 
 GemmShape plan_gemm_big(int M, int N, int K) {
@@ -718,15 +974,17 @@ static void launch_dma_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) 
 
 template <int EPI, int WN, int WMB>
 static void launch_dmaw_g(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
+  constexpr int LDS = kDmawLds + (EPI == 3 ? kLmRunBytes : 0);
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_dmaw<EPI, WN, WMB>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kDmawLds);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     attr = true;
   }
+  // one workgroup per CU at most, each walking its XCD's share of the tiles
   const int total = s.ntiles * s.mtiles * s.S;
-  hipLaunchKernelGGL((k_gemm_dmaw<EPI, WN, WMB>), dim3(((total + 7) / 8) * 8), dim3(512), kDmawLds, st,
-                     a, s.ntiles, s.mtiles, s.S);
+  hipLaunchKernelGGL((k_gemm_dmaw<EPI, WN, WMB>), dim3(std::min(((total + 7) / 8) * 8, 256)), dim3(512),
+                     LDS, st, a, s.ntiles, s.mtiles, s.S);
 }
 template <int EPI>
 static void launch_dmaw_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
@@ -736,6 +994,10 @@ static void launch_dmaw_t(const GemmArgs& a, const GemmShape& s, hipStream_t st)
 
 void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
   a.kps = s.kps;
+  if (a.lm_top_k > 0) {   // lm_fused_ok: the 8 x 1 grid, one split
+    launch_dmaw_g<3, 8, 5>(a, s, st);
+    return;
+  }
   if (s.NB == 2) {
     const bool sw = a.pair_F > 0;
     if (a.row_epi) {   // big_rowepi_ok: 256-row tiles, one split
@@ -743,8 +1005,8 @@ void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st) {
       return;
     }
     if (s.MB == 16) sw ? launch_dma_t<1, 256, 256>(a, s, st) : launch_dma_t<0, 256, 256>(a, s, st);
-    else if (a.ksplit_x % 64 == 0) sw ? launch_dmaw_t<1>(a, s, st) : launch_dmaw_t<0>(a, s, st);
-    else sw ? launch_dma_t<1, 256, 128>(a, s, st) : launch_dma_t<0, 256, 128>(a, s, st);  // 64-K stages would straddle the A split
+    else if (dmaw_plan_ok(a, s)) sw ? launch_dmaw_t<1>(a, s, st) : launch_dmaw_t<0>(a, s, st);
+    else sw ? launch_dma_t<1, 256, 128>(a, s, st) : launch_dma_t<0, 256, 128>(a, s, st);  // 32-K stages
     return;
   }
   if (s.MB == 16) launch_big_t<4, 4, 4>(a, s, st);

@@ -31,7 +31,20 @@ struct GemmArgs {
   void* out_g = nullptr;
   const void* gain = nullptr;
   float* stats = nullptr;
+  // LM-head epilogue of the 64-K-stage tiled GEMM (65..80 rows, one split,
+  // top_k <= kLmFusedTopK): each persistent workgroup keeps, per row, the
+  // running max and sum of exp(s * (logit - max)) and the top_k (logit desc,
+  // id asc) over its tiles, and writes them once as its part p (the layout
+  // of the tile partials: part_max/part_sum[p][m], part_val/part_id[p][m][k],
+  // p < lm_fused_parts); P, if set, also receives the fp32 logits
+  int lm_top_k = 0;
+  float lm_inv_temp = 1.f;
+  float* lm_max = nullptr;
+  float* lm_sum = nullptr;
+  float* lm_val = nullptr;
+  int* lm_id = nullptr;
 };
+constexpr int kLmFusedTopK = 16;
 struct GemmShape {
   int MB, NB, mtiles, ntiles, S, kps;
   int BN = 256;        // direct-to-LDS kernel (NB == 2): tile width (columns of W)
@@ -52,6 +65,10 @@ void launch_gemm_big(GemmArgs a, const GemmShape& s, hipStream_t st);
 // the big-GEMM plan uses the direct-to-LDS kernel with one split, so the
 // SwiGLU epilogue can be fused (gate|up of F rows each, F % 128 == 0)
 bool big_swiglu_ok(int dtype, int M, int F, int K);
+// whether the LM head (M x V logits over K) takes the fused LM-head epilogue,
+// and the number of parts it writes (one per workgroup, at most 256)
+bool lm_fused_ok(int dtype, int M, int V, int K, int top_k);
+int lm_fused_parts(int M, int V, int K);
 
 // y = sum_s P + src1 + src2 ; out / out_scatter = y ; out_norm = Norm(y)
 struct ReduceArgs {

@@ -314,15 +314,6 @@ void launch_lmhead(int dtype, const LmArgs& a, const LmShape& s, hipStream_t st)
 // every step of its top-k rounds.
 constexpr int kLogitTile = 2048;
 
-// float -> unsigned with the same order (-0 taken as +0, NaN below everything)
-__device__ __forceinline__ uint32_t float_order(float x) {
-  const uint32_t u = __float_as_uint(x + 0.0f);
-  const uint32_t o = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-  return x != x ? 0u : o;
-}
-__device__ __forceinline__ float order_float(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
 __device__ __forceinline__ uint64_t tile_key(float x, int col) {
   return ((uint64_t)float_order(x) << 11) | (uint32_t)(kLogitTile - 1 - col);
 }
@@ -437,7 +428,10 @@ __global__ __launch_bounds__(256) void k_logits_partials(LmArgs a, const float* 
       w = rows_umax64(best);
     }
     if (lane == 0) {
-      const int bi = c0 + key_col(w);
+      // a padding column (past |V|, keyed as -inf) is only reached when the
+      // tile holds fewer than top_k real ones or its logits are NaN; its id
+      // is clamped so that no consumer indexes past the vocabulary
+      const int bi = min(c0 + key_col(w), a.V - 1);
       a.part_val[pi * a.top_k + k] = key_value(w);
       a.part_id[pi * a.top_k + k] = bi;
       if (a.gumbel) a.part_logit[pi * a.top_k + k] = bi < a.V ? row[bi - c0] : -INFINITY;

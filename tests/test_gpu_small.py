@@ -13,7 +13,7 @@ SMALL = ["c0_tiny_chain", "c0r_tiny_chain_rope", "s1_static", "s2_dynamic", "s3_
          "s10_chain_63", "s11_eagle3_steady_dynamic", "s12_eagle3_steady_chain", "s13_target_static",
          "s14_target_dynamic", "s15_target_f32", "s16_target_chain_rows",
          "s17_eagle1_steady_dynamic", "s18_eagle1_steady_chain", "s19_sampled_dynamic",
-         "s20_sampled_chain_b40", "s20_sampled_chain_b70", "s21_dynamic_264", "s22_sampled_static"] + sorted(
+         "s20_sampled_chain_b40", "s20_sampled_chain_b70", "s21_dynamic_264", "s22_sampled_static", "s24_dynamic_80_v69648", "s25_dynamic_72_v16400"] + sorted(
              k for k in C.SMALL_CONFIGS if k.startswith("s7_chain_b"))
 
 
