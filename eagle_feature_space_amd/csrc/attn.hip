@@ -563,7 +563,9 @@ __device__ __forceinline__ uint2 ld_tr16(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-template <int NW, int PF>
+// RB 16-row blocks per wave: each K fragment and each transposed V fragment
+// read from LDS feeds RB MFMAs (RB = 2 halves the LDS reads per query row)
+template <int NW, int PF, int RB>
 __global__ __launch_bounds__(64 * NW) void k_attn_dma(AttnArgs a) {
   constexpr int HD = 128, DSTEPS = 4, DB = 8, NV = 2;
   constexpr int S = PF + 1;                          // ring slots
@@ -582,19 +584,26 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dma(AttnArgs a) {
   const int R = a.W * G;
   const int M = a.B * a.W;
 
-  const int qrow = rg * 16 * NW + w * 16 + c;
-  const bool qok = qrow < R;
-  const bool wave_live = rg * 16 * NW + w * 16 < R;
-  const int rl = qok ? qrow / G : 0, gi = qok ? qrow % G : 0;
-  const int qm = qok ? b * a.W + rl : -1;
-  const int qh = kvh * G + gi;
-  const uint64_t msk = qok ? a.mask[b * a.W + rl] : 0ull;
-  u32x4 qf[DSTEPS];
-  {
-    const bf16s* qp = (const bf16s*)a.q + ((int64_t)(b * a.W + rl) * a.Hq + qh) * HD;
+  // block rb of wave w: query rows rg 16 NW RB + (w RB + rb) 16 + c
+  bool blive[RB];
+  int qm[RB], qh[RB];
+  uint64_t msk[RB];
+  u32x4 qf[RB][DSTEPS];
 #pragma unroll
-    for (int u = 0; u < DSTEPS; ++u) qf[u] = qok ? ld16(qp + u * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r0 = rg * 16 * NW * RB + (w * RB + rb) * 16;
+    const int qrow = r0 + c;
+    const bool qok = qrow < R;
+    blive[rb] = r0 < R;
+    const int rl = qok ? qrow / G : 0, gi = qok ? qrow % G : 0;
+    qm[rb] = qok ? b * a.W + rl : -1;
+    qh[rb] = kvh * G + gi;
+    msk[rb] = qok ? a.mask[b * a.W + rl] : 0ull;
+    const bf16s* qp = (const bf16s*)a.q + ((int64_t)(b * a.W + rl) * a.Hq + qh[rb]) * HD;
+#pragma unroll
+    for (int u = 0; u < DSTEPS; ++u) qf[rb][u] = qok ? ld16(qp + u * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
   }
+  const bool wave_live = blive[0];
 
   const bool extra = split == a.nsplit;
   int kbeg, kend;
@@ -632,10 +641,15 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dma(AttnArgs a) {
     }
   };
 
-  float mrun = -INFINITY, lrun = 0.f;
-  f32x4 o[DB];
+  float mrun[RB], lrun[RB];
+  f32x4 o[RB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb) {
+    mrun[rb] = -INFINITY;
+    lrun[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // lane-constant parts of the fragment addresses
   const int kslot = (c >> 2) | ((c & 3) << 2);       // kv_slot of this lane's K rows
@@ -644,70 +658,83 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dma(AttnArgs a) {
 
   auto compute = [&](const char* cur, int t0) {
     if (!wave_live) return;
-    f32x4 sc[4];
+    f32x4 sc[RB][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kl = (c >> 2) * 16 + j * 4 + (c & 3);
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[RB];
 #pragma unroll
-      for (int u = 0; u < DSTEPS; ++u)
-        acc = DT<bf16s>::mma(ld16(cur + kl * 256 + ((4 * u + g) ^ kslot) * 16), qf[u], acc);
-      sc[j] = acc;
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < DSTEPS; ++u) {
+        const u32x4 kf = ld16(cur + kl * 256 + ((4 * u + g) ^ kslot) * 16);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = DT<bf16s>::mma(kf, qf[rb][u], acc[rb]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sc[rb][j] = acc[rb];
     }
     const bool full = !extra && t0 + 64 <= kend;     // wave-uniform
-    float tmax = -INFINITY;
-    if (full) {
+    float p[RB][16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int rb = 0; rb < RB; ++rb) {
+      float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[j][i] *= a.scale_log2;
-          tmax = fmaxf(tmax, sc[j][i]);
-        }
-    } else {
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+          for (int i = 0; i < 4; ++i) {
+            sc[rb][j][i] *= a.scale_log2;
+            tmax = fmaxf(tmax, sc[rb][j][i]);
+          }
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t0 + g * 16 + j * 4 + i;
-          bool valid = key < kend;
-          if (extra) valid = valid && ((msk >> key) & 1ull);
-          const float v = valid ? sc[j][i] * a.scale_log2 : -INFINITY;
-          sc[j][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-    }
-    tmax = max_x32(max_x16(tmax));
-    const float mnew = fmaxf(mrun, tmax);
-    const bool empty = mnew == -INFINITY;
-    const float alpha = empty ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
-    float p[16];
-    float psum = 0.f;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = empty ? 0.f : __builtin_amdgcn_exp2f(sc[j][i] - mnew);
-        p[4 * j + i] = e;
-        psum += e;
+          for (int i = 0; i < 4; ++i) {
+            const int key = t0 + g * 16 + j * 4 + i;
+            bool valid = key < kend;
+            if (extra) valid = valid && ((msk[rb] >> key) & 1ull);
+            const float v = valid ? sc[rb][j][i] * a.scale_log2 : -INFINITY;
+            sc[rb][j][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
       }
-    psum = sum_x32(sum_x16(psum));
-    lrun = lrun * alpha + psum;
-    mrun = mnew;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
+      tmax = max_x32(max_x16(tmax));
+      const float mnew = fmaxf(mrun[rb], tmax);
+      const bool empty = mnew == -INFINITY;
+      const float alpha = empty ? 1.f : __builtin_amdgcn_exp2f(mrun[rb] - mnew);
+      float psum = 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = empty ? 0.f : __builtin_amdgcn_exp2f(sc[rb][j][i] - mnew);
+          p[rb][4 * j + i] = e;
+          psum += e;
+        }
+      psum = sum_x32(sum_x16(psum));
+      lrun[rb] = lrun[rb] * alpha + psum;
+      mrun[rb] = mnew;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+    }
     const char* vt = cur + kDmaTile;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const u32x4 pf = pack_p<bf16s>(p + v * 8);
+      u32x4 pf[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) pf[rb] = pack_p<bf16s>(p[rb] + v * 8);
       const char* vrow = vt + (16 * g + 8 * v + te) * 256 + 8 * (tp & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int off = 16 * ((2 * db + (tp >> 1)) ^ vslot);
         const uint2 lo = ld_tr16(vrow + off);             // keys 16g + 8v + 0..3
         const uint2 hi = ld_tr16(vrow + 4 * 256 + off);   // keys 16g + 8v + 4..7
-        o[db] = DT<bf16s>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, o[db]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][db] = DT<bf16s>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[rb], o[rb][db]);
       }
     }
   };
@@ -731,30 +758,33 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dma(AttnArgs a) {
     compute(lds + (it % S) * SLOT, kbeg + it * 64);
   }
 
-  if (qm < 0) return;
-  const int64_t idx = ((int64_t)split * M + qm) * a.Hq + qh;
-  if (g == 0) {
-    a.part_ml[2 * idx] = mrun;
-    a.part_ml[2 * idx + 1] = lrun;
-  }
-  float* po = a.part_o + idx * HD;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * g) = o[db];
+  for (int rb = 0; rb < RB; ++rb) {
+    if (qm[rb] < 0) continue;
+    const int64_t idx = ((int64_t)split * M + qm[rb]) * a.Hq + qh[rb];
+    if (g == 0) {
+      a.part_ml[2 * idx] = mrun[rb];
+      a.part_ml[2 * idx + 1] = lrun[rb];
+    }
+    float* po = a.part_o + idx * HD;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * g) = o[rb][db];
+  }
 }
 
-template <int NW, int PF>
+template <int NW, int PF, int RB = 1>
 static void launch_dma(const AttnArgs& a, hipStream_t st) {
   constexpr int LDS = (PF + 1) * 2 * kDmaTile;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_dma<NW, PF>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_dma<NW, PF, RB>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     attr = true;
   }
   const int R = a.W * (a.Hq / a.Hkv);
-  const int rowgroups = (R + 16 * NW - 1) / (16 * NW);
+  const int rowgroups = (R + 16 * NW * RB - 1) / (16 * NW * RB);
   dim3 grid(a.Hkv * rowgroups, a.nsplit + 1, a.B);
-  hipLaunchKernelGGL((k_attn_dma<NW, PF>), grid, dim3(64 * NW), LDS, st, a);
+  hipLaunchKernelGGL((k_attn_dma<NW, PF, RB>), grid, dim3(64 * NW), LDS, st, a);
 }
 
 template <typename T, int HD, int NW>
@@ -787,11 +817,12 @@ void launch_attention(int dtype, const AttnArgs& a0, hipStream_t st) {
     // more than one 16-row block per (request, kv head): workgroup kernel
     if (dtype == EAGLE_BF16) {
       if (a.hd == 128) {   // direct-to-LDS tiles
-        // 16 rows per wave; past 64 rows one 8-wave workgroup per CU reads
-        // each K / V tile once for 128 rows instead of twice for 2 x 64
+        // 16 rows per wave up to 64; past that 8 waves of two 16-row blocks
+        // (each K / V fragment read from LDS serves 32 rows, each tile is
+        // loaded once for 256 rows)
         if (R <= 32) launch_dma<2, kAttnPF>(a, st);
         else if (R <= 64) launch_dma<4, kAttnPF>(a, st);
-        else launch_dma<8, kAttnPF>(a, st);
+        else launch_dma<8, kAttnPF, 2>(a, st);
       }
       else launch_wide<bf16s, 64>(a, R, st);
     } else {

@@ -574,7 +574,8 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
   a.mask = mask;
   a.split_len = w.ap.split_len;
   a.nsplit = w.ap.nsplit;
-  if (W * (h->n_q_heads / h->n_kv_heads) > 16) {
+  const int Rkv = W * (h->n_q_heads / h->n_kv_heads);
+  if (Rkv > 16) {
     // the workgroup kernel (more than 16 query rows per kv head) keeps two
     // tiles in flight: splits of an eighth of the context, between two and
     // eight tiles, amortise its prologue (fewer splits than the workspace
@@ -585,7 +586,22 @@ void attend(const eagle_head* h, const eagle_kv* kv, const char* ws, const Ws& w
       a.split_len = min_len;
       a.nsplit = (max_n + a.split_len - 1) / a.split_len;
     }
-  } else if (W * (h->n_q_heads / h->n_kv_heads) <= 16) {
+    // and where a few (request, kv head) pairs leave the grid short of one
+    // pass of resident workgroups, the splits are lengthened to exactly one
+    // pass: a partial second pass idles most CUs, and every split writes
+    // fp32 partials for all of its rows (the 256-row workgroups of the
+    // verify-side tree, one per CU, write as many bytes as they read)
+    if (h->dtype == EAGLE_BF16 && h->head_dim == 128) {
+      const int rows_wg = Rkv <= 32 ? 32 : (Rkv <= 64 ? 64 : 256);
+      const int64_t per_split = (int64_t)h->n_kv_heads * kv->B * ((Rkv + rows_wg - 1) / rows_wg);
+      const int64_t resident = 256LL * (Rkv <= 64 ? 2 : 1);
+      const int64_t fit = resident / per_split - 1;    // context splits beside the tree split
+      if (fit >= 1 && (int64_t)(a.nsplit + 1) * per_split > resident) {
+        a.split_len = (int)(((max_n + fit - 1) / fit + 63) / 64 * 64);
+        a.nsplit = (max_n + a.split_len - 1) / a.split_len;
+      }
+    }
+  } else {
     // the per-wave kernel (two waves of LDS-staged V per workgroup): when the
     // grid would need more than one pass of resident workgroups over the 256
     // CUs, the splits are lengthened until it fits in one (a short last pass
