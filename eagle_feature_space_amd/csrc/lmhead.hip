@@ -483,14 +483,6 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
   // the candidates staged in LDS, so the row pays one memory latency
   const int ncand = a.ntiles * a.top_k;
   const bool staged = ncand <= kMergeLds;
-  if (staged) {
-    for (int q = tid; q < ncand; q += 256) {
-      const int t = q / a.top_k, j = q - t * a.top_k;
-      const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
-      cval[q] = a.part_val[i];
-      cid[q] = a.part_id[i];
-    }
-  }
   constexpr int TPT = 4;                  // tiles per thread held in registers
   float tm[TPT], ts[TPT];
 #pragma unroll
@@ -501,6 +493,33 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
     if (t < a.ntiles) {
       tm[i] = a.part_max[(int64_t)t * a.M + m];
       ts[i] = a.part_sum[(int64_t)t * a.M + m];
+    }
+  }
+  if (staged) {
+    // eight candidates a thread in flight at once (a load-then-store loop
+    // waits one memory latency per candidate)
+    constexpr int SB = 8;
+    for (int q0 = tid; q0 < ncand; q0 += 256 * SB) {
+      float vv[SB];
+      int vi[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int q = q0 + 256 * u;
+        if (q < ncand) {
+          const int t = q / a.top_k, j = q - t * a.top_k;
+          const int64_t i = ((int64_t)t * a.M + m) * a.top_k + j;
+          vv[u] = a.part_val[i];
+          vi[u] = a.part_id[i];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int q = q0 + 256 * u;
+        if (q < ncand) {
+          cval[q] = vv[u];
+          cid[q] = vi[u];
+        }
+      }
     }
   }
   // log-partition of s * logits
