@@ -562,21 +562,28 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
       bi[r] = 0x7fffffff;
       bq[r] = -1;
     }
-    for (int q = tid; q < ncand; q += 64) {
-      const float v = cval[q];
-      const int id = cid[q];
-      if (better(v, id, b[LD - 1], bi[LD - 1])) {
-        // replace the last and let it bubble up (value desc, id asc)
-        b[LD - 1] = v; bi[LD - 1] = id; bq[LD - 1] = q;
+    // a lane owns whole parts (t = lane mod 64); every part lists its
+    // candidates by value, descending, so a part is left at its first entry
+    // below the lane's LD-th kept value
+    for (int t = tid; t < a.ntiles; t += 64)
+      for (int j = 0; j < a.top_k; ++j) {
+        const int q = t * a.top_k + j;
+        const float v = cval[q];
+        const int id = cid[q];
+        if (better(v, id, b[LD - 1], bi[LD - 1])) {
+          // replace the last and let it bubble up (value desc, id asc)
+          b[LD - 1] = v; bi[LD - 1] = id; bq[LD - 1] = q;
 #pragma unroll
-        for (int r = LD - 1; r > 0; --r)
-          if (better(b[r], bi[r], b[r - 1], bi[r - 1])) {
-            const float tv = b[r]; b[r] = b[r - 1]; b[r - 1] = tv;
-            const int ti = bi[r]; bi[r] = bi[r - 1]; bi[r - 1] = ti;
-            const int tq = bq[r]; bq[r] = bq[r - 1]; bq[r - 1] = tq;
-          }
+          for (int r = LD - 1; r > 0; --r)
+            if (better(b[r], bi[r], b[r - 1], bi[r - 1])) {
+              const float tv = b[r]; b[r] = b[r - 1]; b[r - 1] = tv;
+              const int ti = bi[r]; bi[r] = bi[r - 1]; bi[r - 1] = ti;
+              const int tq = bq[r]; bq[r] = bq[r - 1]; bq[r - 1] = tq;
+            }
+        } else if (v < b[LD - 1]) {
+          break;
+        }
       }
-    }
     int used = 0;
     float pv = INFINITY;
     int pid = -1;
@@ -594,11 +601,15 @@ __global__ __launch_bounds__(256) void k_topk_merge(MergeArgs a) {
         lv = -INFINITY;
         li = 0x7fffffff;
         lq = -1;
-        for (int q = tid; q < ncand; q += 64) {
-          const float v = cval[q];
-          const int id = cid[q];
-          if (better(pv, pid, v, id) && better(v, id, lv, li)) { lv = v; li = id; lq = q; }
-        }
+        for (int t = tid; t < a.ntiles; t += 64)
+          for (int j = 0; j < a.top_k; ++j) {
+            const int q = t * a.top_k + j;
+            const float v = cval[q];
+            const int id = cid[q];
+            if (!better(pv, pid, v, id)) continue;   // taken already
+            if (better(v, id, lv, li)) { lv = v; li = id; lq = q; }
+            else if (v < lv) break;
+          }
       }
       // (value desc, id asc) as one 64-bit key, reduced with DPP row moves
       const uint64_t lk = ((uint64_t)float_order(lv) << 32) | (0xffffffffu - (uint32_t)li);
