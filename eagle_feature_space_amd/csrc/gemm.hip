@@ -637,32 +637,78 @@ __device__ __forceinline__ float row_rstd(const float* st, int nblk, int N, floa
 }
 
 // RoPE + scatter of the fused q|k|v projection.  One thread per (row, head,
-// pair i) rotates elements (i, i + hd/2) by pos * theta^(-2i/hd); the angle
-// is formed and reduced in double precision.
+// four consecutive pairs i .. i + 3) rotates elements (i, i + hd/2) by
+// pos * theta^(-2i/hd); the angle is formed and reduced in double precision
+// (in revolutions: the hardware sine and cosine take revolutions).  Four
+// pairs a thread: 16-byte partial loads, 8- or 16-byte stores, and the row's
+// statistics, position and addresses formed once per four pairs.
+template <int NB>
+__device__ __forceinline__ f32x4 sum_parts4_n(const float* p, int64_t stride, int S) {
+  f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    f32x4 v[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) v[q] = *reinterpret_cast<const f32x4*>(p + (int64_t)min(s0 + q, S - 1) * stride);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] += s0 + q < S ? v[q][e] : 0.f;
+  }
+  return y;
+}
+__device__ __forceinline__ f32x4 sum_parts4(const float* p, int64_t stride, int S) {
+  if (S <= 0) return f32x4{0.f, 0.f, 0.f, 0.f};
+  if (S <= 2) return sum_parts4_n<2>(p, stride, S);
+  if (S <= 4) return sum_parts4_n<4>(p, stride, S);
+  if (S <= 8) return sum_parts4_n<8>(p, stride, S);
+  return sum_parts4_n<16>(p, stride, S);
+}
+
+// four consecutive elements (8- or 16-byte aligned)
+template <typename T>
+__device__ __forceinline__ void qkv_store4(T* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void qkv_store4<bf16s>(bf16s* p, const f32x4& v) {
+  uint2 o;
+  o.x = f2bf(v[0]) | (f2bf(v[1]) << 16);
+  o.y = f2bf(v[2]) | (f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = o;
+}
+template <>
+__device__ __forceinline__ void qkv_store4<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
-  // grid (pair blocks of a row, rows): the row and its position are uniform
-  // across the workgroup, the (head, pair) index needs only 32-bit arithmetic
+  // grid (quad blocks of a row, rows): the row and its position are uniform
+  // across the workgroup, the (head, quad) index needs only 32-bit arithmetic
   const int half = a.hd / 2;
+  const int quads = half / 4;            // quads of pairs per head
   const int heads = a.Hq + 2 * a.Hkv;
   const int t0 = blockIdx.x * 256 + threadIdx.x;
-  const bool live = t0 < heads * half;   // lanes past the last pair only help form rstd
+  const bool live = t0 < heads * quads;  // lanes past the last quad only help form rstd
   const int t = live ? t0 : 0;
   if (!a.xstats && !live) return;
-  const int i = t % half;
-  const int h = t / half;
+  const int h = t / quads;
+  const int i = (t % quads) * 4;
   const int N = heads * a.hd;
   const int c1 = h * a.hd + i, c2 = c1 + half;
   const int64_t pst = (int64_t)a.M * N;
   const bool is_v = h >= a.Hq + a.Hkv;
-  // the rotation's frequency depends on the pair only
-  double inv = 0.0;
-  if (!is_v && a.theta > 0.f) inv = exp2(-(2.0 * i / a.hd) * log2((double)a.theta));
+  const bool rope = !is_v && a.theta > 0.f;
+  // the rotations' frequencies (revolutions per position) depend on the pair only
+  double inv[4] = {0.0, 0.0, 0.0, 0.0};
+  if (rope) {
+    const double lt = log2((double)a.theta);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) inv[e] = exp2(-(2.0 * (i + e) / a.hd) * lt) * 0.15915494309189535;
+  }
   for (int m = blockIdx.y; m < a.M; m += gridDim.y) {
-    float x1 = 0.f, x2 = 0.f;
+    f32x4 x1 = f32x4{0.f, 0.f, 0.f, 0.f}, x2 = x1;
     if (live) {      // partial loads first: the statistics load overlaps them
-      x1 = sum_parts(a.P + (int64_t)m * N + c1, pst, a.S);
-      x2 = sum_parts(a.P + (int64_t)m * N + c2, pst, a.S);
+      x1 = sum_parts4(a.P + (int64_t)m * N + c1, pst, a.S);
+      x2 = sum_parts4(a.P + (int64_t)m * N + c2, pst, a.S);
     }
     if (a.xstats) {
       const float rs = row_rstd(a.xstats + (int64_t)m * a.xnblk * 2, a.xnblk, a.xN, a.eps);
@@ -693,15 +739,18 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
       }
     }
     if (skip) continue;
-    if (!is_v && a.theta > 0.f) {
-      double ang = (double)pos * inv;
-      ang -= 6.283185307179586 * rint(ang / 6.283185307179586);
-      float cs, sn;
-      sincosf((float)ang, &sn, &cs);
-      float y1 = x1 * cs - x2 * sn;
-      float y2 = x2 * cs + x1 * sn;
-      x1 = y1;
-      x2 = y2;
+    if (rope) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        double rev = (double)pos * inv[e];
+        rev -= rint(rev);
+        const float cs = __builtin_amdgcn_cosf((float)rev);
+        const float sn = __builtin_amdgcn_sinf((float)rev);
+        const float y1 = x1[e] * cs - x2[e] * sn;
+        const float y2 = x2[e] * cs + x1[e] * sn;
+        x1[e] = y1;
+        x2[e] = y2;
+      }
     }
     T* dst;
     if (h < a.Hq) {
@@ -711,17 +760,17 @@ __global__ __launch_bounds__(256) void k_epi_qkv(QkvArgs a) {
       const int64_t r = a.kv_idx ? (int64_t)a.kv_idx[m] : row;
       dst = (T*)(is_v ? a.v : a.k) + (r * a.Hkv + kh) * a.hd;
     }
-    DT<T>::st(dst + i, x1);
-    DT<T>::st(dst + i + half, x2);
+    qkv_store4<T>(dst + i, x1);
+    qkv_store4<T>(dst + i + half, x2);
   }
 }
 
 void launch_epi_qkv(int dtype, const QkvArgs& a, hipStream_t st) {
-  const int pairs = (a.Hq + 2 * a.Hkv) * (a.hd / 2);
+  const int quads = (a.Hq + 2 * a.Hkv) * (a.hd / 8);
   // at most 2048 row slots: a workgroup takes every 2048th row, so the
   // rotation frequencies (double-precision exp2 / log2 per pair) are formed
   // once per ~M/2048 rows instead of once per row (the ~20k-row ingest)
-  dim3 grid((unsigned)((pairs + 255) / 256), (unsigned)std::min(a.M, 2048));
+  dim3 grid((unsigned)((quads + 255) / 256), (unsigned)std::min(a.M, 2048));
   if (a.M <= 0) return;
   if (dtype == EAGLE_BF16) hipLaunchKernelGGL(k_epi_qkv<bf16s>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_epi_qkv<float>, grid, dim3(256), 0, st, a);
