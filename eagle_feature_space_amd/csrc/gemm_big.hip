@@ -855,7 +855,7 @@ __global__ __launch_bounds__(512) void k_gemm_dmaw(GemmArgs a, int nt, int mt, i
 // of at most 256 workgroups (one per CU); 256-row tiles from 256 rows where
 // the tiles alone give >= 128 workgroups.
 static bool plan_dma(int M, int N, int K, GemmShape* s) {
-  if (M < 64 || K % (2 * kDK) != 0) return false;
+  if (M < 17 || K % (2 * kDK) != 0) return false;
   const int BM = M >= 256 ? 256 : 128;
   const int BN = kDN;
   const int nt = (N + BN - 1) / BN, mt = (M + BM - 1) / BM;
@@ -882,6 +882,11 @@ static bool plan_dma(int M, int N, int K, GemmShape* s) {
 
 bool big_gemm_ok(int dtype, int M, int N, int K) {
   return dtype == EAGLE_BF16 && M >= 64 && K % kBK == 0 && N % 16 == 0;
+}
+
+bool wide_rows_ok(int dtype, int M, int N, int K) {
+  GemmShape s;
+  return dtype == EAGLE_BF16 && M > 16 && M <= 32 && K % kBK == 0 && N % 16 == 0 && plan_dma(M, N, K, &s);
 }
 
 bool big_rowepi_ok(int dtype, int M, int N, int K) {
@@ -988,7 +993,8 @@ static void launch_dmaw_g(const GemmArgs& a, const GemmShape& s, hipStream_t st)
 }
 template <int EPI>
 static void launch_dmaw_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
-  if (a.M > 64 && a.M <= 80) launch_dmaw_g<EPI, 8, 5>(a, s, st);   // one m-tile, five live blocks
+  if (a.M <= 32) launch_dmaw_g<EPI, 8, 2>(a, s, st);               // two live blocks
+  else if (a.M > 64 && a.M <= 80) launch_dmaw_g<EPI, 8, 5>(a, s, st);   // one m-tile, five live blocks
   else launch_dmaw_g<EPI, 2, 2>(a, s, st);
 }
 
