@@ -993,8 +993,10 @@ static void launch_dmaw_g(const GemmArgs& a, const GemmShape& s, hipStream_t st)
 }
 template <int EPI>
 static void launch_dmaw_t(const GemmArgs& a, const GemmShape& s, hipStream_t st) {
-  if (a.M <= 32) launch_dmaw_g<EPI, 8, 2>(a, s, st);               // two live blocks
-  else if (a.M > 64 && a.M <= 80) launch_dmaw_g<EPI, 8, 5>(a, s, st);   // one m-tile, five live blocks
+  // one m-tile: 8 x 1 waves over the live 16-row blocks only
+  if (a.M <= 32) launch_dmaw_g<EPI, 8, 2>(a, s, st);
+  else if (a.M <= 64) launch_dmaw_g<EPI, 8, 4>(a, s, st);
+  else if (a.M <= 80) launch_dmaw_g<EPI, 8, 5>(a, s, st);
   else launch_dmaw_g<EPI, 2, 2>(a, s, st);
 }
 
