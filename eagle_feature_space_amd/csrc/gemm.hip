@@ -278,9 +278,9 @@ static int kc_of(int dtype) { return dtype == EAGLE_BF16 ? 256 : 128; }
 GemmShape plan_gemm(int dtype, int M, int N, int K) {
   GemmShape s;
   if (big_gemm_ok(dtype, M, N, K)) return plan_gemm_big(M, N, K);
-  // 17..32 rows: the 64-K-stage tiled GEMM streams 8 rows x 128 B per load
-  // where the activation-sharing kernel below streams 16 rows x 64 B
-  // (32-row projections of the 8B shape: 10-20% faster)
+  // 17..63 rows: the 64-K-stage tiled GEMM streams 8 rows x 128 B per load
+  // where the kernels below stream 16 rows x 64 B (8B-shaped projections:
+  // 10-20% faster at 32 rows, 30-45% at 48)
   if (wide_rows_ok(dtype, M, N, K)) return plan_gemm_big(M, N, K);
   if (M > 16 && M <= 32) {
     // activation-sharing kernel: waves of 2 n-blocks (32 columns), ~2048

@@ -886,7 +886,7 @@ bool big_gemm_ok(int dtype, int M, int N, int K) {
 
 bool wide_rows_ok(int dtype, int M, int N, int K) {
   GemmShape s;
-  return dtype == EAGLE_BF16 && M > 16 && M <= 32 && K % kBK == 0 && N % 16 == 0 && plan_dma(M, N, K, &s);
+  return dtype == EAGLE_BF16 && M > 16 && M < 64 && K % kBK == 0 && N % 16 == 0 && plan_dma(M, N, K, &s);
 }
 
 bool big_rowepi_ok(int dtype, int M, int N, int K) {

@@ -58,7 +58,7 @@ struct GemmShape {
 GemmShape plan_gemm(int dtype, int M, int N, int K);
 void launch_gemm(int dtype, GemmArgs a, const GemmShape& s, hipStream_t st);
 bool big_gemm_ok(int dtype, int M, int N, int K);
-// 17..32 rows on the 64-K-stage tiled GEMM (8 x 1 waves, two live 16-row
+// 17..63 rows on the 64-K-stage tiled GEMM (8 x 1 waves over the live 16-row
 // blocks): the projections' plan when this holds (bf16, K % 64 == 0)
 bool wide_rows_ok(int dtype, int M, int N, int K);
 // whether launch_gemm_big takes the row epilogue (row_epi) for this shape
